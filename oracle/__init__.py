@@ -1,0 +1,177 @@
+"""CPU oracle of the GPTQ fold and the q4tp sweep (f64; plain C behind ctypes).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The product library never links, loads or calls
+it, and this package imports nothing from the product package.
+
+What each function follows (docs.rs source pages of the cortiq project):
+
+* :func:`fold` -- "cortiq-cli 0.8.45 src/gptq.rs", ``gptq_fold_operator_par``: dead channels,
+  damping ``lambda * mean(diag)``, the x10 retry, ``U`` = upper Cholesky factor of ``H_d^-1``.
+* :func:`ladder` -- the per-row rung ladder; the pages take it from a converter whose rule is
+  not printed, so the rule here is a stated reading (see the C source).
+* :func:`sweep` -- "cortiq-cli 0.8.45 src/gptq.rs", ``gptq_quantize_q4tp``, and
+  "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs", ``q4tp_group``: rung rule, rounding and
+  column-by-column error feedback.
+* :func:`output_error` -- the layer-output error ``tr(dW H dW^T)`` with the raw Hessian, the
+  quantity the pages' device-versus-host test compares ("cortiq-cli 0.8.45 src/gptq.rs",
+  test ``device_fold_and_sweep_match_host``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gptq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_gptq.so")
+_lib = None
+
+OK, FAILED, DEGENERATE = 0, 1, 4
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no multiply-add contraction, OpenMP)."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+         "-Wall", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.orc_fold.argtypes = [P, i64, i64, ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                             P, P, P, P, ctypes.c_int]
+    lib.orc_fold.restype = ctypes.c_int
+    lib.orc_ladder.argtypes = [P, P, i64, i64, i64, P, P]
+    lib.orc_ladder.restype = None
+    lib.orc_sweep.argtypes = [P, i64, i64, i64, P, P, P, P, P, P, P, P, P, P, P, P,
+                              ctypes.c_double, ctypes.c_double, P, ctypes.c_int]
+    lib.orc_sweep.restype = ctypes.c_int
+    lib.orc_f16_round.argtypes = [ctypes.c_double]
+    lib.orc_f16_round.restype = ctypes.c_double
+    lib.orc_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads(nt=None) -> int:
+    return int(nt) if nt else int(_load().orc_max_threads())
+
+
+def fold(H, lam, retry=True, route=0, nt=None):
+    """Fold ``H`` (f32, ``n x ldh``; the upper triangle is read) at starting damping ``lam``.
+
+    ``route`` 0 is the pages' host route (the oracle's definition); 1 and 2 are the reversed
+    and reversed-equilibrated cross-check routes.  Returns a dict with ``U`` (f64, upper),
+    ``hdiag`` (f32), ``dead`` (bool), ``lam``, ``base``, ``damp``, ``attempts``, ``status``.
+    """
+    H = np.ascontiguousarray(H, dtype=np.float32)
+    n = H.shape[0]
+    U = np.empty((n, n), dtype=np.float64)
+    hdiag = np.empty(n, dtype=np.float32)
+    dead = np.empty(n, dtype=np.uint8)
+    info = np.zeros(4, dtype=np.float64)
+    st = _load().orc_fold(_ptr(H), n, H.shape[1], float(lam), int(bool(retry)), int(route),
+                          _ptr(U), _ptr(hdiag), _ptr(dead), _ptr(info), threads(nt))
+    return dict(U=U, hdiag=hdiag, dead=dead.astype(bool), lam=float(info[0]),
+                base=float(info[1]), damp=float(info[2]), attempts=int(info[3]), status=st)
+
+
+def ladder(W0, dead, gs=32):
+    """Per-row ``lost`` (rows x 2: lo, step) and ``tab`` (rows x 32) from the dead-zeroed W0."""
+    W0 = np.ascontiguousarray(W0, dtype=np.float32)
+    rows, n = W0.shape
+    d = np.ascontiguousarray(dead, dtype=np.uint8)
+    lost = np.empty((rows, 2), dtype=np.float32)
+    tab = np.empty((rows, 32), dtype=np.float32)
+    _load().orc_ladder(_ptr(W0), _ptr(d), rows, n, gs, _ptr(lost), _ptr(tab))
+    return lost, tab
+
+
+def sweep(W0, U, hdiag, dead, tab, lost, gs=32, force_code=None, force_rung=None,
+          tie_band=1e-3, rung_band=1e-4, want_E=True, want_Wc=False, nt=None):
+    """Column-sequential q4tp sweep.  ``code`` holds ``q + 8`` one per byte (rows x n).
+
+    With ``force_code`` / ``force_rung`` (another implementation's decisions) the sweep runs
+    as a tie-forced replay and ``stats`` counts {code ties, code hard, rung ties, rung hard}.
+    """
+    W0 = np.ascontiguousarray(W0, dtype=np.float32)
+    rows, n = W0.shape
+    U = np.ascontiguousarray(U, dtype=np.float64)
+    hdiag = np.ascontiguousarray(hdiag, dtype=np.float32)
+    d = np.ascontiguousarray(dead, dtype=np.uint8)
+    tab = np.ascontiguousarray(tab, dtype=np.float32)
+    lost = np.ascontiguousarray(lost, dtype=np.float32)
+    ng = n // gs
+    code = np.empty((rows, n), dtype=np.uint8)
+    rung = np.empty((rows, ng), dtype=np.uint8)
+    scale = np.empty((rows, ng), dtype=np.float32)
+    E = np.empty((rows, n), dtype=np.float64) if want_E else None
+    Wc = np.empty((rows, n), dtype=np.float64) if want_Wc else None
+    fc = None if force_code is None else np.ascontiguousarray(force_code, dtype=np.uint8)
+    fr = None if force_rung is None else np.ascontiguousarray(force_rung, dtype=np.uint8)
+    stats = np.zeros(4, dtype=np.int64)
+    st = _load().orc_sweep(_ptr(W0), rows, n, gs, _ptr(U), _ptr(hdiag), _ptr(d), _ptr(tab),
+                           _ptr(lost), _ptr(code), _ptr(rung), _ptr(scale), _ptr(E), _ptr(Wc),
+                           _ptr(fc), _ptr(fr), float(tie_band), float(rung_band), _ptr(stats),
+                           threads(nt))
+    if st != OK:
+        raise ValueError("oracle sweep rejected its arguments (n % gs, gs <= 64)")
+    return dict(code=code, rung=rung, scale=scale, E=E, Wc=Wc,
+                stats=dict(code_ties=int(stats[0]), code_hard=int(stats[1]),
+                           rung_ties=int(stats[2]), rung_hard=int(stats[3])))
+
+
+def f16_round(x: float) -> float:
+    """Round to the nearest binary16 value (ties to even), returned as a float."""
+    return float(_load().orc_f16_round(float(x)))
+
+
+def pack_nibbles(code):
+    """Nibble plane (rows x n/2 bytes): column 2m in the low nibble, 2m+1 in the high one."""
+    code = np.asarray(code, dtype=np.uint8)
+    return (code[:, 0::2] & 0x0F) | ((code[:, 1::2] & 0x0F) << 4)
+
+
+def unpack_nibbles(nib):
+    nib = np.asarray(nib, dtype=np.uint8)
+    rows, half = nib.shape
+    out = np.empty((rows, half * 2), dtype=np.uint8)
+    out[:, 0::2] = nib & 0x0F
+    out[:, 1::2] = nib >> 4
+    return out
+
+
+def dequant(code, scale, gs=32):
+    """W_hat[r, j] = (code - 8) * scale[r, j // gs] in f64."""
+    q = np.asarray(code, dtype=np.float64) - 8.0
+    return q * np.repeat(np.asarray(scale, dtype=np.float64), gs, axis=1)
+
+
+def output_error(W0, dead, code, scale, H, gs=32):
+    """tr(dW H dW^T) with dW = W0 (dead columns zeroed) - W_hat and the raw Hessian H (f64).
+
+    H is read from its upper triangle, as the fold reads it."""
+    W = np.asarray(W0, dtype=np.float64).copy()
+    W[:, np.asarray(dead, dtype=bool)] = 0.0
+    dW = W - dequant(code, scale, gs)
+    Hu = np.triu(np.asarray(H, dtype=np.float64))
+    Hs = Hu + np.triu(Hu, 1).T
+    return float(np.einsum("ij,ij->", dW @ Hs, dW))
