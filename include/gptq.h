@@ -1,0 +1,139 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ fold-and-quantize library, libgptq_mi355x.so.
+ *
+ * Two calls make the method, plus the per-row ladder that the sweep consumes:
+ *
+ *   gptq_fold   : H (Hessian of one layer's inputs)  ->  U, the upper Cholesky factor of
+ *                 H_d^-1 with H_d = H' + lambda*mean(diag)*I (dead channels zeroed, unit
+ *                 diagonal).  Source: page "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs",
+ *                 module documentation steps 1-4 and the driver `fold`; page "cortiq-cli 0.8.45
+ *                 src/gptq.rs", `gptq_fold_operator_par` (same operator on the host).
+ *   gptq_ladder : W -> per-row (lo, step) and the 32 rung scales TAB[c] = 2^(lo + c*step).
+ *                 The pages take this from a converter whose rule is not printed; the rule
+ *                 implemented is stated at the declaration below.
+ *   gptq_sweep  : W, U -> 4-bit codes, one f32 scale per (row, 32-column group), and the scaled
+ *                 residuals E.  Source: page "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs",
+ *                 module documentation step 5, kernels `q4tp_group` / `q4tp_trail`; page
+ *                 "cortiq-cli 0.8.45 src/gptq.rs", `gptq_quantize_q4tp`.
+ *
+ * Conventions shared by every call:
+ *   - Matrices are row-major f32.  Every pointer argument except `report` is DEVICE memory
+ *     owned by the caller; the library allocates nothing and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on it.
+ *   - Return value: a GPTQ_* status.  On GPTQ_EINVAL or GPTQ_EWORKSPACE nothing is written.
+ *   - Calls on different streams may run concurrently if their buffers are disjoint.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GPTQ_OK = 0,
+    GPTQ_EINVAL = 1,      /* bad size or null required pointer */
+    GPTQ_EWORKSPACE = 2,  /* workspace smaller than the matching *_workspace_size() */
+    GPTQ_EHIP = 3,        /* a HIP runtime call failed */
+    GPTQ_DEGENERATE = 4   /* the damping passed 10 without a factor: U = I was written */
+};
+
+/* Host-side record of one fold. */
+typedef struct {
+    double lambda_used; /* damping factor of the attempt that factored; on GPTQ_DEGENERATE the
+                           first schedule value past 10 */
+    double base;        /* max(mean of the diagonal with dead entries counted as 1, 1e-12) */
+    double damp;        /* lambda_used * base, added to the diagonal */
+    int32_t attempts;   /* factorizations tried (1 when the starting lambda factors) */
+    int32_t n_dead;     /* channels with !(H_ii > 0) */
+    int32_t degenerate; /* 1 when U = I was written */
+    int32_t reserved;
+} gptq_fold_report;
+
+/* Bytes of device workspace gptq_fold needs for size n: two padded n_p x n_p f32 matrices
+ * (n_p = n rounded up to 128) plus O(n_p * 128).  0 for n <= 0. */
+size_t gptq_fold_workspace_size(int64_t n);
+
+/*
+ * gptq_fold -- the damped, equilibrated fold of one Hessian.
+ *
+ *   H        [n, ldh] f32, device.  Only the UPPER triangle (j >= i) is read; the lower one
+ *            may hold anything.  Non-finite entries are allowed: a non-finite or non-positive
+ *            diagonal marks the channel dead, anything else fails pivots and raises lambda.
+ *   n        channels, >= 1.  ldh >= n.
+ *   lambda   starting relative damping (negative or NaN is treated as 0).  A pivot that is
+ *            not positive (or NaN) in the f32 factorization restarts it with lambda -> 1e-4
+ *            (from 0) or lambda * 10; past 10 the call writes U = I and returns
+ *            GPTQ_DEGENERATE (the round-to-nearest operator of the host fold).
+ *   U        [n, n] f32 out, device: U[j][k] for k >= j, zeros below the diagonal.
+ *   hdiag    [n] f32 out, device: the raw H_ii (the sweep's rung-search weights).
+ *   dead     [n] u8 out, device: 1 where !(H_ii > 0).
+ *   workspace / workspace_bytes: device scratch of at least gptq_fold_workspace_size(n).
+ *   stream   hipStream_t.
+ *   report   host pointer (may be NULL).
+ *
+ * Steps on the device: diagonal, dead mask and mean (f64) -> per attempt: D_i^-1 =
+ * (H_ii + damp)^-1/2 (dead: (1 + damp)^-1/2), the reversed equilibrated matrix
+ * A = P D^-1 H_d D^-1 P, blocked Cholesky A = L L^T fused with the blocked right-looking
+ * inverse X = L^-1 -> U = P X P D^-1.  The host reads the pivot flag once per attempt
+ * (one stream synchronisation); U is still being written when the call returns.
+ */
+int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, float* U, float* hdiag,
+              uint8_t* dead, void* workspace, size_t workspace_bytes, void* stream,
+              gptq_fold_report* report);
+
+/*
+ * gptq_ladder -- per-row rung ladder from the dead-zeroed weights, groups of 32 columns.
+ *
+ *   W      [rows, n] f32, device (n % 32 == 0).   dead [n] u8, device (dead columns ignored).
+ *   lost   [rows, 2] f32 out: (lo, step), both binary16 values.
+ *   tab    [rows, 32] f32 out: TAB[c] = f32(2^(lo + c*step)), evaluated in f64.
+ *
+ * Rule (a stated reading; the pages' converter is not printed): with a_g the absmax of group g
+ * and only a_g > 0 counted, lo = f16(log2(min a_g / 7)), hi = log2(max a_g / 7),
+ * step = f16((hi - lo) / 31) when hi > lo else 0 (a non-positive rounded step is 0); a row with
+ * no nonzero group gets lo = 0, step = 0, TAB = 1.  f16 rounding is to nearest, ties to even.
+ * Asynchronous.
+ */
+int gptq_ladder(const float* W, const uint8_t* dead, int64_t rows, int64_t n, float* lost,
+                float* tab, void* stream);
+
+/* Bytes of device workspace gptq_sweep needs: the corrected working copy of W (rows x n f32)
+ * plus one block of residuals (rows x 128 f32). */
+size_t gptq_sweep_workspace_size(int64_t rows, int64_t n);
+
+/*
+ * gptq_sweep -- the q4tp GPTQ sweep of W against a fold.
+ *
+ *   W      [rows, n] f32, device, read only (dead columns are treated as zero).  Finite.
+ *   U      [n, n] f32, device: the fold's output.   hdiag [n] f32, dead [n] u8: the fold's.
+ *   tab    [rows, 32] f32, lost [rows, 2] f32: the ladder (gptq_ladder's layout).
+ *   rows >= 1; n >= 32 with n % 32 == 0.
+ *   nib    [rows, n/2] u8 out: 4-bit codes q + 8 (q in -8..7); column 2m in the low nibble of
+ *          byte m, 2m+1 in the high nibble (each (row, group) is one 16-byte tile).
+ *   rung   [rows, n/32] u8 out: the chosen rung c.   scale [rows, n/32] f32 out: TAB[row][c].
+ *   E      [rows, n] f32 out or NULL: scaled residuals e_j = (w_j - q_j s) / U_jj.
+ *   workspace / workspace_bytes: at least gptq_sweep_workspace_size(rows, n).
+ *
+ * Per group of 32 columns and row: the rung is chosen from the corrected tile (nominal from
+ * its absmax, best of nominal-2 .. nominal+1 by the H_ii-weighted error of round-to-nearest-
+ * even codes, strict improvement, lowest wins ties), then the columns are rounded in order
+ * with error feedback inside the group.  The residuals of a block of up to 4 groups reach the
+ * rest of the block column by column and the columns right of the block through one f32 MFMA
+ * GEMM, W[:, c1:] -= E[:, c0:c1] U[c0:c1, c1:].  Asynchronous.
+ */
+int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
+               const float* tab, const float* lost, int64_t rows, int64_t n, uint8_t* nib,
+               uint8_t* rung, float* scale, float* E, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Static string for a GPTQ_* status. */
+const char* gptq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

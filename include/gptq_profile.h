@@ -1,0 +1,37 @@
+/*
+ * gptq_profile.h -- optional per-kernel timing of libgptq_mi355x (measurement only).
+ *
+ * When enabled, every launch of the library's kernels is bracketed by two HIP events recorded
+ * on the launch's own stream, and the algorithmic flops and bytes of that launch are noted.
+ * gptq_profile_collect() waits for the recorded events and returns, per kernel family, the sum
+ * of the event intervals, the launch count and the summed algorithmic flops / bytes, then
+ * forgets the records.  Families (index: name):
+ *   0 fold_update  trailing Cholesky update + inverse update (one GEMM launch per block step)
+ *   1 fold_panel   panel solve + inverse row block (one GEMM launch per block step)
+ *   2 fold_diag    diagonal block factor and inverse
+ *   3 fold_build   prep, scaling and the reversed equilibrated matrix
+ *   4 fold_make_u  U from L^-1
+ *   5 sweep_group  rung choice, rounding, in-group feedback
+ *   6 sweep_trail  trailing E * U GEMM
+ *   7 ladder
+ * The recording adds two event records per launch; it is off by default.
+ */
+#ifndef GPTQ_MI355X_PROFILE_H
+#define GPTQ_MI355X_PROFILE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+void gptq_profile_enable(int on);
+/* Arrays of length nfam (host memory).  Returns GPTQ_OK or GPTQ_EHIP. */
+int gptq_profile_collect(double* ms, int64_t* launches, double* flops, double* bytes, int nfam);
+int gptq_profile_family_count(void);
+const char* gptq_profile_family_name(int fam);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,212 @@
+"""Python binding of libgptq_mi355x (ctypes): argument marshalling only.
+
+Every step of the method runs in the library's HIP kernels; PyTorch supplies device memory
+and the current stream.  There is no fallback: without the built library or a GPU the calls
+raise.  Names follow the C ABI in ``include/gptq.h``:
+
+* :func:`gptq_fold` -- H -> U, hdiag, dead, report
+* :func:`gptq_ladder` -- W, dead -> lost, tab
+* :func:`gptq_sweep` -- W, U, hdiag, dead, tab, lost -> nib, rung, scale, E
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgptq_mi355x.so")
+
+GPTQ_OK, GPTQ_EINVAL, GPTQ_EWORKSPACE, GPTQ_EHIP, GPTQ_DEGENERATE = 0, 1, 2, 3, 4
+
+_lib = None
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class FoldReport(ctypes.Structure):
+    _fields_ = [("lambda_used", ctypes.c_double), ("base", ctypes.c_double),
+                ("damp", ctypes.c_double), ("attempts", ctypes.c_int32),
+                ("n_dead", ctypes.c_int32), ("degenerate", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+
+
+def load():
+    """Load the in-tree library (built by ``build.build()``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m post_weight_quantization_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.gptq_fold_workspace_size.argtypes = [i64]
+    lib.gptq_fold_workspace_size.restype = sz
+    lib.gptq_fold.argtypes = [P, i64, i64, ctypes.c_double, P, P, P, P, sz, P,
+                              ctypes.POINTER(FoldReport)]
+    lib.gptq_fold.restype = ctypes.c_int
+    lib.gptq_ladder.argtypes = [P, P, i64, i64, P, P, P]
+    lib.gptq_ladder.restype = ctypes.c_int
+    lib.gptq_sweep_workspace_size.argtypes = [i64, i64]
+    lib.gptq_sweep_workspace_size.restype = sz
+    lib.gptq_sweep.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
+    lib.gptq_sweep.restype = ctypes.c_int
+    lib.gptq_status_string.argtypes = [ctypes.c_int]
+    lib.gptq_status_string.restype = ctypes.c_char_p
+    lib.gptq_profile_enable.argtypes = [ctypes.c_int]
+    lib.gptq_profile_enable.restype = None
+    lib.gptq_profile_collect.argtypes = [P, P, P, P, ctypes.c_int]
+    lib.gptq_profile_collect.restype = ctypes.c_int
+    lib.gptq_profile_family_count.restype = ctypes.c_int
+    lib.gptq_profile_family_name.argtypes = [ctypes.c_int]
+    lib.gptq_profile_family_name.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def require_native():
+    """Raise unless the HIP library loads and a GPU is visible."""
+    load()
+    if not torch.cuda.is_available():
+        raise RuntimeError("libgptq_mi355x needs a visible MI355X GPU")
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().gptq_status_string(int(status)).decode()
+    except Exception:
+        return "unknown"
+
+
+def _dev(t: torch.Tensor, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fold_workspace_size(n: int) -> int:
+    return int(load().gptq_fold_workspace_size(int(n)))
+
+
+def sweep_workspace_size(rows: int, n: int) -> int:
+    return int(load().gptq_sweep_workspace_size(int(rows), int(n)))
+
+
+def gptq_fold(H: torch.Tensor, lam: float, workspace: torch.Tensor | None = None, stream=None,
+              out=None, check=True):
+    """Fold H (f32 [n, n], upper triangle read).  Returns (U, hdiag, dead, report dict)."""
+    lib = load()
+    n = H.shape[0]
+    dev = H.device
+    if out is None:
+        U = torch.empty(n, n, dtype=torch.float32, device=dev)
+        hdiag = torch.empty(n, dtype=torch.float32, device=dev)
+        dead = torch.empty(n, dtype=torch.uint8, device=dev)
+    else:
+        U, hdiag, dead = out
+    need = lib.gptq_fold_workspace_size(n)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    rep = FoldReport()
+    st = lib.gptq_fold(_dev(H, torch.float32, "H"), n, H.stride(0), float(lam),
+                       _dev(U, torch.float32, "U"), _dev(hdiag, torch.float32, "hdiag"),
+                       _dev(dead, torch.uint8, "dead"), _dev(workspace, torch.uint8, "workspace"),
+                       workspace.numel(), _stream(stream), ctypes.byref(rep))
+    if check and st not in (GPTQ_OK, GPTQ_DEGENERATE):
+        raise GptqError(st, "gptq_fold")
+    r = rep.as_dict()
+    r["status"] = st
+    return U, hdiag, dead, r
+
+
+def gptq_ladder(W: torch.Tensor, dead: torch.Tensor, stream=None, out=None):
+    """Per-row (lo, step) and the 32 rung scales of the dead-zeroed W."""
+    lib = load()
+    rows, n = W.shape
+    if out is None:
+        lost = torch.empty(rows, 2, dtype=torch.float32, device=W.device)
+        tab = torch.empty(rows, 32, dtype=torch.float32, device=W.device)
+    else:
+        lost, tab = out
+    st = lib.gptq_ladder(_dev(W, torch.float32, "W"), _dev(dead, torch.uint8, "dead"), rows, n,
+                         _dev(lost, torch.float32, "lost"), _dev(tab, torch.float32, "tab"),
+                         _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_ladder")
+    return lost, tab
+
+
+def gptq_sweep(W, U, hdiag, dead, tab, lost, want_E=False, workspace=None, stream=None,
+               out=None):
+    """The q4tp sweep.  Returns (nib [rows, n/2] u8, rung [rows, n/32] u8,
+    scale [rows, n/32] f32, E [rows, n] f32 or None)."""
+    lib = load()
+    rows, n = W.shape
+    dev = W.device
+    if out is None:
+        nib = torch.empty(rows, n // 2, dtype=torch.uint8, device=dev)
+        rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+        scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+        E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
+    else:
+        nib, rung, scale, E = out
+    if workspace is None:
+        workspace = torch.empty(lib.gptq_sweep_workspace_size(rows, n), dtype=torch.uint8,
+                                device=dev)
+    st = lib.gptq_sweep(_dev(W, torch.float32, "W"), _dev(U, torch.float32, "U"),
+                        _dev(hdiag, torch.float32, "hdiag"), _dev(dead, torch.uint8, "dead"),
+                        _dev(tab, torch.float32, "tab"), _dev(lost, torch.float32, "lost"),
+                        rows, n, _dev(nib, torch.uint8, "nib"), _dev(rung, torch.uint8, "rung"),
+                        _dev(scale, torch.float32, "scale"),
+                        None if E is None else _dev(E, torch.float32, "E"),
+                        _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                        _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_sweep")
+    return nib, rung, scale, E
+
+
+def profile_enable(on: bool = True):
+    load().gptq_profile_enable(1 if on else 0)
+
+
+def profile_collect():
+    """{family: dict(ms, launches, flops, bytes)} for the launches since the last collect."""
+    import numpy as np
+    lib = load()
+    nf = lib.gptq_profile_family_count()
+    ms = np.zeros(nf)
+    ln = np.zeros(nf, dtype=np.int64)
+    fl = np.zeros(nf)
+    by = np.zeros(nf)
+    P = ctypes.c_void_p
+    st = lib.gptq_profile_collect(P(ms.ctypes.data), P(ln.ctypes.data), P(fl.ctypes.data),
+                                  P(by.ctypes.data), nf)
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_profile_collect")
+    return {lib.gptq_profile_family_name(f).decode(): dict(ms=float(ms[f]), launches=int(ln[f]),
+                                                           flops=float(fl[f]), bytes=float(by[f]))
+            for f in range(nf)}
+
+
+__all__ = ["gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
+           "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
+           "profile_collect", "LIB_PATH"]

@@ -1,0 +1,115 @@
+// api.hip -- status strings and the optional per-kernel event timing of libgptq_mi355x.
+#include <mutex>
+#include <vector>
+
+#include "../../include/gptq_profile.h"
+#include "common.hpp"
+
+namespace gptq {
+
+namespace {
+struct Rec {
+    hipEvent_t a, b;
+    int fam;
+    double flops, bytes;
+};
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+ProfScope::ProfScope(int fam_, hipStream_t s_, double flops_, double bytes_)
+    : fam(fam_), s(s_), flops(flops_), bytes(bytes_), on(false), rec(nullptr) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_on) return;
+    Rec* r = new Rec{take_event(), take_event(), fam, flops, bytes};
+    if (!r->a || !r->b) {
+        delete r;
+        return;
+    }
+    hipEventRecord(r->a, s);
+    rec = r;
+    on = true;
+}
+
+ProfScope::~ProfScope() {
+    if (!on) return;
+    Rec* r = (Rec*)rec;
+    hipEventRecord(r->b, s);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_recs.push_back(*r);
+    delete r;
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" const char* gptq_status_string(int status) {
+    switch (status) {
+        case GPTQ_OK: return "ok";
+        case GPTQ_EINVAL: return "invalid argument";
+        case GPTQ_EWORKSPACE: return "workspace too small";
+        case GPTQ_EHIP: return "HIP runtime error";
+        case GPTQ_DEGENERATE: return "damping passed 10 without a factor; U = I";
+        default: return "unknown status";
+    }
+}
+
+extern "C" void gptq_profile_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_on = on != 0;
+}
+
+extern "C" int gptq_profile_collect(double* ms, int64_t* launches, double* flops, double* bytes,
+                                    int nfam) {
+    std::vector<Rec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        recs.swap(g_recs);
+    }
+    for (int f = 0; f < nfam; ++f) {
+        ms[f] = 0.0;
+        launches[f] = 0;
+        flops[f] = 0.0;
+        bytes[f] = 0.0;
+    }
+    int status = GPTQ_OK;
+    for (const Rec& r : recs) {
+        float t = 0.0f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+            status = GPTQ_EHIP;
+        if (r.fam >= 0 && r.fam < nfam) {
+            ms[r.fam] += t;
+            launches[r.fam] += 1;
+            flops[r.fam] += r.flops;
+            bytes[r.fam] += r.bytes;
+        }
+    }
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (const Rec& r : recs) {
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    return status;
+}
+
+extern "C" int gptq_profile_family_count(void) { return FAM_COUNT; }
+
+extern "C" const char* gptq_profile_family_name(int fam) {
+    static const char* names[FAM_COUNT] = {"fold_update", "fold_panel", "fold_diag", "fold_build",
+                                           "fold_make_u", "sweep_group", "sweep_trail", "ladder"};
+    return (fam >= 0 && fam < FAM_COUNT) ? names[fam] : "?";
+}

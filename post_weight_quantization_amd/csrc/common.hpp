@@ -1,0 +1,44 @@
+// common.hpp -- shared host/device helpers of libgptq_mi355x: status codes, HIP error checks,
+// and the optional per-kernel event timing used by the benchmark.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gptq.h"
+
+namespace gptq {
+
+#define GPTQ_HIP(call)                                  \
+    do {                                                \
+        hipError_t e_ = (call);                         \
+        if (e_ != hipSuccess) return GPTQ_EHIP;         \
+    } while (0)
+
+// Kernel families timed by the profiling hooks (include/gptq_profile.h).
+enum Family {
+    FAM_FOLD_UPDATE = 0,  // trailing Cholesky update + inverse update (one GEMM launch per step)
+    FAM_FOLD_PANEL = 1,   // panel solve + inverse row block (one GEMM launch per step)
+    FAM_FOLD_DIAG = 2,    // diagonal block factor + inverse
+    FAM_FOLD_BUILD = 3,   // prep, scaling and the reversed equilibrated matrix
+    FAM_FOLD_MAKEU = 4,
+    FAM_SWEEP_GROUP = 5,  // rung choice + rounding + in-block feedback
+    FAM_SWEEP_TRAIL = 6,  // trailing E * U GEMM
+    FAM_LADDER = 7,
+    FAM_COUNT = 8
+};
+
+// Records an event pair around one launch when profiling is on; no-op otherwise.
+struct ProfScope {
+    int fam;
+    hipStream_t s;
+    double flops, bytes;
+    bool on;
+    void* rec;
+    ProfScope(int fam, hipStream_t s, double flops, double bytes);
+    ~ProfScope();
+};
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace gptq

@@ -1,0 +1,253 @@
+// gemm_mfma.hpp -- f32 MFMA tile GEMM for gfx950: the dense contractions of the fold
+// (trailing Cholesky update, panel solve, triangular inverse) and of the sweep (E * U).
+//
+//   C_out[i][j] = beta * C_in[i][j] + alpha * sum_k A[i][k] * B(k, j)
+//
+// A is row-major (k contiguous).  B is either "T" (B(k, j) = Bm[j][k], rows of Bm contiguous in
+// k) or "N" (B(k, j) = Bm[k][j]).  One workgroup of 256 threads (4 waves, 2 x 2) computes a
+// 128 x 128 tile; each wave holds a 64 x 64 sub-tile as 2 x 2 accumulators of
+// v_mfma_f32_32x32x2_f32.  K is consumed in chunks of 32 staged through LDS, double buffered
+// (one barrier per chunk).  A launch carries up to two independent problems so that the fold
+// can update the Cholesky trailing matrix and the inverse in the same grid.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptq {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int GT_M = 128;        // tile rows
+constexpr int GT_N = 128;        // tile cols
+constexpr int GT_K = 32;         // K chunk
+constexpr int G_THREADS = 256;
+constexpr int LDS_KROW = GT_K + 4;   // row stride (floats) of k-contiguous LDS tiles
+constexpr int LDS_NROW = GT_N + 4;   // row stride of the j-contiguous ("N") B tile
+constexpr int LDS_TILE = GT_M * LDS_KROW;  // >= GT_K * LDS_NROW
+
+struct GemmProblem {
+    const float* A;
+    const float* B;
+    const float* Cin;
+    float* Cout;
+    int64_t lda, ldb, ldc;
+    int M, N, K;          // K % 32 == 0; N % 4 == 0 for the N layout
+    int transB;           // 1: B(k,j) = B[j*ldb + k]; 0: B(k,j) = B[k*ldb + j]
+    int lower;            // 1: square tile grid, only tiles tn <= tm; diagonal tiles store i >= j
+    int tiles_n;          // tile columns (full grid) or tile rows = cols (lower)
+    int ntiles;
+    float alpha;
+    int beta;             // 1: add C_in (tiles with tn < beta0_from_tn), 0: never read C_in
+    int beta0_from_tn;    // tiles with tn >= this ignore C_in
+};
+
+struct GemmBatch {
+    GemmProblem p[2];
+    int nprob;
+};
+
+__device__ __forceinline__ void tile_of(const GemmProblem& P, int t, int& tm, int& tn) {
+    if (P.lower) {
+        int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+        while ((r + 1) * (r + 2) / 2 <= t) ++r;
+        while (r * (r + 1) / 2 > t) --r;
+        tm = r;
+        tn = t - r * (r + 1) / 2;
+    } else {
+        tm = t / P.tiles_n;
+        tn = t - tm * P.tiles_n;
+    }
+}
+
+// Global -> registers for one K chunk.  A (and "T" B): 128 rows x 32 k as 4 float4 per thread,
+// 8 threads per 128-byte row segment.  "N" B: 32 k-rows x 128 j as 4 float4 per thread.
+__device__ __forceinline__ void load_rows_k(const float* __restrict__ base, int64_t ld, int row0,
+                                            int nrows, int k0, int tid, f32x4 (&r)[4]) {
+    const int kq = (tid & 7) * 4;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = (tid >> 3) + 32 * p;
+        if (row0 + row < nrows)
+            r[p] = *reinterpret_cast<const f32x4*>(base + (int64_t)(row0 + row) * ld + k0 + kq);
+        else
+            r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+__device__ __forceinline__ void store_rows_k(float* lds, int tid, const f32x4 (&r)[4]) {
+    const int kq = (tid & 7) * 4;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = (tid >> 3) + 32 * p;
+        *reinterpret_cast<f32x4*>(lds + row * LDS_KROW + kq) = r[p];
+    }
+}
+
+__device__ __forceinline__ void load_krows_n(const float* __restrict__ base, int64_t ld, int col0,
+                                             int ncols, int k0, int tid, f32x4 (&r)[4]) {
+    const int jq = (tid & 31) * 4;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int kr = (tid >> 5) + 8 * p;
+        if (col0 + jq < ncols)
+            r[p] = *reinterpret_cast<const f32x4*>(base + (int64_t)(k0 + kr) * ld + col0 + jq);
+        else
+            r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+__device__ __forceinline__ void store_krows_n(float* lds, int tid, const f32x4 (&r)[4]) {
+    const int jq = (tid & 31) * 4;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int kr = (tid >> 5) + 8 * p;
+        *reinterpret_cast<f32x4*>(lds + kr * LDS_NROW + jq) = r[p];
+    }
+}
+
+// One 128 x 128 tile of problem P.  Lane l of a wave feeds MFMA row/col (l % 32) and k-half
+// h = l / 32; in step s of a chunk the k index is 16 h + s for both operands, so the two lane
+// halves together cover the chunk's 32 k values over 16 steps.
+__device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, float* As, float* Bs) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int i0 = tm * GT_M, j0 = tn * GT_N;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+    f32x4 ra[4], rb[4];
+    load_rows_k(P.A, P.lda, i0, P.M, 0, tid, ra);
+    if (P.transB) load_rows_k(P.B, P.ldb, j0, P.N, 0, tid, rb);
+    else load_krows_n(P.B, P.ldb, j0, P.N, 0, tid, rb);
+    store_rows_k(As, tid, ra);
+    if (P.transB) store_rows_k(Bs, tid, rb);
+    else store_krows_n(Bs, tid, rb);
+    __syncthreads();
+
+    const int nchunk = P.K / GT_K;
+    for (int c = 0; c < nchunk; ++c) {
+        const int buf = c & 1;
+        const float* as = As + buf * LDS_TILE;
+        const float* bs = Bs + buf * LDS_TILE;
+        const bool more = c + 1 < nchunk;
+        if (more) {
+            const int k0 = (c + 1) * GT_K;
+            load_rows_k(P.A, P.lda, i0, P.M, k0, tid, ra);
+            if (P.transB) load_rows_k(P.B, P.ldb, j0, P.N, k0, tid, rb);
+            else load_krows_n(P.B, P.ldb, j0, P.N, k0, tid, rb);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 a4[2], b4[2];
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+                a4[bi] = *reinterpret_cast<const f32x4*>(
+                    as + (wm * 64 + bi * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
+            if (P.transB) {
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    b4[bj] = *reinterpret_cast<const f32x4*>(
+                        bs + (wn * 64 + bj * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
+            } else {
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        b4[bj][q] = bs[(16 * h + 4 * m + q) * LDS_NROW + wn * 64 + bj * 32 + l32];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < 2; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[bi][q], b4[bj][q],
+                                                                          acc[bi][bj], 0, 0, 0);
+        }
+        if (more) {
+            float* asn = As + (buf ^ 1) * LDS_TILE;
+            float* bsn = Bs + (buf ^ 1) * LDS_TILE;
+            store_rows_k(asn, tid, ra);
+            if (P.transB) store_rows_k(bsn, tid, rb);
+            else store_krows_n(bsn, tid, rb);
+        }
+        __syncthreads();
+    }
+
+    const bool use_c = P.beta && tn < P.beta0_from_tn;
+    const bool diag_tile = P.lower && tm == tn;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int lj = wn * 64 + bj * 32 + l32;
+                const int i = i0 + li, j = j0 + lj;
+                if (i < P.M && j < P.N && (!diag_tile || li >= lj)) {
+                    const int64_t off = (int64_t)i * P.ldc + j;
+                    float cv = use_c ? P.Cin[off] : 0.0f;
+                    P.Cout[off] = cv + P.alpha * acc[bi][bj][v];
+                }
+            }
+}
+
+// TAG only separates the launch sites in profiles (one symbol per use).
+template <int TAG>
+__global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
+    if (abort_flag && __atomic_load_n(abort_flag, __ATOMIC_RELAXED)) return;
+    __shared__ __attribute__((aligned(16))) float As[2 * LDS_TILE];
+    __shared__ __attribute__((aligned(16))) float Bs[2 * LDS_TILE];
+    int t = blockIdx.x;
+    if (t < batch.p[0].ntiles) {
+        int tm, tn;
+        tile_of(batch.p[0], t, tm, tn);
+        gemm_tile(batch.p[0], tm, tn, As, Bs);
+    } else {
+        t -= batch.p[0].ntiles;
+        int tm, tn;
+        tile_of(batch.p[1], t, tm, tn);
+        gemm_tile(batch.p[1], tm, tn, As, Bs);
+    }
+}
+
+// Host helpers ---------------------------------------------------------------------------------
+inline GemmProblem gemm_full(const float* A, int64_t lda, const float* B, int64_t ldb, int transB,
+                             const float* Cin, float* Cout, int64_t ldc, int M, int N, int K,
+                             float alpha, int beta) {
+    GemmProblem p{};
+    p.A = A; p.B = B; p.Cin = Cin; p.Cout = Cout;
+    p.lda = lda; p.ldb = ldb; p.ldc = ldc;
+    p.M = M; p.N = N; p.K = K;
+    p.transB = transB; p.lower = 0;
+    p.tiles_n = (N + GT_N - 1) / GT_N;
+    p.ntiles = ((M + GT_M - 1) / GT_M) * p.tiles_n;
+    p.alpha = alpha; p.beta = beta; p.beta0_from_tn = p.tiles_n;
+    if (M <= 0 || N <= 0) p.ntiles = 0;
+    return p;
+}
+
+// C (M x M, lower tiles) = beta*C + alpha * A A^T with A M x K (k contiguous).
+inline GemmProblem gemm_syrk_lower(const float* A, int64_t lda, const float* Cin, float* Cout,
+                                   int64_t ldc, int M, int K, float alpha, int beta) {
+    GemmProblem p = gemm_full(A, lda, A, lda, 1, Cin, Cout, ldc, M, M, K, alpha, beta);
+    const int T = (M + GT_M - 1) / GT_M;
+    p.lower = 1;
+    p.tiles_n = T;
+    p.ntiles = M > 0 ? T * (T + 1) / 2 : 0;
+    p.beta0_from_tn = T;
+    return p;
+}
+
+}  // namespace gptq

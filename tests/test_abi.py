@@ -1,0 +1,54 @@
+"""The C-ABI library loads on a machine without a GPU and exports every symbol the headers in
+include/ declare; size queries are host arithmetic and need no device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import post_weight_quantization_amd as pwq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"\b(gptq_\w+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_headers_declare_the_boundary():
+    names = _declared()
+    for n in ("gptq_fold", "gptq_ladder", "gptq_sweep", "gptq_fold_workspace_size",
+              "gptq_sweep_workspace_size", "gptq_status_string"):
+        assert n in names
+
+
+@pytest.mark.parametrize("name", _declared())
+def test_library_exports_declared_symbol(name):
+    lib = ctypes.CDLL(pwq.LIB_PATH)
+    assert hasattr(lib, name), name
+
+
+def test_workspace_sizes_are_host_arithmetic():
+    lib = pwq.load()
+    assert lib.gptq_fold_workspace_size(0) == 0
+    np_ = 17408
+    assert lib.gptq_fold_workspace_size(17408) >= 2 * 4 * np_ * np_
+    assert lib.gptq_fold_workspace_size(100) >= 2 * 4 * 128 * 128
+    assert lib.gptq_sweep_workspace_size(5120, 17408) >= 4 * 5120 * 17408
+    assert lib.gptq_status_string(4).decode().startswith("damping")
+
+
+def test_product_path_has_no_cpu_fallback(monkeypatch):
+    """Without a visible GPU the binding refuses instead of computing anything elsewhere."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(RuntimeError):
+        pwq.require_native()

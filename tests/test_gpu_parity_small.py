@@ -1,0 +1,131 @@
+"""GPU parity at sizes the oracle finishes in seconds: the HIP path through the C ABI against
+the oracle, element by element, plus the closed-form and edge cases of the method."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import (assert_sweep_bar, check_fold, check_sweep_isolated, output_error, say,
+                    OUT_ERR_TOL)
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x):
+    return torch.as_tensor(np.ascontiguousarray(x)).cuda()
+
+
+@pytest.mark.parametrize("name", ["tiny", "fixture"])
+def test_fold_and_sweep_small_workloads(gpu, name):
+    say("case", name)
+    H, W, lam = workloads.make(name)
+    Hd, Wd = H.cuda(), W.cuda()
+    (U, hdiag, dead, rep), orc, err = check_fold(gpu, Hd, lam)
+    assert rep["attempts"] == 1 and rep["lambda_used"] == lam
+    st, (nib, rung, scale, E, lost, tab) = check_sweep_isolated(gpu, Wd, U, hdiag, dead)
+    assert_sweep_bar(st)
+    assert st["E_relF"] < 1e-4
+    # End to end against the free-running oracle (its own fold, its own damping).
+    Hn, Wn = H.numpy(), W.numpy()
+    of = oracle.fold(Hn, lam)
+    lost_o, tab_o = oracle.ladder(Wn, of["dead"])
+    os_ = oracle.sweep(Wn, of["U"], of["hdiag"], of["dead"], tab_o, lost_o, want_E=False)
+    t_orc = oracle.output_error(Wn, of["dead"], os_["code"], os_["scale"], Hn)
+    t_gpu = output_error(Wn, of["dead"], nib.cpu().numpy(), scale.cpu().numpy(), Hn)
+    say(f"{name}: tr(dW H dW^T) gpu={t_gpu:.6e} oracle={t_orc:.6e} rel={(t_gpu - t_orc) / t_orc:.2e}")
+    assert abs(t_gpu - t_orc) <= OUT_ERR_TOL * t_orc
+
+
+@pytest.mark.parametrize("n,rows", [(32, 1), (160, 70), (288, 130), (384, 257)])
+def test_ragged_shapes(gpu, n, rows):
+    """n not a multiple of the 128 block, rows not a multiple of the 64/128 row tiles."""
+    say("ragged", n, rows)
+    rng = np.random.default_rng(n + rows)
+    X = rng.standard_normal((n, 2 * n)) * np.exp(rng.standard_normal(n))[:, None]
+    H = (X @ X.T).astype(np.float32)
+    H[5 % n, :] = 0.0
+    H[:, 5 % n] = 0.0
+    W = (rng.standard_normal((rows, n)) * 0.02).astype(np.float32)
+    (U, hdiag, dead, rep), orc, err = check_fold(gpu, _dev(H), 0.01, H_np=H)
+    st, _ = check_sweep_isolated(gpu, _dev(W), U, hdiag, dead)
+    assert_sweep_bar(st)
+
+
+def test_identity_hessian_closed_form_and_rtn(gpu):
+    n, rows, lam = 256, 96, 0.01
+    say("identity hessian")
+    U, hdiag, dead, rep = gpu.gptq_fold(_dev(np.eye(n, dtype=np.float32)), lam)
+    Ug = U.cpu().numpy()
+    np.testing.assert_allclose(Ug, np.eye(n) / np.sqrt(1 + lam), rtol=1e-6, atol=1e-7)
+    rng = np.random.default_rng(1)
+    W = (rng.standard_normal((rows, n)) * 0.02).astype(np.float32)
+    Wd = _dev(W)
+    lost, tab = gpu.gptq_ladder(Wd, dead)
+    nib, rung, scale, E = gpu.gptq_sweep(Wd, U, hdiag, dead, tab, lost, want_E=True)
+    code = oracle.unpack_nibbles(nib.cpu().numpy()).astype(np.int16) - 8
+    sc = np.repeat(scale.cpu().numpy(), 32, axis=1)
+    # U is diagonal, so the feedback adds nothing and the codes are plain rounding at the
+    # chosen scale, bit for bit.
+    np.testing.assert_array_equal(code, np.clip(np.rint(W / sc), -8, 7).astype(np.int16))
+
+
+def test_retry_and_degenerate_cases(gpu):
+    say("retry cases")
+    # [[1,1],[1,1]]: singular at 0; f32 needs at least the f64 damping.
+    U, hd, dd, rep = gpu.gptq_fold(_dev(np.array([[1, 1], [1, 1]], np.float32)), 0.0)
+    orc = oracle.fold(np.array([[1, 1], [1, 1]], np.float32), 0.0)
+    assert rep["status"] == 0 and rep["lambda_used"] >= orc["lam"] and rep["attempts"] >= 2
+    # [[1,20],[20,1]] cannot be damped into a factor below 10: U = I, DEGENERATE.
+    U, hd, dd, rep = gpu.gptq_fold(_dev(np.array([[1, 20], [20, 1]], np.float32)), 0.01)
+    assert rep["status"] == 4 and rep["degenerate"] == 1
+    np.testing.assert_array_equal(U.cpu().numpy(), np.eye(2, dtype=np.float32))
+    # A NaN off-diagonal fails every attempt.
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((64, 200))
+    H = (X @ X.T).astype(np.float32)
+    H[3, 40] = np.nan
+    U, hd, dd, rep = gpu.gptq_fold(_dev(H), 0.01)
+    assert rep["status"] == 4
+    assert oracle.fold(H, 0.01)["status"] == oracle.DEGENERATE
+    # Dead channels: zero, negative and NaN diagonals.
+    H = (X @ X.T).astype(np.float32)
+    H[7, :] = 0.0
+    H[:, 7] = 0.0
+    H[9, 9] = -2.0
+    H[11, 11] = np.nan
+    (U, hd, dd, rep), orc, err = check_fold(gpu, _dev(H), 0.01, H_np=H)
+    assert rep["n_dead"] == 3
+
+
+def test_invalid_arguments_write_nothing(gpu):
+    say("invalid arguments")
+    lib = gpu.load()
+    assert lib.gptq_fold_workspace_size(0) == 0
+    H = _dev(np.eye(64, dtype=np.float32))
+    U = torch.full((64, 64), 7.0, device="cuda")
+    hd = torch.zeros(64, device="cuda")
+    dd = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gpu.GptqError) as e:
+        gpu.gptq_fold(H, 0.01, workspace=ws, out=(U, hd, dd))
+    assert e.value.status == 2
+    assert torch.all(U == 7.0)
+    W = torch.zeros(4, 48, device="cuda")  # n % 32 != 0
+    with pytest.raises(gpu.GptqError):
+        gpu.gptq_ladder(W, torch.zeros(48, dtype=torch.uint8, device="cuda"))
+
+
+def test_repeat_runs_are_bitwise_identical(gpu):
+    say("determinism")
+    H, W, lam = workloads.make("tiny")
+    Hd, Wd = H.cuda(), W.cuda()
+    outs = []
+    for _ in range(2):
+        U, hd, dd, rep = gpu.gptq_fold(Hd, lam)
+        lost, tab = gpu.gptq_ladder(Wd, dd)
+        nib, rung, scale, E = gpu.gptq_sweep(Wd, U, hd, dd, tab, lost, want_E=True)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (U, nib, rung, scale, E)])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
