@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the GPTQ fold-and-quantize hot path on one MI355X.
+
+One step = gptq_fold (H -> U) + gptq_ladder + gptq_sweep (W, U -> codes, scales) of one
+Hessian group, inputs already resident in HBM.  The workload is the down_proj-shaped layer:
+n = 17408 input channels, W [5120, 17408] f32, H = X X^T from X [17408, 32768] with lognormal
+channel energies, lambda = 0.01, groups of 32 (synthetic, seeded; see workloads/).
+
+Prints one JSON line: groups/s over the timed steps, the roofline of the dominant kernel (the
+fold's trailing-update GEMM, timed live with HIP events on its own stream) and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def sweep_bytes(rows: int, n: int) -> float:
+    """HBM bytes of the per-group (K = 32) sweep: trailing W read + write, U panel, group read,
+    residual write + read, nibbles / rung / scale."""
+    b = 0.0
+    for g in range(n // 32):
+        rest = n - 32 * (g + 1)
+        b += 8.0 * rows * rest + 128.0 * rest
+    return b + rows * n * 12.5 + 5.0 * rows * n / 32.0
+
+
+def sweep_flops(rows: int, n: int) -> float:
+    return rows * (n * n - 32.0 * n) + 51.0 * rows * n
+
+
+def cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows, m_fold=4608, rows_sweep=128):
+    """The oracle on a bounded sample: the fold of the trailing m x m block of H and the sweep
+    of `rows_sweep` rows at full width against the GPU's U, scaled to one whole group."""
+    import numpy as np
+
+    import oracle
+    nt = oracle.threads()
+    Hb = H[n - m_fold:, n - m_fold:].contiguous().cpu().numpy()
+    t0 = time.perf_counter()
+    f = oracle.fold(Hb, 0.01, nt=nt)
+    t_fold = time.perf_counter() - t0
+    Ud = U.cpu().numpy().astype(np.float64)
+    sel = slice(0, rows_sweep)
+    Wn = W[sel].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.sweep(Wn, Ud, hdiag.cpu().numpy(), dead.cpu().numpy().astype(bool),
+                 tab[sel].cpu().numpy(), lost[sel].cpu().numpy(), want_E=False, nt=nt)
+    t_sweep = time.perf_counter() - t0
+    del Ud
+    t_group = t_fold * (n / m_fold) ** 3 + t_sweep * rows / rows_sweep
+    return {
+        "value": 1.0 / t_group, "unit": "groups/s", "cores": nt, "kind": "oracle",
+        "sample": (f"fold of the trailing {m_fold}x{m_fold} block of H ({t_fold:.2f} s, scaled by "
+                   f"(n/{m_fold})^3) + sweep of {rows_sweep} of {rows} rows at n={n} against the "
+                   f"GPU's U ({t_sweep:.2f} s, scaled by rows); f64, {nt} threads; status "
+                   f"{f['status']}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="down")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the fold and sweep of a Hessian group run on a single "
+              "MI355X in this build; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import post_weight_quantization_amd as pwq
+    import workloads
+
+    pwq.require_native()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = workloads.SPECS[args.workload]
+    n, rows = spec.n, spec.rows
+    log(f"generating workload {args.workload}: n={n} rows={rows} T={spec.T}")
+    t0 = time.perf_counter()
+    H, W, lam = workloads.make(args.workload, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    U = torch.empty(n, n, dtype=torch.float32, device=dev)
+    hdiag = torch.empty(n, dtype=torch.float32, device=dev)
+    dead = torch.empty(n, dtype=torch.uint8, device=dev)
+    lost = torch.empty(rows, 2, dtype=torch.float32, device=dev)
+    tab = torch.empty(rows, 32, dtype=torch.float32, device=dev)
+    nib = torch.empty(rows, n // 2, dtype=torch.uint8, device=dev)
+    rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+    scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+    ws_f = torch.empty(pwq.fold_workspace_size(n), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(pwq.sweep_workspace_size(rows, n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    phase_ms = {"fold": 0.0, "ladder": 0.0, "sweep": 0.0}
+    reports = []
+
+    def step(record):
+        if record:
+            ev[0].record(stream)
+        _, _, _, rep = pwq.gptq_fold(H, lam, workspace=ws_f, out=(U, hdiag, dead))
+        if record:
+            ev[1].record(stream)
+        pwq.gptq_ladder(W, dead, out=(lost, tab))
+        if record:
+            ev[2].record(stream)
+        pwq.gptq_sweep(W, U, hdiag, dead, tab, lost, workspace=ws_s,
+                       out=(nib, rung, scale, None))
+        if record:
+            ev[3].record(stream)
+        reports.append(rep)
+
+    for i in range(args.warmup):
+        step(False)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    pwq.profile_enable(["fold_update"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+        ev[3].synchronize()
+        phase_ms["fold"] += ev[0].elapsed_time(ev[1])
+        phase_ms["ladder"] += ev[1].elapsed_time(ev[2])
+        phase_ms["sweep"] += ev[2].elapsed_time(ev[3])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pwq.profile_enable([])
+    prof = pwq.profile_collect()
+    elapsed = t1 - t0
+    K = args.steps
+    log(f"timed {K} steps in {elapsed:.3f} s")
+
+    fold_ms = phase_ms["fold"] / K
+    sweep_ms = phase_ms["sweep"] / K
+    ladder_ms = phase_ms["ladder"] / K
+    fold_flops = 2.0 * n ** 3 / 3.0
+    fu = prof["fold_update"]
+    achieved = fu["flops"] / (fu["ms"] * 1e-3) / 1e12 if fu["ms"] > 0 else 0.0
+    rep = reports[-1]
+    result = {
+        "metric": "Hessian groups/s + fold TFLOP/s (%FP32 MFMA peak) at n=17408; sweep GB/s",
+        "value": K / elapsed,
+        "unit": "groups/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: down_proj-shaped layer, n={n}, "
+                               f"W[{rows},{n}] f32, H=X X^T from X[{n},{spec.T}]",
+                   "n": n, "rows": rows, "lambda": lam, "group": 32},
+        "roofline": {
+            "kernel": "gemm_kernel<0> (fold trailing update: Cholesky SYRK + inverse GEMM)",
+            "bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+            "launches": fu["launches"], "avg_launch_us": 1e3 * fu["ms"] / max(fu["launches"], 1),
+            "flops_per_launch": fu["flops"] / max(fu["launches"], 1),
+        },
+        "detail": {
+            "fold_ms": fold_ms, "ladder_ms": ladder_ms, "sweep_ms": sweep_ms,
+            "fold_tflops": fold_flops / (fold_ms * 1e-3) / 1e12,
+            "fold_frac_fp32_mfma": fold_flops / (fold_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+            "sweep_gbps_per_group_bytes": sweep_bytes(rows, n) / (sweep_ms * 1e-3) / 1e9,
+            "sweep_frac_hbm": sweep_bytes(rows, n) / (sweep_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "sweep_tflops": sweep_flops(rows, n) / (sweep_ms * 1e-3) / 1e12,
+            "lambda_used": rep["lambda_used"], "attempts": rep["attempts"],
+            "n_dead": rep["n_dead"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

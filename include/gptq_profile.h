@@ -1,7 +1,7 @@
 /*
  * gptq_profile.h -- optional per-kernel timing of libgptq_mi355x (measurement only).
  *
- * When enabled, every launch of the library's kernels is bracketed by two HIP events recorded
+ * For the kernel families whose bit is set in the mask, every launch is bracketed by two HIP events recorded
  * on the launch's own stream, and the algorithmic flops and bytes of that launch are noted.
  * gptq_profile_collect() waits for the recorded events and returns, per kernel family, the sum
  * of the event intervals, the launch count and the summed algorithmic flops / bytes, then
@@ -14,7 +14,7 @@
  *   5 sweep_group  rung choice, rounding, in-group feedback
  *   6 sweep_trail  trailing E * U GEMM
  *   7 ladder
- * The recording adds two event records per launch; it is off by default.
+ * The recording adds two event records per timed launch; the mask is 0 by default.
  */
 #ifndef GPTQ_MI355X_PROFILE_H
 #define GPTQ_MI355X_PROFILE_H
@@ -25,7 +25,7 @@
 extern "C" {
 #endif
 
-void gptq_profile_enable(int on);
+void gptq_profile_enable(unsigned family_mask); /* bit f set: time family f */
 /* Arrays of length nfam (host memory).  Returns GPTQ_OK or GPTQ_EHIP. */
 int gptq_profile_collect(double* ms, int64_t* launches, double* flops, double* bytes, int nfam);
 int gptq_profile_family_count(void);

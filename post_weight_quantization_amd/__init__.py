@@ -62,7 +62,7 @@ def load():
     lib.gptq_sweep.restype = ctypes.c_int
     lib.gptq_status_string.argtypes = [ctypes.c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
-    lib.gptq_profile_enable.argtypes = [ctypes.c_int]
+    lib.gptq_profile_enable.argtypes = [ctypes.c_uint]
     lib.gptq_profile_enable.restype = None
     lib.gptq_profile_collect.argtypes = [P, P, P, P, ctypes.c_int]
     lib.gptq_profile_collect.restype = ctypes.c_int
@@ -184,8 +184,19 @@ def gptq_sweep(W, U, hdiag, dead, tab, lost, want_E=False, workspace=None, strea
     return nib, rung, scale, E
 
 
-def profile_enable(on: bool = True):
-    load().gptq_profile_enable(1 if on else 0)
+PROFILE_FAMILIES = ["fold_update", "fold_panel", "fold_diag", "fold_build", "fold_make_u",
+                    "sweep_group", "sweep_trail", "ladder"]
+
+
+def profile_enable(families=None):
+    """Time the named kernel families (all when None; none for an empty list)."""
+    if families is None:
+        mask = (1 << len(PROFILE_FAMILIES)) - 1
+    else:
+        mask = 0
+        for f in families:
+            mask |= 1 << PROFILE_FAMILIES.index(f)
+    load().gptq_profile_enable(mask)
 
 
 def profile_collect():

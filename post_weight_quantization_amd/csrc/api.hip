@@ -14,7 +14,7 @@ struct Rec {
     double flops, bytes;
 };
 std::mutex g_mu;
-bool g_on = false;
+unsigned g_mask = 0u;
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -33,7 +33,7 @@ hipEvent_t take_event() {
 ProfScope::ProfScope(int fam_, hipStream_t s_, double flops_, double bytes_)
     : fam(fam_), s(s_), flops(flops_), bytes(bytes_), on(false), rec(nullptr) {
     std::lock_guard<std::mutex> lk(g_mu);
-    if (!g_on) return;
+    if (!(g_mask >> fam & 1u)) return;
     Rec* r = new Rec{take_event(), take_event(), fam, flops, bytes};
     if (!r->a || !r->b) {
         delete r;
@@ -68,9 +68,9 @@ extern "C" const char* gptq_status_string(int status) {
     }
 }
 
-extern "C" void gptq_profile_enable(int on) {
+extern "C" void gptq_profile_enable(unsigned family_mask) {
     std::lock_guard<std::mutex> lk(g_mu);
-    g_on = on != 0;
+    g_mask = family_mask;
 }
 
 extern "C" int gptq_profile_collect(double* ms, int64_t* launches, double* flops, double* bytes,
