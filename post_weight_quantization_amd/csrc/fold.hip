@@ -28,7 +28,6 @@
 namespace gptq {
 
 constexpr int NB = 128;
-constexpr int LDL = NB + 1;
 
 struct FoldState {
     double base;
@@ -123,64 +122,158 @@ __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict
     }
 }
 
-// L_kk = chol(A_kk) and MI_k = L_kk^-1 for the NB x NB diagonal block at k * NB.
-// Cholesky: right-looking by columns with the column scaling deferred (the trailing update
-// uses a_rc a_sc / p_c); a pivot that is not > 0 (or NaN) sets the flag and is replaced by 1.
-// Inverse: column c of L^-1 by forward substitution, one thread per column.
+// ---------------------------------------------------------------------------------------------
+// Diagonal block: L_kk = chol(A_kk) and MI_k = L_kk^-1 for the NB x NB block at k * NB, in one
+// workgroup of 4 waves, LDS resident.  The block is factored as 4 sub-panels of 32 columns:
+//   wave 0: 32 x 32 Cholesky of the sub-panel's diagonal block in registers (one lane per row,
+//           column values broadcast with readlane) and its inverse T_p (one lane per column);
+//   waves : panel rows below, L = A T_p^T, and the lower trailing blocks A -= L L^T, each a
+//           32 x 32 x 32 product on v_mfma_f32_32x32x2_f32;
+// then the off-diagonal blocks of L^-1 by block forward substitution down each block column,
+//   M_IJ = -T_I sum_{J <= Q < I} L_IQ M_QJ   (waves 0..2 take block columns 0..2).
+// A pivot that is not > 0 (or NaN) sets the flag and is replaced by 1.
+constexpr int DLD = NB + 1;  // row stride of the block in LDS (odd: column reads spread banks)
+constexpr int SLD = 33;      // row stride of 32 x 32 blocks in LDS
+
+__device__ __forceinline__ float lane_bcast(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+// acc += A * B on one wave, 32 x 32 x 32.  A[i][k] = A[i*lda + k];
+// B(k, j) = TRANS ? B[j*ldb + k] : B[k*ldb + j].  MFMA k index of lane l in step s: 2 s + l/32.
+template <bool TRANS>
+__device__ __forceinline__ f32x16 mm32(const float* A, int lda, const float* B, int ldb,
+                                       f32x16 acc) {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const int k = 2 * s + h;
+        const float a = A[l32 * lda + k];
+        const float b = TRANS ? B[l32 * ldb + k] : B[k * ldb + l32];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+    return z;
+}
+
+// Element (i, j) of a 32 x 32 MFMA result held by this lane in slot v.
+__device__ __forceinline__ int mrow(int v) { return 8 * (v >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (v & 3); }
+__device__ __forceinline__ int mcol() { return threadIdx.x & 31; }
+
 __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, float* __restrict__ X,
                                                         float* __restrict__ MI, int64_t np, int k,
                                                         unsigned* flag) {
     if (__atomic_load_n(flag, __ATOMIC_RELAXED)) return;
-    __shared__ float Ls[NB * LDL];
-    __shared__ float Ms[NB * LDL];
-    __shared__ float piv[NB];
-    const int tid = threadIdx.x;
+    __shared__ float Ls[NB * DLD];        // the block, L in place (lower)
+    __shared__ float Ts[4][32 * SLD];     // T_p = inverse of L's diagonal 32-blocks
+    __shared__ float Mo[6][32 * SLD];     // off-diagonal 32-blocks of L^-1, index (I,J)
+    __shared__ float Sc[3][32 * SLD];     // per-wave scratch
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31;
     const int64_t kb = (int64_t)k * NB;
     for (int e = tid; e < NB * NB; e += 256) {
         const int r = e / NB, c = e % NB;
-        Ls[r * LDL + c] = (c <= r) ? A[(kb + r) * np + kb + c] : 0.0f;
+        Ls[r * DLD + c] = (c <= r) ? A[(kb + r) * np + kb + c] : 0.0f;
     }
     __syncthreads();
-    const int s = tid & (NB - 1), par = tid >> 7;
-    bool bad_any = false;
-    for (int c = 0; c < NB; ++c) {
-        const float p = Ls[c * LDL + c];
-        const bool bad = !(p > 0.0f);
-        const float pp = bad ? 1.0f : p;
-        if (s > c) {
-            const float lsc = Ls[s * LDL + c] / pp;
-            for (int r = s + par; r < NB; r += 2) Ls[r * LDL + s] -= Ls[r * LDL + c] * lsc;
-        }
-        if (tid == 0) {
-            piv[c] = pp;
-            bad_any = bad_any || bad;
-        }
-        __syncthreads();
-    }
-    if (tid == 0 && bad_any) atomicOr(flag, 1u);
-    for (int e = tid; e < NB * NB; e += 256) {
-        const int r = e / NB, c = e % NB;
-        if (c < r) Ls[r * LDL + c] = Ls[r * LDL + c] / sqrtf(piv[c]);
-        else if (c == r) Ls[r * LDL + c] = sqrtf(piv[c]);
-    }
-    __syncthreads();
-    if (tid < NB) {
-        const int c = tid;
-        for (int r = 0; r < NB; ++r) Ms[r * LDL + c] = (r == c) ? 1.0f : 0.0f;
-        for (int q = 0; q < NB; ++q) {
-            if (q >= c) {
-                const float mq = Ms[q * LDL + c] / Ls[q * LDL + q];
-                Ms[q * LDL + c] = mq;
-                for (int r = q + 1; r < NB; ++r) Ms[r * LDL + c] -= Ls[r * LDL + q] * mq;
+    bool bad = false;
+    for (int p = 0; p < 4; ++p) {
+        const int c0 = 32 * p;
+        if (wave == 0) {
+            // Factor: lane r (and r + 32) holds row r of the 32 x 32 block.
+            float a[32];
+#pragma unroll
+            for (int c = 0; c < 32; ++c) a[c] = Ls[(c0 + l32) * DLD + c0 + c];
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                float pv = lane_bcast(a[c], c);
+                const bool b = !(pv > 0.0f);
+                bad = bad || b;
+                pv = b ? 1.0f : pv;
+                const float d = sqrtf(pv);
+                const float l = (l32 == c) ? d : a[c] / d;
+                a[c] = l;
+#pragma unroll
+                for (int s2 = c + 1; s2 < 32; ++s2) a[s2] -= l * lane_bcast(l, s2);
+            }
+            // Inverse, right-looking: lane c builds column c of T = L^-1.
+            float t[32];
+#pragma unroll
+            for (int q = 0; q < 32; ++q) t[q] = (q == l32) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                t[q] = t[q] / lane_bcast(a[q], q);
+#pragma unroll
+                for (int r = q + 1; r < 32; ++r) t[r] -= lane_bcast(a[q], r) * t[q];
+            }
+            if (lane < 32) {
+#pragma unroll
+                for (int c = 0; c < 32; ++c) {
+                    Ls[(c0 + l32) * DLD + c0 + c] = (c <= l32) ? a[c] : 0.0f;
+                    Ts[p][c * SLD + l32] = t[c];
+                }
             }
         }
+        __syncthreads();
+        // Panel: rows below, L_rb = A_rb T_p^T.
+        if (wave < 3 - p) {
+            const int r0 = c0 + 32 * (wave + 1);
+            f32x16 acc = mm32<true>(&Ls[r0 * DLD + c0], DLD, Ts[p], SLD, zero16());
+#pragma unroll
+            for (int v = 0; v < 16; ++v) Ls[(r0 + mrow(v)) * DLD + c0 + mcol()] = acc[v];
+        }
+        __syncthreads();
+        // Trailing lower 32-blocks (rb >= cb > p): A_rb,cb -= L_rb,p L_cb,p^T.
+        int item = 0;
+        for (int rb = p + 1; rb < 4; ++rb)
+            for (int cb = p + 1; cb <= rb; ++cb, ++item) {
+                if ((item & 3) != wave) continue;
+                f32x16 acc = mm32<true>(&Ls[32 * rb * DLD + c0], DLD, &Ls[32 * cb * DLD + c0], DLD,
+                                        zero16());
+#pragma unroll
+                for (int v = 0; v < 16; ++v) Ls[(32 * rb + mrow(v)) * DLD + 32 * cb + mcol()] -= acc[v];
+            }
+        __syncthreads();
     }
+    // Off-diagonal blocks of L^-1, block column J = wave.
+    if (wave < 3) {
+        const int J = wave;
+        float* sc = Sc[J];
+        for (int I = J + 1; I < 4; ++I) {
+            f32x16 acc = zero16();
+            for (int Q = J; Q < I; ++Q) {
+                const float* m = (Q == J) ? Ts[J] : Mo[Q * (Q - 1) / 2 + J];
+                acc = mm32<false>(&Ls[32 * I * DLD + 32 * Q], DLD, m, SLD, acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sc[mrow(v) * SLD + mcol()] = acc[v];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            f32x16 m2 = mm32<false>(Ts[I], SLD, sc, SLD, zero16());
+            float* dst = Mo[I * (I - 1) / 2 + J];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dst[mrow(v) * SLD + mcol()] = -m2[v];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+    if (wave == 0 && lane == 0 && bad) atomicOr(flag, 1u);
     __syncthreads();
     float* mi = MI + (int64_t)k * NB * NB;
     for (int e = tid; e < NB * NB; e += 256) {
         const int r = e / NB, c = e % NB;
-        const float m = (c <= r) ? Ms[r * LDL + c] : 0.0f;
-        if (c <= r) A[(kb + r) * np + kb + c] = Ls[r * LDL + c];
+        const int I = r >> 5, J = c >> 5;
+        float m = 0.0f;
+        if (I == J) m = Ts[I][(r & 31) * SLD + (c & 31)];
+        else if (I > J) m = Mo[I * (I - 1) / 2 + J][(r & 31) * SLD + (c & 31)];
+        if (c <= r) A[(kb + r) * np + kb + c] = Ls[r * DLD + c];
         mi[e] = m;
         X[(kb + r) * np + kb + c] = m;
     }

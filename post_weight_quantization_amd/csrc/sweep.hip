@@ -5,11 +5,15 @@
 // "cortiq-cli 0.8.45 src/gptq.rs" (gptq_quantize_q4tp: rung rule, rounding, feedback;
 // gptq_quantize_q4tp_dev: tab / lost layout).
 //
-// Per group of 32 columns (c0 = 32 g):
-//   group kernel : one thread per row holds the corrected tile in registers, picks the rung,
-//                  rounds the 32 columns in order with feedback inside the tile, and writes the
-//                  nibbles, rung, scale and the scaled residuals E[:, c0:c0+32];
-//   trail GEMM   : W[:, c0+32:] -= E[:, c0:c0+32] U[c0:c0+32, c0+32:]  (f32 MFMA, K = 32).
+// Blocks of 128 columns (4 groups of 32), c0 = 128 b:
+//   block kernel : 16 lanes per row hold the row's corrected block in registers; per group the
+//                  rung is chosen from the corrected tile, then the columns are rounded in order
+//                  and each residual is fed into the rest of the block, column by column (the
+//                  host sweep's full-row update restricted to the block);
+//   trail GEMM   : W[:, c0+128:] -= E[:, c0:c0+128] U[c0:c0+128, c0+128:]  (f32 MFMA, K = 128).
+// Deferring the update of the columns right of the block to one K = 128 product is the blocked
+// ("lazy") form of the same elimination -- the pages' own q2tp host sweep is blocked the same
+// way -- and moves a quarter of the HBM traffic of a K = 32 update per group.
 // W is never modified: the first trailing update reads the caller's W and writes the working
 // copy, later ones update the copy in place.  Dead columns are zeroed whenever a tile is read
 // (U has no off-diagonal entries in a dead row or column, so the GEMM leaves them alone).
@@ -95,21 +99,8 @@ __global__ __launch_bounds__(256) void ladder_kernel(const float* __restrict__ W
 // Rung choice inputs are the f32 corrected weights; the weighted error is summed in column
 // order with every product and sum rounded separately (no contraction), the nominal rung is
 // evaluated in f64, and codes come from correctly rounded f32 division, ties to even.
+// The nominal rung is evaluated in f64 from the f32 absmax of the corrected tile.
 #pragma clang fp contract(off)
-__device__ __forceinline__ float tile_err(const float (&w)[32], const float* hs, float s) {
-    float err = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-        const float q = fminf(fmaxf(rintf(w[t] / s), -8.0f), 7.0f);
-        const float qs = q * s;
-        const float d = w[t] - qs;
-        const float hd = hs[t] * d;
-        const float hdd = hd * d;
-        err = err + hdd;
-    }
-    return err;
-}
-
 __device__ __forceinline__ int nominal_rung(float amax, float lo, float st) {
     if (amax == 0.0f || st <= 0.0f) return 0;
     const double v = (log2((double)amax / 7.0) - (double)lo) / (double)st;
@@ -119,75 +110,126 @@ __device__ __forceinline__ int nominal_rung(float amax, float lo, float st) {
 }
 #pragma clang fp contract(on)
 
-// One 32-column group: 64 rows per workgroup, one thread per row.
-__global__ __launch_bounds__(64) void sweep_group_kernel(
+// Sum / max over the 16 lanes of a row group (xor butterflies stay inside the group).
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) v += __shfl_xor(v, m, 16);
+    return v;
+}
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
+    return v;
+}
+
+#pragma clang fp contract(off)
+// Partial H_ii-weighted rounding error of two columns at scale s (each product and sum rounded).
+__device__ __forceinline__ float pair_err(float w0, float w1, float h0, float h1, float s) {
+    const float q0 = fminf(fmaxf(rintf(w0 / s), -8.0f), 7.0f);
+    const float q1 = fminf(fmaxf(rintf(w1 / s), -8.0f), 7.0f);
+    const float qs0 = q0 * s, qs1 = q1 * s;
+    const float d0 = w0 - qs0, d1 = w1 - qs1;
+    const float e0 = h0 * d0, e1 = h1 * d1;
+    const float f0 = e0 * d0, f1 = e1 * d1;
+    return f0 + f1;
+}
+#pragma clang fp contract(on)
+
+constexpr int SB = 128;          // columns per block (4 groups)
+constexpr int ULD = SB + 4;      // LDS row stride of the block's U
+
+// One block of up to 4 groups for 16 rows per workgroup, 16 lanes per row.  Lane k of a row
+// owns columns 2k and 2k+1 of every group in the block (8 values in registers).  For each group:
+// rung from the group's absmax and the 16-lane sums of the weighted error of each candidate;
+// then the group's 32 columns in order: the column's corrected value is broadcast from its
+// owner, every lane of the row computes the same code and residual, and each lane feeds the
+// residual into its own later columns of the block through row j of U (held in LDS).
+template <int G>
+__global__ __launch_bounds__(256) void sweep_block_kernel(
     const float* __restrict__ src, int64_t n, int64_t c0, const float* __restrict__ U,
-    const float* __restrict__ hdiag, const uint8_t* __restrict__ dead, const float* __restrict__ tab,
-    const float* __restrict__ lost, int64_t rows, uint8_t* __restrict__ nib,
-    uint8_t* __restrict__ rung, float* __restrict__ scale, float* __restrict__ E, int64_t ldE) {
-    __shared__ float Us[32 * 33];
-    __shared__ float hs[32];
-    const int t = threadIdx.x;
-    for (int e = t; e < 32 * 32; e += 64) {
-        const int j = e >> 5, c = e & 31;
-        Us[j * 33 + c] = (c >= j) ? U[(c0 + j) * n + c0 + c] : 0.0f;
+    const float* __restrict__ hdiag, const uint8_t* __restrict__ dead,
+    const float* __restrict__ tab, const float* __restrict__ lost, int64_t rows,
+    uint8_t* __restrict__ nib, uint8_t* __restrict__ rung, float* __restrict__ scale,
+    float* __restrict__ E, int64_t ldE) {
+    constexpr int NC = 32 * G;
+    __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
+    __shared__ float hs[SB];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < NC * (NC / 4); e += 256) {
+        const int j = e / (NC / 4), t4 = (e % (NC / 4)) * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(U + (c0 + j) * n + c0 + t4);
+        *reinterpret_cast<f32x4*>(&Us[j * ULD + t4]) = v;
     }
-    if (t < 32) hs[t] = hdiag[c0 + t];
+    if (tid < NC) hs[tid] = hdiag[c0 + tid];
     __syncthreads();
-    const int64_t r = (int64_t)blockIdx.x * 64 + t;
+    const int k = tid & 15;
+    const int64_t r = (int64_t)blockIdx.x * 16 + (tid >> 4);
     if (r >= rows) return;
 
-    float w[32];
-    const float* srow = src + r * n + c0;
+    float w[G][2];
 #pragma unroll
-    for (int q = 0; q < 32; q += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(srow + q);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) w[q + u] = dead[c0 + q + u] ? 0.0f : v[u];
+    for (int g = 0; g < G; ++g) {
+        const int64_t c = c0 + 32 * g + 2 * k;
+        const float2 v = *reinterpret_cast<const float2*>(src + r * n + c);
+        w[g][0] = dead[c] ? 0.0f : v.x;
+        w[g][1] = dead[c + 1] ? 0.0f : v.y;
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(w[q]));
     const float lo = lost[r * 2], st = lost[r * 2 + 1];
     const float* tb = tab + r * 32;
-    const int nominal = nominal_rung(amax, lo, st);
-    int best = nominal;
-    if (amax > 0.0f) {
-        float best_e = INFINITY;
-        const int lo_c = nominal >= 2 ? nominal - 2 : 0;
-        const int hi_c = nominal + 1 < 31 ? nominal + 1 : 31;
-        for (int cand = lo_c; cand <= hi_c; ++cand) {
-            const float s_c = tb[cand];
-            if (s_c <= 0.0f) continue;
-            const float err = tile_err(w, hs, s_c);
-            if (err < best_e) {
-                best_e = err;
-                best = cand;
+    const int lane = tid & 63;
+    const int base_lane = lane & ~15;
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float amax = group16_max(fmaxf(fabsf(w[g][0]), fabsf(w[g][1])));
+        const int nominal = nominal_rung(amax, lo, st);
+        int best = nominal;
+        if (amax > 0.0f) {
+            float best_e = INFINITY;
+            const int lo_c = nominal >= 2 ? nominal - 2 : 0;
+            const int hi_c = nominal + 1 < 31 ? nominal + 1 : 31;
+            const float h0 = hs[32 * g + 2 * k], h1 = hs[32 * g + 2 * k + 1];
+            for (int cand = lo_c; cand <= hi_c; ++cand) {
+                const float s_c = tb[cand];
+                if (s_c <= 0.0f) continue;
+                const float err = group16_sum(pair_err(w[g][0], w[g][1], h0, h1, s_c));
+                if (err < best_e) {
+                    best_e = err;
+                    best = cand;
+                }
             }
         }
+        const float s = tb[best];
+        if (k == 0) {
+            const int64_t gi = r * (n / 32) + (c0 / 32) + g;
+            rung[gi] = (uint8_t)best;
+            scale[gi] = s;
+        }
+        uint32_t byte = 0u;
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) {
+            const int owner = jj >> 1, slot = jj & 1;
+            const float wj = __shfl(w[g][slot], base_lane + owner, 64);
+            const float q = (s > 0.0f) ? fminf(fmaxf(rintf(wj / s), -8.0f), 7.0f) : 0.0f;
+            const int col = 32 * g + jj;
+            const float ujj = Us[col * ULD + col];
+            const float e = (ujj > 0.0f) ? (wj - q * s) / ujj : 0.0f;
+            if (k == owner) {
+                byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
+                w[g][slot] = e;
+            }
+            // Feed e into this lane's later columns of the block.
+#pragma unroll
+            for (int g2 = g; g2 < G; ++g2) {
+                const float2 u = *reinterpret_cast<const float2*>(&Us[col * ULD + 32 * g2 + 2 * k]);
+                const int t0 = 32 * g2 + 2 * k;
+                if (t0 > col) w[g2][0] -= e * u.x;
+                if (t0 + 1 > col) w[g2][1] -= e * u.y;
+            }
+        }
+        nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
+        *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
     }
-    const float s = tb[best];
-    const int64_t gi = r * (n / 32) + c0 / 32;
-    rung[gi] = (uint8_t)best;
-    scale[gi] = s;
-
-    uint32_t words[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        const float q = (s > 0.0f) ? fminf(fmaxf(rintf(w[j] / s), -8.0f), 7.0f) : 0.0f;
-        words[j >> 3] |= ((uint32_t)((int)q + 8) & 15u) << (4 * (j & 7));
-        const float ujj = Us[j * 33 + j];
-        const float e = (ujj > 0.0f) ? (w[j] - q * s) / ujj : 0.0f;
-        w[j] = e;  // the column is done: its slot now holds the residual
-#pragma unroll
-        for (int c = j + 1; c < 32; ++c) w[c] -= e * Us[j * 33 + c];
-    }
-    uint4* np4 = reinterpret_cast<uint4*>(nib + r * (n / 2) + c0 / 2);
-    *np4 = make_uint4(words[0], words[1], words[2], words[3]);
-    float* erow = E + r * ldE;
-#pragma unroll
-    for (int q = 0; q < 32; q += 4)
-        *reinterpret_cast<f32x4*>(erow + q) = f32x4{w[q], w[q + 1], w[q + 2], w[q + 3]};
 }
 
 }  // namespace gptq
@@ -208,12 +250,21 @@ extern "C" int gptq_ladder(const float* W, const uint8_t* dead, int64_t rows, in
 static size_t sweep_ws(int64_t rows, int64_t n, size_t* off_e) {
     const size_t wc = align256(sizeof(float) * (size_t)(rows * n));
     if (off_e) *off_e = wc;
-    return wc + align256(sizeof(float) * (size_t)(rows * 32));
+    return wc + align256(sizeof(float) * (size_t)(rows * SB));
 }
 
 extern "C" size_t gptq_sweep_workspace_size(int64_t rows, int64_t n) {
     if (rows <= 0 || n <= 0) return 0;
     return sweep_ws(rows, n, nullptr);
+}
+
+template <int G>
+static void launch_block(unsigned nwg, hipStream_t st, const float* src, int64_t n, int64_t c0,
+                         const float* U, const float* hdiag, const uint8_t* dead, const float* tab,
+                         const float* lost, int64_t rows, uint8_t* nib, uint8_t* rung, float* scale,
+                         float* E, int64_t ldE) {
+    sweep_block_kernel<G><<<nwg, 256, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows, nib,
+                                               rung, scale, E, ldE);
 }
 
 extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
@@ -223,32 +274,37 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !hdiag || !dead || !tab || !lost ||
         !nib || !rung || !scale || !workspace)
         return GPTQ_EINVAL;
-    if (rows > ((int64_t)1 << 31) - 64) return GPTQ_EINVAL;
+    if (rows > ((int64_t)1 << 31) - 64 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
     size_t off_e = 0;
     if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     float* Wc = (float*)workspace;
     float* Eblk = (float*)((char*)workspace + off_e);
-    const int64_t ng = n / 32;
-    const unsigned nwg = (unsigned)((rows + 63) / 64);
-    for (int64_t g = 0; g < ng; ++g) {
-        const int64_t c0 = g * 32;
-        const float* src = (g == 0) ? W : Wc;
+    const unsigned nwg = (unsigned)((rows + 15) / 16);
+    for (int64_t c0 = 0; c0 < n; c0 += SB) {
+        const int G = (int)((n - c0 >= SB) ? 4 : (n - c0) / 32);
+        const int64_t nc = 32 * G;
+        const float* src = (c0 == 0) ? W : Wc;
         float* Eo = E ? E + c0 : Eblk;
-        const int64_t ldE = E ? n : 32;
+        const int64_t ldE = E ? n : SB;
         {
-            ProfScope ps(FAM_SWEEP_GROUP, st, 51.0 * 32.0 * rows, 4.0 * rows * 32 * 2 + 4.0 * 1024);
-            sweep_group_kernel<<<nwg, 64, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows, nib,
-                                                   rung, scale, Eo, ldE);
+            ProfScope ps(FAM_SWEEP_GROUP, st, 51.0 * nc * rows + (double)rows * nc * nc,
+                         4.0 * rows * nc * 2 + 4.0 * nc * nc);
+            switch (G) {
+                case 4: launch_block<4>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+                case 3: launch_block<3>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+                case 2: launch_block<2>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+                default: launch_block<1>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+            }
         }
-        const int64_t rest = n - c0 - 32;
+        const int64_t rest = n - c0 - nc;
         if (rest > 0) {
             GemmBatch b{};
-            b.p[0] = gemm_full(Eo, ldE, U + c0 * n + c0 + 32, n, 0, src + c0 + 32, Wc + c0 + 32, n,
-                               (int)rows, (int)rest, 32, -1.0f, 1);
+            b.p[0] = gemm_full(Eo, ldE, U + c0 * n + c0 + nc, n, 0, src + c0 + nc, Wc + c0 + nc, n,
+                               (int)rows, (int)rest, (int)nc, -1.0f, 1);
             b.nprob = 1;
-            ProfScope ps(FAM_SWEEP_TRAIL, st, 2.0 * 32.0 * rows * rest,
-                         8.0 * rows * rest + 128.0 * rest + 128.0 * rows);
+            ProfScope ps(FAM_SWEEP_TRAIL, st, 2.0 * nc * rows * rest,
+                         8.0 * rows * rest + 4.0 * nc * rest + 4.0 * rows * nc);
             gemm_kernel<2><<<b.p[0].ntiles, G_THREADS, 0, st>>>(b, nullptr);
         }
         GPTQ_HIP(hipGetLastError());
