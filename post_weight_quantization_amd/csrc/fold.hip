@@ -373,30 +373,32 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)k, &state->flag);
             }
             const float* mik = MI + k * NB * NB;
-            GemmBatch pb{};
-            pb.p[0] = gemm_full(A + (kb + NB) * np + kb, np, mik, NB, 1, nullptr,
-                                A + (kb + NB) * np + kb, np, (int)rest, NB, NB, 1.0f, 0);
-            pb.p[1] = gemm_full(mik, NB, X + kb * np, np, 0, nullptr, X + kb * np, np, NB,
-                                (int)kb, NB, 1.0f, 0);
-            pb.nprob = 2;
-            const int pt = pb.p[0].ntiles + pb.p[1].ntiles;
-            if (pt > 0) {
+            // Panel: L_ik = A_ik MI_k^T below the block; X_k,<k = MI_k X_k,<k (both in place:
+            // every workgroup reads its whole tile before writing it).
+            const GemmProblem pa = gemm_full(A + (kb + NB) * np + kb, np, mik, NB, nullptr,
+                                             A + (kb + NB) * np + kb, np, (int)rest, NB, NB, 1.0f, 0);
+            const GemmProblem pxr = gemm_full(mik, NB, X + kb * np, np, nullptr, X + kb * np, np, NB,
+                                              (int)kb, NB, 1.0f, 0);
+            const GemmBatch pb = gemm_batch(pa, &pxr);
+            if (pb.total > 0) {
                 ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * NB * ((double)rest + kb), 0.0);
-                gemm_kernel<1><<<pt, G_THREADS, 0, st>>>(pb, &state->flag);
+                gemm_kernel<1, true, false, false><<<pb.total, G_THREADS, 0, st>>>(pb, &state->flag);
             }
             if (rest > 0) {
+                // Update: A_ij -= L_ik L_jk^T (lower tiles); X_i,<=k -= L_ik X_k,<=k, where the
+                // block column k of X is written for the first time (no C read).
                 const float* P = A + (kb + NB) * np + kb;
-                GemmBatch ub{};
-                ub.p[0] = gemm_syrk_lower(P, np, A + (kb + NB) * np + kb + NB,
-                                          A + (kb + NB) * np + kb + NB, np, (int)rest, NB, -1.0f, 1);
-                ub.p[1] = gemm_full(P, np, X + kb * np, np, 0, X + (kb + NB) * np,
-                                    X + (kb + NB) * np, np, (int)rest, (int)(kb + NB), NB, -1.0f, 1);
-                ub.p[1].beta0_from_tn = (int)k;
-                ub.nprob = 2;
+                const GemmProblem sy = gemm_syrk_lower(P, np, A + (kb + NB) * np + kb + NB,
+                                                       A + (kb + NB) * np + kb + NB, np, (int)rest,
+                                                       NB, -1.0f, 1);
+                GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + NB) * np,
+                                           X + (kb + NB) * np, np, (int)rest, (int)(kb + NB), NB,
+                                           -1.0f, 1);
+                xu.beta0_from_tn = (int)k;
+                const GemmBatch ub = gemm_batch(sy, &xu);
                 const double fl = (double)NB * rest * (rest + 1) + 2.0 * NB * rest * (kb + NB);
                 ProfScope ps(FAM_FOLD_UPDATE, st, fl, 0.0);
-                gemm_kernel<0><<<ub.p[0].ntiles + ub.p[1].ntiles, G_THREADS, 0, st>>>(ub,
-                                                                                     &state->flag);
+                gemm_kernel<0, true, false, false><<<ub.total, G_THREADS, 0, st>>>(ub, &state->flag);
             }
             GPTQ_HIP(hipGetLastError());
         }

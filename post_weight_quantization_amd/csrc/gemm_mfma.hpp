@@ -4,11 +4,16 @@
 //   C_out[i][j] = beta * C_in[i][j] + alpha * sum_k A[i][k] * B(k, j)
 //
 // A is row-major (k contiguous).  B is either "T" (B(k, j) = Bm[j][k], rows of Bm contiguous in
-// k) or "N" (B(k, j) = Bm[k][j]).  One workgroup of 256 threads (4 waves, 2 x 2) computes a
-// 128 x 128 tile; each wave holds a 64 x 64 sub-tile as 2 x 2 accumulators of
-// v_mfma_f32_32x32x2_f32.  K is consumed in chunks of 32 staged through LDS, double buffered
-// (one barrier per chunk).  A launch carries up to two independent problems so that the fold
-// can update the Cholesky trailing matrix and the inverse in the same grid.
+// k) or "N" (B(k, j) = Bm[k][j]); the layout is a compile-time parameter, as is the bounds
+// checking (the fold's matrices are padded to whole tiles and need none).  One workgroup of
+// 256 threads (4 waves, 2 x 2) computes a 128 x 128 tile; each wave holds a 64 x 64 sub-tile as
+// 2 x 2 accumulators of v_mfma_f32_32x32x2_f32.  K is consumed in chunks of 32 staged through
+// LDS, double buffered (one barrier per chunk); the C tile is fetched into registers before the
+// K loop so its latency hides behind the MFMAs.  A launch carries up to two independent
+// problems so that the fold can update the Cholesky trailing matrix and the inverse in one
+// grid.  Workgroups are dealt to the 8 XCDs round-robin by the hardware; tiles are renumbered
+// so that each XCD works on a contiguous range (neighbouring tiles share operand rows in the
+// XCD's L2).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,6 +30,7 @@ constexpr int G_THREADS = 256;
 constexpr int LDS_KROW = GT_K + 4;   // row stride (floats) of k-contiguous LDS tiles
 constexpr int LDS_NROW = GT_N + 4;   // row stride of the j-contiguous ("N") B tile
 constexpr int LDS_TILE = GT_M * LDS_KROW;  // >= GT_K * LDS_NROW
+constexpr int NUM_XCD = 8;
 
 struct GemmProblem {
     const float* A;
@@ -33,7 +39,6 @@ struct GemmProblem {
     float* Cout;
     int64_t lda, ldb, ldc;
     int M, N, K;          // K % 32 == 0; N % 4 == 0 for the N layout
-    int transB;           // 1: B(k,j) = B[j*ldb + k]; 0: B(k,j) = B[k*ldb + j]
     int lower;            // 1: square tile grid, only tiles tn <= tm; diagonal tiles store i >= j
     int tiles_n;          // tile columns (full grid) or tile rows = cols (lower)
     int ntiles;
@@ -45,6 +50,7 @@ struct GemmProblem {
 struct GemmBatch {
     GemmProblem p[2];
     int nprob;
+    int total;            // p[0].ntiles + p[1].ntiles
 };
 
 __device__ __forceinline__ void tile_of(const GemmProblem& P, int t, int& tm, int& tn) {
@@ -60,18 +66,26 @@ __device__ __forceinline__ void tile_of(const GemmProblem& P, int t, int& tm, in
     }
 }
 
+// Bijective renumbering: the hardware sends workgroup b to XCD b % 8; give XCD x the
+// contiguous tile range [o_x, o_x + c_x).
+__device__ __forceinline__ int xcd_order(int b, int total) {
+    const int q = total / NUM_XCD, r = total % NUM_XCD;
+    const int x = b % NUM_XCD, i = b / NUM_XCD;
+    return x * q + (x < r ? x : r) + i;
+}
+
 // Global -> registers for one K chunk.  A (and "T" B): 128 rows x 32 k as 4 float4 per thread,
 // 8 threads per 128-byte row segment.  "N" B: 32 k-rows x 128 j as 4 float4 per thread.
-__device__ __forceinline__ void load_rows_k(const float* __restrict__ base, int64_t ld, int row0,
-                                            int nrows, int k0, int tid, f32x4 (&r)[4]) {
+template <bool CHK>
+__device__ __forceinline__ void load_rows_k(const float* base, int64_t ld, int row0, int nrows,
+                                            int k0, int tid, f32x4 (&r)[4]) {
     const int kq = (tid & 7) * 4;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int row = (tid >> 3) + 32 * p;
-        if (row0 + row < nrows)
-            r[p] = *reinterpret_cast<const f32x4*>(base + (int64_t)(row0 + row) * ld + k0 + kq);
-        else
-            r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const float* src = base + (int64_t)(row0 + row) * ld + k0 + kq;
+        if (!CHK || row0 + row < nrows) r[p] = *reinterpret_cast<const f32x4*>(src);
+        else r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
 
@@ -84,16 +98,16 @@ __device__ __forceinline__ void store_rows_k(float* lds, int tid, const f32x4 (&
     }
 }
 
-__device__ __forceinline__ void load_krows_n(const float* __restrict__ base, int64_t ld, int col0,
-                                             int ncols, int k0, int tid, f32x4 (&r)[4]) {
+template <bool CHK>
+__device__ __forceinline__ void load_krows_n(const float* base, int64_t ld, int col0, int ncols,
+                                             int k0, int tid, f32x4 (&r)[4]) {
     const int jq = (tid & 31) * 4;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int kr = (tid >> 5) + 8 * p;
-        if (col0 + jq < ncols)
-            r[p] = *reinterpret_cast<const f32x4*>(base + (int64_t)(k0 + kr) * ld + col0 + jq);
-        else
-            r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const float* src = base + (int64_t)(k0 + kr) * ld + col0 + jq;
+        if (!CHK || col0 + jq < ncols) r[p] = *reinterpret_cast<const f32x4*>(src);
+        else r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
 
@@ -106,10 +120,26 @@ __device__ __forceinline__ void store_krows_n(float* lds, int tid, const f32x4 (
     }
 }
 
+template <bool TB, bool CHK>
+__device__ __forceinline__ void load_b(const GemmProblem& P, int j0, int k0, int tid,
+                                       f32x4 (&r)[4]) {
+    if (TB) load_rows_k<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
+    else load_krows_n<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
+}
+
+template <bool TB>
+__device__ __forceinline__ void store_b(float* lds, int tid, const f32x4 (&r)[4]) {
+    if (TB) store_rows_k(lds, tid, r);
+    else store_krows_n(lds, tid, r);
+}
+
 // One 128 x 128 tile of problem P.  Lane l of a wave feeds MFMA row/col (l % 32) and k-half
 // h = l / 32; in step s of a chunk the k index is 16 h + s for both operands, so the two lane
-// halves together cover the chunk's 32 k values over 16 steps.
-__device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, float* As, float* Bs) {
+// halves together cover the chunk's 32 k values over 16 steps.  Output slot v of a 32 x 32
+// accumulator holds row 8 (v / 4) + 4 h + v % 4, column l % 32.
+template <bool TB, bool CHK>
+__device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, float* As,
+                                          float* Bs) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -126,12 +156,32 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
     f32x4 ra[4], rb[4];
-    load_rows_k(P.A, P.lda, i0, P.M, 0, tid, ra);
-    if (P.transB) load_rows_k(P.B, P.ldb, j0, P.N, 0, tid, rb);
-    else load_krows_n(P.B, P.ldb, j0, P.N, 0, tid, rb);
+    load_rows_k<CHK>(P.A, P.lda, i0, P.M, 0, tid, ra);
+    load_b<TB, CHK>(P, j0, 0, tid, rb);
+
+    // The C tile, fetched now and consumed after the K loop.
+    const bool use_c = P.beta && tn < P.beta0_from_tn;
+    const bool diag_tile = P.lower && tm == tn;
+    float cv[2][2][16];
+    if (use_c) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    const int lj = wn * 64 + bj * 32 + l32;
+                    // Unconditional load (clamped inside the matrix); masked values are
+                    // never stored.
+                    const int i = CHK ? min(i0 + li, P.M - 1) : i0 + li;
+                    const int j = CHK ? min(j0 + lj, P.N - 1) : j0 + lj;
+                    cv[bi][bj][v] = P.Cin[(int64_t)i * P.ldc + j];
+                }
+    }
+
     store_rows_k(As, tid, ra);
-    if (P.transB) store_rows_k(Bs, tid, rb);
-    else store_krows_n(Bs, tid, rb);
+    store_b<TB>(Bs, tid, rb);
     __syncthreads();
 
     const int nchunk = P.K / GT_K;
@@ -142,9 +192,8 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
         const bool more = c + 1 < nchunk;
         if (more) {
             const int k0 = (c + 1) * GT_K;
-            load_rows_k(P.A, P.lda, i0, P.M, k0, tid, ra);
-            if (P.transB) load_rows_k(P.B, P.ldb, j0, P.N, k0, tid, rb);
-            else load_krows_n(P.B, P.ldb, j0, P.N, k0, tid, rb);
+            load_rows_k<CHK>(P.A, P.lda, i0, P.M, k0, tid, ra);
+            load_b<TB, CHK>(P, j0, k0, tid, rb);
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -153,7 +202,7 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
             for (int bi = 0; bi < 2; ++bi)
                 a4[bi] = *reinterpret_cast<const f32x4*>(
                     as + (wm * 64 + bi * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
-            if (P.transB) {
+            if (TB) {
 #pragma unroll
                 for (int bj = 0; bj < 2; ++bj)
                     b4[bj] = *reinterpret_cast<const f32x4*>(
@@ -175,17 +224,12 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
                                                                           acc[bi][bj], 0, 0, 0);
         }
         if (more) {
-            float* asn = As + (buf ^ 1) * LDS_TILE;
-            float* bsn = Bs + (buf ^ 1) * LDS_TILE;
-            store_rows_k(asn, tid, ra);
-            if (P.transB) store_rows_k(bsn, tid, rb);
-            else store_krows_n(bsn, tid, rb);
+            store_rows_k(As + (buf ^ 1) * LDS_TILE, tid, ra);
+            store_b<TB>(Bs + (buf ^ 1) * LDS_TILE, tid, rb);
         }
         __syncthreads();
     }
 
-    const bool use_c = P.beta && tn < P.beta0_from_tn;
-    const bool diag_tile = P.lower && tm == tn;
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -195,42 +239,42 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
                 const int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
                 const int lj = wn * 64 + bj * 32 + l32;
                 const int i = i0 + li, j = j0 + lj;
-                if (i < P.M && j < P.N && (!diag_tile || li >= lj)) {
-                    const int64_t off = (int64_t)i * P.ldc + j;
-                    float cv = use_c ? P.Cin[off] : 0.0f;
-                    P.Cout[off] = cv + P.alpha * acc[bi][bj][v];
+                if ((!CHK || (i < P.M && j < P.N)) && (!diag_tile || li >= lj)) {
+                    const float base = use_c ? cv[bi][bj][v] : 0.0f;
+                    P.Cout[(int64_t)i * P.ldc + j] = base + P.alpha * acc[bi][bj][v];
                 }
             }
 }
 
-// TAG only separates the launch sites in profiles (one symbol per use).
-template <int TAG>
+// TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
+// of problems 0 and 1; CHK: bounds checks on M and N.
+template <int TAG, bool TB0, bool TB1, bool CHK>
 __global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
     if (abort_flag && __atomic_load_n(abort_flag, __ATOMIC_RELAXED)) return;
     __shared__ __attribute__((aligned(16))) float As[2 * LDS_TILE];
     __shared__ __attribute__((aligned(16))) float Bs[2 * LDS_TILE];
-    int t = blockIdx.x;
+    int t = xcd_order(blockIdx.x, batch.total);
     if (t < batch.p[0].ntiles) {
         int tm, tn;
         tile_of(batch.p[0], t, tm, tn);
-        gemm_tile(batch.p[0], tm, tn, As, Bs);
+        gemm_tile<TB0, CHK>(batch.p[0], tm, tn, As, Bs);
     } else {
         t -= batch.p[0].ntiles;
         int tm, tn;
         tile_of(batch.p[1], t, tm, tn);
-        gemm_tile(batch.p[1], tm, tn, As, Bs);
+        gemm_tile<TB1, CHK>(batch.p[1], tm, tn, As, Bs);
     }
 }
 
 // Host helpers ---------------------------------------------------------------------------------
-inline GemmProblem gemm_full(const float* A, int64_t lda, const float* B, int64_t ldb, int transB,
+inline GemmProblem gemm_full(const float* A, int64_t lda, const float* B, int64_t ldb,
                              const float* Cin, float* Cout, int64_t ldc, int M, int N, int K,
                              float alpha, int beta) {
     GemmProblem p{};
     p.A = A; p.B = B; p.Cin = Cin; p.Cout = Cout;
     p.lda = lda; p.ldb = ldb; p.ldc = ldc;
     p.M = M; p.N = N; p.K = K;
-    p.transB = transB; p.lower = 0;
+    p.lower = 0;
     p.tiles_n = (N + GT_N - 1) / GT_N;
     p.ntiles = ((M + GT_M - 1) / GT_M) * p.tiles_n;
     p.alpha = alpha; p.beta = beta; p.beta0_from_tn = p.tiles_n;
@@ -238,16 +282,28 @@ inline GemmProblem gemm_full(const float* A, int64_t lda, const float* B, int64_
     return p;
 }
 
-// C (M x M, lower tiles) = beta*C + alpha * A A^T with A M x K (k contiguous).
+// C (M x M, lower tiles) = beta*C + alpha * A A^T with A M x K (k contiguous): use TB = true.
 inline GemmProblem gemm_syrk_lower(const float* A, int64_t lda, const float* Cin, float* Cout,
                                    int64_t ldc, int M, int K, float alpha, int beta) {
-    GemmProblem p = gemm_full(A, lda, A, lda, 1, Cin, Cout, ldc, M, M, K, alpha, beta);
+    GemmProblem p = gemm_full(A, lda, A, lda, Cin, Cout, ldc, M, M, K, alpha, beta);
     const int T = (M + GT_M - 1) / GT_M;
     p.lower = 1;
     p.tiles_n = T;
     p.ntiles = M > 0 ? T * (T + 1) / 2 : 0;
     p.beta0_from_tn = T;
     return p;
+}
+
+inline GemmBatch gemm_batch(const GemmProblem& a, const GemmProblem* b) {
+    GemmBatch g{};
+    g.p[0] = a;
+    g.nprob = 1;
+    if (b) {
+        g.p[1] = *b;
+        g.nprob = 2;
+    }
+    g.total = g.p[0].ntiles + (b ? g.p[1].ntiles : 0);
+    return g;
 }
 
 }  // namespace gptq

@@ -299,13 +299,13 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
         }
         const int64_t rest = n - c0 - nc;
         if (rest > 0) {
-            GemmBatch b{};
-            b.p[0] = gemm_full(Eo, ldE, U + c0 * n + c0 + nc, n, 0, src + c0 + nc, Wc + c0 + nc, n,
-                               (int)rows, (int)rest, (int)nc, -1.0f, 1);
-            b.nprob = 1;
+            const GemmBatch b = gemm_batch(
+                gemm_full(Eo, ldE, U + c0 * n + c0 + nc, n, src + c0 + nc, Wc + c0 + nc, n,
+                          (int)rows, (int)rest, (int)nc, -1.0f, 1),
+                nullptr);
             ProfScope ps(FAM_SWEEP_TRAIL, st, 2.0 * nc * rows * rest,
                          8.0 * rows * rest + 4.0 * nc * rest + 4.0 * rows * nc);
-            gemm_kernel<2><<<b.p[0].ntiles, G_THREADS, 0, st>>>(b, nullptr);
+            gemm_kernel<2, false, false, true><<<b.total, G_THREADS, 0, st>>>(b, nullptr);
         }
         GPTQ_HIP(hipGetLastError());
     }
