@@ -123,10 +123,21 @@ __device__ __forceinline__ float group16_max(float v) {
 }
 
 #pragma clang fp contract(off)
+// rint(fl(w / s)) -- the code decision on the correctly rounded quotient -- from w * fl(1/s):
+// that product is within 3u|w/s| (u = 2^-24) of the quotient, so both round to the same integer
+// unless the product lies within 4e-7 max(|w/s|, 1) of a half-integer; then (rarely) divide.
+__device__ __forceinline__ float rint_quot(float w, float s, float inv_s) {
+    const float r = w * inv_s;
+    const float f = r - floorf(r);
+    if (fabsf(f - 0.5f) > 4e-7f * fmaxf(fabsf(r), 1.0f)) return rintf(r);
+    return rintf(w / s);
+}
+
 // Partial H_ii-weighted rounding error of two columns at scale s (each product and sum rounded).
-__device__ __forceinline__ float pair_err(float w0, float w1, float h0, float h1, float s) {
-    const float q0 = fminf(fmaxf(rintf(w0 / s), -8.0f), 7.0f);
-    const float q1 = fminf(fmaxf(rintf(w1 / s), -8.0f), 7.0f);
+__device__ __forceinline__ float pair_err(float w0, float w1, float h0, float h1, float s,
+                                          float inv_s) {
+    const float q0 = fminf(fmaxf(rint_quot(w0, s, inv_s), -8.0f), 7.0f);
+    const float q1 = fminf(fmaxf(rint_quot(w1, s, inv_s), -8.0f), 7.0f);
     const float qs0 = q0 * s, qs1 = q1 * s;
     const float d0 = w0 - qs0, d1 = w1 - qs1;
     const float e0 = h0 * d0, e1 = h1 * d1;
@@ -137,6 +148,80 @@ __device__ __forceinline__ float pair_err(float w0, float w1, float h0, float h1
 
 constexpr int SB = 128;          // columns per block (4 groups)
 constexpr int ULD = SB + 4;      // LDS row stride of the block's U
+
+struct BlockCtx {
+    const float* Us;     // U[c0 + j][c0 + t] in LDS, row stride ULD
+    const float* uinv;   // 1 / U_jj (0 where U_jj <= 0), LDS
+    const float* hs;     // H_ii of the block's columns, LDS
+    const float* tb;     // the row's 32 rung scales
+    float lo, st;
+    int k, base_lane;
+};
+
+// Group g of the block, with every register index a compile-time constant (the groups are
+// unrolled by template recursion).
+template <int G, int g>
+__device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx, int64_t r,
+                                            int64_t n, int64_t c0, uint8_t* __restrict__ nib,
+                                            uint8_t* __restrict__ rung, float* __restrict__ scale,
+                                            float* __restrict__ E, int64_t ldE) {
+    const int k = cx.k;
+    const float amax = group16_max(fmaxf(fabsf(w[g][0]), fabsf(w[g][1])));
+    const int nominal = nominal_rung(amax, cx.lo, cx.st);
+    int best = nominal;
+    if (amax > 0.0f) {
+        float best_e = INFINITY;
+        const int lo_c = nominal >= 2 ? nominal - 2 : 0;
+        const int hi_c = nominal + 1 < 31 ? nominal + 1 : 31;
+        const float h0 = cx.hs[32 * g + 2 * k], h1 = cx.hs[32 * g + 2 * k + 1];
+        for (int cand = lo_c; cand <= hi_c; ++cand) {
+            const float s_c = cx.tb[cand];
+            if (s_c <= 0.0f) continue;
+            const float err = group16_sum(pair_err(w[g][0], w[g][1], h0, h1, s_c, 1.0f / s_c));
+            if (err < best_e) {
+                best_e = err;
+                best = cand;
+            }
+        }
+    }
+    const float s = cx.tb[best];
+    const float inv_s = (s > 0.0f) ? 1.0f / s : 0.0f;
+    if (k == 0) {
+        const int64_t gi = r * (n / 32) + (c0 / 32) + g;
+        rung[gi] = (uint8_t)best;
+        scale[gi] = s;
+    }
+    uint32_t byte = 0u;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) {
+        const int owner = jj >> 1, slot = jj & 1;
+        const float wj = __shfl(w[g][slot], cx.base_lane + owner, 64);
+        const float q = (s > 0.0f) ? fminf(fmaxf(rint_quot(wj, s, inv_s), -8.0f), 7.0f) : 0.0f;
+        const int col = 32 * g + jj;
+        const float e = (wj - q * s) * cx.uinv[col];
+        if (k == owner) {
+            byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
+            w[g][slot] = e;  // the column is done: its slot now holds the residual
+        }
+        // This lane's later columns of the same group...
+        {
+            const float2 u = *reinterpret_cast<const float2*>(&cx.Us[col * ULD + 32 * g + 2 * k]);
+            const int t0 = 2 * k;
+            if (t0 > jj) w[g][0] -= e * u.x;
+            if (t0 + 1 > jj) w[g][1] -= e * u.y;
+        }
+        // ... and all of its columns of the later groups of the block.
+#pragma unroll
+        for (int g2 = g + 1; g2 < G; ++g2) {
+            const float2 u = *reinterpret_cast<const float2*>(&cx.Us[col * ULD + 32 * g2 + 2 * k]);
+            w[g2][0] -= e * u.x;
+            w[g2][1] -= e * u.y;
+        }
+    }
+    nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
+    *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
+    if constexpr (g + 1 < G) block_group<G, g + 1>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
+}
 
 // One block of up to 4 groups for 16 rows per workgroup, 16 lanes per row.  Lane k of a row
 // owns columns 2k and 2k+1 of every group in the block (8 values in registers).  For each group:
@@ -154,16 +239,25 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     constexpr int NC = 32 * G;
     __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
     __shared__ float hs[SB];
+    __shared__ float uinv[SB];
+    __shared__ float tabs[16 * 32];
     const int tid = threadIdx.x;
     for (int e = tid; e < NC * (NC / 4); e += 256) {
         const int j = e / (NC / 4), t4 = (e % (NC / 4)) * 4;
         f32x4 v = *reinterpret_cast<const f32x4*>(U + (c0 + j) * n + c0 + t4);
         *reinterpret_cast<f32x4*>(&Us[j * ULD + t4]) = v;
     }
-    if (tid < NC) hs[tid] = hdiag[c0 + tid];
+    if (tid < NC) {
+        hs[tid] = hdiag[c0 + tid];
+        const float d = U[(c0 + tid) * n + c0 + tid];
+        uinv[tid] = (d > 0.0f) ? 1.0f / d : 0.0f;
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * 16;
+    for (int e = tid; e < 16 * 32; e += 256)
+        tabs[e] = (r0 + e / 32 < rows) ? tab[(r0 + e / 32) * 32 + (e & 31)] : 1.0f;
     __syncthreads();
     const int k = tid & 15;
-    const int64_t r = (int64_t)blockIdx.x * 16 + (tid >> 4);
+    const int64_t r = r0 + (tid >> 4);
     if (r >= rows) return;
 
     float w[G][2];
@@ -174,62 +268,16 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
         w[g][0] = dead[c] ? 0.0f : v.x;
         w[g][1] = dead[c + 1] ? 0.0f : v.y;
     }
-    const float lo = lost[r * 2], st = lost[r * 2 + 1];
-    const float* tb = tab + r * 32;
-    const int lane = tid & 63;
-    const int base_lane = lane & ~15;
-
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float amax = group16_max(fmaxf(fabsf(w[g][0]), fabsf(w[g][1])));
-        const int nominal = nominal_rung(amax, lo, st);
-        int best = nominal;
-        if (amax > 0.0f) {
-            float best_e = INFINITY;
-            const int lo_c = nominal >= 2 ? nominal - 2 : 0;
-            const int hi_c = nominal + 1 < 31 ? nominal + 1 : 31;
-            const float h0 = hs[32 * g + 2 * k], h1 = hs[32 * g + 2 * k + 1];
-            for (int cand = lo_c; cand <= hi_c; ++cand) {
-                const float s_c = tb[cand];
-                if (s_c <= 0.0f) continue;
-                const float err = group16_sum(pair_err(w[g][0], w[g][1], h0, h1, s_c));
-                if (err < best_e) {
-                    best_e = err;
-                    best = cand;
-                }
-            }
-        }
-        const float s = tb[best];
-        if (k == 0) {
-            const int64_t gi = r * (n / 32) + (c0 / 32) + g;
-            rung[gi] = (uint8_t)best;
-            scale[gi] = s;
-        }
-        uint32_t byte = 0u;
-#pragma unroll
-        for (int jj = 0; jj < 32; ++jj) {
-            const int owner = jj >> 1, slot = jj & 1;
-            const float wj = __shfl(w[g][slot], base_lane + owner, 64);
-            const float q = (s > 0.0f) ? fminf(fmaxf(rintf(wj / s), -8.0f), 7.0f) : 0.0f;
-            const int col = 32 * g + jj;
-            const float ujj = Us[col * ULD + col];
-            const float e = (ujj > 0.0f) ? (wj - q * s) / ujj : 0.0f;
-            if (k == owner) {
-                byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
-                w[g][slot] = e;
-            }
-            // Feed e into this lane's later columns of the block.
-#pragma unroll
-            for (int g2 = g; g2 < G; ++g2) {
-                const float2 u = *reinterpret_cast<const float2*>(&Us[col * ULD + 32 * g2 + 2 * k]);
-                const int t0 = 32 * g2 + 2 * k;
-                if (t0 > col) w[g2][0] -= e * u.x;
-                if (t0 + 1 > col) w[g2][1] -= e * u.y;
-            }
-        }
-        nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
-        *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
-    }
+    BlockCtx cx;
+    cx.Us = Us;
+    cx.uinv = uinv;
+    cx.hs = hs;
+    cx.tb = &tabs[(tid >> 4) * 32];
+    cx.lo = lost[r * 2];
+    cx.st = lost[r * 2 + 1];
+    cx.k = k;
+    cx.base_lane = (tid & 63) & ~15;
+    block_group<G, 0>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
 }
 
 }  // namespace gptq
