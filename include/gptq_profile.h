@@ -6,7 +6,7 @@
  * gptq_profile_collect() waits for the recorded events and returns, per kernel family, the sum
  * of the event intervals, the launch count and the summed algorithmic flops / bytes, then
  * forgets the records.  Families (index: name):
- *   0 fold_update  trailing Cholesky update + inverse update (one GEMM launch per block step)
+ *   0 fold_update  bulk of the trailing Cholesky update + inverse update (one GEMM per step)
  *   1 fold_panel   panel solve + inverse row block (one GEMM launch per block step)
  *   2 fold_diag    diagonal block factor and inverse
  *   3 fold_build   prep, scaling and the reversed equilibrated matrix
@@ -14,6 +14,7 @@
  *   5 sweep_group  rung choice, rounding, in-group feedback
  *   6 sweep_trail  trailing E * U GEMM
  *   7 ladder
+ *   8 fold_next    look-ahead part of the update: next block column and next block row
  * The recording adds two event records per timed launch; the mask is 0 by default.
  */
 #ifndef GPTQ_MI355X_PROFILE_H

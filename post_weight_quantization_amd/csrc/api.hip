@@ -17,6 +17,8 @@ std::mutex g_mu;
 unsigned g_mask = 0u;
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
+std::mutex g_hmu;
+std::vector<Helper> g_helpers;
 
 hipEvent_t take_event() {
     if (!g_pool.empty()) {
@@ -29,6 +31,33 @@ hipEvent_t take_event() {
     return e;
 }
 }  // namespace
+
+int helper_acquire(Helper* h) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GPTQ_EHIP;
+    {
+        std::lock_guard<std::mutex> lk(g_hmu);
+        for (size_t i = 0; i < g_helpers.size(); ++i)
+            if (g_helpers[i].device == dev) {
+                *h = g_helpers[i];
+                g_helpers.erase(g_helpers.begin() + (long)i);
+                return GPTQ_OK;
+            }
+    }
+    Helper n{};
+    n.device = dev;
+    if (hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking) != hipSuccess) return GPTQ_EHIP;
+    if (hipEventCreateWithFlags(&n.ev_a, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.ev_b, hipEventDisableTiming) != hipSuccess)
+        return GPTQ_EHIP;
+    *h = n;
+    return GPTQ_OK;
+}
+
+void helper_release(const Helper& h) {
+    std::lock_guard<std::mutex> lk(g_hmu);
+    g_helpers.push_back(h);
+}
 
 ProfScope::ProfScope(int fam_, hipStream_t s_, double flops_, double bytes_)
     : fam(fam_), s(s_), flops(flops_), bytes(bytes_), on(false), rec(nullptr) {
@@ -110,6 +139,7 @@ extern "C" int gptq_profile_family_count(void) { return FAM_COUNT; }
 
 extern "C" const char* gptq_profile_family_name(int fam) {
     static const char* names[FAM_COUNT] = {"fold_update", "fold_panel", "fold_diag", "fold_build",
-                                           "fold_make_u", "sweep_group", "sweep_trail", "ladder"};
+                                           "fold_make_u", "sweep_group", "sweep_trail", "ladder",
+                                           "fold_next"};
     return (fam >= 0 && fam < FAM_COUNT) ? names[fam] : "?";
 }

@@ -24,8 +24,19 @@ enum Family {
     FAM_SWEEP_GROUP = 5,  // rung choice + rounding + in-block feedback
     FAM_SWEEP_TRAIL = 6,  // trailing E * U GEMM
     FAM_LADDER = 7,
-    FAM_COUNT = 8
+    FAM_FOLD_NEXT = 8,    // look-ahead update of the next block column / block row
+    FAM_COUNT = 9
 };
+
+// A helper stream (non-blocking, default priority) with two events, taken from a per-process
+// pool for the duration of one call so that independent calls never share one.
+struct Helper {
+    hipStream_t stream;
+    hipEvent_t ev_a, ev_b;
+    int device;
+};
+int helper_acquire(Helper* h);   // GPTQ_OK or GPTQ_EHIP
+void helper_release(const Helper& h);
 
 // Records an event pair around one launch when profiling is on; no-op otherwise.
 struct ProfScope {

@@ -17,9 +17,12 @@
 // Blocked right-looking Cholesky fused with the blocked right-looking inverse, per step k:
 //   diag   : L_kk = chol(A_kk), MI_k = L_kk^-1 (one workgroup, LDS resident)
 //   panel  : L_ik = A_ik MI_k^T for the rows below;  X_k,<k = MI_k X_k,<k     (one GEMM launch)
-//   update : A_ij -= L_ik L_jk^T (lower tiles);      X_i,<=k -= L_ik X_k,<=k   (one GEMM launch)
+//   update : A_ij -= L_ik L_jk^T (lower tiles);      X_i,<=k -= L_ik X_k,<=k
 // The pages factor and invert in two separate passes; both are right-looking and the inverse
-// of step k only needs L's column block k, so one pass does both.
+// of step k only needs L's column block k, so one pass does both.  The update is split with a
+// look-ahead of one step: its next block column / block row (needed by step k+1's diag and
+// panel) runs on the caller's stream, and the bulk runs on a helper stream, overlapping the
+// serial diag / panel chain of the next step.
 #include <math.h>
 
 #include "common.hpp"
@@ -351,6 +354,14 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
     }
     GPTQ_HIP(hipGetLastError());
 
+    Helper hp{};
+    if (helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
+    hipStream_t ts = hp.stream;
+    struct Release {
+        const Helper& h;
+        ~Release() { helper_release(h); }
+    } release{hp};
+
     double lam = (lambda > 0.0) ? lambda : 0.0;
     int attempts = 0;
     FoldState host{};
@@ -365,6 +376,10 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 H, ldh, dinv, dead, state, lam, A, n, np);
         }
         GPTQ_HIP(hipGetLastError());
+        // Step k on the caller's stream st: diag(k), panel(k), then -- once the helper stream has
+        // finished the bulk of step k-1 -- the look-ahead part of step k's update (block column
+        // k+1 of A, block row k+1 of X).  The bulk of step k (everything else) runs on the
+        // helper stream ts as soon as panel(k) is done, overlapping diag(k+1) and panel(k+1).
         for (int64_t k = 0; k < L.nbk; ++k) {
             const int64_t kb = k * NB;
             const int64_t rest = np - kb - NB;
@@ -384,24 +399,51 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * NB * ((double)rest + kb), 0.0);
                 gemm_kernel<1, true, false, false><<<pb.total, G_THREADS, 0, st>>>(pb, &state->flag);
             }
-            if (rest > 0) {
-                // Update: A_ij -= L_ik L_jk^T (lower tiles); X_i,<=k -= L_ik X_k,<=k, where the
-                // block column k of X is written for the first time (no C read).
-                const float* P = A + (kb + NB) * np + kb;
-                const GemmProblem sy = gemm_syrk_lower(P, np, A + (kb + NB) * np + kb + NB,
-                                                       A + (kb + NB) * np + kb + NB, np, (int)rest,
-                                                       NB, -1.0f, 1);
-                GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + NB) * np,
-                                           X + (kb + NB) * np, np, (int)rest, (int)(kb + NB), NB,
-                                           -1.0f, 1);
+            GPTQ_HIP(hipGetLastError());
+            if (rest <= 0) continue;
+            const float* P = A + (kb + NB) * np + kb;  // L's column block k below the diagonal
+            // Bulk: A_ij -= L_ik L_jk^T for block columns >= k+2; X_i,<=k -= L_ik X_k,<=k for
+            // block rows >= k+2.  Block column k of X is written there for the first time.
+            const int64_t rest2 = rest - NB;
+            if (rest2 > 0) {
+                GPTQ_HIP(hipEventRecord(hp.ev_a, st));
+                GPTQ_HIP(hipStreamWaitEvent(ts, hp.ev_a, 0));
+                const GemmProblem sy = gemm_syrk_lower(P + NB * np, np, A + (kb + 2 * NB) * np + kb + 2 * NB,
+                                                       A + (kb + 2 * NB) * np + kb + 2 * NB, np,
+                                                       (int)rest2, NB, -1.0f, 1);
+                GemmProblem xu = gemm_full(P + NB * np, np, X + kb * np, np, X + (kb + 2 * NB) * np,
+                                           X + (kb + 2 * NB) * np, np, (int)rest2, (int)(kb + NB),
+                                           NB, -1.0f, 1);
                 xu.beta0_from_tn = (int)k;
                 const GemmBatch ub = gemm_batch(sy, &xu);
-                const double fl = (double)NB * rest * (rest + 1) + 2.0 * NB * rest * (kb + NB);
-                ProfScope ps(FAM_FOLD_UPDATE, st, fl, 0.0);
-                gemm_kernel<0, true, false, false><<<ub.total, G_THREADS, 0, st>>>(ub, &state->flag);
+                const double fl = (double)NB * rest2 * (rest2 + 1) + 2.0 * NB * rest2 * (kb + NB);
+                {
+                    ProfScope ps(FAM_FOLD_UPDATE, ts, fl, 0.0);
+                    gemm_kernel<0, true, false, false><<<ub.total, G_THREADS, 0, ts>>>(ub, &state->flag);
+                }
+                GPTQ_HIP(hipGetLastError());
+            }
+            // Look-ahead: block column k+1 of A (rows >= k+1, diagonal tile lower only) and block
+            // row k+1 of X; they need the bulk of step k-1 (the latest record of ev_b).
+            if (k > 0) GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
+            GemmProblem strip = gemm_full(P, np, P, np, A + (kb + NB) * np + kb + NB,
+                                          A + (kb + NB) * np + kb + NB, np, (int)rest, NB, NB,
+                                          -1.0f, 1);
+            strip.mask_diag = 1;
+            GemmProblem xr = gemm_full(P, np, X + kb * np, np, X + (kb + NB) * np, X + (kb + NB) * np,
+                                       np, NB, (int)(kb + NB), NB, -1.0f, 1);
+            xr.beta0_from_tn = (int)k;
+            const GemmBatch nb_ = gemm_batch(strip, &xr);
+            {
+                ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * NB * NB * ((double)rest + kb + NB), 0.0);
+                gemm_kernel<3, true, false, false><<<nb_.total, G_THREADS, 0, st>>>(nb_, &state->flag);
             }
             GPTQ_HIP(hipGetLastError());
+            if (rest2 > 0) GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
         }
+        // Join the helper stream, then read the pivot flag.
+        GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
+        GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
         GPTQ_HIP(hipMemcpyAsync(&host, state, sizeof(FoldState), hipMemcpyDeviceToHost, st));
         GPTQ_HIP(hipStreamSynchronize(st));
         if (host.flag == 0u) break;

@@ -40,6 +40,7 @@ struct GemmProblem {
     int64_t lda, ldb, ldc;
     int M, N, K;          // K % 32 == 0; N % 4 == 0 for the N layout
     int lower;            // 1: square tile grid, only tiles tn <= tm; diagonal tiles store i >= j
+    int mask_diag;        // 1: tiles with tm == tn store only i >= j (set whenever lower is)
     int tiles_n;          // tile columns (full grid) or tile rows = cols (lower)
     int ntiles;
     float alpha;
@@ -161,7 +162,7 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
 
     // The C tile, fetched now and consumed after the K loop.
     const bool use_c = P.beta && tn < P.beta0_from_tn;
-    const bool diag_tile = P.lower && tm == tn;
+    const bool diag_tile = P.mask_diag && tm == tn;
     float cv[2][2][16];
     if (use_c) {
 #pragma unroll
@@ -275,6 +276,7 @@ inline GemmProblem gemm_full(const float* A, int64_t lda, const float* B, int64_
     p.lda = lda; p.ldb = ldb; p.ldc = ldc;
     p.M = M; p.N = N; p.K = K;
     p.lower = 0;
+    p.mask_diag = 0;
     p.tiles_n = (N + GT_N - 1) / GT_N;
     p.ntiles = ((M + GT_M - 1) / GT_M) * p.tiles_n;
     p.alpha = alpha; p.beta = beta; p.beta0_from_tn = p.tiles_n;
@@ -288,6 +290,7 @@ inline GemmProblem gemm_syrk_lower(const float* A, int64_t lda, const float* Cin
     GemmProblem p = gemm_full(A, lda, A, lda, Cin, Cout, ldc, M, M, K, alpha, beta);
     const int T = (M + GT_M - 1) / GT_M;
     p.lower = 1;
+    p.mask_diag = 1;
     p.tiles_n = T;
     p.ntiles = M > 0 ? T * (T + 1) / 2 : 0;
     p.beta0_from_tn = T;
