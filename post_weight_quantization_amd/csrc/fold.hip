@@ -134,7 +134,8 @@ __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict
 //           32 x 32 x 32 product on v_mfma_f32_32x32x2_f32;
 // then the off-diagonal blocks of L^-1 by block forward substitution down each block column,
 //   M_IJ = -T_I sum_{J <= Q < I} L_IQ M_QJ   (waves 0..2 take block columns 0..2).
-// A pivot that is not > 0 (or NaN) sets the flag and is replaced by 1.
+// A pivot that is not above its own f32 rounding bound (in particular one that is not > 0, or
+// NaN) sets the flag and is replaced by 1.
 constexpr int DLD = NB + 1;  // row stride of the block in LDS (odd: column reads spread banks)
 constexpr int SLD = 33;      // row stride of 32 x 32 blocks in LDS
 
@@ -195,7 +196,11 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
 #pragma unroll
             for (int c = 0; c < 32; ++c) {
                 float pv = lane_bcast(a[c], c);
-                const bool b = !(pv > 0.0f);
+                // Pivot test at f32 resolution: the computed Schur complement of a unit-diagonal
+                // matrix is exact only up to (i + 1) 2^-24 for pivot index i, so a pivot at or
+                // below that bound is not known to be positive.
+                const float tau = (float)(kb + c0 + c + 1) * 5.9604645e-8f;
+                const bool b = !(pv > tau);
                 bad = bad || b;
                 pv = b ? 1.0f : pv;
                 const float d = sqrtf(pv);

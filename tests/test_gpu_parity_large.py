@@ -46,7 +46,7 @@ def test_ill_conditioned_retry_path(gpu):
     Hn = H.cpu().numpy()
     (U, hdiag, dead, rep), orc, err = check_fold(gpu, H, lam, H_np=Hn)
     say(f"stress: lambda_gpu={rep['lambda_used']} attempts={rep['attempts']} n_dead={rep['n_dead']}")
-    assert rep["attempts"] >= 2 and rep["lambda_used"] > lam
+    assert rep["attempts"] >= 2 and rep["lambda_used"] > lam, rep
     assert rep["n_dead"] == 164
     # The f64 oracle's own schedule from the same start ends no later than the f32 one.
     free = oracle.fold(Hn, lam)
