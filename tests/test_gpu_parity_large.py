@@ -53,8 +53,16 @@ def test_ill_conditioned_retry_path(gpu):
     say(f"stress: lambda_oracle={free['lam']} attempts={free['attempts']}")
     assert free["lam"] <= rep["lambda_used"]
     sel = _rows(W.shape[0], 128, 1)
-    st, _ = check_sweep_isolated(gpu, W, U, hdiag, dead, rows_sel=sel)
+    st, (nib, rung, scale, E, lost, tab) = check_sweep_isolated(gpu, W, U, hdiag, dead, rows_sel=sel)
     assert_sweep_bar(st)
+    # End to end on the sampled rows: the oracle at its own (smaller) damping.
+    Wn = W.cpu().numpy()
+    lo, tb = oracle.ladder(Wn[sel], free["dead"])
+    os_ = oracle.sweep(Wn[sel], free["U"], free["hdiag"], free["dead"], tb, lo, want_E=False)
+    t_orc = oracle.output_error(Wn[sel], free["dead"], os_["code"], os_["scale"], Hn)
+    t_gpu = output_error(Wn[sel], free["dead"], nib.cpu().numpy()[sel], scale.cpu().numpy()[sel], Hn)
+    say(f"stress: tr(dW H dW^T) gpu={t_gpu:.6e} oracle={t_orc:.6e} rel={(t_gpu - t_orc) / t_orc:.2e}")
+    assert abs(t_gpu - t_orc) <= OUT_ERR_TOL * t_orc
 
 
 def test_down_proj_full_size_sampled(gpu):
