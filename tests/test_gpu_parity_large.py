@@ -55,14 +55,21 @@ def test_ill_conditioned_retry_path(gpu):
     sel = _rows(W.shape[0], 128, 1)
     st, (nib, rung, scale, E, lost, tab) = check_sweep_isolated(gpu, W, U, hdiag, dead, rows_sel=sel)
     assert_sweep_bar(st)
-    # End to end on the sampled rows: the oracle at its own (smaller) damping.
+    # End to end on the sampled rows.  The f32 factor needs more damping than the f64 one here,
+    # so the two-sided 1% bar is taken against the oracle at the GPU's damping, and against the
+    # free-running oracle (its own, smaller damping) the GPU must not be worse by more than 1%.
     Wn = W.cpu().numpy()
-    lo, tb = oracle.ladder(Wn[sel], free["dead"])
-    os_ = oracle.sweep(Wn[sel], free["U"], free["hdiag"], free["dead"], tb, lo, want_E=False)
-    t_orc = oracle.output_error(Wn[sel], free["dead"], os_["code"], os_["scale"], Hn)
     t_gpu = output_error(Wn[sel], free["dead"], nib.cpu().numpy()[sel], scale.cpu().numpy()[sel], Hn)
-    say(f"stress: tr(dW H dW^T) gpu={t_gpu:.6e} oracle={t_orc:.6e} rel={(t_gpu - t_orc) / t_orc:.2e}")
-    assert abs(t_gpu - t_orc) <= OUT_ERR_TOL * t_orc
+    for tag, f in (("oracle at lambda_gpu", orc), ("free-running oracle", free)):
+        lo, tb = oracle.ladder(Wn[sel], f["dead"])
+        os_ = oracle.sweep(Wn[sel], f["U"], f["hdiag"], f["dead"], tb, lo, want_E=False)
+        t_orc = oracle.output_error(Wn[sel], f["dead"], os_["code"], os_["scale"], Hn)
+        rel = (t_gpu - t_orc) / t_orc
+        say(f"stress: tr(dW H dW^T) gpu={t_gpu:.6e} {tag}={t_orc:.6e} rel={rel:.2e}")
+        if f is orc:
+            assert abs(rel) <= OUT_ERR_TOL
+        else:
+            assert rel <= OUT_ERR_TOL
 
 
 def test_down_proj_full_size_sampled(gpu):
