@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one plain 1 GiB device copy first (a known-size reference for "
+                         "hardware traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -102,6 +105,14 @@ def main():
     H, W, lam = workloads.make(args.workload, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written")
+        del src, dst
 
     U = torch.empty(n, n, dtype=torch.float32, device=dev)
     hdiag = torch.empty(n, dtype=torch.float32, device=dev)
