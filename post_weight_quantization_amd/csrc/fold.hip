@@ -25,6 +25,8 @@
 // serial diag / panel chain of the next step.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "gemm_mfma.hpp"
 
@@ -308,23 +310,50 @@ __global__ __launch_bounds__(256) void fold_identity_kernel(float* __restrict__ 
     }
 }
 
+// Outer panel width (columns per bulk trailing update, its K) for a padded size n_p.
+static int64_t outer_width(int64_t np) { return np >= 2048 ? 4 * NB : (np >= 512 ? 2 * NB : NB); }
+
 struct FoldLayout {
-    int64_t np, nbk;
-    size_t off_state, off_dinv, off_mi, off_a, off_x, total;
+    int64_t np, nbk, nb2;
+    size_t off_state, off_dinv, off_mi, off_t, off_xt, off_a, off_x, total;
 };
 
 static FoldLayout fold_layout(int64_t n) {
     FoldLayout L{};
     L.np = round_up(n, NB);
     L.nbk = L.np / NB;
+    L.nb2 = outer_width(L.np);
     size_t o = 0;
     L.off_state = o; o += align256(sizeof(FoldState));
     L.off_dinv = o; o += align256(sizeof(float) * (size_t)L.np);
     L.off_mi = o; o += align256(sizeof(float) * (size_t)(L.nbk * NB * NB));
+    L.off_t = o; o += align256(sizeof(float) * (size_t)(NB * L.nb2));
+    L.off_xt = o; o += align256(sizeof(float) * (size_t)(L.nb2 * L.np));
     L.off_a = o; o += align256(sizeof(float) * (size_t)(L.np * L.np));
     L.off_x = o; o += align256(sizeof(float) * (size_t)(L.np * L.np));
     L.total = o;
     return L;
+}
+
+// Zero the strictly upper 128-blocks of X's w x w diagonal block at kb, and copy the rows
+// multiplied out of place back into X (both small, on the critical stream).
+__global__ __launch_bounds__(256) void fold_zero_upper_kernel(float* __restrict__ X, int64_t np,
+                                                              int64_t kb, int64_t w) {
+    const int64_t r = blockIdx.y;                // row within the block
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= w) return;
+    if ((c / NB) > (r / NB)) X[(kb + r) * np + kb + c] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void fold_copy_rows_kernel(const float* __restrict__ src,
+                                                             float* __restrict__ dst, int64_t ld,
+                                                             int64_t cols) {
+    const int64_t r = blockIdx.y;
+    for (int64_t c = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4; c < cols;
+         c += (int64_t)gridDim.x * 1024) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + r * ld + c);
+        *reinterpret_cast<f32x4*>(dst + r * ld + c) = v;
+    }
 }
 
 }  // namespace gptq
@@ -350,6 +379,8 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
     float* MI = (float*)(ws + L.off_mi);
     float* A = (float*)(ws + L.off_a);
     float* X = (float*)(ws + L.off_x);
+    float* Tb = (float*)(ws + L.off_t);
+    float* Xt = (float*)(ws + L.off_xt);
     const int64_t np = L.np;
     const double n3 = (double)n * n * n;
 
@@ -381,70 +412,132 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 H, ldh, dinv, dead, state, lam, A, n, np);
         }
         GPTQ_HIP(hipGetLastError());
-        // Step k on the caller's stream st: diag(k), panel(k), then -- once the helper stream has
-        // finished the bulk of step k-1 -- the look-ahead part of step k's update (block column
-        // k+1 of A, block row k+1 of X).  The bulk of step k (everything else) runs on the
-        // helper stream ts as soon as panel(k) is done, overlapping diag(k+1) and panel(k+1).
-        for (int64_t k = 0; k < L.nbk; ++k) {
-            const int64_t kb = k * NB;
-            const int64_t rest = np - kb - NB;
-            {
-                ProfScope ps(FAM_FOLD_DIAG, st, 2.0 * NB * NB * NB / 3.0, 0.0);
-                fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)k, &state->flag);
+        // Outer panels of width w (the K of the bulk update); inside a panel, 128-wide steps
+        // factor the diagonal block, solve the rows below and update the rest of the panel.
+        // The caller's stream st carries the serial chain; the bulk trailing update of a panel
+        // runs on the helper stream ts and overlaps the next panel's chain (look-ahead of one
+        // panel: the next panel's columns are updated first, on st).
+        bool first_bulk = true;
+        for (int64_t kb = 0; kb < np; kb += L.nb2) {
+            const int64_t w = std::min<int64_t>(L.nb2, np - kb);
+            const int64_t R = w / NB;
+            for (int64_t r = 0; r < R; ++r) {
+                const int64_t cb = kb + r * NB;
+                const int64_t rest_c = np - cb - NB;
+                {
+                    ProfScope ps(FAM_FOLD_DIAG, st, 2.0 * NB * NB * NB / 3.0, 0.0);
+                    fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)(cb / NB), &state->flag);
+                }
+                if (rest_c <= 0) continue;
+                const float* mic = MI + (cb / NB) * NB * NB;
+                // L_ic = A_ic MI_c^T for every row below (in place, whole tiles per workgroup).
+                const GemmProblem pa = gemm_full(A + (cb + NB) * np + cb, np, mic, NB, nullptr,
+                                                 A + (cb + NB) * np + cb, np, (int)rest_c, NB, NB,
+                                                 1.0f, 0);
+                const GemmBatch pb = gemm_batch(pa, nullptr);
+                {
+                    ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * NB * (double)rest_c, 0.0);
+                    gemm_kernel<1, true, false, false><<<pb.total, G_THREADS, 0, st>>>(pb, &state->flag);
+                }
+                // The rest of the panel's columns: A[cb+128:, cb+128:kb+w] -= L_ic L_jc^T.
+                const int64_t ncol = kb + w - cb - NB;
+                if (ncol > 0) {
+                    GemmProblem iu = gemm_full(A + (cb + NB) * np + cb, np, A + (cb + NB) * np + cb,
+                                               np, A + (cb + NB) * np + cb + NB,
+                                               A + (cb + NB) * np + cb + NB, np, (int)rest_c,
+                                               (int)ncol, NB, -1.0f, 1);
+                    iu.mask_diag = 1;
+                    iu.skip_upper = 1;
+                    const GemmBatch ib = gemm_batch(iu, nullptr);
+                    ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * NB * (double)rest_c * ncol, 0.0);
+                    gemm_kernel<4, true, true, false><<<ib.total, G_THREADS, 0, st>>>(ib, &state->flag);
+                }
+                GPTQ_HIP(hipGetLastError());
             }
-            const float* mik = MI + k * NB * NB;
-            // Panel: L_ik = A_ik MI_k^T below the block; X_k,<k = MI_k X_k,<k (both in place:
-            // every workgroup reads its whole tile before writing it).
-            const GemmProblem pa = gemm_full(A + (kb + NB) * np + kb, np, mik, NB, nullptr,
-                                             A + (kb + NB) * np + kb, np, (int)rest, NB, NB, 1.0f, 0);
-            const GemmProblem pxr = gemm_full(mik, NB, X + kb * np, np, nullptr, X + kb * np, np, NB,
-                                              (int)kb, NB, 1.0f, 0);
-            const GemmBatch pb = gemm_batch(pa, &pxr);
-            if (pb.total > 0) {
-                ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * NB * ((double)rest + kb), 0.0);
-                gemm_kernel<1, true, false, false><<<pb.total, G_THREADS, 0, st>>>(pb, &state->flag);
+            // Inverse of the panel's w x w diagonal block of L, into X[kb:kb+w, kb:kb+w]: the
+            // 128-blocks on the diagonal are the MI_c written by the diagonal kernel; block row I
+            // is -MI_I (L[I, <I] X[<I, <I]) (block forward substitution).
+            if (R > 1) {
+                fold_zero_upper_kernel<<<dim3((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, st>>>(
+                    X, np, kb, w);
+                for (int64_t I = 1; I < R; ++I) {
+                    const int64_t ci = kb + I * NB;
+                    const GemmBatch t1 = gemm_batch(
+                        gemm_full(A + ci * np + kb, np, X + kb * np + kb, np, nullptr, Tb, w, NB,
+                                  (int)(I * NB), (int)(I * NB), 1.0f, 0),
+                        nullptr);
+                    const GemmBatch t2 = gemm_batch(
+                        gemm_full(MI + (ci / NB) * NB * NB, NB, Tb, w, nullptr, X + ci * np + kb, np,
+                                  NB, (int)(I * NB), NB, -1.0f, 0),
+                        nullptr);
+                    ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * (double)(I * NB) * (I * NB + NB), 0.0);
+                    gemm_kernel<5, false, false, false><<<t1.total, G_THREADS, 0, st>>>(t1, &state->flag);
+                    gemm_kernel<5, false, false, false><<<t2.total, G_THREADS, 0, st>>>(t2, &state->flag);
+                }
+                GPTQ_HIP(hipGetLastError());
             }
-            GPTQ_HIP(hipGetLastError());
+            // Rows of X in this panel: X[kb:kb+w, 0:kb] = Minv_w X[kb:kb+w, 0:kb] (out of place,
+            // then copied back: a workgroup tile spans only 128 of the w rows it reads).
+            if (kb > 0) {
+                const GemmBatch xb = gemm_batch(
+                    gemm_full(X + kb * np + kb, np, X + kb * np, np, nullptr, Xt, np, (int)w, (int)kb,
+                              (int)w, 1.0f, 0),
+                    nullptr);
+                {
+                    ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * (double)w * w * kb, 0.0);
+                    gemm_kernel<1, false, false, false><<<xb.total, G_THREADS, 0, st>>>(xb, &state->flag);
+                }
+                fold_copy_rows_kernel<<<dim3((unsigned)((kb + 1023) / 1024), (unsigned)w), 256, 0, st>>>(
+                    Xt, X + kb * np, np, kb);
+                GPTQ_HIP(hipGetLastError());
+            }
+            const int64_t rest = np - kb - w;
             if (rest <= 0) continue;
-            const float* P = A + (kb + NB) * np + kb;  // L's column block k below the diagonal
-            // Bulk: A_ij -= L_ik L_jk^T for block columns >= k+2; X_i,<=k -= L_ik X_k,<=k for
-            // block rows >= k+2.  Block column k of X is written there for the first time.
-            const int64_t rest2 = rest - NB;
+            const float* P = A + (kb + w) * np + kb;  // the panel's rows below its diagonal block
+            const int64_t nw = std::min<int64_t>(L.nb2, rest);  // width of the next panel
+            const int64_t rest2 = rest - nw;
+            // Bulk: A_ij -= P_i P_j^T beyond the next panel, X_i,<kb+w -= P_i X[kb:kb+w, <kb+w]
+            // for the rows beyond the next panel; X's columns kb..kb+w-1 are written there first.
             if (rest2 > 0) {
                 GPTQ_HIP(hipEventRecord(hp.ev_a, st));
                 GPTQ_HIP(hipStreamWaitEvent(ts, hp.ev_a, 0));
-                const GemmProblem sy = gemm_syrk_lower(P + NB * np, np, A + (kb + 2 * NB) * np + kb + 2 * NB,
-                                                       A + (kb + 2 * NB) * np + kb + 2 * NB, np,
-                                                       (int)rest2, NB, -1.0f, 1);
-                GemmProblem xu = gemm_full(P + NB * np, np, X + kb * np, np, X + (kb + 2 * NB) * np,
-                                           X + (kb + 2 * NB) * np, np, (int)rest2, (int)(kb + NB),
-                                           NB, -1.0f, 1);
-                xu.beta0_from_tn = (int)k;
+                const GemmProblem sy = gemm_syrk_lower(P + nw * np, np,
+                                                       A + (kb + w + nw) * np + kb + w + nw,
+                                                       A + (kb + w + nw) * np + kb + w + nw, np,
+                                                       (int)rest2, (int)w, -1.0f, 1);
+                GemmProblem xu = gemm_full(P + nw * np, np, X + kb * np, np, X + (kb + w + nw) * np,
+                                           X + (kb + w + nw) * np, np, (int)rest2, (int)(kb + w),
+                                           (int)w, -1.0f, 1);
+                xu.beta0_from_tn = (int)(kb / NB);
                 const GemmBatch ub = gemm_batch(sy, &xu);
-                const double fl = (double)NB * rest2 * (rest2 + 1) + 2.0 * NB * rest2 * (kb + NB);
+                const double fl = (double)w * rest2 * (rest2 + 1) + 2.0 * w * rest2 * (kb + w);
                 {
                     ProfScope ps(FAM_FOLD_UPDATE, ts, fl, 0.0);
                     gemm_kernel<0, true, false, false><<<ub.total, G_THREADS, 0, ts>>>(ub, &state->flag);
                 }
                 GPTQ_HIP(hipGetLastError());
             }
-            // Look-ahead: block column k+1 of A (rows >= k+1, diagonal tile lower only) and block
-            // row k+1 of X; they need the bulk of step k-1 (the latest record of ev_b).
-            if (k > 0) GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
-            GemmProblem strip = gemm_full(P, np, P, np, A + (kb + NB) * np + kb + NB,
-                                          A + (kb + NB) * np + kb + NB, np, (int)rest, NB, NB,
-                                          -1.0f, 1);
+            // Look-ahead: the next panel's columns (rows below kb+w, diagonal tiles lower only)
+            // and X's rows of the next panel; they need the previous panel's bulk update.
+            if (!first_bulk) GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
+            GemmProblem strip = gemm_full(P, np, P, np, A + (kb + w) * np + kb + w,
+                                          A + (kb + w) * np + kb + w, np, (int)rest, (int)nw,
+                                          (int)w, -1.0f, 1);
             strip.mask_diag = 1;
-            GemmProblem xr = gemm_full(P, np, X + kb * np, np, X + (kb + NB) * np, X + (kb + NB) * np,
-                                       np, NB, (int)(kb + NB), NB, -1.0f, 1);
-            xr.beta0_from_tn = (int)k;
+            strip.skip_upper = 1;
+            GemmProblem xr = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np, X + (kb + w) * np,
+                                       np, (int)nw, (int)(kb + w), (int)w, -1.0f, 1);
+            xr.beta0_from_tn = (int)(kb / NB);
             const GemmBatch nb_ = gemm_batch(strip, &xr);
             {
-                ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * NB * NB * ((double)rest + kb + NB), 0.0);
+                ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * w * ((double)rest * nw + (double)nw * (kb + w)), 0.0);
                 gemm_kernel<3, true, false, false><<<nb_.total, G_THREADS, 0, st>>>(nb_, &state->flag);
             }
             GPTQ_HIP(hipGetLastError());
-            if (rest2 > 0) GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
+            if (rest2 > 0) {
+                GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
+                first_bulk = false;
+            }
         }
         // Join the helper stream, then read the pivot flag.
         GPTQ_HIP(hipEventRecord(hp.ev_b, ts));

@@ -41,6 +41,7 @@ struct GemmProblem {
     int M, N, K;          // K % 32 == 0; N % 4 == 0 for the N layout
     int lower;            // 1: square tile grid, only tiles tn <= tm; diagonal tiles store i >= j
     int mask_diag;        // 1: tiles with tm == tn store only i >= j (set whenever lower is)
+    int skip_upper;       // 1: tiles with tn > tm do nothing (full grid over a lower-triangular C)
     int tiles_n;          // tile columns (full grid) or tile rows = cols (lower)
     int ntiles;
     float alpha;
@@ -258,11 +259,13 @@ __global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmBatch batch, const 
     if (t < batch.p[0].ntiles) {
         int tm, tn;
         tile_of(batch.p[0], t, tm, tn);
+        if (batch.p[0].skip_upper && tn > tm) return;
         gemm_tile<TB0, CHK>(batch.p[0], tm, tn, As, Bs);
     } else {
         t -= batch.p[0].ntiles;
         int tm, tn;
         tile_of(batch.p[1], t, tm, tn);
+        if (batch.p[1].skip_upper && tn > tm) return;
         gemm_tile<TB1, CHK>(batch.p[1], tm, tn, As, Bs);
     }
 }
@@ -277,6 +280,7 @@ inline GemmProblem gemm_full(const float* A, int64_t lda, const float* B, int64_
     p.M = M; p.N = N; p.K = K;
     p.lower = 0;
     p.mask_diag = 0;
+    p.skip_upper = 0;
     p.tiles_n = (N + GT_N - 1) / GT_N;
     p.ntiles = ((M + GT_M - 1) / GT_M) * p.tiles_n;
     p.alpha = alpha; p.beta = beta; p.beta0_from_tn = p.tiles_n;
