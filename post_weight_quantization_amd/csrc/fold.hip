@@ -176,10 +176,10 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
                                                         float* __restrict__ MI, int64_t np, int k,
                                                         unsigned* flag) {
     if (__atomic_load_n(flag, __ATOMIC_RELAXED)) return;
+    // 81 KB of LDS, so that the kernel fits on a CU beside one GEMM workgroup.  The off-diagonal
+    // 32-blocks M_IJ (I > J) of L^-1 live in the unused upper triangle of Ls, at block (J, I).
     __shared__ float Ls[NB * DLD];        // the block, L in place (lower)
     __shared__ float Ts[4][32 * SLD];     // T_p = inverse of L's diagonal 32-blocks
-    __shared__ float Mo[6][32 * SLD];     // off-diagonal 32-blocks of L^-1, index (I,J)
-    __shared__ float Sc[3][32 * SLD];     // per-wave scratch
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31;
     const int64_t kb = (int64_t)k * NB;
     for (int e = tid; e < NB * NB; e += 256) {
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
         const int c0 = 32 * p;
         if (wave == 0) {
             // Factor: lane r (and r + 32) holds row r of the 32 x 32 block.
-            float a[32];
+            float a[32], invd[32];
 #pragma unroll
             for (int c = 0; c < 32; ++c) a[c] = Ls[(c0 + l32) * DLD + c0 + c];
 #pragma unroll
@@ -205,8 +205,9 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
                 const bool b = !(pv > tau);
                 bad = bad || b;
                 pv = b ? 1.0f : pv;
-                const float d = sqrtf(pv);
-                const float l = (l32 == c) ? d : a[c] / d;
+                const float r = rsqrtf(pv);  // 1 / L_cc
+                invd[c] = r;
+                const float l = (l32 == c) ? pv * r : a[c] * r;
                 a[c] = l;
 #pragma unroll
                 for (int s2 = c + 1; s2 < 32; ++s2) a[s2] -= l * lane_bcast(l, s2);
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
             for (int q = 0; q < 32; ++q) t[q] = (q == l32) ? 1.0f : 0.0f;
 #pragma unroll
             for (int q = 0; q < 32; ++q) {
-                t[q] = t[q] / lane_bcast(a[q], q);
+                t[q] *= invd[q];
 #pragma unroll
                 for (int r = q + 1; r < 32; ++r) t[r] -= lane_bcast(a[q], r) * t[q];
             }
@@ -250,25 +251,32 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
             }
         __syncthreads();
     }
-    // Off-diagonal blocks of L^-1, block column J = wave.
+    // Off-diagonal blocks of L^-1, block column J = wave: M_IJ = -T_I sum_{J<=Q<I} L_IQ M_QJ,
+    // each kept at block (J, I) of Ls (the partial sum is staged in the same place).
     if (wave < 3) {
         const int J = wave;
-        float* sc = Sc[J];
         for (int I = J + 1; I < 4; ++I) {
             f32x16 acc = zero16();
             for (int Q = J; Q < I; ++Q) {
-                const float* m = (Q == J) ? Ts[J] : Mo[Q * (Q - 1) / 2 + J];
-                acc = mm32<false>(&Ls[32 * I * DLD + 32 * Q], DLD, m, SLD, acc);
+                const float* m = (Q == J) ? Ts[J] : &Ls[32 * J * DLD + 32 * Q];
+                const int ldm = (Q == J) ? SLD : DLD;
+                acc = mm32<false>(&Ls[32 * I * DLD + 32 * Q], DLD, m, ldm, acc);
             }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sc[mrow(v) * SLD + mcol()] = acc[v];
+            float* slot = &Ls[32 * J * DLD + 32 * I];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            f32x16 m2 = mm32<false>(Ts[I], SLD, sc, SLD, zero16());
-            float* dst = Mo[I * (I - 1) / 2 + J];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) dst[mrow(v) * SLD + mcol()] = -m2[v];
+            for (int v = 0; v < 16; ++v) slot[mrow(v) * DLD + mcol()] = acc[v];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            f32x16 m2 = mm32<false>(Ts[I], SLD, slot, DLD, zero16());
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int v = 0; v < 16; ++v) slot[mrow(v) * DLD + mcol()] = -m2[v];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
         const int I = r >> 5, J = c >> 5;
         float m = 0.0f;
         if (I == J) m = Ts[I][(r & 31) * SLD + (c & 31)];
-        else if (I > J) m = Mo[I * (I - 1) / 2 + J][(r & 31) * SLD + (c & 31)];
+        else if (I > J) m = Ls[(32 * J + (r & 31)) * DLD + 32 * I + (c & 31)];
         if (c <= r) A[(kb + r) * np + kb + c] = Ls[r * DLD + c];
         mi[e] = m;
         X[(kb + r) * np + kb + c] = m;
