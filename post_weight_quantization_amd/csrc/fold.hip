@@ -182,9 +182,20 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
     __shared__ float Ts[4][32 * SLD];     // T_p = inverse of L's diagonal 32-blocks
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31;
     const int64_t kb = (int64_t)k * NB;
-    for (int e = tid; e < NB * NB; e += 256) {
-        const int r = e / NB, c = e % NB;
-        Ls[r * DLD + c] = (c <= r) ? A[(kb + r) * np + kb + c] : 0.0f;
+    {
+        // 16 float4 per thread, all issued before any is stored (32 threads per 128-float row).
+        f32x4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = (tid >> 5) + 8 * i, c = (tid & 31) * 4;
+            v[i] = *reinterpret_cast<const f32x4*>(A + (kb + r) * np + kb + c);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = (tid >> 5) + 8 * i, c = (tid & 31) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Ls[r * DLD + c + q] = (c + q <= r) ? v[i][q] : 0.0f;
+        }
     }
     __syncthreads();
     bool bad = false;
@@ -284,16 +295,25 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
     }
     if (wave == 0 && lane == 0 && bad) atomicOr(flag, 1u);
     __syncthreads();
+    // Outputs as float4 rows: L (zeros above the diagonal; the upper triangle of A's diagonal
+    // block is never read), MI_k and X's diagonal block (both with zeros above).
     float* mi = MI + (int64_t)k * NB * NB;
-    for (int e = tid; e < NB * NB; e += 256) {
-        const int r = e / NB, c = e % NB;
-        const int I = r >> 5, J = c >> 5;
-        float m = 0.0f;
-        if (I == J) m = Ts[I][(r & 31) * SLD + (c & 31)];
-        else if (I > J) m = Ls[(32 * J + (r & 31)) * DLD + 32 * I + (c & 31)];
-        if (c <= r) A[(kb + r) * np + kb + c] = Ls[r * DLD + c];
-        mi[e] = m;
-        X[(kb + r) * np + kb + c] = m;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+        const int r = (tid >> 5) + 8 * i, c = (tid & 31) * 4;
+        f32x4 l4, m4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int cc = c + q, I = r >> 5, J = cc >> 5;
+            float m = 0.0f;
+            if (I == J) m = Ts[I][(r & 31) * SLD + (cc & 31)];
+            else if (I > J) m = Ls[(32 * J + (r & 31)) * DLD + 32 * I + (cc & 31)];
+            m4[q] = m;
+            l4[q] = (cc <= r) ? Ls[r * DLD + cc] : 0.0f;
+        }
+        *reinterpret_cast<f32x4*>(A + (kb + r) * np + kb + c) = l4;
+        *reinterpret_cast<f32x4*>(mi + r * NB + c) = m4;
+        *reinterpret_cast<f32x4*>(X + (kb + r) * np + kb + c) = m4;
     }
 }
 
