@@ -202,44 +202,58 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
     for (int p = 0; p < 4; ++p) {
         const int c0 = 32 * p;
         if (wave == 0) {
-            // Factor: lane r (and r + 32) holds row r of the 32 x 32 block.
+            // Factor: lane r (and r + 32) holds row r of the 32 x 32 block; column values are
+            // broadcast with readlane.  An opaque copy of the row index keeps comparisons against
+            // it inside the sub-panel (instead of hoisted out of the loop and spilled), and each
+            // step's updates are pinned in place so the compiler does not defer them.
+            int row = l32;
+            asm volatile("" : "+v"(row));
             float a[32], invd[32];
 #pragma unroll
-            for (int c = 0; c < 32; ++c) a[c] = Ls[(c0 + l32) * DLD + c0 + c];
+            for (int c = 0; c < 32; ++c) a[c] = Ls[(c0 + row) * DLD + c0 + c];
+            // Pivot test at f32 resolution: the computed Schur complement of a unit-diagonal
+            // matrix is exact only up to (i + 1) 2^-24 for pivot index i, so a pivot at or below
+            // that bound is not known to be positive.
+            const float tau0 = (float)(int)(kb + c0 + 1) * 5.9604645e-8f;
+            int nbad = 0;
 #pragma unroll
             for (int c = 0; c < 32; ++c) {
                 float pv = lane_bcast(a[c], c);
-                // Pivot test at f32 resolution: the computed Schur complement of a unit-diagonal
-                // matrix is exact only up to (i + 1) 2^-24 for pivot index i, so a pivot at or
-                // below that bound is not known to be positive.
-                const float tau = (float)(kb + c0 + c + 1) * 5.9604645e-8f;
+                const float tau = tau0 + (float)c * 5.9604645e-8f;
                 const bool b = !(pv > tau);
-                bad = bad || b;
+                nbad += b ? 1 : 0;
+                asm volatile("" : "+v"(nbad));
                 pv = b ? 1.0f : pv;
-                const float r = rsqrtf(pv);  // 1 / L_cc
+                const float r = __builtin_amdgcn_rsqf(pv);  // 1 / L_cc (pv is a normal float)
                 invd[c] = r;
-                const float l = (l32 == c) ? pv * r : a[c] * r;
+                // On the pivot's own lane a[c] is the pivot, so this is L_cc = sqrt(pv) there.
+                const float l = a[c] * r;
                 a[c] = l;
 #pragma unroll
                 for (int s2 = c + 1; s2 < 32; ++s2) a[s2] -= l * lane_bcast(l, s2);
+#pragma unroll
+                for (int s2 = c + 1; s2 < 32; ++s2) asm volatile("" : "+v"(a[s2]));
             }
             // Inverse, right-looking: lane c builds column c of T = L^-1.
             float t[32];
 #pragma unroll
-            for (int q = 0; q < 32; ++q) t[q] = (q == l32) ? 1.0f : 0.0f;
+            for (int q = 0; q < 32; ++q) t[q] = (q == row) ? 1.0f : 0.0f;
 #pragma unroll
             for (int q = 0; q < 32; ++q) {
                 t[q] *= invd[q];
 #pragma unroll
                 for (int r = q + 1; r < 32; ++r) t[r] -= lane_bcast(a[q], r) * t[q];
+#pragma unroll
+                for (int r = q + 1; r < 32; ++r) asm volatile("" : "+v"(t[r]));
             }
             if (lane < 32) {
 #pragma unroll
                 for (int c = 0; c < 32; ++c) {
-                    Ls[(c0 + l32) * DLD + c0 + c] = (c <= l32) ? a[c] : 0.0f;
-                    Ts[p][c * SLD + l32] = t[c];
+                    Ls[(c0 + row) * DLD + c0 + c] = (c <= row) ? a[c] : 0.0f;
+                    Ts[p][c * SLD + row] = t[c];
                 }
             }
+            bad = bad || nbad != 0;
         }
         __syncthreads();
         // Panel: rows below, L_rb = A_rb T_p^T.
