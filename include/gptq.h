@@ -20,6 +20,9 @@
  *   - Matrices are row-major f32.  Every pointer argument except `report` is DEVICE memory
  *     owned by the caller; the library allocates nothing and keeps no per-call state.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on it.
+ *     gptq_fold and gptq_sweep also run part of it on a helper stream of the library's own
+ *     (default priority, one per concurrent call) that waits on `stream` and is joined back
+ *     into it before the call returns, so `stream` orders everything the call does.
  *   - Return value: a GPTQ_* status.  On GPTQ_EINVAL or GPTQ_EWORKSPACE nothing is written.
  *   - Calls on different streams may run concurrently if their buffers are disjoint.
  */
@@ -102,7 +105,7 @@ int gptq_ladder(const float* W, const uint8_t* dead, int64_t rows, int64_t n, fl
                 float* tab, void* stream);
 
 /* Bytes of device workspace gptq_sweep needs: the corrected working copy of W (rows x n f32)
- * plus one block of residuals (rows x 128 f32). */
+ * plus two panel buffers of residuals (rows x 512 f32 each). */
 size_t gptq_sweep_workspace_size(int64_t rows, int64_t n);
 
 /*
@@ -122,8 +125,9 @@ size_t gptq_sweep_workspace_size(int64_t rows, int64_t n);
  * its absmax, best of nominal-2 .. nominal+1 by the H_ii-weighted error of round-to-nearest-
  * even codes, strict improvement, lowest wins ties), then the columns are rounded in order
  * with error feedback inside the group.  The residuals of a block of up to 4 groups reach the
- * rest of the block column by column and the columns right of the block through one f32 MFMA
- * GEMM, W[:, c1:] -= E[:, c0:c1] U[c0:c1, c1:].  Asynchronous.
+ * rest of the block column by column, the rest of its 512-column panel through one f32 MFMA
+ * GEMM, W[:, c1:p1] -= E[:, c0:c1] U[c0:c1, c1:p1], and the columns right of the panel through
+ * one K = 512 GEMM per panel, W[:, p1:] -= E[:, p0:p1] U[p0:p1, p1:].  Asynchronous.
  */
 int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
                const float* tab, const float* lost, int64_t rows, int64_t n, uint8_t* nib,

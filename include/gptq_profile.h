@@ -12,9 +12,10 @@
  *   3 fold_build   prep, scaling and the reversed equilibrated matrix
  *   4 fold_make_u  U from L^-1
  *   5 sweep_group  rung choice, rounding, in-group feedback
- *   6 sweep_trail  trailing E * U GEMM
+ *   6 sweep_trail  bulk of the trailing E * U update (columns beyond the next panel)
  *   7 ladder
  *   8 fold_next    look-ahead part of the update: next block column and next block row
+ *   9 sweep_next   sweep updates on the serial chain: rest of the panel, next panel
  * The recording adds two event records per timed launch; the mask is 0 by default.
  */
 #ifndef GPTQ_MI355X_PROFILE_H

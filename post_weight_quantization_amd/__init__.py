@@ -185,7 +185,7 @@ def gptq_sweep(W, U, hdiag, dead, tab, lost, want_E=False, workspace=None, strea
 
 
 PROFILE_FAMILIES = ["fold_update", "fold_panel", "fold_diag", "fold_build", "fold_make_u",
-                    "sweep_group", "sweep_trail", "ladder", "fold_next"]
+                    "sweep_group", "sweep_trail", "ladder", "fold_next", "sweep_next"]
 
 
 def profile_enable(families=None):

@@ -22,10 +22,11 @@ enum Family {
     FAM_FOLD_BUILD = 3,   // prep, scaling and the reversed equilibrated matrix
     FAM_FOLD_MAKEU = 4,
     FAM_SWEEP_GROUP = 5,  // rung choice + rounding + in-block feedback
-    FAM_SWEEP_TRAIL = 6,  // trailing E * U GEMM
+    FAM_SWEEP_TRAIL = 6,  // bulk of the trailing E * U update (beyond the next panel)
     FAM_LADDER = 7,
     FAM_FOLD_NEXT = 8,    // look-ahead update of the next block column / block row
-    FAM_COUNT = 9
+    FAM_SWEEP_NEXT = 9,   // sweep updates on the serial chain: rest of the panel, next panel
+    FAM_COUNT = 10
 };
 
 // A helper stream (non-blocking, default priority) with two events, taken from a per-process

@@ -5,19 +5,26 @@
 // "cortiq-cli 0.8.45 src/gptq.rs" (gptq_quantize_q4tp: rung rule, rounding, feedback;
 // gptq_quantize_q4tp_dev: tab / lost layout).
 //
-// Blocks of 128 columns (4 groups of 32), c0 = 128 b:
+// Blocks of 128 columns (4 groups of 32) inside outer panels of 512 columns:
 //   block kernel : 16 lanes per row hold the row's corrected block in registers; per group the
 //                  rung is chosen from the corrected tile, then the columns are rounded in order
 //                  and each residual is fed into the rest of the block, column by column (the
 //                  host sweep's full-row update restricted to the block);
-//   trail GEMM   : W[:, c0+128:] -= E[:, c0:c0+128] U[c0:c0+128, c0+128:]  (f32 MFMA, K = 128).
-// Deferring the update of the columns right of the block to one K = 128 product is the blocked
-// ("lazy") form of the same elimination -- the pages' own q2tp host sweep is blocked the same
-// way -- and moves a quarter of the HBM traffic of a K = 32 update per group.
-// W is never modified: the first trailing update reads the caller's W and writes the working
+//   inner update : the panel's columns right of the block, W[:, c0+128:P1] -= E_blk U_blk
+//                  (f32 MFMA, K = 128);
+//   panel update : every column right of the panel, W[:, P1:] -= E_pan U_pan (K = 512).
+// Deferring the update of the columns right of a block (panel) to one product over its columns
+// is the blocked ("lazy") form of the same elimination -- the pages' own q2tp host sweep is
+// blocked the same way -- and a K = 512 product reads and writes the trailing W once per 16
+// groups.  The panel update is split as in the fold: the next panel's 512 columns are updated
+// first on the caller's stream, the rest on a helper stream, where it overlaps the next panel's
+// blocks (look-ahead of one panel).
+// W is never modified: the first update of a column reads the caller's W and writes the working
 // copy, later ones update the copy in place.  Dead columns are zeroed whenever a tile is read
 // (U has no off-diagonal entries in a dead row or column, so the GEMM leaves them alone).
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "gemm_mfma.hpp"
@@ -295,10 +302,15 @@ extern "C" int gptq_ladder(const float* W, const uint8_t* dead, int64_t rows, in
     return GPTQ_OK;
 }
 
+constexpr int SOB = 512;         // columns per outer panel
+
+// Workspace: the working copy of W (rows x n) and two panel buffers of residuals (rows x 512,
+// alternating between panels so that a panel's update can still read them while the next
+// panel's blocks write the other one).
 static size_t sweep_ws(int64_t rows, int64_t n, size_t* off_e) {
     const size_t wc = align256(sizeof(float) * (size_t)(rows * n));
     if (off_e) *off_e = wc;
-    return wc + align256(sizeof(float) * (size_t)(rows * SB));
+    return wc + 2 * align256(sizeof(float) * (size_t)(rows * SOB));
 }
 
 extern "C" size_t gptq_sweep_workspace_size(int64_t rows, int64_t n) {
@@ -327,35 +339,95 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     float* Wc = (float*)workspace;
-    float* Eblk = (float*)((char*)workspace + off_e);
+    float* Epan[2] = {(float*)((char*)workspace + off_e),
+                      (float*)((char*)workspace + off_e + align256(sizeof(float) * (size_t)(rows * SOB)))};
     const unsigned nwg = (unsigned)((rows + 15) / 16);
-    for (int64_t c0 = 0; c0 < n; c0 += SB) {
-        const int G = (int)((n - c0 >= SB) ? 4 : (n - c0) / 32);
-        const int64_t nc = 32 * G;
-        const float* src = (c0 == 0) ? W : Wc;
-        float* Eo = E ? E + c0 : Eblk;
-        const int64_t ldE = E ? n : SB;
-        {
-            ProfScope ps(FAM_SWEEP_GROUP, st, 51.0 * nc * rows + (double)rows * nc * nc,
-                         4.0 * rows * nc * 2 + 4.0 * nc * nc);
-            switch (G) {
-                case 4: launch_block<4>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
-                case 3: launch_block<3>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
-                case 2: launch_block<2>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
-                default: launch_block<1>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+
+    Helper hp{};
+    if (helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
+    hipStream_t ts = hp.stream;
+    struct Release {
+        const Helper& h;
+        ~Release() { helper_release(h); }
+    } release{hp};
+
+    bool first_bulk = true;
+    int pan = 0;
+    for (int64_t P0 = 0; P0 < n; P0 += SOB, pan ^= 1) {
+        const int64_t w = std::min<int64_t>(SOB, n - P0);
+        float* Ep = E ? E + P0 : Epan[pan];
+        const int64_t ldE = E ? n : SOB;
+        for (int64_t c0 = P0; c0 < P0 + w; c0 += SB) {
+            const int G = (int)((P0 + w - c0 >= SB) ? 4 : (P0 + w - c0) / 32);
+            const int64_t nc = 32 * G;
+            const float* src = (c0 == 0) ? W : Wc;
+            float* Eo = Ep + (c0 - P0);
+            {
+                ProfScope ps(FAM_SWEEP_GROUP, st, 51.0 * nc * rows + (double)rows * nc * nc,
+                             4.0 * rows * nc * 2 + 4.0 * nc * nc);
+                switch (G) {
+                    case 4: launch_block<4>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+                    case 3: launch_block<3>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+                    case 2: launch_block<2>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+                    default: launch_block<1>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
+                }
             }
+            // The rest of the panel: columns c0 + nc .. P0 + w (last read at the same source).
+            const int64_t rest_in = P0 + w - c0 - nc;
+            if (rest_in > 0) {
+                const GemmBatch b = gemm_batch(
+                    gemm_full(Eo, ldE, U + c0 * n + c0 + nc, n, src + c0 + nc, Wc + c0 + nc, n,
+                              (int)rows, (int)rest_in, (int)nc, -1.0f, 1),
+                    nullptr);
+                ProfScope ps(FAM_SWEEP_NEXT, st, 2.0 * nc * rows * rest_in,
+                             8.0 * rows * rest_in + 4.0 * nc * rest_in + 4.0 * rows * nc);
+                gemm_kernel<6, false, false, true><<<b.total, G_THREADS, 0, st>>>(b, nullptr);
+            }
+            GPTQ_HIP(hipGetLastError());
         }
-        const int64_t rest = n - c0 - nc;
-        if (rest > 0) {
+        const int64_t rest = n - P0 - w;
+        if (rest <= 0) continue;
+        // Columns right of the panel still hold the caller's W when this is the first panel.
+        const float* src = (P0 == 0) ? W : Wc;
+        const float* Up = U + P0 * n;  // the panel's rows of U
+        const int64_t nw = std::min<int64_t>(SOB, rest);
+        const int64_t rest2 = rest - nw;
+        // Bulk: every column beyond the next panel, on the helper stream once the panel's
+        // residuals are complete.
+        if (rest2 > 0) {
+            GPTQ_HIP(hipEventRecord(hp.ev_a, st));
+            GPTQ_HIP(hipStreamWaitEvent(ts, hp.ev_a, 0));
+            const int64_t j0 = P0 + w + nw;
             const GemmBatch b = gemm_batch(
-                gemm_full(Eo, ldE, U + c0 * n + c0 + nc, n, src + c0 + nc, Wc + c0 + nc, n,
-                          (int)rows, (int)rest, (int)nc, -1.0f, 1),
+                gemm_full(Ep, ldE, Up + j0, n, src + j0, Wc + j0, n, (int)rows, (int)rest2, (int)w,
+                          -1.0f, 1),
                 nullptr);
-            ProfScope ps(FAM_SWEEP_TRAIL, st, 2.0 * nc * rows * rest,
-                         8.0 * rows * rest + 4.0 * nc * rest + 4.0 * rows * nc);
-            gemm_kernel<2, false, false, true><<<b.total, G_THREADS, 0, st>>>(b, nullptr);
+            ProfScope ps(FAM_SWEEP_TRAIL, ts, 2.0 * w * rows * rest2,
+                         8.0 * rows * rest2 + 4.0 * w * rest2 + 4.0 * rows * w);
+            gemm_kernel<2, false, false, true><<<b.total, G_THREADS, 0, ts>>>(b, nullptr);
+            GPTQ_HIP(hipGetLastError());
         }
-        GPTQ_HIP(hipGetLastError());
+        // Look-ahead: the next panel's columns, after the previous panel's bulk update (which
+        // wrote them, and read the residual buffer the next panel's blocks overwrite).
+        if (!first_bulk) GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
+        {
+            const int64_t j0 = P0 + w;
+            const GemmBatch b = gemm_batch(
+                gemm_full(Ep, ldE, Up + j0, n, src + j0, Wc + j0, n, (int)rows, (int)nw, (int)w,
+                          -1.0f, 1),
+                nullptr);
+            ProfScope ps(FAM_SWEEP_NEXT, st, 2.0 * w * rows * nw,
+                         8.0 * rows * nw + 4.0 * w * nw + 4.0 * rows * w);
+            gemm_kernel<7, false, false, true><<<b.total, G_THREADS, 0, st>>>(b, nullptr);
+            GPTQ_HIP(hipGetLastError());
+        }
+        if (rest2 > 0) {
+            GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
+            first_bulk = false;
+        }
     }
+    // Join the helper stream.
+    GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
+    GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
     return GPTQ_OK;
 }
