@@ -46,7 +46,31 @@ def sweep_flops(rows: int, n: int) -> float:
     return rows * (n * n - 32.0 * n) + 51.0 * rows * n
 
 
-def cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows, m_fold=4608, rows_sweep=128):
+def recorded_traffic():
+    """HBM bytes per launch of the fold's bulk update from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the kernel's sources
+    have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "fold_update_traffic_n17408.md")
+    try:
+        rec = {}
+        for line in open(path):
+            k, sep, v = line.partition(":")
+            if sep and k.strip() in ("traffic_bytes_per_launch", "kernel_sources_sha256",
+                                     "kernel_sources"):
+                rec[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in rec["kernel_sources"].split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != rec["kernel_sources_sha256"]:
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows, m_fold=7680, rows_sweep=512):
     """The oracle on a bounded sample: the fold of the trailing m x m block of H and the sweep
     of `rows_sweep` rows at full width against the GPU's U, scaled to one whole group."""
     import numpy as np
@@ -194,7 +218,10 @@ def main():
         "roofline": {
             "kernel": "gemm_kernel<0> (fold trailing update: Cholesky SYRK + inverse GEMM)",
             "bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS,
+            "traffic": recorded_traffic(),
+            "traffic_note": "HBM bytes per launch: rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 "
+                            "(factors from a plain 1 GiB copy); null once the kernel changed",
             "launches": fu["launches"], "avg_launch_us": 1e3 * fu["ms"] / max(fu["launches"], 1),
             "flops_per_launch": fu["flops"] / max(fu["launches"], 1),
         },
