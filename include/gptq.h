@@ -41,7 +41,8 @@ enum {
     GPTQ_EINVAL = 1,      /* bad size or null required pointer */
     GPTQ_EWORKSPACE = 2,  /* workspace smaller than the matching *_workspace_size() */
     GPTQ_EHIP = 3,        /* a HIP runtime call failed */
-    GPTQ_DEGENERATE = 4   /* the damping passed 10 without a factor: U = I was written */
+    GPTQ_DEGENERATE = 4,  /* the damping passed 10 without a factor: U = I was written */
+    GPTQ_ECHECK = 5       /* check mode only (gptq_check.h): the schedule failed its check */
 };
 
 /* Host-side record of one fold. */

@@ -18,7 +18,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgptq_mi355x.so")
 
-GPTQ_OK, GPTQ_EINVAL, GPTQ_EWORKSPACE, GPTQ_EHIP, GPTQ_DEGENERATE = 0, 1, 2, 3, 4
+GPTQ_OK, GPTQ_EINVAL, GPTQ_EWORKSPACE, GPTQ_EHIP, GPTQ_DEGENERATE, GPTQ_ECHECK = 0, 1, 2, 3, 4, 5
 
 _lib = None
 
@@ -69,6 +69,11 @@ def load():
     lib.gptq_profile_family_count.restype = ctypes.c_int
     lib.gptq_profile_family_name.argtypes = [ctypes.c_int]
     lib.gptq_profile_family_name.restype = ctypes.c_char_p
+    lib.gptq_check_mode.argtypes = [ctypes.c_int]
+    lib.gptq_check_mode.restype = None
+    lib.gptq_check_message.restype = ctypes.c_char_p
+    lib.gptq_check_selftest.argtypes = [ctypes.c_int]
+    lib.gptq_check_selftest.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -218,6 +223,28 @@ def profile_collect():
             for f in range(nf)}
 
 
-__all__ = ["gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
+class check_mode:
+    """Context manager: the library's calls run as dry runs of their schedule (no GPU; device
+    pointers are never dereferenced) and return GPTQ_ECHECK when an access leaves its buffers
+    or two launches on different streams race; see include/gptq_check.h."""
+
+    def __enter__(self):
+        load().gptq_check_mode(1)
+        return self
+
+    def __exit__(self, *exc):
+        load().gptq_check_mode(0)
+        return False
+
+
+def check_message() -> str:
+    return load().gptq_check_message().decode()
+
+
+def check_selftest(which: int) -> int:
+    return int(load().gptq_check_selftest(int(which)))
+
+
+__all__ = ["check_mode", "check_message", "check_selftest", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
            "profile_collect", "LIB_PATH"]

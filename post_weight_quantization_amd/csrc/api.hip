@@ -3,6 +3,7 @@
 #include <vector>
 
 #include "../../include/gptq_profile.h"
+#include "check.hpp"
 #include "common.hpp"
 
 namespace gptq {
@@ -33,6 +34,10 @@ hipEvent_t take_event() {
 }  // namespace
 
 int helper_acquire(Helper* h) {
+    if (dry_run()) {
+        *h = Helper{dry_stream(1), dry_stream(2), dry_event(1), dry_event(2), dry_event(3), -1};
+        return GPTQ_OK;
+    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return GPTQ_EHIP;
     {
@@ -46,21 +51,26 @@ int helper_acquire(Helper* h) {
     }
     Helper n{};
     n.device = dev;
-    if (hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking) != hipSuccess) return GPTQ_EHIP;
+    if (hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipStreamCreateWithFlags(&n.stream2, hipStreamNonBlocking) != hipSuccess)
+        return GPTQ_EHIP;
     if (hipEventCreateWithFlags(&n.ev_a, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.ev_b, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&n.ev_b, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.ev_c, hipEventDisableTiming) != hipSuccess)
         return GPTQ_EHIP;
     *h = n;
     return GPTQ_OK;
 }
 
 void helper_release(const Helper& h) {
+    if (h.device < 0) return;  // a dry run's stand-in
     std::lock_guard<std::mutex> lk(g_hmu);
     g_helpers.push_back(h);
 }
 
 ProfScope::ProfScope(int fam_, hipStream_t s_, double flops_, double bytes_)
     : fam(fam_), s(s_), flops(flops_), bytes(bytes_), on(false), rec(nullptr) {
+    if (dry_run()) return;
     std::lock_guard<std::mutex> lk(g_mu);
     if (!(g_mask >> fam & 1u)) return;
     Rec* r = new Rec{take_event(), take_event(), fam, flops, bytes};
@@ -93,6 +103,7 @@ extern "C" const char* gptq_status_string(int status) {
         case GPTQ_EWORKSPACE: return "workspace too small";
         case GPTQ_EHIP: return "HIP runtime error";
         case GPTQ_DEGENERATE: return "damping passed 10 without a factor; U = I";
+        case GPTQ_ECHECK: return "schedule check failed (check mode)";
         default: return "unknown status";
     }
 }

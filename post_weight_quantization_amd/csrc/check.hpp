@@ -1,0 +1,70 @@
+// check.hpp -- schedule checking for libgptq_mi355x (dry run).
+//
+// In check mode (gptq_check_mode(1), include/gptq_check.h) an entry point runs its host-side
+// schedule without touching the GPU: every kernel launch, event record, stream wait and host
+// synchronisation goes through the functions below, which record it instead.  Each launch
+// names the memory it reads and writes as 2-D spans (rows x cols elements, row stride ld).
+// At the end of the call two properties are checked:
+//   bounds   every span lies inside one buffer the call was given (inputs, outputs,
+//            workspace), so no launch of the schedule can fault;
+//   races    two launches on different streams that touch overlapping memory, one of them
+//            writing, are ordered by the streams' event waits or a host synchronisation
+//            (vector clocks over streams), so the multi-stream pipelines cannot race.
+// Outside check mode the wrappers issue the HIP calls and the spans cost nothing.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gptq {
+
+struct Span {
+    const void* p;
+    int64_t ld, rows, cols;  // elements
+    int esize;               // bytes per element
+    bool write;
+};
+inline Span rd(const void* p, int64_t ld, int64_t rows, int64_t cols, int esize = 4) {
+    return Span{p, ld, rows, cols, esize, false};
+}
+inline Span wr(const void* p, int64_t ld, int64_t rows, int64_t cols, int esize = 4) {
+    return Span{p, ld, rows, cols, esize, true};
+}
+
+// True while the calling thread runs an entry point in check mode.
+bool dry_run();
+
+// One entry-point call.  In check mode the constructor starts a fresh record; finish() runs
+// the checks and returns GPTQ_OK or GPTQ_ECHECK.  Outside check mode both do nothing.
+struct CheckScope {
+    CheckScope();
+    ~CheckScope();
+    int finish();
+    CheckScope(const CheckScope&) = delete;
+    CheckScope& operator=(const CheckScope&) = delete;
+};
+
+void check_buffer(const void* p, size_t bytes, const char* name);
+// GPTQ_OK, or GPTQ_ECHECK when a span leaves every registered buffer.
+int check_launch(const char* name, hipStream_t s, const Span* acc, int nacc);
+int ev_record(hipEvent_t e, hipStream_t s);            // hipEventRecord
+int stream_wait(hipStream_t s, hipEvent_t e);          // hipStreamWaitEvent
+int launch_status();                                   // hipGetLastError (GPTQ_OK in a dry run)
+void host_sync_record(hipStream_t s);                  // the host waits for s (dry run only)
+
+// Fake stream / event handles for helper streams in a dry run.
+hipStream_t dry_stream(int k);
+hipEvent_t dry_event(int k);
+
+}  // namespace gptq
+
+// Launch a kernel after recording its accesses: LAUNCH is a parenthesised launch expression,
+// the rest are Span values.  Returns the enclosing function's status on a check failure.
+#define GPTQ_LAUNCH(stream, name, launch, ...)                                       \
+    do {                                                                             \
+        const ::gptq::Span acc_[] = {__VA_ARGS__};                                  \
+        const int rc_ = ::gptq::check_launch(name, stream, acc_,                     \
+                                             (int)(sizeof(acc_) / sizeof(acc_[0]))); \
+        if (rc_ != GPTQ_OK) return rc_;                                              \
+        if (!::gptq::dry_run()) launch;                                              \
+    } while (0)

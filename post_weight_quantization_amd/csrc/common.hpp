@@ -29,11 +29,11 @@ enum Family {
     FAM_COUNT = 10
 };
 
-// A helper stream (non-blocking, default priority) with two events, taken from a per-process
-// pool for the duration of one call so that independent calls never share one.
+// Two helper streams (non-blocking, default priority) and three events, taken from a
+// per-process pool for the duration of one call so that independent calls never share one.
 struct Helper {
-    hipStream_t stream;
-    hipEvent_t ev_a, ev_b;
+    hipStream_t stream, stream2;
+    hipEvent_t ev_a, ev_b, ev_c;
     int device;
 };
 int helper_acquire(Helper* h);   // GPTQ_OK or GPTQ_EHIP

@@ -414,6 +414,12 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
     if (n > (int64_t)1 << 20) return GPTQ_EINVAL;
     const FoldLayout L = fold_layout(n);
     if (workspace_bytes < L.total) return GPTQ_EWORKSPACE;
+    CheckScope check;
+    check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
+    check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
+    check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
+    check_buffer(dead, (size_t)n, "dead");
+    check_buffer(workspace, workspace_bytes, "workspace");
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
     FoldState* state = (FoldState*)(ws + L.off_state);
@@ -424,13 +430,14 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
     float* Tb = (float*)(ws + L.off_t);
     float* Xt = (float*)(ws + L.off_xt);
     const int64_t np = L.np;
-    const double n3 = (double)n * n * n;
+    const Span st_rw = wr(state, 1, 1, sizeof(FoldState), 1);
 
     {
         ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 8.0 * n);
-        fold_prep_kernel<<<1, 1024, 0, st>>>(H, n, ldh, hdiag, dead, state);
+        GPTQ_LAUNCH(st, "fold_prep", (fold_prep_kernel<<<1, 1024, 0, st>>>(H, n, ldh, hdiag, dead, state)),
+                    rd(H, ldh + 1, n, 1), wr(hdiag, n, 1, n), wr(dead, n, 1, n, 1), st_rw);
     }
-    GPTQ_HIP(hipGetLastError());
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
 
     Helper hp{};
     if (helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
@@ -439,6 +446,11 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
         const Helper& h;
         ~Release() { helper_release(h); }
     } release{hp};
+#define FOLD_OK(call)                           \
+    do {                                        \
+        const int rc_ = (call);                 \
+        if (rc_ != GPTQ_OK) return rc_;         \
+    } while (0)
 
     double lam = (lambda > 0.0) ? lambda : 0.0;
     int attempts = 0;
@@ -448,17 +460,28 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
         ++attempts;
         {
             ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 4.0 * (double)n * n + 4.0 * (double)np * np / 2);
-            fold_scale_kernel<<<(unsigned)((np + 255) / 256), 256, 0, st>>>(hdiag, dead, state, lam,
-                                                                            n, np, dinv);
-            fold_build_kernel<<<dim3((unsigned)(np / 32), (unsigned)(np / 32)), 256, 0, st>>>(
-                H, ldh, dinv, dead, state, lam, A, n, np);
+            GPTQ_LAUNCH(st, "fold_scale",
+                        (fold_scale_kernel<<<(unsigned)((np + 255) / 256), 256, 0, st>>>(
+                            hdiag, dead, state, lam, n, np, dinv)),
+                        rd(hdiag, n, 1, n), rd(dead, n, 1, n, 1), st_rw, wr(dinv, np, 1, np));
+            GPTQ_LAUNCH(st, "fold_build",
+                        (fold_build_kernel<<<dim3((unsigned)(np / 32), (unsigned)(np / 32)), 256, 0, st>>>(
+                            H, ldh, dinv, dead, state, lam, A, n, np)),
+                        rd(H, ldh, n, n), rd(dinv, np, 1, np), rd(dead, n, 1, n, 1),
+                        rd(state, 1, 1, sizeof(FoldState), 1), wr(A, np, np, np));
         }
-        GPTQ_HIP(hipGetLastError());
-        // Outer panels of width w (the K of the bulk update); inside a panel, 128-wide steps
+        if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+        // Outer panels of width w (the K of the bulk updates); inside a panel, 128-wide steps
         // factor the diagonal block, solve the rows below and update the rest of the panel.
-        // The caller's stream st carries the serial chain; the bulk trailing update of a panel
-        // runs on the helper stream ts and overlaps the next panel's chain (look-ahead of one
-        // panel: the next panel's columns are updated first, on st).
+        // Three streams:
+        //   st  the Cholesky's serial chain: the panel steps, then the next panel's columns
+        //       (look-ahead of one panel);
+        //   ts  the Cholesky's bulk trailing update beyond the next panel, overlapping the next
+        //       panel's chain;
+        //   tx  the inverse X = L^-1, a pipeline of its own: once panel k of L is final it
+        //       inverts the panel's diagonal block, finishes the panel's rows of X and updates
+        //       every row of X below.  Nothing in the Cholesky waits for it.
+        hipStream_t tx = hp.stream2;
         bool first_bulk = true;
         for (int64_t kb = 0; kb < np; kb += L.nb2) {
             const int64_t w = std::min<int64_t>(L.nb2, np - kb);
@@ -468,7 +491,10 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 const int64_t rest_c = np - cb - NB;
                 {
                     ProfScope ps(FAM_FOLD_DIAG, st, 2.0 * NB * NB * NB / 3.0, 0.0);
-                    fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)(cb / NB), &state->flag);
+                    GPTQ_LAUNCH(st, "fold_diag",
+                                (fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)(cb / NB), &state->flag)),
+                                wr(A + cb * np + cb, np, NB, NB), wr(X + cb * np + cb, np, NB, NB),
+                                wr(MI + (cb / NB) * NB * NB, NB, NB, NB), st_rw);
                 }
                 if (rest_c <= 0) continue;
                 const float* mic = MI + (cb / NB) * NB * NB;
@@ -476,10 +502,10 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 const GemmProblem pa = gemm_full(A + (cb + NB) * np + cb, np, mic, NB, nullptr,
                                                  A + (cb + NB) * np + cb, np, (int)rest_c, NB, NB,
                                                  1.0f, 0);
-                const GemmBatch pb = gemm_batch(pa, nullptr);
                 {
                     ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * NB * (double)rest_c, 0.0);
-                    gemm_kernel<1, true, false, false><<<pb.total, G_THREADS, 0, st>>>(pb, &state->flag);
+                    FOLD_OK((launch_gemm<1, true, false, false>("fold_panel", st, gemm_batch(pa, nullptr),
+                                                                &state->flag)));
                 }
                 // The rest of the panel's columns: A[cb+128:, cb+128:kb+w] -= L_ic L_jc^T.
                 const int64_t ncol = kb + w - cb - NB;
@@ -490,18 +516,27 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                                                (int)ncol, NB, -1.0f, 1);
                     iu.mask_diag = 1;
                     iu.skip_upper = 1;
-                    const GemmBatch ib = gemm_batch(iu, nullptr);
                     ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * NB * (double)rest_c * ncol, 0.0);
-                    gemm_kernel<4, true, true, false><<<ib.total, G_THREADS, 0, st>>>(ib, &state->flag);
+                    FOLD_OK((launch_gemm<4, true, true, false>("fold_in_panel", st, gemm_batch(iu, nullptr),
+                                                               &state->flag)));
                 }
-                GPTQ_HIP(hipGetLastError());
+                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             }
+            // Panel k of L (and the inverses of its diagonal 128-blocks) is final.
+            FOLD_OK(ev_record(hp.ev_a, st));
+            const int64_t rest = np - kb - w;
+            const float* P = A + (kb + w) * np + kb;  // the panel's rows below its diagonal block
+
+            // --- the inverse, on tx ---
+            FOLD_OK(stream_wait(tx, hp.ev_a));
             // Inverse of the panel's w x w diagonal block of L, into X[kb:kb+w, kb:kb+w]: the
             // 128-blocks on the diagonal are the MI_c written by the diagonal kernel; block row I
             // is -MI_I (L[I, <I] X[<I, <I]) (block forward substitution).
             if (R > 1) {
-                fold_zero_upper_kernel<<<dim3((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, st>>>(
-                    X, np, kb, w);
+                GPTQ_LAUNCH(tx, "fold_zero_upper",
+                            (fold_zero_upper_kernel<<<dim3((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, tx>>>(
+                                X, np, kb, w)),
+                            wr(X + kb * np + kb, np, w, w));
                 for (int64_t I = 1; I < R; ++I) {
                     const int64_t ci = kb + I * NB;
                     const GemmBatch t1 = gemm_batch(
@@ -512,11 +547,11 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                         gemm_full(MI + (ci / NB) * NB * NB, NB, Tb, w, nullptr, X + ci * np + kb, np,
                                   NB, (int)(I * NB), NB, -1.0f, 0),
                         nullptr);
-                    ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * (double)(I * NB) * (I * NB + NB), 0.0);
-                    gemm_kernel<5, false, false, false><<<t1.total, G_THREADS, 0, st>>>(t1, &state->flag);
-                    gemm_kernel<5, false, false, false><<<t2.total, G_THREADS, 0, st>>>(t2, &state->flag);
+                    ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * NB * (double)(I * NB) * (I * NB + NB), 0.0);
+                    FOLD_OK((launch_gemm<5, false, false, false>("fold_inv_block_a", tx, t1, &state->flag)));
+                    FOLD_OK((launch_gemm<5, false, false, false>("fold_inv_block_b", tx, t2, &state->flag)));
                 }
-                GPTQ_HIP(hipGetLastError());
+                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             }
             // Rows of X in this panel: X[kb:kb+w, 0:kb] = Minv_w X[kb:kb+w, 0:kb] (out of place,
             // then copied back: a workgroup tile spans only 128 of the w rows it reads).
@@ -526,66 +561,82 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                               (int)w, 1.0f, 0),
                     nullptr);
                 {
-                    ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * (double)w * w * kb, 0.0);
-                    gemm_kernel<1, false, false, false><<<xb.total, G_THREADS, 0, st>>>(xb, &state->flag);
+                    ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * (double)w * w * kb, 0.0);
+                    FOLD_OK((launch_gemm<1, false, false, false>("fold_x_rows", tx, xb, &state->flag)));
                 }
-                fold_copy_rows_kernel<<<dim3((unsigned)((kb + 1023) / 1024), (unsigned)w), 256, 0, st>>>(
-                    Xt, X + kb * np, np, kb);
-                GPTQ_HIP(hipGetLastError());
+                GPTQ_LAUNCH(tx, "fold_copy_rows",
+                            (fold_copy_rows_kernel<<<dim3((unsigned)((kb + 1023) / 1024), (unsigned)w), 256, 0, tx>>>(
+                                Xt, X + kb * np, np, kb)),
+                            rd(Xt, np, w, kb), wr(X + kb * np, np, w, kb));
+                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             }
-            const int64_t rest = np - kb - w;
+            // Every row below: X_i,<kb+w -= L_i,k X[kb:kb+w, <kb+w] (X's columns kb..kb+w-1 are
+            // first written here, so those tiles ignore C_in).
+            if (rest > 0) {
+                GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np,
+                                           X + (kb + w) * np, np, (int)rest, (int)(kb + w), (int)w,
+                                           -1.0f, 1);
+                xu.beta0_from_tn = (int)(kb / NB);
+                // Second slot of the bulk kernel (its B layout there is "N": rows of X).
+                const GemmProblem none = gemm_none();
+                ProfScope ps(FAM_FOLD_UPDATE, tx, 2.0 * w * (double)rest * (kb + w), 0.0);
+                FOLD_OK((launch_gemm<0, true, false, false>("fold_x_update", tx, gemm_batch(none, &xu),
+                                                            &state->flag)));
+                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+            }
             if (rest <= 0) continue;
-            const float* P = A + (kb + w) * np + kb;  // the panel's rows below its diagonal block
+
+            // --- the Cholesky's trailing update ---
             const int64_t nw = std::min<int64_t>(L.nb2, rest);  // width of the next panel
             const int64_t rest2 = rest - nw;
-            // Bulk: A_ij -= P_i P_j^T beyond the next panel, X_i,<kb+w -= P_i X[kb:kb+w, <kb+w]
-            // for the rows beyond the next panel; X's columns kb..kb+w-1 are written there first.
+            // Bulk, on ts: A_ij -= P_i P_j^T beyond the next panel.
             if (rest2 > 0) {
-                GPTQ_HIP(hipEventRecord(hp.ev_a, st));
-                GPTQ_HIP(hipStreamWaitEvent(ts, hp.ev_a, 0));
+                FOLD_OK(stream_wait(ts, hp.ev_a));
                 const GemmProblem sy = gemm_syrk_lower(P + nw * np, np,
                                                        A + (kb + w + nw) * np + kb + w + nw,
                                                        A + (kb + w + nw) * np + kb + w + nw, np,
                                                        (int)rest2, (int)w, -1.0f, 1);
-                GemmProblem xu = gemm_full(P + nw * np, np, X + kb * np, np, X + (kb + w + nw) * np,
-                                           X + (kb + w + nw) * np, np, (int)rest2, (int)(kb + w),
-                                           (int)w, -1.0f, 1);
-                xu.beta0_from_tn = (int)(kb / NB);
-                const GemmBatch ub = gemm_batch(sy, &xu);
-                const double fl = (double)w * rest2 * (rest2 + 1) + 2.0 * w * rest2 * (kb + w);
+                const double fl = (double)w * rest2 * (rest2 + 1);
                 {
                     ProfScope ps(FAM_FOLD_UPDATE, ts, fl, 0.0);
-                    gemm_kernel<0, true, false, false><<<ub.total, G_THREADS, 0, ts>>>(ub, &state->flag);
+                    FOLD_OK((launch_gemm<0, true, false, false>("fold_bulk", ts, gemm_batch(sy, nullptr),
+                                                                &state->flag)));
                 }
-                GPTQ_HIP(hipGetLastError());
+                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             }
-            // Look-ahead: the next panel's columns (rows below kb+w, diagonal tiles lower only)
-            // and X's rows of the next panel; they need the previous panel's bulk update.
-            if (!first_bulk) GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
+            // Look-ahead, on st: the next panel's columns (rows below kb+w, diagonal tiles lower
+            // only); they need the previous panel's bulk update.
+            if (!first_bulk) FOLD_OK(stream_wait(st, hp.ev_b));
             GemmProblem strip = gemm_full(P, np, P, np, A + (kb + w) * np + kb + w,
                                           A + (kb + w) * np + kb + w, np, (int)rest, (int)nw,
                                           (int)w, -1.0f, 1);
             strip.mask_diag = 1;
             strip.skip_upper = 1;
-            GemmProblem xr = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np, X + (kb + w) * np,
-                                       np, (int)nw, (int)(kb + w), (int)w, -1.0f, 1);
-            xr.beta0_from_tn = (int)(kb / NB);
-            const GemmBatch nb_ = gemm_batch(strip, &xr);
             {
-                ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * w * ((double)rest * nw + (double)nw * (kb + w)), 0.0);
-                gemm_kernel<3, true, false, false><<<nb_.total, G_THREADS, 0, st>>>(nb_, &state->flag);
+                ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * w * (double)rest * nw, 0.0);
+                FOLD_OK((launch_gemm<3, true, false, false>("fold_look_ahead", st, gemm_batch(strip, nullptr),
+                                                            &state->flag)));
             }
-            GPTQ_HIP(hipGetLastError());
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             if (rest2 > 0) {
-                GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
+                FOLD_OK(ev_record(hp.ev_b, ts));
                 first_bulk = false;
             }
         }
-        // Join the helper stream, then read the pivot flag.
-        GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
-        GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
-        GPTQ_HIP(hipMemcpyAsync(&host, state, sizeof(FoldState), hipMemcpyDeviceToHost, st));
-        GPTQ_HIP(hipStreamSynchronize(st));
+        // Join both helper streams, then read the pivot flag.
+        FOLD_OK(ev_record(hp.ev_c, tx));
+        FOLD_OK(stream_wait(st, hp.ev_c));
+        FOLD_OK(ev_record(hp.ev_b, ts));
+        FOLD_OK(stream_wait(st, hp.ev_b));
+        if (dry_run()) {
+            host_sync_record(st);
+            host.flag = 0u;
+            host.base = 1.0;
+            host.n_dead = 0;
+        } else {
+            GPTQ_HIP(hipMemcpyAsync(&host, state, sizeof(FoldState), hipMemcpyDeviceToHost, st));
+            GPTQ_HIP(hipStreamSynchronize(st));
+        }
         if (host.flag == 0u) break;
         lam = (lam == 0.0) ? 1e-4 : lam * 10.0;
         if (lam > 10.0) {
@@ -593,14 +644,20 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
             break;
         }
     }
+#undef FOLD_OK
     const dim3 g((unsigned)((n + 31) / 32), (unsigned)((n + 31) / 32));
     if (degenerate) {
-        fold_identity_kernel<<<g, 256, 0, st>>>(U, n);
+        GPTQ_LAUNCH(st, "fold_identity", (fold_identity_kernel<<<g, 256, 0, st>>>(U, n)), wr(U, n, n, n));
     } else {
         ProfScope ps(FAM_FOLD_MAKEU, st, 0.0, 4.0 * (double)n * n);
-        fold_make_u_kernel<<<g, 256, 0, st>>>(X, dinv, U, n, np);
+        GPTQ_LAUNCH(st, "fold_make_u", (fold_make_u_kernel<<<g, 256, 0, st>>>(X, dinv, U, n, np)),
+                    rd(X, np, np, np), rd(dinv, np, 1, np), wr(U, n, n, n));
     }
-    GPTQ_HIP(hipGetLastError());
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    {
+        const int rc = check.finish();
+        if (rc != GPTQ_OK) return rc;
+    }
     if (report) {
         report->lambda_used = lam;
         report->base = host.base;
@@ -610,6 +667,5 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
         report->degenerate = degenerate ? 1 : 0;
         report->reserved = 0;
     }
-    (void)n3;
     return degenerate ? GPTQ_DEGENERATE : GPTQ_OK;
 }

@@ -18,6 +18,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "check.hpp"
+#include "common.hpp"
+
 namespace gptq {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -301,6 +304,15 @@ inline GemmProblem gemm_syrk_lower(const float* A, int64_t lda, const float* Cin
     return p;
 }
 
+// A problem with no tiles: fills the first slot of a batch whose only problem needs the
+// second slot's B layout.
+inline GemmProblem gemm_none() {
+    GemmProblem p{};
+    p.tiles_n = 1;
+    p.ntiles = 0;
+    return p;
+}
+
 inline GemmBatch gemm_batch(const GemmProblem& a, const GemmProblem* b) {
     GemmBatch g{};
     g.p[0] = a;
@@ -311,6 +323,46 @@ inline GemmBatch gemm_batch(const GemmProblem& a, const GemmProblem* b) {
     }
     g.total = g.p[0].ntiles + (b ? g.p[1].ntiles : 0);
     return g;
+}
+
+// Memory one batch touches, as spans for the schedule checker: per problem A, B, C_in (when
+// read) and C_out, over whole tiles unless the launch checks bounds.  Returns the span count,
+// or -1 when a problem breaks the kernel's shape rules (K a multiple of 32; with bounds checks
+// and the "N" layout, N a multiple of 4).
+template <bool TB0, bool TB1, bool CHK>
+inline int gemm_spans(const GemmBatch& b, Span* out) {
+    int n = 0;
+    for (int q = 0; q < b.nprob && q < 2; ++q) {
+        const GemmProblem& P = b.p[q];
+        if (P.ntiles <= 0) continue;
+        const bool TB = (q == 0) ? TB0 : TB1;
+        if (P.K <= 0 || P.K % GT_K != 0 || (CHK && !TB && P.N % 4 != 0) || P.tiles_n <= 0)
+            return -1;
+        const int64_t tm = P.lower ? P.tiles_n : P.ntiles / P.tiles_n;
+        const int64_t rows = CHK ? P.M : tm * GT_M;
+        const int64_t cols = CHK ? P.N : (int64_t)P.tiles_n * GT_N;
+        out[n++] = rd(P.A, P.lda, rows, P.K);
+        out[n++] = TB ? rd(P.B, P.ldb, cols, P.K) : rd(P.B, P.ldb, P.K, cols);
+        if (P.beta && P.beta0_from_tn > 0)
+            out[n++] = rd(P.Cin, P.ldc, rows,
+                          cols < (int64_t)P.beta0_from_tn * GT_N ? cols : (int64_t)P.beta0_from_tn * GT_N);
+        out[n++] = wr(P.Cout, P.ldc, rows, cols);
+    }
+    return n;
+}
+
+// Launch one batch on stream s with `grid` workgroups (normally batch.total), after checking
+// its shape rules (GPTQ_EINVAL) and recording its accesses (check mode).
+template <int TAG, bool TB0, bool TB1, bool CHK>
+inline int launch_gemm(const char* name, hipStream_t s, const GemmBatch& b, const unsigned* flag) {
+    if (b.total <= 0) return GPTQ_OK;
+    Span acc[8];
+    const int na = gemm_spans<TB0, TB1, CHK>(b, acc);
+    if (na < 0) return GPTQ_EINVAL;
+    const int rc = check_launch(name, s, acc, na);
+    if (rc != GPTQ_OK) return rc;
+    if (!dry_run()) gemm_kernel<TAG, TB0, TB1, CHK><<<b.total, G_THREADS, 0, s>>>(b, flag);
+    return GPTQ_OK;
 }
 
 }  // namespace gptq

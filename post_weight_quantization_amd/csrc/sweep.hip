@@ -295,11 +295,20 @@ extern "C" int gptq_ladder(const float* W, const uint8_t* dead, int64_t rows, in
                            float* lost, float* tab, void* stream) {
     if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !dead || !lost || !tab) return GPTQ_EINVAL;
     if (rows > ((int64_t)1 << 31) - 1) return GPTQ_EINVAL;
+    CheckScope check;
+    check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
+    check_buffer(dead, (size_t)n, "dead");
+    check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
+    check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
     hipStream_t st = (hipStream_t)stream;
-    ProfScope ps(FAM_LADDER, st, 0.0, 4.0 * (double)rows * n);
-    ladder_kernel<<<(unsigned)rows, 256, 0, st>>>(W, dead, n, lost, tab);
-    GPTQ_HIP(hipGetLastError());
-    return GPTQ_OK;
+    {
+        ProfScope ps(FAM_LADDER, st, 0.0, 4.0 * (double)rows * n);
+        GPTQ_LAUNCH(st, "ladder", (ladder_kernel<<<(unsigned)rows, 256, 0, st>>>(W, dead, n, lost, tab)),
+                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), wr(lost, 2, rows, 2),
+                    wr(tab, 32, rows, 32));
+    }
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    return check.finish();
 }
 
 constexpr int SOB = 512;         // columns per outer panel
@@ -337,6 +346,18 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     if (rows > ((int64_t)1 << 31) - 64 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
     size_t off_e = 0;
     if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
+    CheckScope check;
+    check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
+    check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
+    check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
+    check_buffer(dead, (size_t)n, "dead");
+    check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
+    check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
+    check_buffer(nib, (size_t)(rows * (n / 2)), "nib");
+    check_buffer(rung, (size_t)(rows * (n / 32)), "rung");
+    check_buffer(scale, sizeof(float) * (size_t)(rows * (n / 32)), "scale");
+    if (E) check_buffer(E, sizeof(float) * (size_t)(rows * n), "E");
+    check_buffer(workspace, workspace_bytes, "workspace");
     hipStream_t st = (hipStream_t)stream;
     float* Wc = (float*)workspace;
     float* Epan[2] = {(float*)((char*)workspace + off_e),
@@ -350,6 +371,11 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
         const Helper& h;
         ~Release() { helper_release(h); }
     } release{hp};
+#define SWEEP_OK(call)                          \
+    do {                                        \
+        const int rc_ = (call);                 \
+        if (rc_ != GPTQ_OK) return rc_;         \
+    } while (0)
 
     bool first_bulk = true;
     int pan = 0;
@@ -365,12 +391,17 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
             {
                 ProfScope ps(FAM_SWEEP_GROUP, st, 51.0 * nc * rows + (double)rows * nc * nc,
                              4.0 * rows * nc * 2 + 4.0 * nc * nc);
-                switch (G) {
-                    case 4: launch_block<4>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
-                    case 3: launch_block<3>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
-                    case 2: launch_block<2>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
-                    default: launch_block<1>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE); break;
-                }
+                GPTQ_LAUNCH(st, "sweep_block",
+                            (G == 4   ? launch_block<4>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE)
+                             : G == 3 ? launch_block<3>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE)
+                             : G == 2 ? launch_block<2>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE)
+                                      : launch_block<1>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE)),
+                            rd(src + c0, n, rows, nc), rd(U + c0 * n + c0, n, nc, nc),
+                            rd(hdiag + c0, n, 1, nc), rd(dead + c0, n, 1, nc, 1),
+                            rd(tab, 32, rows, 32), rd(lost, 2, rows, 2),
+                            wr(nib + c0 / 2, n / 2, rows, nc / 2, 1),
+                            wr(rung + c0 / 32, n / 32, rows, G, 1),
+                            wr(scale + c0 / 32, n / 32, rows, G), wr(Eo, ldE, rows, nc));
             }
             // The rest of the panel: columns c0 + nc .. P0 + w (last read at the same source).
             const int64_t rest_in = P0 + w - c0 - nc;
@@ -381,9 +412,9 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
                     nullptr);
                 ProfScope ps(FAM_SWEEP_NEXT, st, 2.0 * nc * rows * rest_in,
                              8.0 * rows * rest_in + 4.0 * nc * rest_in + 4.0 * rows * nc);
-                gemm_kernel<6, false, false, true><<<b.total, G_THREADS, 0, st>>>(b, nullptr);
+                SWEEP_OK((launch_gemm<6, false, false, true>("sweep_in_panel", st, b, nullptr)));
             }
-            GPTQ_HIP(hipGetLastError());
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
         const int64_t rest = n - P0 - w;
         if (rest <= 0) continue;
@@ -395,8 +426,8 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
         // Bulk: every column beyond the next panel, on the helper stream once the panel's
         // residuals are complete.
         if (rest2 > 0) {
-            GPTQ_HIP(hipEventRecord(hp.ev_a, st));
-            GPTQ_HIP(hipStreamWaitEvent(ts, hp.ev_a, 0));
+            SWEEP_OK(ev_record(hp.ev_a, st));
+            SWEEP_OK(stream_wait(ts, hp.ev_a));
             const int64_t j0 = P0 + w + nw;
             const GemmBatch b = gemm_batch(
                 gemm_full(Ep, ldE, Up + j0, n, src + j0, Wc + j0, n, (int)rows, (int)rest2, (int)w,
@@ -404,12 +435,12 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
                 nullptr);
             ProfScope ps(FAM_SWEEP_TRAIL, ts, 2.0 * w * rows * rest2,
                          8.0 * rows * rest2 + 4.0 * w * rest2 + 4.0 * rows * w);
-            gemm_kernel<2, false, false, true><<<b.total, G_THREADS, 0, ts>>>(b, nullptr);
-            GPTQ_HIP(hipGetLastError());
+            SWEEP_OK((launch_gemm<2, false, false, true>("sweep_bulk", ts, b, nullptr)));
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
         // Look-ahead: the next panel's columns, after the previous panel's bulk update (which
         // wrote them, and read the residual buffer the next panel's blocks overwrite).
-        if (!first_bulk) GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
+        if (!first_bulk) SWEEP_OK(stream_wait(st, hp.ev_b));
         {
             const int64_t j0 = P0 + w;
             const GemmBatch b = gemm_batch(
@@ -418,16 +449,17 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
                 nullptr);
             ProfScope ps(FAM_SWEEP_NEXT, st, 2.0 * w * rows * nw,
                          8.0 * rows * nw + 4.0 * w * nw + 4.0 * rows * w);
-            gemm_kernel<7, false, false, true><<<b.total, G_THREADS, 0, st>>>(b, nullptr);
-            GPTQ_HIP(hipGetLastError());
+            SWEEP_OK((launch_gemm<7, false, false, true>("sweep_look_ahead", st, b, nullptr)));
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
         if (rest2 > 0) {
-            GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
+            SWEEP_OK(ev_record(hp.ev_b, ts));
             first_bulk = false;
         }
     }
     // Join the helper stream.
-    GPTQ_HIP(hipEventRecord(hp.ev_b, ts));
-    GPTQ_HIP(hipStreamWaitEvent(st, hp.ev_b, 0));
-    return GPTQ_OK;
+    SWEEP_OK(ev_record(hp.ev_b, ts));
+    SWEEP_OK(stream_wait(st, hp.ev_b));
+#undef SWEEP_OK
+    return check.finish();
 }

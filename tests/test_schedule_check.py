@@ -1,0 +1,86 @@
+"""The library's launch schedules, checked on the CPU by its dry-run mode (include/gptq_check.h):
+every kernel's reads and writes stay inside the buffers of the call, and no two launches on
+different streams touch the same memory unordered.  The fold runs on three streams (serial
+chain, Cholesky bulk update, inverse pipeline) and the sweep on two, so these checks cover the
+event waits between them at the sizes the GPU runs, ragged sizes included."""
+import ctypes
+
+import pytest
+
+import post_weight_quantization_amd as pwq
+
+GPTQ_OK, GPTQ_ECHECK = pwq.GPTQ_OK, pwq.GPTQ_ECHECK
+P = ctypes.c_void_p
+BASE = 1 << 44          # fake device addresses: never dereferenced in a dry run
+STRIDE = 1 << 38
+
+
+def addrs(k):
+    return [P(BASE + i * STRIDE) for i in range(k)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pwq.load()
+
+
+def test_checker_selftest(lib):
+    assert pwq.check_selftest(0) == GPTQ_OK
+    assert pwq.check_selftest(1) == GPTQ_ECHECK
+    assert "race" in pwq.check_message()
+    assert pwq.check_selftest(2) == GPTQ_OK
+    assert pwq.check_selftest(3) == GPTQ_ECHECK
+    assert "bounds" in pwq.check_message()
+
+
+@pytest.mark.parametrize("n", [8, 96, 128, 256, 600, 1024, 2048, 2080, 4096, 8192, 17408])
+def test_fold_schedule(lib, n):
+    H, U, hd, dead, ws = addrs(5)
+    need = lib.gptq_fold_workspace_size(n)
+    rep = pwq.FoldReport()
+    with pwq.check_mode():
+        st = lib.gptq_fold(H, n, n, 0.01, U, hd, dead, ws, need, None, ctypes.byref(rep))
+    assert st == GPTQ_OK, pwq.check_message()
+    assert pwq.check_message() == ""
+
+
+def test_fold_schedule_padded_rows_of_h(lib):
+    H, U, hd, dead, ws = addrs(5)
+    n = 1000
+    rep = pwq.FoldReport()
+    with pwq.check_mode():
+        st = lib.gptq_fold(H, n, 1024, 0.0, U, hd, dead, ws, lib.gptq_fold_workspace_size(n),
+                           None, ctypes.byref(rep))
+    assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(16, 32), (37, 96), (512, 256), (100, 544), (300, 1056),
+                                    (4096, 4096), (2048, 8192), (5120, 17408)])
+@pytest.mark.parametrize("want_e", [False, True])
+def test_sweep_schedule(lib, rows, n, want_e):
+    W, U, hd, dead, tab, lost, nib, rung, scale, E, ws = addrs(11)
+    need = lib.gptq_sweep_workspace_size(rows, n)
+    with pwq.check_mode():
+        st = lib.gptq_sweep(W, U, hd, dead, tab, lost, rows, n, nib, rung, scale,
+                            E if want_e else None, ws, need, None)
+    assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(1, 32), (512, 256), (5120, 17408)])
+def test_ladder_schedule(lib, rows, n):
+    W, dead, lost, tab = addrs(4)
+    with pwq.check_mode():
+        st = lib.gptq_ladder(W, dead, rows, n, lost, tab, None)
+    assert st == GPTQ_OK, pwq.check_message()
+
+
+def test_undersized_buffers_are_caught(lib):
+    """A caller's workspace is checked by size before anything runs; the dry run's own bounds
+    check then sees every launch inside the buffers it was given."""
+    H, U, hd, dead, ws = addrs(5)
+    n = 512
+    rep = pwq.FoldReport()
+    with pwq.check_mode():
+        st = lib.gptq_fold(H, n, n, 0.01, U, hd, dead, ws, lib.gptq_fold_workspace_size(n) - 1,
+                           None, ctypes.byref(rep))
+    assert st == pwq.GPTQ_EWORKSPACE
