@@ -202,15 +202,21 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
     for (int p = 0; p < 4; ++p) {
         const int c0 = 32 * p;
         if (wave == 0) {
-            // Factor: lane r (and r + 32) holds row r of the 32 x 32 block; column values are
-            // broadcast with readlane.  An opaque copy of the row index keeps comparisons against
-            // it inside the sub-panel (instead of hoisted out of the loop and spilled), and each
-            // step's updates are pinned in place so the compiler does not defer them.
+            // Factor and invert together: lane r (and r + 32) holds row r of the 32 x 32 block
+            // (a) and column r of its inverse T = L^-1 (t).  Step c makes column c of L final;
+            // its entries L_sc (s > c), broadcast once each with readlane, drive both the
+            // right-looking Cholesky update of the later columns and the right-looking
+            // substitution step c of every column of T.  An opaque copy of the row index keeps
+            // comparisons against it inside the sub-panel (instead of hoisted out of the loop and
+            // spilled), and each step's updates are pinned in place so the compiler does not
+            // defer them.
             int row = l32;
             asm volatile("" : "+v"(row));
-            float a[32], invd[32];
+            float a[32], t[32];
 #pragma unroll
             for (int c = 0; c < 32; ++c) a[c] = Ls[(c0 + row) * DLD + c0 + c];
+#pragma unroll
+            for (int q = 0; q < 32; ++q) t[q] = (q == row) ? 1.0f : 0.0f;
             // Pivot test at f32 resolution: the computed Schur complement of a unit-diagonal
             // matrix is exact only up to (i + 1) 2^-24 for pivot index i, so a pivot at or below
             // that bound is not known to be positive.
@@ -225,26 +231,18 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
                 asm volatile("" : "+v"(nbad));
                 pv = b ? 1.0f : pv;
                 const float r = __builtin_amdgcn_rsqf(pv);  // 1 / L_cc (pv is a normal float)
-                invd[c] = r;
                 // On the pivot's own lane a[c] is the pivot, so this is L_cc = sqrt(pv) there.
                 const float l = a[c] * r;
                 a[c] = l;
+                t[c] *= r;  // T_c,row is final: (e_row - sum_{k<c} L_ck T_k,row) / L_cc
 #pragma unroll
-                for (int s2 = c + 1; s2 < 32; ++s2) a[s2] -= l * lane_bcast(l, s2);
+                for (int s2 = c + 1; s2 < 32; ++s2) {
+                    const float L_sc = lane_bcast(l, s2);
+                    a[s2] -= l * L_sc;
+                    t[s2] -= L_sc * t[c];
+                }
 #pragma unroll
-                for (int s2 = c + 1; s2 < 32; ++s2) asm volatile("" : "+v"(a[s2]));
-            }
-            // Inverse, right-looking: lane c builds column c of T = L^-1.
-            float t[32];
-#pragma unroll
-            for (int q = 0; q < 32; ++q) t[q] = (q == row) ? 1.0f : 0.0f;
-#pragma unroll
-            for (int q = 0; q < 32; ++q) {
-                t[q] *= invd[q];
-#pragma unroll
-                for (int r = q + 1; r < 32; ++r) t[r] -= lane_bcast(a[q], r) * t[q];
-#pragma unroll
-                for (int r = q + 1; r < 32; ++r) asm volatile("" : "+v"(t[r]));
+                for (int s2 = c + 1; s2 < 32; ++s2) asm volatile("" : "+v"(a[s2]), "+v"(t[s2]));
             }
             if (lane < 32) {
 #pragma unroll
