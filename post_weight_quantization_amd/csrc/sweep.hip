@@ -117,27 +117,69 @@ __device__ __forceinline__ int nominal_rung(float amax, float lo, float st) {
 }
 #pragma clang fp contract(on)
 
-// Sum / max over the 16 lanes of a row group (xor butterflies stay inside the group).
+// Cross-lane moves inside the 16-lane rows of a wave, as DPP operand modifiers (a VALU move,
+// no LDS round trip).  C is the DPP control: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_mirror = 0x140, row_half_mirror = 0x141, row_newbcast:L = 0x150 + L (lane L of each row
+// to the whole row).
+template <int C>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), C, 0xf, 0xf, false));
+}
+// Lane L of each 16-lane row group, broadcast to the whole group; L folds to a constant once
+// the column loop is unrolled.
+__device__ __forceinline__ float row_bcast(float v, int L) {
+    switch (L) {
+        case 0: return dpp_mov<0x150>(v);
+        case 1: return dpp_mov<0x151>(v);
+        case 2: return dpp_mov<0x152>(v);
+        case 3: return dpp_mov<0x153>(v);
+        case 4: return dpp_mov<0x154>(v);
+        case 5: return dpp_mov<0x155>(v);
+        case 6: return dpp_mov<0x156>(v);
+        case 7: return dpp_mov<0x157>(v);
+        case 8: return dpp_mov<0x158>(v);
+        case 9: return dpp_mov<0x159>(v);
+        case 10: return dpp_mov<0x15a>(v);
+        case 11: return dpp_mov<0x15b>(v);
+        case 12: return dpp_mov<0x15c>(v);
+        case 13: return dpp_mov<0x15d>(v);
+        case 14: return dpp_mov<0x15e>(v);
+        default: return dpp_mov<0x15f>(v);
+    }
+}
+
+// Sum / max over the 16 lanes of a row group: pairs within quads, quads within halves
+// (half mirror), halves within the row (mirror).  A fixed tree; every lane gets the same value.
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-    for (int m = 8; m > 0; m >>= 1) v += __shfl_xor(v, m, 16);
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
     return v;
 }
 __device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-    for (int m = 8; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
     return v;
 }
 
 #pragma clang fp contract(off)
 // rint(fl(w / s)) -- the code decision on the correctly rounded quotient -- from w * fl(1/s):
 // that product is within 3u|w/s| (u = 2^-24) of the quotient, so both round to the same integer
-// unless the product lies within 4e-7 max(|w/s|, 1) of a half-integer; then (rarely) divide.
+// unless the product lies within 4e-7 max(|w/s|, 1) of a half-integer; then divide.  The
+// division sits behind a wave-uniform branch that is almost never taken, so the common path
+// does not wait for it.
 __device__ __forceinline__ float rint_quot(float w, float s, float inv_s) {
     const float r = w * inv_s;
     const float f = r - floorf(r);
-    if (fabsf(f - 0.5f) > 4e-7f * fmaxf(fabsf(r), 1.0f)) return rintf(r);
-    return rintf(w / s);
+    const bool near = !(fabsf(f - 0.5f) > 4e-7f * fmaxf(fabsf(r), 1.0f));
+    float q = rintf(r);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near) != 0, 0)) {
+        if (near) q = rintf(w / s);
+    }
+    return q;
 }
 
 // Partial H_ii-weighted rounding error of two columns at scale s (each product and sum rounded).
@@ -162,7 +204,7 @@ struct BlockCtx {
     const float* hs;     // H_ii of the block's columns, LDS
     const float* tb;     // the row's 32 rung scales
     float lo, st;
-    int k, base_lane;
+    int k;
 };
 
 // Group g of the block, with every register index a compile-time constant (the groups are
@@ -199,31 +241,51 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         scale[gi] = s;
     }
     uint32_t byte = 0u;
+    // This lane's entries of row j of U (own group and later groups) and 1 / U_jj are read one
+    // column step ahead, so the serial chain -- broadcast, code, residual, the owner's next
+    // column -- never waits on LDS; a scheduling barrier closes each step (otherwise the reads
+    // of every step are hoisted together and the registers run out).
+    float2 uo, ul[G];
+    float ui;
+    auto load_u = [&](int col, float2& o, float2 (&l)[G], float& iv) {
+        iv = cx.uinv[col];
+        o = *reinterpret_cast<const float2*>(&cx.Us[col * ULD + 32 * g + 2 * k]);
+#pragma unroll
+        for (int g2 = g + 1; g2 < G; ++g2)
+            l[g2] = *reinterpret_cast<const float2*>(&cx.Us[col * ULD + 32 * g2 + 2 * k]);
+    };
+    load_u(32 * g, uo, ul, ui);
 #pragma unroll
     for (int jj = 0; jj < 32; ++jj) {
         const int owner = jj >> 1, slot = jj & 1;
-        const float wj = __shfl(w[g][slot], cx.base_lane + owner, 64);
-        const float q = (s > 0.0f) ? fminf(fmaxf(rint_quot(wj, s, inv_s), -8.0f), 7.0f) : 0.0f;
-        const int col = 32 * g + jj;
-        const float e = (wj - q * s) * cx.uinv[col];
+        float2 uo_n = uo, ul_n[G];
+        float ui_n = ui;
+#pragma unroll
+        for (int g2 = g + 1; g2 < G; ++g2) ul_n[g2] = ul[g2];
+        if (jj + 1 < 32) load_u(32 * g + jj + 1, uo_n, ul_n, ui_n);
+        const float wj = row_bcast(w[g][slot], owner);
+        float q = fminf(fmaxf(rint_quot(wj, s, inv_s), -8.0f), 7.0f);
+        q = (s > 0.0f) ? q : 0.0f;
+        const float e = (wj - q * s) * ui;
+        // This lane's columns of the same group: U_jt is 0 for t < j, so the update touches
+        // only the later ones; the owner's column j then takes the residual.
+        w[g][0] -= e * uo.x;
+        w[g][1] -= e * uo.y;
         if (k == owner) {
             byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
-            w[g][slot] = e;  // the column is done: its slot now holds the residual
-        }
-        // This lane's later columns of the same group...
-        {
-            const float2 u = *reinterpret_cast<const float2*>(&cx.Us[col * ULD + 32 * g + 2 * k]);
-            const int t0 = 2 * k;
-            if (t0 > jj) w[g][0] -= e * u.x;
-            if (t0 + 1 > jj) w[g][1] -= e * u.y;
+            w[g][slot] = e;
         }
         // ... and all of its columns of the later groups of the block.
 #pragma unroll
         for (int g2 = g + 1; g2 < G; ++g2) {
-            const float2 u = *reinterpret_cast<const float2*>(&cx.Us[col * ULD + 32 * g2 + 2 * k]);
-            w[g2][0] -= e * u.x;
-            w[g2][1] -= e * u.y;
+            w[g2][0] -= e * ul[g2].x;
+            w[g2][1] -= e * ul[g2].y;
         }
+        uo = uo_n;
+        ui = ui_n;
+#pragma unroll
+        for (int g2 = g + 1; g2 < G; ++g2) ul[g2] = ul_n[g2];
+        __builtin_amdgcn_sched_barrier(0);
     }
     nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
     *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
@@ -249,9 +311,13 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     __shared__ float uinv[SB];
     __shared__ float tabs[16 * 32];
     const int tid = threadIdx.x;
+    // The block's U with its entries below the diagonal set to 0 (only the upper triangle of U
+    // is read): the feedback of column j then runs unconditionally over every column.
     for (int e = tid; e < NC * (NC / 4); e += 256) {
         const int j = e / (NC / 4), t4 = (e % (NC / 4)) * 4;
         f32x4 v = *reinterpret_cast<const f32x4*>(U + (c0 + j) * n + c0 + t4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (t4 + q < j) ? 0.0f : v[q];
         *reinterpret_cast<f32x4*>(&Us[j * ULD + t4]) = v;
     }
     if (tid < NC) {
@@ -283,7 +349,6 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     cx.lo = lost[r * 2];
     cx.st = lost[r * 2 + 1];
     cx.k = k;
-    cx.base_lane = (tid & 63) & ~15;
     block_group<G, 0>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
 }
 
