@@ -106,6 +106,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gram", action="store_true", help="skip the Hessian accumulation timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size reference for "
                          "hardware traffic counters)")
@@ -237,6 +238,27 @@ def main():
             "n_dead": rep["n_dead"],
         },
     }
+    # The device Hessian accumulation (a next-step row of the path, not part of the step):
+    # H += X^T X for X [T, n] tokens x channels at the same shape, timed alone on the stream.
+    if not args.no_gram:
+        Xg = workloads.activations(spec, device=dev)
+        Hg = torch.zeros(n, n, dtype=torch.float32, device=dev)
+        pwq.gptq_gram_add(Hg, Xg)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pwq.gptq_gram_add(Hg, Xg)
+        e1.record(stream)
+        e1.synchronize()
+        gram_ms = e0.elapsed_time(e1) / reps
+        gram_flops = float(n) * (n + 1) * Xg.shape[0]
+        result["detail"]["gram_ms"] = gram_ms
+        result["detail"]["gram_tflops"] = gram_flops / (gram_ms * 1e-3) / 1e12
+        result["detail"]["gram_frac_fp32_mfma"] = result["detail"]["gram_tflops"] / FP32_MFMA_PEAK_TFLOPS
+        result["detail"]["gram_shape"] = f"H[{n},{n}] += X^T X, X[{Xg.shape[0]},{n}]"
+        del Xg, Hg
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows)

@@ -20,8 +20,8 @@
  *   - Matrices are row-major f32.  Every pointer argument except `report` is DEVICE memory
  *     owned by the caller; the library allocates nothing and keeps no per-call state.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on it.
- *     gptq_fold and gptq_sweep also run part of it on a helper stream of the library's own
- *     (default priority, one per concurrent call) that waits on `stream` and is joined back
+ *     gptq_fold and gptq_sweep also run parts of it on helper streams of the library's own
+ *     (default priority, two per concurrent call) that wait on `stream` and are joined back
  *     into it before the call returns, so `stream` orders everything the call does.
  *   - Return value: a GPTQ_* status.  On GPTQ_EINVAL or GPTQ_EWORKSPACE nothing is written.
  *   - Calls on different streams may run concurrently if their buffers are disjoint.
@@ -81,8 +81,8 @@ size_t gptq_fold_workspace_size(int64_t n);
  *
  * Steps on the device: diagonal, dead mask and mean (f64) -> per attempt: D_i^-1 =
  * (H_ii + damp)^-1/2 (dead: (1 + damp)^-1/2), the reversed equilibrated matrix
- * A = P D^-1 H_d D^-1 P, blocked Cholesky A = L L^T fused with the blocked right-looking
- * inverse X = L^-1 -> U = P X P D^-1.  The host reads the pivot flag once per attempt
+ * A = P D^-1 H_d D^-1 P, blocked Cholesky A = L L^T and, one 512-column panel behind on a
+ * helper stream, the blocked right-looking inverse X = L^-1 -> U = P X P D^-1.  The host reads the pivot flag once per attempt
  * (one stream synchronisation); U is still being written when the call returns.
  */
 int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, float* U, float* hdiag,
@@ -134,6 +134,26 @@ int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t
                const float* tab, const float* lost, int64_t rows, int64_t n, uint8_t* nib,
                uint8_t* rung, float* scale, float* E, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * gptq_gram_add -- accumulate one batch of layer inputs into the device Hessian.
+ * Source: page "cortiq-cli 0.8.45 src/gptq.rs" (calibration adds every window's inputs to a
+ * device Hessian, gram_add_dev; the test device_fold_and_sweep_match_host accumulates
+ * h[i][j] += x[r][i] x[r][j] over the rows of x [t, n]); the fold reads the upper triangle.
+ *
+ *   H      [n, ldh] f32, device, in/out: H[i][j] += sum_{k < t} X[k][i] X[k][j] for j >= i
+ *          (the upper triangle with the diagonal, which gptq_fold reads).  The lower triangle
+ *          is neither read nor written.  f32 products, f32 MFMA accumulation (the pages'
+ *          device Hessian is f32).
+ *   n      channels: 4 <= n, n % 4 == 0, ldh >= n.
+ *   X      [t, ldx] f32, device, row-major: one row per token, column i = input channel i;
+ *          16-byte aligned, ldx >= n, ldx % 4 == 0.  Read only.
+ *   t      tokens in this batch, >= 0 (0: nothing is done and X may be NULL).  Any t: the
+ *          last block of 32 tokens is zero-filled.
+ * Returns GPTQ_OK, GPTQ_EINVAL (nothing written) or GPTQ_EHIP.  Asynchronous on `stream`.
+ */
+int gptq_gram_add(float* H, int64_t n, int64_t ldh, const float* X, int64_t t, int64_t ldx,
+                  void* stream);
 
 /* Static string for a GPTQ_* status. */
 const char* gptq_status_string(int status);

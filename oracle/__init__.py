@@ -13,6 +13,10 @@ What each function follows (docs.rs source pages of the cortiq project):
 * :func:`sweep` -- "cortiq-cli 0.8.45 src/gptq.rs", ``gptq_quantize_q4tp``, and
   "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs", ``q4tp_group``: rung rule, rounding and
   column-by-column error feedback.
+* :func:`gram` -- the device Hessian's accumulation ``H += X^T X`` over the rows (tokens) of an
+  activation matrix ``X [t, n]`` ("cortiq-cli 0.8.45 src/gptq.rs": calibration's
+  ``gram_add_dev`` and the test ``device_fold_and_sweep_match_host``, which accumulates
+  ``h[i][j] += x[r][i] x[r][j]``), in f64 from the f32 inputs.
 * :func:`output_error` -- the layer-output error ``tr(dW H dW^T)`` with the raw Hessian, the
   quantity the pages' device-versus-host test compares ("cortiq-cli 0.8.45 src/gptq.rs",
   test ``device_fold_and_sweep_match_host``).
@@ -175,3 +179,15 @@ def output_error(W0, dead, code, scale, H, gs=32):
     Hu = np.triu(np.asarray(H, dtype=np.float64))
     Hs = Hu + np.triu(Hu, 1).T
     return float(np.einsum("ij,ij->", dW @ Hs, dW))
+
+
+def gram(X, H0=None):
+    """H0 + X^T X in f64 for X [t, n] (tokens x channels): the definition, one library matmul.
+    Also returns the elementwise magnitude |X|^T |X|, the scale of any summation's rounding."""
+    X = np.asarray(X, dtype=np.float64)
+    H = X.T @ X
+    if H0 is not None:
+        H = H + np.asarray(H0, dtype=np.float64)
+    A = np.abs(X)
+    return H, A.T @ A
+

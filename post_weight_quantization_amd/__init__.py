@@ -60,6 +60,8 @@ def load():
     lib.gptq_sweep_workspace_size.restype = sz
     lib.gptq_sweep.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
     lib.gptq_sweep.restype = ctypes.c_int
+    lib.gptq_gram_add.argtypes = [P, i64, i64, P, i64, i64, P]
+    lib.gptq_gram_add.restype = ctypes.c_int
     lib.gptq_status_string.argtypes = [ctypes.c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_profile_enable.argtypes = [ctypes.c_uint]
@@ -189,8 +191,22 @@ def gptq_sweep(W, U, hdiag, dead, tab, lost, want_E=False, workspace=None, strea
     return nib, rung, scale, E
 
 
+def gptq_gram_add(H: torch.Tensor, X: torch.Tensor, stream=None):
+    """H (f32 [n, n], device) += X^T X on its upper triangle, X f32 [t, n] (tokens x channels).
+    Returns H."""
+    lib = load()
+    n = H.shape[0]
+    if X.dim() != 2 or X.shape[1] != n:
+        raise ValueError("X must be [t, n] with n = H.shape[0]")
+    st = lib.gptq_gram_add(_dev(H, torch.float32, "H"), n, H.stride(0),
+                           _dev(X, torch.float32, "X"), X.shape[0], X.stride(0), _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_gram_add")
+    return H
+
+
 PROFILE_FAMILIES = ["fold_update", "fold_panel", "fold_diag", "fold_build", "fold_make_u",
-                    "sweep_group", "sweep_trail", "ladder", "fold_next", "sweep_next"]
+                    "sweep_group", "sweep_trail", "ladder", "fold_next", "sweep_next", "gram"]
 
 
 def profile_enable(families=None):
@@ -245,6 +261,6 @@ def check_selftest(which: int) -> int:
     return int(load().gptq_check_selftest(int(which)))
 
 
-__all__ = ["check_mode", "check_message", "check_selftest", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
+__all__ = ["check_mode", "check_message", "check_selftest", "gptq_gram_add", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
            "profile_collect", "LIB_PATH"]

@@ -84,3 +84,11 @@ def test_undersized_buffers_are_caught(lib):
         st = lib.gptq_fold(H, n, n, 0.01, U, hd, dead, ws, lib.gptq_fold_workspace_size(n) - 1,
                            None, ctypes.byref(rep))
     assert st == pwq.GPTQ_EWORKSPACE
+
+
+@pytest.mark.parametrize("n,t", [(4, 1), (200, 777), (4096, 8192), (17408, 32768)])
+def test_gram_schedule(lib, n, t):
+    H, X = addrs(2)
+    with pwq.check_mode():
+        st = lib.gptq_gram_add(H, n, n, X, t, n, None)
+    assert st == GPTQ_OK, pwq.check_message()

@@ -134,10 +134,8 @@ def make(name: str, k: int = 0, device="cpu", n: int | None = None, rows: int | 
     return H, W, spec.lam
 
 
-def fixture(device="cpu"):
-    """The pages' device-versus-host test data: n=160 channels, 48 rows, 700 samples
-    (element formulas evaluated in f32, the Hessian summed in f64 then stored as f32)."""
-    n, rows, t = 160, 48, 700
+def _fixture_x():
+    n, t = 160, 700
     ri = torch.arange(t).unsqueeze(1)
     ci = torch.arange(n).unsqueeze(0)
     f32 = torch.float32
@@ -146,6 +144,33 @@ def fixture(device="cpu"):
     loud = torch.where(ci % 41 == 3, torch.tensor(30.0), torch.tensor(1.0)).to(f32)
     x = (v + 0.3 * base) * loud
     x[:, [17, 90]] = 0.0
+    return x
+
+
+def pages_fixture_activations():
+    """The activations x [700, 160] (tokens x channels, f32) of the pages' device-versus-host
+    test, whose Hessian is sum over tokens of x_r^T x_r; channels 17 and 90 are dead."""
+    return _fixture_x().numpy()
+
+
+def activations(spec: Spec, k: int = 0, T: int | None = None, n: int | None = None,
+                device="cpu", seed_offset: int = 7):
+    """X [T, n] f32, tokens x channels, with the workload's channel energies and dead channels
+    (the layout the Hessian accumulation takes; drawn from its own seed)."""
+    n = spec.n if n is None else n
+    T = spec.T if T is None else T
+    scale, keep, _ = channel_scales(spec, k, n, device)
+    g = _gen(1000 * spec.cfg + 2 * k + seed_offset, device)
+    X = torch.randn(T, n, generator=g, device=device, dtype=torch.float32)
+    return X * (scale * keep).unsqueeze(0)
+
+
+def fixture(device="cpu"):
+    """The pages' device-versus-host test data: n=160 channels, 48 rows, 700 samples
+    (element formulas evaluated in f32, the Hessian summed in f64 then stored as f32)."""
+    n, rows = 160, 48
+    x = _fixture_x()
+    f32 = torch.float32
     H = (x.double().t() @ x.double()).float()
     kk = torch.arange(rows * n, dtype=torch.int64)
     w = (((kk * 2654435761) % 2003).to(f32) / 2003.0 - 0.5) * 0.08
@@ -187,4 +212,4 @@ def sizes(name: str):
 
 
 __all__ = ["SPECS", "Spec", "make", "hessian", "weights", "fixture", "lcg_fixture", "sizes",
-           "channel_scales"]
+           "channel_scales", "activations", "pages_fixture_activations"]
