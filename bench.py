@@ -107,6 +107,7 @@ def main():
     ap.add_argument("--workload", default="down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gram", action="store_true", help="skip the Hessian accumulation timing")
+    ap.add_argument("--no-debias", action="store_true", help="skip the output debias timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size reference for "
                          "hardware traffic counters)")
@@ -259,6 +260,26 @@ def main():
         result["detail"]["gram_frac_fp32_mfma"] = result["detail"]["gram_tflops"] / FP32_MFMA_PEAK_TFLOPS
         result["detail"]["gram_shape"] = f"H[{n},{n}] += X^T X, X[{Xg.shape[0]},{n}]"
         del Xg, Hg
+    # The output debias on the step's codes (a next-step row of the path, not part of the step):
+    # symmetrised H, the product W H and the per-row slopes, timed alone on the stream.
+    if not args.no_debias:
+        ws_d = torch.empty(pwq.debias_workspace_size(rows, n), dtype=torch.uint8, device=dev)
+        lost_d, scale_d = lost.clone(), scale.clone()
+        pwq.gptq_debias(W, H, dead, nib, rung, lost_d, scale_d, workspace=ws_d)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            lost_d.copy_(lost)
+            scale_d.copy_(scale)
+            pwq.gptq_debias(W, H, dead, nib, rung, lost_d, scale_d, workspace=ws_d)
+        e1.record(stream)
+        e1.synchronize()
+        debias_ms = e0.elapsed_time(e1) / reps
+        result["detail"]["debias_ms"] = debias_ms
+        result["detail"]["debias_gemm_tflops_whole_call"] = 2.0 * rows * n * n / (debias_ms * 1e-3) / 1e12
+        del ws_d, lost_d, scale_d
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows)

@@ -155,6 +155,38 @@ int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t
 int gptq_gram_add(float* H, int64_t n, int64_t ldh, const float* X, int64_t t, int64_t ldx,
                   void* stream);
 
+/* Bytes of device workspace gptq_debias needs: n x n f32 (the symmetrised Hessian) plus
+ * rows x n f32 (W H).  0 for rows <= 0 or n <= 0. */
+size_t gptq_debias_workspace_size(int64_t rows, int64_t n);
+
+/*
+ * gptq_debias -- output debias of a quantized layer in the calibration metric.
+ * Source: page "cortiq-cli 0.8.45 src/gptq.rs", q4tp_debias_hessian / q2tp_debias_hessian and
+ * their GEMM form debias_gemm: per row, the regression slope b = (W^ H W^T)_rr / (W H W^T)_rr
+ * is removed through the row's f16 lo; codes, rungs and steps stay.  The helper that applies b
+ * is not printed on the pages; the reading implemented: lo <- f16(lo - log2 b) (round to
+ * nearest even), kept when num or den is not positive and finite.
+ *
+ *   W      [rows, n] f32, device: the original weights (dead columns read as 0).
+ *   H      [n, ldh] f32, device: the raw Hessian, upper triangle read (as gptq_fold).  Dead
+ *          channels (dead[i] != 0) count as zero rows and columns.
+ *   dead   [n] u8, device (gptq_fold's output).
+ *   nib, rung   gptq_sweep's codes: nibble plane [rows, n/2] and rungs [rows, n/32].
+ *   lost   [rows, 2] f32, device, in/out: (lo, step); lo is replaced.
+ *   tab    [rows, 32] f32 out or NULL: the row's new rung scales f32(2^(lo + c*step)) (f64).
+ *   scale  [rows, n/32] f32, device, in/out: in, the scales the codes were made with (W^ =
+ *          (nib - 8) * scale); out, TAB_new[rung].
+ *   slope  [rows] f64 out or NULL: b = num / den (num, den summed in f64 over f32 products;
+ *          W H is an f32 MFMA product, as the pages' GEMM form).
+ *   n % 32 == 0.  Workspace: gptq_debias_workspace_size(rows, n).
+ * Returns GPTQ_OK, GPTQ_EINVAL / GPTQ_EWORKSPACE (nothing written) or GPTQ_EHIP.
+ * Asynchronous on `stream`.
+ */
+int gptq_debias(const float* W, const float* H, int64_t ldh, const uint8_t* dead,
+                const uint8_t* nib, const uint8_t* rung, float* lost, float* tab, float* scale,
+                double* slope, int64_t rows, int64_t n, void* workspace, size_t workspace_bytes,
+                void* stream);
+
 /* Static string for a GPTQ_* status. */
 const char* gptq_status_string(int status);
 

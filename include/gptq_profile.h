@@ -17,6 +17,7 @@
  *   8 fold_next    look-ahead part of the update: next block column and next block row
  *   9 sweep_next   sweep updates on the serial chain: rest of the panel, next panel
  *  10 gram         Hessian accumulation H += X^T X (gptq_gram_add)
+ *  11 debias       output debias: symmetrised H, W H, per-row slopes (gptq_debias)
  * The recording adds two event records per timed launch; the mask is 0 by default.
  */
 #ifndef GPTQ_MI355X_PROFILE_H

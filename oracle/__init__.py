@@ -17,6 +17,10 @@ What each function follows (docs.rs source pages of the cortiq project):
   activation matrix ``X [t, n]`` ("cortiq-cli 0.8.45 src/gptq.rs": calibration's
   ``gram_add_dev`` and the test ``device_fold_and_sweep_match_host``, which accumulates
   ``h[i][j] += x[r][i] x[r][j]``), in f64 from the f32 inputs.
+* :func:`debias` -- the output debias ("cortiq-cli 0.8.45 src/gptq.rs", ``q4tp_debias_hessian``
+  and its GEMM form ``debias_gemm``): per row the slope ``b = (W^ H W^T)_rr / (W H W^T)_rr``
+  removed through the row's f16 ``lo``.  The helper that applies ``b`` is not printed; the
+  reading is ``lo <- f16(lo - log2 b)``, kept unless num and den are positive and finite.
 * :func:`output_error` -- the layer-output error ``tr(dW H dW^T)`` with the raw Hessian, the
   quantity the pages' device-versus-host test compares ("cortiq-cli 0.8.45 src/gptq.rs",
   test ``device_fold_and_sweep_match_host``).
@@ -190,4 +194,54 @@ def gram(X, H0=None):
         H = H + np.asarray(H0, dtype=np.float64)
     A = np.abs(X)
     return H, A.T @ A
+
+
+def symmetric_from_upper(H, dead=None):
+    """H read through its upper triangle, f64, dead channels' rows and columns zeroed."""
+    H = np.asarray(H, dtype=np.float64)
+    Hs = np.triu(H) + np.triu(H, 1).T
+    if dead is not None:
+        d = np.asarray(dead, dtype=bool)
+        Hs[d, :] = 0.0
+        Hs[:, d] = 0.0
+    return Hs
+
+
+def debias(W0, H, dead, code, rung, lost, scale, gs=32, rows=None):
+    """Output debias in f64.  ``code`` [rows, n] (0..15), ``rung`` [rows, n/gs], ``lost``
+    [rows, 2] (lo, step), ``scale`` [rows, n/gs] the scales the codes were made with.  ``rows``
+    restricts the work to those row indices.  Returns dict(num, den, b, v = lo - log2 b before
+    rounding (nan where lo is kept), lo, tab [rows, 32], scale)."""
+    W0 = np.asarray(W0, dtype=np.float32)
+    sel = np.arange(W0.shape[0]) if rows is None else np.asarray(rows)
+    d = np.asarray(dead, dtype=bool)
+    Wd = W0[sel].astype(np.float64)
+    Wd[:, d] = 0.0
+    What = dequant(np.asarray(code)[sel], np.asarray(scale)[sel], gs)
+    Y = Wd @ symmetric_from_upper(H, d)          # H w for each row (H symmetric)
+    num = np.sum(What * Y, axis=1)
+    den = np.sum(Wd * Y, axis=1)
+    lo = np.asarray(lost, dtype=np.float64)[sel, 0].copy()
+    st = np.asarray(lost, dtype=np.float64)[sel, 1]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        b = num / den
+    v = np.full(len(sel), np.nan)
+    for k in range(len(sel)):
+        if num[k] > 0 and den[k] > 0 and np.isfinite(b[k]) and b[k] > 0:
+            v[k] = lo[k] - np.log2(b[k])
+            lo2 = f16_round(v[k])
+            if np.isfinite(lo2):
+                lo[k] = lo2
+    tab = np.float32(np.exp2(lo[:, None] + np.arange(32)[None, :] * st[:, None]))
+    rg = np.asarray(rung)[sel].astype(np.int64) & 31
+    new_scale = np.take_along_axis(tab, rg, axis=1)
+    return dict(num=num, den=den, b=b, v=v, lo=lo, tab=tab, scale=new_scale)
+
+
+def f16_ulp(x: float) -> float:
+    """Spacing of binary16 values at |x| (normal range)."""
+    a = abs(float(x))
+    if a < 2.0 ** -14:
+        return 2.0 ** -24
+    return 2.0 ** (np.floor(np.log2(a)) - 10)
 

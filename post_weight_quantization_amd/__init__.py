@@ -62,6 +62,10 @@ def load():
     lib.gptq_sweep.restype = ctypes.c_int
     lib.gptq_gram_add.argtypes = [P, i64, i64, P, i64, i64, P]
     lib.gptq_gram_add.restype = ctypes.c_int
+    lib.gptq_debias_workspace_size.argtypes = [i64, i64]
+    lib.gptq_debias_workspace_size.restype = sz
+    lib.gptq_debias.argtypes = [P, P, i64, P, P, P, P, P, P, P, i64, i64, P, sz, P]
+    lib.gptq_debias.restype = ctypes.c_int
     lib.gptq_status_string.argtypes = [ctypes.c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_profile_enable.argtypes = [ctypes.c_uint]
@@ -205,8 +209,39 @@ def gptq_gram_add(H: torch.Tensor, X: torch.Tensor, stream=None):
     return H
 
 
+def debias_workspace_size(rows: int, n: int) -> int:
+    return int(load().gptq_debias_workspace_size(int(rows), int(n)))
+
+
+def gptq_debias(W, H, dead, nib, rung, lost, scale, want_tab=True, want_slope=True,
+                workspace=None, stream=None):
+    """Output debias in place on (lost, scale).  Returns (lost, tab or None, scale,
+    slope f64 [rows] or None)."""
+    lib = load()
+    rows, n = W.shape
+    dev = W.device
+    tab = torch.empty(rows, 32, dtype=torch.float32, device=dev) if want_tab else None
+    slope = torch.empty(rows, dtype=torch.float64, device=dev) if want_slope else None
+    if workspace is None:
+        workspace = torch.empty(lib.gptq_debias_workspace_size(rows, n), dtype=torch.uint8,
+                                device=dev)
+    if H.stride(1) != 1:
+        raise ValueError("H must be row-major")
+    st = lib.gptq_debias(_dev(W, torch.float32, "W"), ctypes.c_void_p(H.data_ptr()), H.stride(0),
+                         _dev(dead, torch.uint8, "dead"), _dev(nib, torch.uint8, "nib"),
+                         _dev(rung, torch.uint8, "rung"), _dev(lost, torch.float32, "lost"),
+                         None if tab is None else _dev(tab, torch.float32, "tab"),
+                         _dev(scale, torch.float32, "scale"),
+                         None if slope is None else _dev(slope, torch.float64, "slope"),
+                         rows, n, _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                         _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_debias")
+    return lost, tab, scale, slope
+
+
 PROFILE_FAMILIES = ["fold_update", "fold_panel", "fold_diag", "fold_build", "fold_make_u",
-                    "sweep_group", "sweep_trail", "ladder", "fold_next", "sweep_next", "gram"]
+                    "sweep_group", "sweep_trail", "ladder", "fold_next", "sweep_next", "gram", "debias"]
 
 
 def profile_enable(families=None):
@@ -261,6 +296,7 @@ def check_selftest(which: int) -> int:
     return int(load().gptq_check_selftest(int(which)))
 
 
-__all__ = ["check_mode", "check_message", "check_selftest", "gptq_gram_add", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
+__all__ = ["check_mode", "check_message", "check_selftest", "gptq_gram_add", "gptq_debias",
+           "debias_workspace_size", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
            "profile_collect", "LIB_PATH"]

@@ -151,6 +151,6 @@ extern "C" int gptq_profile_family_count(void) { return FAM_COUNT; }
 extern "C" const char* gptq_profile_family_name(int fam) {
     static const char* names[FAM_COUNT] = {"fold_update", "fold_panel", "fold_diag", "fold_build",
                                            "fold_make_u", "sweep_group", "sweep_trail", "ladder",
-                                           "fold_next", "sweep_next", "gram"};
+                                           "fold_next", "sweep_next", "gram", "debias"};
     return (fam >= 0 && fam < FAM_COUNT) ? names[fam] : "?";
 }

@@ -27,7 +27,8 @@ enum Family {
     FAM_FOLD_NEXT = 8,    // look-ahead update of the next block column / block row
     FAM_SWEEP_NEXT = 9,   // sweep updates on the serial chain: rest of the panel, next panel
     FAM_GRAM = 10,        // Hessian accumulation H += X^T X
-    FAM_COUNT = 11
+    FAM_DEBIAS = 11,      // output debias: symmetrised H, W H, per-row slopes
+    FAM_COUNT = 12
 };
 
 // Two helper streams (non-blocking, default priority) and three events, taken from a

@@ -92,3 +92,13 @@ def test_gram_schedule(lib, n, t):
     with pwq.check_mode():
         st = lib.gptq_gram_add(H, n, n, X, t, n, None)
     assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(1, 32), (70, 160), (5120, 17408)])
+def test_debias_schedule(lib, rows, n):
+    W, H, dead, nib, rung, lost, tab, scale, slope, ws = addrs(10)
+    need = lib.gptq_debias_workspace_size(rows, n)
+    with pwq.check_mode():
+        st = lib.gptq_debias(W, H, n, dead, nib, rung, lost, tab, scale, slope, rows, n, ws,
+                             need, None)
+    assert st == GPTQ_OK, pwq.check_message()
