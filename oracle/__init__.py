@@ -21,6 +21,12 @@ What each function follows (docs.rs source pages of the cortiq project):
   and its GEMM form ``debias_gemm``): per row the slope ``b = (W^ H W^T)_rr / (W H W^T)_rr``
   removed through the row's f16 ``lo``.  The helper that applies ``b`` is not printed; the
   reading is ``lo <- f16(lo - log2 b)``, kept unless num and den are positive and finite.
+* :func:`act_order_perm`, :func:`sweep_act_order` -- act-order GPTQ ("cortiq-cli 0.8.45
+  src/gptq.rs", ``act_order_perm``, ``permute_sym``, ``gptq_quantize_q4tp_act_order``): channels
+  in descending ``H_ii`` (total order, ties by index), the fold of ``H[perm][perm]``, static
+  rungs chosen up front from the original tiles, columns eliminated in ``perm`` order.  The
+  converter's rung choice is not printed; the reading is the sweep's rung rule on the
+  dead-zeroed original tile with unit weights.
 * :func:`output_error` -- the layer-output error ``tr(dW H dW^T)`` with the raw Hessian, the
   quantity the pages' device-versus-host test compares ("cortiq-cli 0.8.45 src/gptq.rs",
   test ``device_fold_and_sweep_match_host``).
@@ -65,6 +71,8 @@ def _load():
     lib.orc_fold.restype = ctypes.c_int
     lib.orc_ladder.argtypes = [P, P, i64, i64, i64, P, P]
     lib.orc_ladder.restype = None
+    lib.orc_sweep_static.argtypes = [P, i64, i64, P, P, P, P, P, ctypes.c_double, P, ctypes.c_int]
+    lib.orc_sweep_static.restype = ctypes.c_int
     lib.orc_sweep.argtypes = [P, i64, i64, i64, P, P, P, P, P, P, P, P, P, P, P, P,
                               ctypes.c_double, ctypes.c_double, P, ctypes.c_int]
     lib.orc_sweep.restype = ctypes.c_int
@@ -244,4 +252,64 @@ def f16_ulp(x: float) -> float:
     if a < 2.0 ** -14:
         return 2.0 ** -24
     return 2.0 ** (np.floor(np.log2(a)) - 10)
+
+
+def _total_key(x: np.float32) -> int:
+    """The f32 total order as an integer (-NaN < -inf < ... < -0 < +0 < ... < +inf < +NaN)."""
+    b = int(np.asarray(x, dtype=np.float32).view(np.int32))
+    return b if b >= 0 else b ^ 0x7FFFFFFF
+
+
+def act_order_perm(hdiag):
+    """Channel order for act-order GPTQ: descending H_ii in the f32 total order, ties by
+    ascending index."""
+    h = np.asarray(hdiag, dtype=np.float32)
+    return np.array(sorted(range(len(h)), key=lambda i: (-_total_key(h[i]), i)), dtype=np.int64)
+
+
+def permute_sym(H, perm):
+    """H[perm][perm] of the Hessian read through its upper triangle (f64)."""
+    Hs = symmetric_from_upper(H)
+    p = np.asarray(perm)
+    return Hs[np.ix_(p, p)]
+
+
+def static_rungs(W0, dead, tab, lost, gs=32):
+    """The rung of every (row, group) chosen up front from the dead-zeroed original tile: the
+    sweep's rung rule with unit weights and no error feedback (U = I)."""
+    n = np.asarray(W0).shape[1]
+    r = sweep(W0, np.eye(n), np.ones(n, np.float32), dead, tab, lost, gs=gs, want_E=False)
+    return r["rung"], r["scale"]
+
+
+def sweep_act_order(W0, Up, dead, perm, tab, lost, gs=32, rung=None, force_code=None,
+                    tie_band=1e-3, want_E=True, nt=None):
+    """Act-order q4tp sweep.  ``Up`` is the fold operator of H[perm][perm]; ``dead`` is in
+    original channel order.  Returns code (rows x n, original order, q + 8), rung and scale
+    (static), E (elimination order) and the tie statistics of a forced replay (force_code in
+    original order)."""
+    W0 = np.asarray(W0, dtype=np.float32)
+    rows, n = W0.shape
+    d = np.asarray(dead, dtype=bool)
+    p = np.asarray(perm, dtype=np.int64)
+    if rung is None:
+        rung, scale = static_rungs(W0, d, tab, lost, gs)
+    else:
+        rung = np.asarray(rung, dtype=np.uint8)
+        scale = np.take_along_axis(np.asarray(tab, np.float32), rung.astype(np.int64) & 31, 1)
+    Wd = W0.copy()
+    Wd[:, d] = 0.0
+    Wp = np.ascontiguousarray(Wd[:, p])
+    sp = np.ascontiguousarray(np.repeat(scale, gs, axis=1)[:, p], dtype=np.float32)
+    Upc = np.ascontiguousarray(Up, dtype=np.float64)
+    code_p = np.empty((rows, n), dtype=np.uint8)
+    E = np.empty((rows, n), dtype=np.float64) if want_E else None
+    fc = None if force_code is None else np.ascontiguousarray(np.asarray(force_code)[:, p], dtype=np.uint8)
+    stats = np.zeros(2, dtype=np.int64)
+    _load().orc_sweep_static(_ptr(Wp), rows, n, _ptr(Upc), _ptr(sp), _ptr(code_p), _ptr(E),
+                             _ptr(fc), float(tie_band), _ptr(stats), threads(nt))
+    code = np.empty_like(code_p)
+    code[:, p] = code_p
+    return dict(code=code, rung=rung, scale=scale, E=E,
+                stats=dict(code_ties=int(stats[0]), code_hard=int(stats[1])))
 

@@ -469,4 +469,63 @@ int orc_sweep(const float* W0, int64_t rows, int64_t n, int64_t gs, const double
     return ORC_OK;
 }
 
+/*
+ * Act-order sweep with static groups ([gptq.rs] gptq_quantize_q4tp_act_order): the columns of
+ * Wp (rows x n, already in elimination order and dead-zeroed) are eliminated in order with the
+ * fold operator Up of the permuted Hessian, each column a with its own fixed scale sp[r][a]
+ * (the rung of its original group, chosen up front):
+ *   q = (s > 0) ? clamp(rne(f32(w_a) / s), -8, 7) : 0,  code = q + 8,
+ *   e_a = (Up_aa > 0) ? (w_a - q s) / Up_aa : 0,  w_t -= e_a Up_at for every t > a.
+ * code_p and E are in elimination order.  force_code: tie-forced replay as in orc_sweep.
+ */
+int orc_sweep_static(const float* Wp, int64_t rows, int64_t n, const double* Up, const float* sp,
+                     uint8_t* code_p, double* E, const uint8_t* force_code, double tie_band,
+                     int64_t* stats, int nt) {
+    const int64_t RB = 16;
+    int64_t ct = 0, ch = 0;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(+ : ct, ch)
+    for (int64_t r0 = 0; r0 < rows; r0 += RB) {
+        int64_t rb = imin(RB, rows - r0);
+        double* w = (double*)malloc(sizeof(double) * (size_t)(rb * n));
+        double e[16];
+        for (int64_t k = 0; k < rb; ++k)
+            for (int64_t a = 0; a < n; ++a) w[k * n + a] = (double)Wp[(r0 + k) * n + a];
+        for (int64_t a = 0; a < n; ++a) {
+            double uaa = Up[a * n + a];
+            for (int64_t k = 0; k < rb; ++k) {
+                int64_t r = r0 + k;
+                double wa = w[k * n + a];
+                float s = sp[r * n + a];
+                float q = 0.0f;
+                if (s > 0.0f) q = clampf(rne_f32((float)wa / s), -8.0f, 7.0f);
+                if (force_code) {
+                    float fq = (float)force_code[r * n + a] - 8.0f;
+                    if (fq != q) {
+                        double x = fabs((double)((float)wa / s));
+                        double fr = x - floor(x);
+                        if (fabsf(fq - q) == 1.0f && fabs(fr - 0.5) < tie_band) ++ct; else ++ch;
+                        q = fq;
+                    }
+                }
+                code_p[r * n + a] = (uint8_t)(q + 8.0f);
+                e[k] = (uaa > 0.0) ? (wa - (double)q * (double)s) / uaa : 0.0;
+                if (E) E[r * n + a] = e[k];
+            }
+            const double* urow = Up + a * n;
+            for (int64_t k = 0; k < rb; ++k) {
+                double ek = e[k];
+                if (ek == 0.0) continue;
+                double* wr = w + k * n;
+                for (int64_t t = a + 1; t < n; ++t) wr[t] -= ek * urow[t];
+            }
+        }
+        free(w);
+    }
+    if (stats) {
+        stats[0] = ct;
+        stats[1] = ch;
+    }
+    return ORC_OK;
+}
+
 int orc_max_threads(void) { return omp_get_max_threads(); }
