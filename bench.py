@@ -108,6 +108,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gram", action="store_true", help="skip the Hessian accumulation timing")
     ap.add_argument("--no-debias", action="store_true", help="skip the output debias timing")
+    ap.add_argument("--no-act-order", action="store_true", help="skip the act-order timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size reference for "
                          "hardware traffic counters)")
@@ -260,6 +261,34 @@ def main():
         result["detail"]["gram_frac_fp32_mfma"] = result["detail"]["gram_tflops"] / FP32_MFMA_PEAK_TFLOPS
         result["detail"]["gram_shape"] = f"H[{n},{n}] += X^T X, X[{Xg.shape[0]},{n}]"
         del Xg, Hg
+    # Act-order GPTQ on the same layer (a next-step row, not part of the step): channel order,
+    # permuted Hessian, fold of it, ladder and the static-group sweep, timed as one group.
+    if not args.no_act_order:
+        ws_a = torch.empty(pwq.sweep_act_order_workspace_size(rows, n), dtype=torch.uint8,
+                           device=dev)
+
+        def ao_step():
+            perm_a, dead_a = pwq.gptq_act_order_perm(H)
+            Hp_a = pwq.gptq_permute_hessian(H, perm_a)
+            Ua, _, _, rep_a = pwq.gptq_fold(Hp_a, lam, workspace=ws_f)
+            del Hp_a
+            lost_a, tab_a = pwq.gptq_ladder(W, dead_a)
+            pwq.gptq_sweep_act_order(W, Ua, dead_a, perm_a, tab_a, lost_a, workspace=ws_a)
+            return rep_a
+
+        ao_step()
+        torch.cuda.synchronize()
+        reps = 2
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            rep_a = ao_step()
+        e1.record(stream)
+        e1.synchronize()
+        result["detail"]["act_order_ms"] = e0.elapsed_time(e1) / reps
+        result["detail"]["act_order_groups_per_s"] = 1e3 / result["detail"]["act_order_ms"]
+        result["detail"]["act_order_lambda_used"] = rep_a["lambda_used"]
+        del ws_a
     # The output debias on the step's codes (a next-step row of the path, not part of the step):
     # symmetrised H, the product W H and the per-row slopes, timed alone on the stream.
     if not args.no_debias:

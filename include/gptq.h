@@ -187,6 +187,53 @@ int gptq_debias(const float* W, const float* H, int64_t ldh, const uint8_t* dead
                 double* slope, int64_t rows, int64_t n, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/*
+ * Act-order GPTQ.  Source: page "cortiq-cli 0.8.45 src/gptq.rs": act_order_perm, permute_sym,
+ * gptq_quantize_q4tp_act_order.  The flow: gptq_act_order_perm(H) -> perm, dead;
+ * gptq_permute_hessian(H, perm) -> Hp; gptq_fold(Hp) -> Up (elimination order);
+ * gptq_ladder(W, dead); gptq_sweep_act_order(W, Up, dead, perm, ...).
+ *
+ * gptq_act_order_perm: perm [n] i32 out, the channels by descending H_ii compared in the f32
+ *   total order (-NaN < -inf < ... < -0 < +0 < ... < +inf < +NaN), ties by ascending index;
+ *   dead [n] u8 out, 1 where !(H_ii > 0) (original order).  H [n, ldh] f32, only its diagonal
+ *   is read.
+ */
+int gptq_act_order_perm(const float* H, int64_t n, int64_t ldh, int32_t* perm, uint8_t* dead,
+                        void* stream);
+
+/* gptq_permute_hessian: Hp [n, n] f32 out (full, symmetric) = H[perm][perm], H read through its
+ * upper triangle (H[min][max]).  perm must be a permutation of 0..n-1; an entry outside that
+ * range gives zero rows and columns. */
+int gptq_permute_hessian(const float* H, int64_t n, int64_t ldh, const int32_t* perm, float* Hp,
+                         void* stream);
+
+/* Bytes of device workspace gptq_sweep_act_order needs: gptq_sweep's plus rows x n f32 (the
+ * per-column scales), rows x n bytes (the codes) and n i32. */
+size_t gptq_sweep_act_order_workspace_size(int64_t rows, int64_t n);
+
+/*
+ * gptq_sweep_act_order -- the q4tp sweep with the columns eliminated in perm order ("static
+ * groups": a tile's channels are no longer consecutive in time, so its rung is fixed up front).
+ *
+ *   W      [rows, n] f32 (original channel order), read only.
+ *   U      [n, n] f32: gptq_fold of gptq_permute_hessian(H, perm) (elimination order).
+ *   dead   [n] u8, original order (gptq_act_order_perm's output).
+ *   perm   [n] i32, the elimination order.
+ *   tab, lost   gptq_ladder(W, dead).
+ *   nib, rung, scale  out, as gptq_sweep (original order).  rung / scale are the static choice:
+ *          the sweep's rung rule on the dead-zeroed original tile with unit weights (the
+ *          pages take it from their converter, whose rule is not printed: a stated reading),
+ *          the error summed in f32 in column order.
+ *   E      [rows, n] f32 out (elimination order) or NULL.
+ *   Per column a of the elimination order: q = clamp(rne(w_a / s_a), -8, 7) with s_a the static
+ *   scale of channel perm[a]'s group, e_a = (w_a - q s_a) / U_aa, w_t -= e_a U_at for t > a.
+ *   rows <= 65535, n % 32 == 0.  Workspace: gptq_sweep_act_order_workspace_size(rows, n).
+ */
+int gptq_sweep_act_order(const float* W, const float* U, const uint8_t* dead, const int32_t* perm,
+                         const float* tab, const float* lost, int64_t rows, int64_t n,
+                         uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Static string for a GPTQ_* status. */
 const char* gptq_status_string(int status);
 

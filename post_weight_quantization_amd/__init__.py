@@ -66,6 +66,14 @@ def load():
     lib.gptq_debias_workspace_size.restype = sz
     lib.gptq_debias.argtypes = [P, P, i64, P, P, P, P, P, P, P, i64, i64, P, sz, P]
     lib.gptq_debias.restype = ctypes.c_int
+    lib.gptq_act_order_perm.argtypes = [P, i64, i64, P, P, P]
+    lib.gptq_act_order_perm.restype = ctypes.c_int
+    lib.gptq_permute_hessian.argtypes = [P, i64, i64, P, P, P]
+    lib.gptq_permute_hessian.restype = ctypes.c_int
+    lib.gptq_sweep_act_order_workspace_size.argtypes = [i64, i64]
+    lib.gptq_sweep_act_order_workspace_size.restype = sz
+    lib.gptq_sweep_act_order.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
+    lib.gptq_sweep_act_order.restype = ctypes.c_int
     lib.gptq_status_string.argtypes = [ctypes.c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_profile_enable.argtypes = [ctypes.c_uint]
@@ -240,6 +248,64 @@ def gptq_debias(W, H, dead, nib, rung, lost, scale, want_tab=True, want_slope=Tr
     return lost, tab, scale, slope
 
 
+def sweep_act_order_workspace_size(rows: int, n: int) -> int:
+    return int(load().gptq_sweep_act_order_workspace_size(int(rows), int(n)))
+
+
+def gptq_act_order_perm(H, stream=None):
+    """(perm i32 [n], dead u8 [n]) of act-order GPTQ from H's diagonal."""
+    lib = load()
+    n = H.shape[0]
+    perm = torch.empty(n, dtype=torch.int32, device=H.device)
+    dead = torch.empty(n, dtype=torch.uint8, device=H.device)
+    if H.stride(1) != 1:
+        raise ValueError("H must be row-major")
+    st = lib.gptq_act_order_perm(ctypes.c_void_p(H.data_ptr()), n, H.stride(0),
+                                 _dev(perm, torch.int32, "perm"), _dev(dead, torch.uint8, "dead"),
+                                 _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_act_order_perm")
+    return perm, dead
+
+
+def gptq_permute_hessian(H, perm, stream=None):
+    """H[perm][perm] (f32 [n, n], full symmetric) from H's upper triangle."""
+    lib = load()
+    n = H.shape[0]
+    Hp = torch.empty(n, n, dtype=torch.float32, device=H.device)
+    st = lib.gptq_permute_hessian(ctypes.c_void_p(H.data_ptr()), n, H.stride(0),
+                                  _dev(perm, torch.int32, "perm"), _dev(Hp, torch.float32, "Hp"),
+                                  _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_permute_hessian")
+    return Hp
+
+
+def gptq_sweep_act_order(W, U, dead, perm, tab, lost, want_E=False, workspace=None, stream=None):
+    """Act-order q4tp sweep.  Returns (nib, rung, scale, E or None); E in elimination order."""
+    lib = load()
+    rows, n = W.shape
+    dev = W.device
+    nib = torch.empty(rows, n // 2, dtype=torch.uint8, device=dev)
+    rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+    scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+    E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
+    if workspace is None:
+        workspace = torch.empty(lib.gptq_sweep_act_order_workspace_size(rows, n),
+                                dtype=torch.uint8, device=dev)
+    st = lib.gptq_sweep_act_order(_dev(W, torch.float32, "W"), _dev(U, torch.float32, "U"),
+                                  _dev(dead, torch.uint8, "dead"), _dev(perm, torch.int32, "perm"),
+                                  _dev(tab, torch.float32, "tab"), _dev(lost, torch.float32, "lost"),
+                                  rows, n, _dev(nib, torch.uint8, "nib"),
+                                  _dev(rung, torch.uint8, "rung"), _dev(scale, torch.float32, "scale"),
+                                  None if E is None else _dev(E, torch.float32, "E"),
+                                  _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                  _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_sweep_act_order")
+    return nib, rung, scale, E
+
+
 PROFILE_FAMILIES = ["fold_update", "fold_panel", "fold_diag", "fold_build", "fold_make_u",
                     "sweep_group", "sweep_trail", "ladder", "fold_next", "sweep_next", "gram", "debias"]
 
@@ -297,6 +363,8 @@ def check_selftest(which: int) -> int:
 
 
 __all__ = ["check_mode", "check_message", "check_selftest", "gptq_gram_add", "gptq_debias",
+           "gptq_act_order_perm", "gptq_permute_hessian", "gptq_sweep_act_order",
+           "sweep_act_order_workspace_size",
            "debias_workspace_size", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
            "profile_collect", "LIB_PATH"]

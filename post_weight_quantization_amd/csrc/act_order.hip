@@ -1,0 +1,104 @@
+// act_order.hip -- the channel order of act-order GPTQ and the permuted Hessian, on gfx950.
+//
+// Source of the method: page "cortiq-cli 0.8.45 src/gptq.rs": act_order_perm (channels by
+// descending input energy H_ii, compared in the f32 total order, ties by ascending index),
+// permute_sym (H[perm][perm]) and gptq_quantize_q4tp_act_order (the fold of the permuted
+// Hessian; dead channels in the original order).
+//
+//   act_rank_kernel    the rank of every channel under that order, by counting (n^2 compares,
+//                      keys staged through LDS); perm[rank[i]] = i, dead[i] = !(H_ii > 0);
+//   act_permute_kernel Hp[a][b] = H[min(pa, pb)][max(pa, pb)] (H read through its upper
+//                      triangle), 32 x 32 output tiles, the full symmetric matrix written.
+#include "check.hpp"
+#include "common.hpp"
+
+namespace gptq {
+
+// The f32 total order as a signed integer: -NaN < -inf < ... < -0 < +0 < ... < +inf < +NaN.
+__device__ __forceinline__ int32_t total_key(float x) {
+    const int32_t b = __float_as_int(x);
+    return b >= 0 ? b : (b ^ 0x7fffffff);
+}
+
+__global__ __launch_bounds__(256) void act_rank_kernel(const float* __restrict__ H, int64_t ldh,
+                                                       int64_t n, int32_t* __restrict__ perm,
+                                                       uint8_t* __restrict__ dead) {
+    __shared__ int32_t keys[1024];
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = i < n;
+    const float hi = live ? H[i * ldh + i] : 0.0f;
+    const int32_t ki = total_key(hi);
+    int64_t rank = 0;
+    for (int64_t j0 = 0; j0 < n; j0 += 1024) {
+        __syncthreads();
+        for (int t = threadIdx.x; t < 1024; t += 256) {
+            const int64_t j = j0 + t;
+            keys[t] = (j < n) ? total_key(H[j * ldh + j]) : INT32_MIN;
+        }
+        __syncthreads();
+        const int64_t m = (n - j0 < 1024) ? n - j0 : 1024;
+        for (int64_t t = 0; t < m; ++t) {
+            const int32_t kj = keys[t];
+            // j before i: a larger key, or the same key at a smaller index.
+            rank += (kj > ki || (kj == ki && j0 + t < i)) ? 1 : 0;
+        }
+    }
+    if (live) {
+        perm[rank] = (int32_t)i;
+        dead[i] = (hi > 0.0f) ? 0 : 1;
+    }
+}
+
+__global__ __launch_bounds__(256) void act_permute_kernel(const float* __restrict__ H,
+                                                          int64_t ldh,
+                                                          const int32_t* __restrict__ perm,
+                                                          int64_t n, float* __restrict__ Hp) {
+    const int64_t a0 = (int64_t)blockIdx.y * 32, b0 = (int64_t)blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const int64_t b = b0 + tx;
+    const int64_t pb = (b < n) ? perm[b] : -1;
+    for (int r = ty; r < 32; r += 8) {
+        const int64_t a = a0 + r;
+        if (a >= n || b >= n) continue;
+        const int64_t pa = perm[a];
+        float v = 0.0f;
+        if (pa >= 0 && pa < n && pb >= 0 && pb < n)
+            v = (pa <= pb) ? H[pa * ldh + pb] : H[pb * ldh + pa];
+        Hp[a * n + b] = v;
+    }
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" int gptq_act_order_perm(const float* H, int64_t n, int64_t ldh, int32_t* perm,
+                                   uint8_t* dead, void* stream) {
+    if (!H || !perm || !dead || n <= 0 || ldh < n || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
+    CheckScope check;
+    check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
+    check_buffer(perm, sizeof(int32_t) * (size_t)n, "perm");
+    check_buffer(dead, (size_t)n, "dead");
+    hipStream_t st = (hipStream_t)stream;
+    GPTQ_LAUNCH(st, "act_rank",
+                (act_rank_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(H, ldh, n, perm, dead)),
+                rd(H, ldh + 1, n, 1), wr(perm, n, 1, n), wr(dead, n, 1, n, 1));
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    return check.finish();
+}
+
+extern "C" int gptq_permute_hessian(const float* H, int64_t n, int64_t ldh, const int32_t* perm,
+                                    float* Hp, void* stream) {
+    if (!H || !perm || !Hp || n <= 0 || ldh < n || n > ((int64_t)1 << 20)) return GPTQ_EINVAL;
+    CheckScope check;
+    check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
+    check_buffer(perm, sizeof(int32_t) * (size_t)n, "perm");
+    check_buffer(Hp, sizeof(float) * (size_t)(n * n), "Hp");
+    hipStream_t st = (hipStream_t)stream;
+    const unsigned nt = (unsigned)((n + 31) / 32);
+    GPTQ_LAUNCH(st, "act_permute",
+                (act_permute_kernel<<<dim3(nt, nt), 256, 0, st>>>(H, ldh, perm, n, Hp)),
+                rd(H, ldh, n, n), rd(perm, n, 1, n), wr(Hp, n, n, n));
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    return check.finish();
+}

@@ -193,6 +193,21 @@ __device__ __forceinline__ float pair_err(float w0, float w1, float h0, float h1
     const float f0 = e0 * d0, f1 = e1 * d1;
     return f0 + f1;
 }
+
+// Unit-weight rounding error of a 32-column tile at scale s, summed in column order with every
+// product and sum rounded separately (the static groups' rung choice).
+__device__ __forceinline__ float unit_tile_err(const float (&w)[32], float s, float inv_s) {
+    float err = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const float q = fminf(fmaxf(rint_quot(w[t], s, inv_s), -8.0f), 7.0f);
+        const float qs = q * s;
+        const float d = w[t] - qs;
+        const float dd = d * d;
+        err = err + dd;
+    }
+    return err;
+}
 #pragma clang fp contract(on)
 
 constexpr int SB = 128;          // columns per block (4 groups)
@@ -203,18 +218,31 @@ struct BlockCtx {
     const float* uinv;   // 1 / U_jj (0 where U_jj <= 0), LDS
     const float* hs;     // H_ii of the block's columns, LDS
     const float* tb;     // the row's 32 rung scales
+    const float* sp;     // static groups: this row's per-column scales from column c0
+    uint8_t* codes;      // static groups: this row's codes (one byte each) from column c0
     float lo, st;
     int k;
 };
 
 // Group g of the block, with every register index a compile-time constant (the groups are
 // unrolled by template recursion).
-template <int G, int g>
+// ST (static groups, act order): no rung search; every column carries its own scale, read
+// from cx.sp and broadcast from its owner like the weight, and the codes go to cx.codes as bytes.
+template <int G, int g, bool ST>
 __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx, int64_t r,
                                             int64_t n, int64_t c0, uint8_t* __restrict__ nib,
                                             uint8_t* __restrict__ rung, float* __restrict__ scale,
                                             float* __restrict__ E, int64_t ldE) {
     const int k = cx.k;
+    float s = 0.0f, inv_s = 0.0f;
+    float s_own[2] = {0.0f, 0.0f}, inv_own[2] = {0.0f, 0.0f};
+    if constexpr (ST) {
+        const float2 sv = *reinterpret_cast<const float2*>(cx.sp + 32 * g + 2 * k);
+        s_own[0] = sv.x;
+        s_own[1] = sv.y;
+        inv_own[0] = (sv.x > 0.0f) ? 1.0f / sv.x : 0.0f;
+        inv_own[1] = (sv.y > 0.0f) ? 1.0f / sv.y : 0.0f;
+    } else {
     const float amax = group16_max(fmaxf(fabsf(w[g][0]), fabsf(w[g][1])));
     const int nominal = nominal_rung(amax, cx.lo, cx.st);
     int best = nominal;
@@ -233,12 +261,13 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
             }
         }
     }
-    const float s = cx.tb[best];
-    const float inv_s = (s > 0.0f) ? 1.0f / s : 0.0f;
+    s = cx.tb[best];
+    inv_s = (s > 0.0f) ? 1.0f / s : 0.0f;
     if (k == 0) {
         const int64_t gi = r * (n / 32) + (c0 / 32) + g;
         rung[gi] = (uint8_t)best;
         scale[gi] = s;
+    }
     }
     uint32_t byte = 0u;
     // This lane's entries of row j of U (own group and later groups) and 1 / U_jj are read one
@@ -263,16 +292,22 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
 #pragma unroll
         for (int g2 = g + 1; g2 < G; ++g2) ul_n[g2] = ul[g2];
         if (jj + 1 < 32) load_u(32 * g + jj + 1, uo_n, ul_n, ui_n);
+        float sj = s, inv_sj = inv_s;
+        if constexpr (ST) {
+            sj = row_bcast(s_own[slot], owner);
+            inv_sj = row_bcast(inv_own[slot], owner);
+        }
         const float wj = row_bcast(w[g][slot], owner);
-        float q = fminf(fmaxf(rint_quot(wj, s, inv_s), -8.0f), 7.0f);
-        q = (s > 0.0f) ? q : 0.0f;
-        const float e = (wj - q * s) * ui;
+        float q = fminf(fmaxf(rint_quot(wj, sj, inv_sj), -8.0f), 7.0f);
+        q = (sj > 0.0f) ? q : 0.0f;
+        const float e = (wj - q * sj) * ui;
         // This lane's columns of the same group: U_jt is 0 for t < j, so the update touches
         // only the later ones; the owner's column j then takes the residual.
         w[g][0] -= e * uo.x;
         w[g][1] -= e * uo.y;
         if (k == owner) {
-            byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
+            if constexpr (ST) byte |= ((uint32_t)((int)q + 8) & 255u) << (8 * slot);
+            else byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
             w[g][slot] = e;
         }
         // ... and all of its columns of the later groups of the block.
@@ -287,9 +322,10 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         for (int g2 = g + 1; g2 < G; ++g2) ul[g2] = ul_n[g2];
         __builtin_amdgcn_sched_barrier(0);
     }
-    nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
+    if constexpr (ST) *reinterpret_cast<uint16_t*>(cx.codes + 32 * g + 2 * k) = (uint16_t)byte;
+    else nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
     *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
-    if constexpr (g + 1 < G) block_group<G, g + 1>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
+    if constexpr (g + 1 < G) block_group<G, g + 1, ST>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
 }
 
 // One block of up to 4 groups for 16 rows per workgroup, 16 lanes per row.  Lane k of a row
@@ -298,13 +334,14 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
 // then the group's 32 columns in order: the column's corrected value is broadcast from its
 // owner, every lane of the row computes the same code and residual, and each lane feeds the
 // residual into its own later columns of the block through row j of U (held in LDS).
-template <int G>
+template <int G, bool ST>
 __global__ __launch_bounds__(256) void sweep_block_kernel(
     const float* __restrict__ src, int64_t n, int64_t c0, const float* __restrict__ U,
     const float* __restrict__ hdiag, const uint8_t* __restrict__ dead,
     const float* __restrict__ tab, const float* __restrict__ lost, int64_t rows,
     uint8_t* __restrict__ nib, uint8_t* __restrict__ rung, float* __restrict__ scale,
-    float* __restrict__ E, int64_t ldE) {
+    float* __restrict__ E, int64_t ldE, const float* __restrict__ sp,
+    uint8_t* __restrict__ codes) {
     constexpr int NC = 32 * G;
     __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
     __shared__ float hs[SB];
@@ -321,7 +358,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
         *reinterpret_cast<f32x4*>(&Us[j * ULD + t4]) = v;
     }
     if (tid < NC) {
-        hs[tid] = hdiag[c0 + tid];
+        hs[tid] = ST ? 1.0f : hdiag[c0 + tid];
         const float d = U[(c0 + tid) * n + c0 + tid];
         uinv[tid] = (d > 0.0f) ? 1.0f / d : 0.0f;
     }
@@ -338,8 +375,9 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     for (int g = 0; g < G; ++g) {
         const int64_t c = c0 + 32 * g + 2 * k;
         const float2 v = *reinterpret_cast<const float2*>(src + r * n + c);
-        w[g][0] = dead[c] ? 0.0f : v.x;
-        w[g][1] = dead[c + 1] ? 0.0f : v.y;
+        // Static groups sweep a gathered, already dead-zeroed copy.
+        w[g][0] = (!ST && dead[c]) ? 0.0f : v.x;
+        w[g][1] = (!ST && dead[c + 1]) ? 0.0f : v.y;
     }
     BlockCtx cx;
     cx.Us = Us;
@@ -349,7 +387,56 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     cx.lo = lost[r * 2];
     cx.st = lost[r * 2 + 1];
     cx.k = k;
-    block_group<G, 0>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
+    cx.sp = ST ? sp + r * n + c0 : nullptr;
+    cx.codes = ST ? codes + r * n + c0 : nullptr;
+    block_group<G, 0, ST>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
+}
+
+// Static groups, step 1: the rung of every (row, group) chosen up front from the dead-zeroed
+// original tile -- the sweep's rung rule with unit weights: nominal from the absmax, then the
+// candidates nominal-2 .. nominal+1 by the f32 squared rounding error summed in column order.
+// One thread per (row, group).
+__global__ __launch_bounds__(256) void static_rung_kernel(const float* __restrict__ W,
+                                                          const uint8_t* __restrict__ dead,
+                                                          const float* __restrict__ tab,
+                                                          const float* __restrict__ lost,
+                                                          int64_t rows, int64_t n,
+                                                          uint8_t* __restrict__ rung,
+                                                          float* __restrict__ scale) {
+    const int64_t ng = n / 32;
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= rows * ng) return;
+    const int64_t r = id / ng, g = id % ng;
+    float w[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 32; t += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(W + r * n + 32 * g + t);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            w[t + u] = dead[32 * g + t + u] ? 0.0f : v[u];
+            amax = fmaxf(amax, fabsf(w[t + u]));
+        }
+    }
+    const float* tb = tab + r * 32;
+    const int nominal = nominal_rung(amax, lost[r * 2], lost[r * 2 + 1]);
+    int best = nominal;
+    if (amax > 0.0f) {
+        float best_e = INFINITY;
+        const int lo_c = nominal >= 2 ? nominal - 2 : 0;
+        const int hi_c = nominal + 1 < 31 ? nominal + 1 : 31;
+        for (int cand = lo_c; cand <= hi_c; ++cand) {
+            const float s_c = tb[cand];
+            if (s_c <= 0.0f) continue;
+            const float err = unit_tile_err(w, s_c, 1.0f / s_c);
+            if (err < best_e) {
+                best_e = err;
+                best = cand;
+            }
+        }
+    }
+    rung[r * ng + g] = (uint8_t)best;
+    scale[r * ng + g] = tb[best];
 }
 
 }  // namespace gptq
@@ -392,41 +479,40 @@ extern "C" size_t gptq_sweep_workspace_size(int64_t rows, int64_t n) {
     return sweep_ws(rows, n, nullptr);
 }
 
-template <int G>
+template <int G, bool ST>
 static void launch_block(unsigned nwg, hipStream_t st, const float* src, int64_t n, int64_t c0,
                          const float* U, const float* hdiag, const uint8_t* dead, const float* tab,
                          const float* lost, int64_t rows, uint8_t* nib, uint8_t* rung, float* scale,
-                         float* E, int64_t ldE) {
-    sweep_block_kernel<G><<<nwg, 256, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows, nib,
-                                               rung, scale, E, ldE);
+                         float* E, int64_t ldE, const float* sp, uint8_t* codes) {
+    sweep_block_kernel<G, ST><<<nwg, 256, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows,
+                                                   nib, rung, scale, E, ldE, sp, codes);
 }
 
-extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
-                          const float* tab, const float* lost, int64_t rows, int64_t n,
-                          uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-    if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !hdiag || !dead || !tab || !lost ||
-        !nib || !rung || !scale || !workspace)
-        return GPTQ_EINVAL;
-    if (rows > ((int64_t)1 << 31) - 64 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
-    size_t off_e = 0;
-    if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
-    CheckScope check;
-    check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
-    check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
-    check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
-    check_buffer(dead, (size_t)n, "dead");
-    check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
-    check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
-    check_buffer(nib, (size_t)(rows * (n / 2)), "nib");
-    check_buffer(rung, (size_t)(rows * (n / 32)), "rung");
-    check_buffer(scale, sizeof(float) * (size_t)(rows * (n / 32)), "scale");
-    if (E) check_buffer(E, sizeof(float) * (size_t)(rows * n), "E");
-    check_buffer(workspace, workspace_bytes, "workspace");
-    hipStream_t st = (hipStream_t)stream;
-    float* Wc = (float*)workspace;
-    float* Epan[2] = {(float*)((char*)workspace + off_e),
-                      (float*)((char*)workspace + off_e + align256(sizeof(float) * (size_t)(rows * SOB)))};
+// One sweep over the columns in their storage order (the channel order for the plain sweep,
+// the elimination order for act order).
+struct SweepRun {
+    const float* first;  // what the first panel reads: the caller's W, or the gathered copy Wc
+    const float* U;
+    const float* hdiag;
+    const uint8_t* dead;
+    const float* tab;
+    const float* lost;
+    int64_t rows, n;
+    uint8_t* nib;
+    uint8_t* rung;
+    float* scale;
+    float* E;
+    float* Wc;
+    float* Epan[2];
+    const float* sp;     // static groups: per-column scales [rows, n] (elimination order)
+    uint8_t* codes;      // static groups: codes [rows, n] (elimination order)
+};
+
+template <bool ST>
+static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
+    const int64_t rows = c.rows, n = c.n;
+    const float* U = c.U;
+    float* Wc = c.Wc;
     const unsigned nwg = (unsigned)((rows + 15) / 16);
 
     Helper hp{};
@@ -446,27 +532,40 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     int pan = 0;
     for (int64_t P0 = 0; P0 < n; P0 += SOB, pan ^= 1) {
         const int64_t w = std::min<int64_t>(SOB, n - P0);
-        float* Ep = E ? E + P0 : Epan[pan];
-        const int64_t ldE = E ? n : SOB;
+        float* Ep = c.E ? c.E + P0 : c.Epan[pan];
+        const int64_t ldE = c.E ? n : SOB;
         for (int64_t c0 = P0; c0 < P0 + w; c0 += SB) {
             const int G = (int)((P0 + w - c0 >= SB) ? 4 : (P0 + w - c0) / 32);
             const int64_t nc = 32 * G;
-            const float* src = (c0 == 0) ? W : Wc;
+            const float* src = (c0 == 0) ? c.first : Wc;
             float* Eo = Ep + (c0 - P0);
             {
                 ProfScope ps(FAM_SWEEP_GROUP, st, 51.0 * nc * rows + (double)rows * nc * nc,
                              4.0 * rows * nc * 2 + 4.0 * nc * nc);
-                GPTQ_LAUNCH(st, "sweep_block",
-                            (G == 4   ? launch_block<4>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE)
-                             : G == 3 ? launch_block<3>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE)
-                             : G == 2 ? launch_block<2>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE)
-                                      : launch_block<1>(nwg, st, src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, Eo, ldE)),
-                            rd(src + c0, n, rows, nc), rd(U + c0 * n + c0, n, nc, nc),
-                            rd(hdiag + c0, n, 1, nc), rd(dead + c0, n, 1, nc, 1),
-                            rd(tab, 32, rows, 32), rd(lost, 2, rows, 2),
-                            wr(nib + c0 / 2, n / 2, rows, nc / 2, 1),
-                            wr(rung + c0 / 32, n / 32, rows, G, 1),
-                            wr(scale + c0 / 32, n / 32, rows, G), wr(Eo, ldE, rows, nc));
+#define BLOCK_ARGS nwg, st, src, n, c0, U, c.hdiag, c.dead, c.tab, c.lost, rows, c.nib, c.rung, c.scale, Eo, ldE, c.sp, c.codes
+                if constexpr (ST) {
+                    GPTQ_LAUNCH(st, "sweep_block_static",
+                                (G == 4   ? launch_block<4, true>(BLOCK_ARGS)
+                                 : G == 3 ? launch_block<3, true>(BLOCK_ARGS)
+                                 : G == 2 ? launch_block<2, true>(BLOCK_ARGS)
+                                          : launch_block<1, true>(BLOCK_ARGS)),
+                                rd(src + c0, n, rows, nc), rd(U + c0 * n + c0, n, nc, nc),
+                                rd(c.sp + c0, n, rows, nc), wr(c.codes + c0, n, rows, nc, 1),
+                                wr(Eo, ldE, rows, nc));
+                } else {
+                    GPTQ_LAUNCH(st, "sweep_block",
+                                (G == 4   ? launch_block<4, false>(BLOCK_ARGS)
+                                 : G == 3 ? launch_block<3, false>(BLOCK_ARGS)
+                                 : G == 2 ? launch_block<2, false>(BLOCK_ARGS)
+                                          : launch_block<1, false>(BLOCK_ARGS)),
+                                rd(src + c0, n, rows, nc), rd(U + c0 * n + c0, n, nc, nc),
+                                rd(c.hdiag + c0, n, 1, nc), rd(c.dead + c0, n, 1, nc, 1),
+                                rd(c.tab, 32, rows, 32), rd(c.lost, 2, rows, 2),
+                                wr(c.nib + c0 / 2, n / 2, rows, nc / 2, 1),
+                                wr(c.rung + c0 / 32, n / 32, rows, G, 1),
+                                wr(c.scale + c0 / 32, n / 32, rows, G), wr(Eo, ldE, rows, nc));
+                }
+#undef BLOCK_ARGS
             }
             // The rest of the panel: columns c0 + nc .. P0 + w (last read at the same source).
             const int64_t rest_in = P0 + w - c0 - nc;
@@ -483,8 +582,8 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
         }
         const int64_t rest = n - P0 - w;
         if (rest <= 0) continue;
-        // Columns right of the panel still hold the caller's W when this is the first panel.
-        const float* src = (P0 == 0) ? W : Wc;
+        // Columns right of the panel still hold the first source when this is the first panel.
+        const float* src = (P0 == 0) ? c.first : Wc;
         const float* Up = U + P0 * n;  // the panel's rows of U
         const int64_t nw = std::min<int64_t>(SOB, rest);
         const int64_t rest2 = rest - nw;
@@ -526,5 +625,192 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     SWEEP_OK(ev_record(hp.ev_b, ts));
     SWEEP_OK(stream_wait(st, hp.ev_b));
 #undef SWEEP_OK
+    return GPTQ_OK;
+}
+
+extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
+                          const float* tab, const float* lost, int64_t rows, int64_t n,
+                          uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !hdiag || !dead || !tab || !lost ||
+        !nib || !rung || !scale || !workspace)
+        return GPTQ_EINVAL;
+    if (rows > ((int64_t)1 << 31) - 64 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
+    size_t off_e = 0;
+    if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
+    CheckScope check;
+    check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
+    check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
+    check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
+    check_buffer(dead, (size_t)n, "dead");
+    check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
+    check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
+    check_buffer(nib, (size_t)(rows * (n / 2)), "nib");
+    check_buffer(rung, (size_t)(rows * (n / 32)), "rung");
+    check_buffer(scale, sizeof(float) * (size_t)(rows * (n / 32)), "scale");
+    if (E) check_buffer(E, sizeof(float) * (size_t)(rows * n), "E");
+    check_buffer(workspace, workspace_bytes, "workspace");
+    SweepRun c{};
+    c.first = W;
+    c.U = U;
+    c.hdiag = hdiag;
+    c.dead = dead;
+    c.tab = tab;
+    c.lost = lost;
+    c.rows = rows;
+    c.n = n;
+    c.nib = nib;
+    c.rung = rung;
+    c.scale = scale;
+    c.E = E;
+    c.Wc = (float*)workspace;
+    c.Epan[0] = (float*)((char*)workspace + off_e);
+    c.Epan[1] = (float*)((char*)workspace + off_e + align256(sizeof(float) * (size_t)(rows * SOB)));
+    const int rc = sweep_pipeline<false>(c, (hipStream_t)stream);
+    if (rc != GPTQ_OK) return rc;
+    return check.finish();
+}
+
+// --- act order (static groups) -------------------------------------------------------------
+
+// Wc[r][a] = W[r][perm[a]] (0 for a dead channel) and sp[r][a] = scale[r][perm[a] / 32]; an
+// index outside 0..n-1 reads as a dead channel, so a malformed perm cannot reach outside W.
+__global__ __launch_bounds__(256) void act_gather_kernel(const float* __restrict__ W,
+                                                         const uint8_t* __restrict__ dead,
+                                                         const int32_t* __restrict__ perm,
+                                                         const float* __restrict__ scale,
+                                                         int64_t n, float* __restrict__ Wc,
+                                                         float* __restrict__ sp) {
+    const int64_t r = blockIdx.y;
+    const int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (a >= n) return;
+    const int64_t pa = perm[a];
+    const bool ok = pa >= 0 && pa < n;
+    Wc[r * n + a] = (ok && !dead[pa]) ? W[r * n + pa] : 0.0f;
+    sp[r * n + a] = ok ? scale[r * (n / 32) + pa / 32] : 0.0f;
+}
+
+// inv[perm[a]] = a, after inv is set to -1 (so that a channel no entry of perm names stays -1).
+__global__ void act_inverse_kernel(const int32_t* __restrict__ perm, int64_t n,
+                                   int32_t* __restrict__ inv, int phase) {
+    const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a >= n) return;
+    if (phase == 0) {
+        inv[a] = -1;
+    } else {
+        const int64_t pa = perm[a];
+        if (pa >= 0 && pa < n) inv[pa] = (int32_t)a;
+    }
+}
+
+// Nibble plane from the codes in elimination order: column 2m in the low nibble.
+__global__ __launch_bounds__(256) void act_pack_kernel(const uint8_t* __restrict__ codes,
+                                                       const int32_t* __restrict__ inv, int64_t n,
+                                                       uint8_t* __restrict__ nib) {
+    const int64_t r = blockIdx.y;
+    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (m >= n / 2) return;
+    const int32_t i0 = inv[2 * m], i1 = inv[2 * m + 1];
+    const uint8_t c0 = (i0 >= 0 && i0 < n) ? codes[r * n + i0] : 8;
+    const uint8_t c1 = (i1 >= 0 && i1 < n) ? codes[r * n + i1] : 8;
+    nib[r * (n / 2) + m] = (uint8_t)((c0 & 15u) | ((c1 & 15u) << 4));
+}
+
+static size_t act_ws(int64_t rows, int64_t n, size_t* off_e, size_t* off_sp, size_t* off_codes,
+                     size_t* off_inv) {
+    size_t o = sweep_ws(rows, n, off_e);
+    if (off_sp) *off_sp = o;
+    o += align256(sizeof(float) * (size_t)(rows * n));
+    if (off_codes) *off_codes = o;
+    o += align256((size_t)(rows * n));
+    if (off_inv) *off_inv = o;
+    o += align256(sizeof(int32_t) * (size_t)n);
+    return o;
+}
+
+extern "C" size_t gptq_sweep_act_order_workspace_size(int64_t rows, int64_t n) {
+    if (rows <= 0 || n <= 0) return 0;
+    return act_ws(rows, n, nullptr, nullptr, nullptr, nullptr);
+}
+
+extern "C" int gptq_sweep_act_order(const float* W, const float* U, const uint8_t* dead,
+                                    const int32_t* perm, const float* tab, const float* lost,
+                                    int64_t rows, int64_t n, uint8_t* nib, uint8_t* rung,
+                                    float* scale, float* E, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !dead || !perm || !tab || !lost ||
+        !nib || !rung || !scale || !workspace)
+        return GPTQ_EINVAL;
+    if (rows > 65535 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;  // rows index grid.y
+    size_t off_e = 0, off_sp = 0, off_codes = 0, off_inv = 0;
+    if (workspace_bytes < act_ws(rows, n, &off_e, &off_sp, &off_codes, &off_inv))
+        return GPTQ_EWORKSPACE;
+    CheckScope check;
+    check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
+    check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
+    check_buffer(dead, (size_t)n, "dead");
+    check_buffer(perm, sizeof(int32_t) * (size_t)n, "perm");
+    check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
+    check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
+    check_buffer(nib, (size_t)(rows * (n / 2)), "nib");
+    check_buffer(rung, (size_t)(rows * (n / 32)), "rung");
+    check_buffer(scale, sizeof(float) * (size_t)(rows * (n / 32)), "scale");
+    if (E) check_buffer(E, sizeof(float) * (size_t)(rows * n), "E");
+    check_buffer(workspace, workspace_bytes, "workspace");
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    float* Wc = (float*)ws;
+    float* sp = (float*)(ws + off_sp);
+    uint8_t* codes = (uint8_t*)(ws + off_codes);
+    int32_t* inv = (int32_t*)(ws + off_inv);
+    const int64_t ng = n / 32;
+    {
+        ProfScope ps(FAM_SWEEP_GROUP, st, 0.0, 4.0 * (double)rows * n);
+        GPTQ_LAUNCH(st, "static_rungs",
+                    (static_rung_kernel<<<(unsigned)((rows * ng + 255) / 256), 256, 0, st>>>(
+                        W, dead, tab, lost, rows, n, rung, scale)),
+                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), rd(tab, 32, rows, 32),
+                    rd(lost, 2, rows, 2), wr(rung, ng, rows, ng, 1), wr(scale, ng, rows, ng));
+        GPTQ_LAUNCH(st, "act_gather",
+                    (act_gather_kernel<<<dim3((unsigned)((n + 255) / 256), (unsigned)rows), 256, 0, st>>>(
+                        W, dead, perm, scale, n, Wc, sp)),
+                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), rd(perm, n, 1, n),
+                    rd(scale, ng, rows, ng), wr(Wc, n, rows, n), wr(sp, n, rows, n));
+        GPTQ_LAUNCH(st, "act_inverse_clear",
+                    (act_inverse_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, n, inv, 0)),
+                    wr(inv, n, 1, n));
+        GPTQ_LAUNCH(st, "act_inverse",
+                    (act_inverse_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, n, inv, 1)),
+                    rd(perm, n, 1, n), wr(inv, n, 1, n));
+    }
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    SweepRun c{};
+    c.first = Wc;
+    c.U = U;
+    c.hdiag = nullptr;
+    c.dead = dead;
+    c.tab = tab;
+    c.lost = lost;
+    c.rows = rows;
+    c.n = n;
+    c.nib = nib;
+    c.rung = rung;
+    c.scale = scale;
+    c.E = E;
+    c.Wc = Wc;
+    c.Epan[0] = (float*)(ws + off_e);
+    c.Epan[1] = (float*)(ws + off_e + align256(sizeof(float) * (size_t)(rows * SOB)));
+    c.sp = sp;
+    c.codes = codes;
+    int rc = sweep_pipeline<true>(c, st);
+    if (rc != GPTQ_OK) return rc;
+    {
+        ProfScope ps(FAM_SWEEP_GROUP, st, 0.0, 1.5 * (double)rows * n);
+        GPTQ_LAUNCH(st, "act_pack",
+                    (act_pack_kernel<<<dim3((unsigned)((n / 2 + 255) / 256), (unsigned)rows), 256, 0, st>>>(
+                        codes, inv, n, nib)),
+                    rd(codes, n, rows, n, 1), rd(inv, n, 1, n), wr(nib, n / 2, rows, n / 2, 1));
+    }
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     return check.finish();
 }

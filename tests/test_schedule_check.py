@@ -102,3 +102,18 @@ def test_debias_schedule(lib, rows, n):
         st = lib.gptq_debias(W, H, n, dead, nib, rung, lost, tab, scale, slope, rows, n, ws,
                              need, None)
     assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(1, 32), (37, 96), (300, 1056), (4096, 4096), (5120, 17408)])
+@pytest.mark.parametrize("want_e", [False, True])
+def test_act_order_schedule(lib, rows, n, want_e):
+    W, U, dead, perm, tab, lost, nib, rung, scale, E, ws, H, Hp = addrs(13)
+    need = lib.gptq_sweep_act_order_workspace_size(rows, n)
+    with pwq.check_mode():
+        st = lib.gptq_act_order_perm(H, n, n, perm, dead, None)
+        assert st == GPTQ_OK, pwq.check_message()
+        st = lib.gptq_permute_hessian(H, n, n, perm, Hp, None)
+        assert st == GPTQ_OK, pwq.check_message()
+        st = lib.gptq_sweep_act_order(W, U, dead, perm, tab, lost, rows, n, nib, rung, scale,
+                                      E if want_e else None, ws, need, None)
+    assert st == GPTQ_OK, pwq.check_message()
