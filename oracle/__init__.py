@@ -27,6 +27,11 @@ What each function follows (docs.rs source pages of the cortiq project):
   rungs chosen up front from the original tiles, columns eliminated in ``perm`` order.  The
   converter's rung choice is not printed; the reading is the sweep's rung rule on the
   dead-zeroed original tile with unit weights.
+* :func:`ladder_q2`, :func:`sweep_q2` -- the q2tp sweep with the "placed" rule ("cortiq-engine
+  0.8.41 src/gpu_wgpu/gptq_dev.rs", ``q2tp_group``; "cortiq-cli 0.8.45 src/gptq.rs",
+  ``sweep_q2tp``, ``gptq_quantize_q2tp``): 2-bit levels, a full search over rungs 1..31 by the
+  clipped-``H_ii``-weighted error, rung 0 for an all-zero group.  The ladder placement is not
+  printed; the ladder here is a stated reading (see the C source).
 * :func:`output_error` -- the layer-output error ``tr(dW H dW^T)`` with the raw Hessian, the
   quantity the pages' device-versus-host test compares ("cortiq-cli 0.8.45 src/gptq.rs",
   test ``device_fold_and_sweep_match_host``).
@@ -73,6 +78,11 @@ def _load():
     lib.orc_ladder.restype = None
     lib.orc_sweep_static.argtypes = [P, i64, i64, P, P, P, P, P, ctypes.c_double, P, ctypes.c_int]
     lib.orc_sweep_static.restype = ctypes.c_int
+    lib.orc_ladder_q2.argtypes = [P, P, i64, i64, i64, P, P]
+    lib.orc_ladder_q2.restype = None
+    lib.orc_sweep_q2.argtypes = [P, i64, i64, i64, P, P, P, P, P, P, P, P, P, P,
+                                 ctypes.c_double, ctypes.c_double, P, ctypes.c_int]
+    lib.orc_sweep_q2.restype = ctypes.c_int
     lib.orc_sweep.argtypes = [P, i64, i64, i64, P, P, P, P, P, P, P, P, P, P, P, P,
                               ctypes.c_double, ctypes.c_double, P, ctypes.c_int]
     lib.orc_sweep.restype = ctypes.c_int
@@ -312,4 +322,64 @@ def sweep_act_order(W0, Up, dead, perm, tab, lost, gs=32, rung=None, force_code=
     code[:, p] = code_p
     return dict(code=code, rung=rung, scale=scale, E=E,
                 stats=dict(code_ties=int(stats[0]), code_hard=int(stats[1])))
+
+
+def ladder_q2(W0, dead, gs=32):
+    """(lost [rows, 2], tab [rows, 32]) of the q2tp ladder (a stated reading), TAB[0] = 0."""
+    W0 = np.ascontiguousarray(W0, dtype=np.float32)
+    rows, n = W0.shape
+    d = np.ascontiguousarray(dead, dtype=np.uint8)
+    lost = np.empty((rows, 2), dtype=np.float32)
+    tab = np.empty((rows, 32), dtype=np.float32)
+    _load().orc_ladder_q2(_ptr(W0), _ptr(d), rows, n, gs, _ptr(lost), _ptr(tab))
+    return lost, tab
+
+
+def sweep_q2(W0, U, hdiag, dead, tab, gs=32, force_code=None, force_rung=None, tie_band=1e-3,
+             rung_band=1e-4, want_E=True, nt=None):
+    """Column-sequential q2tp sweep ("placed" rule).  ``code`` holds the 2-bit level 0..3 one
+    per byte; the weights are max(H_ii, 0)."""
+    W0 = np.ascontiguousarray(W0, dtype=np.float32)
+    rows, n = W0.shape
+    U = np.ascontiguousarray(U, dtype=np.float64)
+    hw = np.ascontiguousarray(np.maximum(np.asarray(hdiag, dtype=np.float32), 0.0), dtype=np.float32)
+    d = np.ascontiguousarray(dead, dtype=np.uint8)
+    tab = np.ascontiguousarray(tab, dtype=np.float32)
+    ng = n // gs
+    code = np.empty((rows, n), dtype=np.uint8)
+    rung = np.empty((rows, ng), dtype=np.uint8)
+    scale = np.empty((rows, ng), dtype=np.float32)
+    E = np.empty((rows, n), dtype=np.float64) if want_E else None
+    fc = None if force_code is None else np.ascontiguousarray(force_code, dtype=np.uint8)
+    fr = None if force_rung is None else np.ascontiguousarray(force_rung, dtype=np.uint8)
+    stats = np.zeros(4, dtype=np.int64)
+    st = _load().orc_sweep_q2(_ptr(W0), rows, n, gs, _ptr(U), _ptr(hw), _ptr(d), _ptr(tab),
+                              _ptr(code), _ptr(rung), _ptr(scale), _ptr(E), _ptr(fc), _ptr(fr),
+                              float(tie_band), float(rung_band), _ptr(stats), threads(nt))
+    if st != OK:
+        raise ValueError("oracle q2 sweep rejected its arguments")
+    return dict(code=code, rung=rung, scale=scale, E=E,
+                stats=dict(code_ties=int(stats[0]), code_hard=int(stats[1]),
+                           rung_ties=int(stats[2]), rung_hard=int(stats[3])))
+
+
+def pack_q2(code):
+    """2-bit plane (rows x n/4 bytes): column 4m + i in bits 2i of byte m."""
+    c = np.asarray(code, dtype=np.uint8) & 3
+    return c[:, 0::4] | (c[:, 1::4] << 2) | (c[:, 2::4] << 4) | (c[:, 3::4] << 6)
+
+
+def unpack_q2(plane):
+    p = np.asarray(plane, dtype=np.uint8)
+    rows, q = p.shape
+    out = np.empty((rows, 4 * q), dtype=np.uint8)
+    for i in range(4):
+        out[:, i::4] = (p >> (2 * i)) & 3
+    return out
+
+
+def dequant_q2(code, scale, gs=32):
+    """W_hat[r, j] = (code - 1.5) * scale[r, j // gs] in f64."""
+    q = np.asarray(code, dtype=np.float64) - 1.5
+    return q * np.repeat(np.asarray(scale, dtype=np.float64), gs, axis=1)
 

@@ -528,4 +528,182 @@ int orc_sweep_static(const float* Wp, int64_t rows, int64_t n, const double* Up,
     return ORC_OK;
 }
 
+/* ------------------------------------------------------------------------------------------ */
+/* q2tp ("placed" rule).  [gptq_dev.rs] q2tp_group and [gptq.rs] sweep_q2tp /
+ * gptq_quantize_q2tp: 2-bit levels (q - 1.5) s with q = q2_level(w / s + 1.5),
+ * q2_level(x) = clamp(rne(clamp(x, -1, 4)), 0, 3); rung 0 is the all-zero group (TAB[0] = 0);
+ * a group with a nonzero entry takes the best of rungs 1..31 by the clipped-H_ii-weighted
+ * rounding error (a strictly smaller error replaces the current best, starting from rung 1). */
+static float q2_level(float x) {
+    float c = clampf(x, -1.0f, 4.0f);
+    return clampf(rne_f32(c), 0.0f, 3.0f);
+}
+
+static float q2_tile_error(const float* wf, const float* hw, int64_t gs, float s) {
+    float err = 0.0f;
+    for (int64_t t = 0; t < gs; ++t) {
+        float q = q2_level(wf[t] / s + 1.5f);
+        float qs = (q - 1.5f) * s;
+        float d = wf[t] - qs;
+        float hd = hw[t] * d;
+        err = err + hd * d;
+    }
+    return err;
+}
+
+/*
+ * The q2tp ladder.  The pages place it with a helper that is not printed (q2tp_place_row, "the
+ * ladder placed at the H_ii-weighted MSE-optimal group scales"); the reading used here is the
+ * absmax rule of the q4tp ladder moved to the 2-bit grid, whose outer level is 1.5 s: over the
+ * groups with a_g > 0, lo = f16(log2(min a_g / 1.5)), hi = log2(max a_g / 1.5),
+ * step = f16((hi - lo) / 30) if hi > lo else 0, TAB[0] = 0 and TAB[c] = f32(2^(lo + (c-1) step))
+ * for c = 1..31 (f64); a row with no nonzero group gets lo = step = 0 and TAB[c >= 1] = 1.
+ * The sweep's full rung search then picks the best rung of this ladder.
+ */
+void orc_ladder_q2(const float* W0, const uint8_t* dead, int64_t rows, int64_t n, int64_t gs,
+                   float* lost, float* tab) {
+    for (int64_t r = 0; r < rows; ++r) {
+        double amin = INFINITY, amax = 0.0;
+        for (int64_t g = 0; g < n / gs; ++g) {
+            float a = 0.0f;
+            for (int64_t t = 0; t < gs; ++t) {
+                int64_t j = g * gs + t;
+                float v = dead[j] ? 0.0f : fabsf(W0[r * n + j]);
+                if (v > a) a = v;
+            }
+            if (a > 0.0f) {
+                if (a < amin) amin = a;
+                if (a > amax) amax = a;
+            }
+        }
+        double lo = 0.0, st = 0.0;
+        if (amax > 0.0) {
+            lo = orc_f16_round(log2(amin / 1.5));
+            double hi = log2(amax / 1.5);
+            st = (hi > lo) ? orc_f16_round((hi - lo) / 30.0) : 0.0;
+            if (!(st > 0.0)) st = 0.0;
+        }
+        lost[r * 2] = (float)lo;
+        lost[r * 2 + 1] = (float)st;
+        tab[r * 32] = 0.0f;
+        for (int c = 1; c < 32; ++c)
+            tab[r * 32 + c] = (amax > 0.0) ? (float)exp2(lo + (double)(c - 1) * st) : 1.0f;
+    }
+}
+
+/*
+ * The q2tp sweep, column by column (f64 state; decisions in f32 as orc_sweep):
+ *   for each group g (c0 = gs g), each row: wf = f32(w[c0 .. c0+gs)); rung 0 if max |wf| = 0,
+ *   else the best of rungs 1..31 with TAB > 0 by q2_tile_error (weights hw = max(H_ii, 0));
+ *   s = TAB[rung]; for j in the group in order: q = (s > 0) ? q2_level(f32(w_j) / s + 1.5) : 0,
+ *   code = q (0..3), e_j = (U_jj > 0) ? (w_j - (q - 1.5) s) / U_jj : 0, w_t -= e_j U_jt (t > j).
+ * Tie-forced replay as orc_sweep; a code tie is a difference of one where f32(w_j)/s + 1.5
+ * lies within tie_band of a half-integer.
+ */
+int orc_sweep_q2(const float* W0, int64_t rows, int64_t n, int64_t gs, const double* U,
+                 const float* hw, const uint8_t* dead, const float* tab, uint8_t* code,
+                 uint8_t* rung, float* scale, double* E, const uint8_t* force_code,
+                 const uint8_t* force_rung, double tie_band, double rung_band, int64_t* stats,
+                 int nt) {
+    if (gs <= 0 || n % gs != 0 || gs > 64) return ORC_FAILED;
+    const int64_t ng = n / gs;
+    const int64_t RB = 16;
+    int64_t ct = 0, ch = 0, rt = 0, rh = 0;
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(+ : ct, ch, rt, rh)
+    for (int64_t r0 = 0; r0 < rows; r0 += RB) {
+        int64_t rb = imin(RB, rows - r0);
+        double* w = (double*)malloc(sizeof(double) * (size_t)(rb * n));
+        double e[16];
+        float sc[16];
+        for (int64_t k = 0; k < rb; ++k)
+            for (int64_t j = 0; j < n; ++j)
+                w[k * n + j] = dead[j] ? 0.0 : (double)W0[(r0 + k) * n + j];
+        for (int64_t g = 0; g < ng; ++g) {
+            int64_t c0 = g * gs;
+            const float* hg = hw + c0;
+            for (int64_t k = 0; k < rb; ++k) {
+                int64_t r = r0 + k;
+                const float* tb = tab + r * 32;
+                float wf[64];
+                float amax = 0.0f;
+                for (int64_t t = 0; t < gs; ++t) {
+                    wf[t] = (float)w[k * n + c0 + t];
+                    float a = fabsf(wf[t]);
+                    if (a > amax) amax = a;
+                }
+                int best = 0;
+                float best_e = INFINITY;
+                if (amax > 0.0f) {
+                    best = 1;
+                    for (int cand = 1; cand < 32; ++cand) {
+                        float s_c = tb[cand];
+                        if (!(s_c > 0.0f)) continue;
+                        float err = q2_tile_error(wf, hg, gs, s_c);
+                        if (err < best_e) {
+                            best_e = err;
+                            best = cand;
+                        }
+                    }
+                }
+                if (force_rung) {
+                    int fr = force_rung[r * ng + g];
+                    if (fr != best) {
+                        int tie = 0;
+                        if (fr >= 1 && fr < 32 && tb[fr] > 0.0f && amax > 0.0f && best_e < INFINITY) {
+                            float ef = q2_tile_error(wf, hg, gs, tb[fr]);
+                            float lo_e = ef < best_e ? ef : best_e;
+                            if (fabs((double)ef - (double)best_e) <= rung_band * (double)lo_e) tie = 1;
+                        }
+                        if (tie) ++rt; else ++rh;
+                        best = fr;
+                    }
+                }
+                rung[r * ng + g] = (uint8_t)best;
+                sc[k] = tb[best & 31];
+                scale[r * ng + g] = sc[k];
+            }
+            for (int64_t j = c0; j < c0 + gs; ++j) {
+                double ujj = U[j * n + j];
+                for (int64_t k = 0; k < rb; ++k) {
+                    int64_t r = r0 + k;
+                    double wj = w[k * n + j];
+                    float s = sc[k];
+                    float q = 0.0f;
+                    float x = 0.0f;
+                    if (s > 0.0f) {
+                        x = (float)wj / s + 1.5f;
+                        q = q2_level(x);
+                    }
+                    if (force_code) {
+                        float fq = (float)force_code[r * n + j];
+                        if (fq != q) {
+                            double fr = (double)x - floor((double)x);
+                            if (fabsf(fq - q) == 1.0f && fabs(fr - 0.5) < tie_band) ++ct; else ++ch;
+                            q = fq;
+                        }
+                    }
+                    code[r * n + j] = (uint8_t)q;
+                    e[k] = (ujj > 0.0) ? (wj - ((double)q - 1.5) * (double)s) / ujj : 0.0;
+                    if (E) E[r * n + j] = e[k];
+                }
+                const double* urow = U + j * n;
+                for (int64_t k = 0; k < rb; ++k) {
+                    double ek = e[k];
+                    if (ek == 0.0) continue;
+                    double* wr = w + k * n;
+                    for (int64_t t = j + 1; t < n; ++t) wr[t] -= ek * urow[t];
+                }
+            }
+        }
+        free(w);
+    }
+    if (stats) {
+        stats[0] = ct;
+        stats[1] = ch;
+        stats[2] = rt;
+        stats[3] = rh;
+    }
+    return ORC_OK;
+}
+
 int orc_max_threads(void) { return omp_get_max_threads(); }
