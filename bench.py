@@ -109,6 +109,7 @@ def main():
     ap.add_argument("--no-gram", action="store_true", help="skip the Hessian accumulation timing")
     ap.add_argument("--no-debias", action="store_true", help="skip the output debias timing")
     ap.add_argument("--no-act-order", action="store_true", help="skip the act-order timing")
+    ap.add_argument("--no-q2", action="store_true", help="skip the q2tp sweep timing")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size reference for "
                          "hardware traffic counters)")
@@ -261,6 +262,20 @@ def main():
         result["detail"]["gram_frac_fp32_mfma"] = result["detail"]["gram_tflops"] / FP32_MFMA_PEAK_TFLOPS
         result["detail"]["gram_shape"] = f"H[{n},{n}] += X^T X, X[{Xg.shape[0]},{n}]"
         del Xg, Hg
+    # The q2tp sweep ("placed" rule) on the step's U (a next-step row, not part of the step).
+    if not args.no_q2:
+        lost_q, tab_q = pwq.gptq_ladder_q2(W, dead)
+        out_q = pwq.gptq_sweep_q2(W, U, hdiag, dead, tab_q, workspace=ws_s)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pwq.gptq_sweep_q2(W, U, hdiag, dead, tab_q, workspace=ws_s)
+        e1.record(stream)
+        e1.synchronize()
+        result["detail"]["q2_sweep_ms"] = e0.elapsed_time(e1) / reps
+        del out_q
     # Act-order GPTQ on the same layer (a next-step row, not part of the step): channel order,
     # permuted Hessian, fold of it, ladder and the static-group sweep, timed as one group.
     if not args.no_act_order:

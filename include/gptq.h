@@ -234,6 +234,33 @@ int gptq_sweep_act_order(const float* W, const float* U, const uint8_t* dead, co
                          uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * q2tp, the "placed" rule.  Source: page "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs",
+ * q2tp_group; page "cortiq-cli 0.8.45 src/gptq.rs", sweep_q2tp / gptq_quantize_q2tp_dev.
+ *
+ * gptq_ladder_q2: lost [rows, 2] (lo, step, binary16 values) and tab [rows, 32] with TAB[0] = 0
+ *   (the all-zero group) and TAB[c] = f32(2^(lo + (c-1) step)), c = 1..31 (f64).  The pages
+ *   place this ladder with a helper that is not printed; the rule implemented is a stated
+ *   reading: over the groups with a_g = max |w| > 0 of the dead-zeroed row, lo = f16(log2(min
+ *   a_g / 1.5)), step = f16((log2(max a_g / 1.5) - lo) / 30) if positive, else 0; an all-zero
+ *   row gets lo = step = 0 and TAB[c >= 1] = 1.  n % 32 == 0.
+ */
+int gptq_ladder_q2(const float* W, const uint8_t* dead, int64_t rows, int64_t n, float* lost,
+                   float* tab, void* stream);
+
+/*
+ * gptq_sweep_q2: the q2tp GPTQ sweep of W against U (gptq_fold's output), groups of 32.  Per
+ * group: rung 0 if every corrected weight is 0, else the best of rungs 1..31 (TAB > 0) by
+ * sum_t max(H_tt, 0) (w_t - (q_t - 1.5) s)^2 (a strictly smaller error replaces the current
+ * best); then per column q = clamp(rne(clamp(w / s + 1.5, -1, 4)), 0, 3), e = (w - (q - 1.5) s)
+ * / U_jj, w_t -= e U_jt.  Outputs: plane [rows, n/4] bytes (column 4m + i in bits 2i of byte
+ * m; level (q - 1.5) * scale), rung [rows, n/32] u8, scale [rows, n/32] f32 = TAB[rung], E
+ * [rows, n] f32 or NULL.  Workspace: gptq_sweep_workspace_size(rows, n).  W is read only.
+ */
+int gptq_sweep_q2(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
+                  const float* tab, int64_t rows, int64_t n, uint8_t* plane, uint8_t* rung,
+                  float* scale, float* E, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static string for a GPTQ_* status. */
 const char* gptq_status_string(int status);
 

@@ -74,6 +74,10 @@ def load():
     lib.gptq_sweep_act_order_workspace_size.restype = sz
     lib.gptq_sweep_act_order.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
     lib.gptq_sweep_act_order.restype = ctypes.c_int
+    lib.gptq_ladder_q2.argtypes = [P, P, i64, i64, P, P, P]
+    lib.gptq_ladder_q2.restype = ctypes.c_int
+    lib.gptq_sweep_q2.argtypes = [P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
+    lib.gptq_sweep_q2.restype = ctypes.c_int
     lib.gptq_status_string.argtypes = [ctypes.c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_profile_enable.argtypes = [ctypes.c_uint]
@@ -248,6 +252,45 @@ def gptq_debias(W, H, dead, nib, rung, lost, scale, want_tab=True, want_slope=Tr
     return lost, tab, scale, slope
 
 
+def gptq_ladder_q2(W, dead, stream=None):
+    """The q2tp ladder: (lost [rows, 2], tab [rows, 32]) with TAB[0] = 0."""
+    lib = load()
+    rows, n = W.shape
+    lost = torch.empty(rows, 2, dtype=torch.float32, device=W.device)
+    tab = torch.empty(rows, 32, dtype=torch.float32, device=W.device)
+    st = lib.gptq_ladder_q2(_dev(W, torch.float32, "W"), _dev(dead, torch.uint8, "dead"), rows, n,
+                            _dev(lost, torch.float32, "lost"), _dev(tab, torch.float32, "tab"),
+                            _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_ladder_q2")
+    return lost, tab
+
+
+def gptq_sweep_q2(W, U, hdiag, dead, tab, want_E=False, workspace=None, stream=None):
+    """The q2tp sweep ("placed" rule).  Returns (plane [rows, n/4] u8, rung, scale, E or None)."""
+    lib = load()
+    rows, n = W.shape
+    dev = W.device
+    plane = torch.empty(rows, n // 4, dtype=torch.uint8, device=dev)
+    rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+    scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+    E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
+    if workspace is None:
+        workspace = torch.empty(lib.gptq_sweep_workspace_size(rows, n), dtype=torch.uint8,
+                                device=dev)
+    st = lib.gptq_sweep_q2(_dev(W, torch.float32, "W"), _dev(U, torch.float32, "U"),
+                           _dev(hdiag, torch.float32, "hdiag"), _dev(dead, torch.uint8, "dead"),
+                           _dev(tab, torch.float32, "tab"), rows, n,
+                           _dev(plane, torch.uint8, "plane"), _dev(rung, torch.uint8, "rung"),
+                           _dev(scale, torch.float32, "scale"),
+                           None if E is None else _dev(E, torch.float32, "E"),
+                           _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                           _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_sweep_q2")
+    return plane, rung, scale, E
+
+
 def sweep_act_order_workspace_size(rows: int, n: int) -> int:
     return int(load().gptq_sweep_act_order_workspace_size(int(rows), int(n)))
 
@@ -364,7 +407,7 @@ def check_selftest(which: int) -> int:
 
 __all__ = ["check_mode", "check_message", "check_selftest", "gptq_gram_add", "gptq_debias",
            "gptq_act_order_perm", "gptq_permute_hessian", "gptq_sweep_act_order",
-           "sweep_act_order_workspace_size",
+           "sweep_act_order_workspace_size", "gptq_ladder_q2", "gptq_sweep_q2",
            "debias_workspace_size", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
            "profile_collect", "LIB_PATH"]

@@ -45,6 +45,8 @@ __device__ double f16_nearest(double x) {
 }
 
 // One workgroup per row: group absmaxes of the dead-zeroed row, then lo / step / TAB.
+// Q2: the q2tp ladder (outer level 1.5 s, 30 steps, TAB[0] = 0 for the all-zero group).
+template <bool Q2>
 __global__ __launch_bounds__(256) void ladder_kernel(const float* __restrict__ W,
                                                      const uint8_t* __restrict__ dead, int64_t n,
                                                      float* __restrict__ lost,
@@ -87,9 +89,10 @@ __global__ __launch_bounds__(256) void ladder_kernel(const float* __restrict__ W
         double lo = 0.0, st = 0.0;
         const int any = smax[0] > 0.0f;
         if (any) {
-            lo = f16_nearest(log2((double)smin[0] / 7.0));
-            const double hi = log2((double)smax[0] / 7.0);
-            st = (hi > lo) ? f16_nearest((hi - lo) / 31.0) : 0.0;
+            const double top = Q2 ? 1.5 : 7.0;
+            lo = f16_nearest(log2((double)smin[0] / top));
+            const double hi = log2((double)smax[0] / top);
+            st = (hi > lo) ? f16_nearest((hi - lo) / (Q2 ? 30.0 : 31.0)) : 0.0;
             if (!(st > 0.0)) st = 0.0;
         }
         s_lo = lo;
@@ -99,7 +102,12 @@ __global__ __launch_bounds__(256) void ladder_kernel(const float* __restrict__ W
         lost[r * 2 + 1] = (float)st;
     }
     __syncthreads();
-    if (t < 32) tab[r * 32 + t] = s_any ? (float)exp2(s_lo + (double)t * s_st) : 1.0f;
+    if (t < 32) {
+        if (Q2)
+            tab[r * 32 + t] = (t == 0) ? 0.0f : (s_any ? (float)exp2(s_lo + (double)(t - 1) * s_st) : 1.0f);
+        else
+            tab[r * 32 + t] = s_any ? (float)exp2(s_lo + (double)t * s_st) : 1.0f;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -208,6 +216,32 @@ __device__ __forceinline__ float unit_tile_err(const float (&w)[32], float s, fl
     }
     return err;
 }
+
+// q2tp level q2_level(fl(w / s) + 1.5) = clamp(rne(clamp(x, -1, 4)), 0, 3), decided on the
+// correctly rounded quotient as rint_quot does: x = w * fl(1/s) + 1.5 lands on the same level
+// unless w * fl(1/s) lies within 4e-7 max(|.|, 1) of an integer (x near a half-integer); then
+// (rarely, behind a wave-uniform branch) divide.
+__device__ __forceinline__ float q2_level_quot(float w, float s, float inv_s) {
+    const float r = w * inv_s;
+    const bool near = !(fabsf(r - rintf(r)) > 4e-7f * fmaxf(fabsf(r), 1.0f));
+    float x = r + 1.5f;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near) != 0, 0)) {
+        if (near) x = w / s + 1.5f;
+    }
+    return fminf(fmaxf(rintf(fminf(fmaxf(x, -1.0f), 4.0f)), 0.0f), 3.0f);
+}
+
+// Clipped-H_ii-weighted q2tp rounding error of two columns at scale s.
+__device__ __forceinline__ float pair_err_q2(float w0, float w1, float h0, float h1, float s,
+                                             float inv_s) {
+    const float q0 = q2_level_quot(w0, s, inv_s), q1 = q2_level_quot(w1, s, inv_s);
+    const float l0 = q0 - 1.5f, l1 = q1 - 1.5f;
+    const float qs0 = l0 * s, qs1 = l1 * s;
+    const float d0 = w0 - qs0, d1 = w1 - qs1;
+    const float e0 = h0 * d0, e1 = h1 * d1;
+    const float f0 = e0 * d0, f1 = e1 * d1;
+    return f0 + f1;
+}
 #pragma clang fp contract(on)
 
 constexpr int SB = 128;          // columns per block (4 groups)
@@ -226,17 +260,44 @@ struct BlockCtx {
 
 // Group g of the block, with every register index a compile-time constant (the groups are
 // unrolled by template recursion).
-// ST (static groups, act order): no rung search; every column carries its own scale, read
-// from cx.sp and broadcast from its owner like the weight, and the codes go to cx.codes as bytes.
-template <int G, int g, bool ST>
+// MODE 0: q4tp.  MODE 1 (static groups, act order): no rung search; every column carries its
+// own scale, read from cx.sp and broadcast from its owner like the weight, and the codes go to
+// cx.codes as bytes.  MODE 2: q2tp ("placed"): the full search over rungs 1..31 (rung 0 for an
+// all-zero group), 2-bit levels (q - 1.5) s, codes packed four to a byte.
+template <int G, int g, int MODE>
 __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx, int64_t r,
                                             int64_t n, int64_t c0, uint8_t* __restrict__ nib,
                                             uint8_t* __restrict__ rung, float* __restrict__ scale,
                                             float* __restrict__ E, int64_t ldE) {
+    constexpr bool ST = MODE == 1, Q2 = MODE == 2;
     const int k = cx.k;
     float s = 0.0f, inv_s = 0.0f;
     float s_own[2] = {0.0f, 0.0f}, inv_own[2] = {0.0f, 0.0f};
-    if constexpr (ST) {
+    if constexpr (Q2) {
+        const float amax = group16_max(fmaxf(fabsf(w[g][0]), fabsf(w[g][1])));
+        int best = 0;
+        if (amax > 0.0f) {
+            best = 1;
+            float best_e = INFINITY;
+            const float h0 = cx.hs[32 * g + 2 * k], h1 = cx.hs[32 * g + 2 * k + 1];
+            for (int cand = 1; cand < 32; ++cand) {
+                const float s_c = cx.tb[cand];
+                if (!(s_c > 0.0f)) continue;
+                const float err = group16_sum(pair_err_q2(w[g][0], w[g][1], h0, h1, s_c, 1.0f / s_c));
+                if (err < best_e) {
+                    best_e = err;
+                    best = cand;
+                }
+            }
+        }
+        s = cx.tb[best];
+        inv_s = (s > 0.0f) ? 1.0f / s : 0.0f;
+        if (k == 0) {
+            const int64_t gi = r * (n / 32) + (c0 / 32) + g;
+            rung[gi] = (uint8_t)best;
+            scale[gi] = s;
+        }
+    } else if constexpr (ST) {
         const float2 sv = *reinterpret_cast<const float2*>(cx.sp + 32 * g + 2 * k);
         s_own[0] = sv.x;
         s_own[1] = sv.y;
@@ -298,15 +359,23 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
             inv_sj = row_bcast(inv_own[slot], owner);
         }
         const float wj = row_bcast(w[g][slot], owner);
-        float q = fminf(fmaxf(rint_quot(wj, sj, inv_sj), -8.0f), 7.0f);
-        q = (sj > 0.0f) ? q : 0.0f;
-        const float e = (wj - q * sj) * ui;
+        float q, lev;  // the code and its level (q for q4tp, q - 1.5 for q2tp)
+        if constexpr (Q2) {
+            q = (sj > 0.0f) ? q2_level_quot(wj, sj, inv_sj) : 0.0f;
+            lev = q - 1.5f;
+        } else {
+            q = fminf(fmaxf(rint_quot(wj, sj, inv_sj), -8.0f), 7.0f);
+            q = (sj > 0.0f) ? q : 0.0f;
+            lev = q;
+        }
+        const float e = (wj - lev * sj) * ui;
         // This lane's columns of the same group: U_jt is 0 for t < j, so the update touches
         // only the later ones; the owner's column j then takes the residual.
         w[g][0] -= e * uo.x;
         w[g][1] -= e * uo.y;
         if (k == owner) {
             if constexpr (ST) byte |= ((uint32_t)((int)q + 8) & 255u) << (8 * slot);
+            else if constexpr (Q2) byte |= ((uint32_t)(int)q & 3u) << (2 * slot);
             else byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
             w[g][slot] = e;
         }
@@ -322,10 +391,17 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         for (int g2 = g + 1; g2 < G; ++g2) ul[g2] = ul_n[g2];
         __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (ST) *reinterpret_cast<uint16_t*>(cx.codes + 32 * g + 2 * k) = (uint16_t)byte;
-    else nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
+    if constexpr (ST) {
+        *reinterpret_cast<uint16_t*>(cx.codes + 32 * g + 2 * k) = (uint16_t)byte;
+    } else if constexpr (Q2) {
+        // Lanes 2m and 2m+1 hold columns 4m .. 4m+3: the even lane writes their byte.
+        const uint32_t nb = (uint32_t)__float_as_int(dpp_mov<0xB1>(__int_as_float((int)byte)));
+        if ((k & 1) == 0) nib[r * (n / 4) + (c0 + 32 * g) / 4 + k / 2] = (uint8_t)(byte | (nb << 4));
+    } else {
+        nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
+    }
     *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
-    if constexpr (g + 1 < G) block_group<G, g + 1, ST>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
+    if constexpr (g + 1 < G) block_group<G, g + 1, MODE>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
 }
 
 // One block of up to 4 groups for 16 rows per workgroup, 16 lanes per row.  Lane k of a row
@@ -334,7 +410,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
 // then the group's 32 columns in order: the column's corrected value is broadcast from its
 // owner, every lane of the row computes the same code and residual, and each lane feeds the
 // residual into its own later columns of the block through row j of U (held in LDS).
-template <int G, bool ST>
+template <int G, int MODE>
 __global__ __launch_bounds__(256) void sweep_block_kernel(
     const float* __restrict__ src, int64_t n, int64_t c0, const float* __restrict__ U,
     const float* __restrict__ hdiag, const uint8_t* __restrict__ dead,
@@ -343,6 +419,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     float* __restrict__ E, int64_t ldE, const float* __restrict__ sp,
     uint8_t* __restrict__ codes) {
     constexpr int NC = 32 * G;
+    constexpr bool ST = MODE == 1;
     __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
     __shared__ float hs[SB];
     __shared__ float uinv[SB];
@@ -358,7 +435,8 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
         *reinterpret_cast<f32x4*>(&Us[j * ULD + t4]) = v;
     }
     if (tid < NC) {
-        hs[tid] = ST ? 1.0f : hdiag[c0 + tid];
+        // q4tp weighs by H_ii, q2tp by max(H_ii, 0); static groups do not search.
+        hs[tid] = ST ? 1.0f : (MODE == 2 ? fmaxf(hdiag[c0 + tid], 0.0f) : hdiag[c0 + tid]);
         const float d = U[(c0 + tid) * n + c0 + tid];
         uinv[tid] = (d > 0.0f) ? 1.0f / d : 0.0f;
     }
@@ -384,12 +462,12 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     cx.uinv = uinv;
     cx.hs = hs;
     cx.tb = &tabs[(tid >> 4) * 32];
-    cx.lo = lost[r * 2];
-    cx.st = lost[r * 2 + 1];
+    cx.lo = (MODE == 0) ? lost[r * 2] : 0.0f;  // only q4tp's nominal rung reads the ladder's lo / step
+    cx.st = (MODE == 0) ? lost[r * 2 + 1] : 0.0f;
     cx.k = k;
     cx.sp = ST ? sp + r * n + c0 : nullptr;
     cx.codes = ST ? codes + r * n + c0 : nullptr;
-    block_group<G, 0, ST>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
+    block_group<G, 0, MODE>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
 }
 
 // Static groups, step 1: the rung of every (row, group) chosen up front from the dead-zeroed
@@ -455,7 +533,7 @@ extern "C" int gptq_ladder(const float* W, const uint8_t* dead, int64_t rows, in
     hipStream_t st = (hipStream_t)stream;
     {
         ProfScope ps(FAM_LADDER, st, 0.0, 4.0 * (double)rows * n);
-        GPTQ_LAUNCH(st, "ladder", (ladder_kernel<<<(unsigned)rows, 256, 0, st>>>(W, dead, n, lost, tab)),
+        GPTQ_LAUNCH(st, "ladder", (ladder_kernel<false><<<(unsigned)rows, 256, 0, st>>>(W, dead, n, lost, tab)),
                     rd(W, n, rows, n), rd(dead, n, 1, n, 1), wr(lost, 2, rows, 2),
                     wr(tab, 32, rows, 32));
     }
@@ -479,12 +557,12 @@ extern "C" size_t gptq_sweep_workspace_size(int64_t rows, int64_t n) {
     return sweep_ws(rows, n, nullptr);
 }
 
-template <int G, bool ST>
+template <int G, int MODE>
 static void launch_block(unsigned nwg, hipStream_t st, const float* src, int64_t n, int64_t c0,
                          const float* U, const float* hdiag, const uint8_t* dead, const float* tab,
                          const float* lost, int64_t rows, uint8_t* nib, uint8_t* rung, float* scale,
                          float* E, int64_t ldE, const float* sp, uint8_t* codes) {
-    sweep_block_kernel<G, ST><<<nwg, 256, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows,
+    sweep_block_kernel<G, MODE><<<nwg, 256, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows,
                                                    nib, rung, scale, E, ldE, sp, codes);
 }
 
@@ -508,7 +586,7 @@ struct SweepRun {
     uint8_t* codes;      // static groups: codes [rows, n] (elimination order)
 };
 
-template <bool ST>
+template <int MODE>
 static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
     const int64_t rows = c.rows, n = c.n;
     const float* U = c.U;
@@ -543,21 +621,33 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
                 ProfScope ps(FAM_SWEEP_GROUP, st, 51.0 * nc * rows + (double)rows * nc * nc,
                              4.0 * rows * nc * 2 + 4.0 * nc * nc);
 #define BLOCK_ARGS nwg, st, src, n, c0, U, c.hdiag, c.dead, c.tab, c.lost, rows, c.nib, c.rung, c.scale, Eo, ldE, c.sp, c.codes
-                if constexpr (ST) {
+                if constexpr (MODE == 1) {
                     GPTQ_LAUNCH(st, "sweep_block_static",
-                                (G == 4   ? launch_block<4, true>(BLOCK_ARGS)
-                                 : G == 3 ? launch_block<3, true>(BLOCK_ARGS)
-                                 : G == 2 ? launch_block<2, true>(BLOCK_ARGS)
-                                          : launch_block<1, true>(BLOCK_ARGS)),
+                                (G == 4   ? launch_block<4, 1>(BLOCK_ARGS)
+                                 : G == 3 ? launch_block<3, 1>(BLOCK_ARGS)
+                                 : G == 2 ? launch_block<2, 1>(BLOCK_ARGS)
+                                          : launch_block<1, 1>(BLOCK_ARGS)),
                                 rd(src + c0, n, rows, nc), rd(U + c0 * n + c0, n, nc, nc),
                                 rd(c.sp + c0, n, rows, nc), wr(c.codes + c0, n, rows, nc, 1),
                                 wr(Eo, ldE, rows, nc));
+                } else if constexpr (MODE == 2) {
+                    GPTQ_LAUNCH(st, "sweep_block_q2",
+                                (G == 4   ? launch_block<4, 2>(BLOCK_ARGS)
+                                 : G == 3 ? launch_block<3, 2>(BLOCK_ARGS)
+                                 : G == 2 ? launch_block<2, 2>(BLOCK_ARGS)
+                                          : launch_block<1, 2>(BLOCK_ARGS)),
+                                rd(src + c0, n, rows, nc), rd(U + c0 * n + c0, n, nc, nc),
+                                rd(c.hdiag + c0, n, 1, nc), rd(c.dead + c0, n, 1, nc, 1),
+                                rd(c.tab, 32, rows, 32),
+                                wr(c.nib + c0 / 4, n / 4, rows, nc / 4, 1),
+                                wr(c.rung + c0 / 32, n / 32, rows, G, 1),
+                                wr(c.scale + c0 / 32, n / 32, rows, G), wr(Eo, ldE, rows, nc));
                 } else {
                     GPTQ_LAUNCH(st, "sweep_block",
-                                (G == 4   ? launch_block<4, false>(BLOCK_ARGS)
-                                 : G == 3 ? launch_block<3, false>(BLOCK_ARGS)
-                                 : G == 2 ? launch_block<2, false>(BLOCK_ARGS)
-                                          : launch_block<1, false>(BLOCK_ARGS)),
+                                (G == 4   ? launch_block<4, 0>(BLOCK_ARGS)
+                                 : G == 3 ? launch_block<3, 0>(BLOCK_ARGS)
+                                 : G == 2 ? launch_block<2, 0>(BLOCK_ARGS)
+                                          : launch_block<1, 0>(BLOCK_ARGS)),
                                 rd(src + c0, n, rows, nc), rd(U + c0 * n + c0, n, nc, nc),
                                 rd(c.hdiag + c0, n, 1, nc), rd(c.dead + c0, n, 1, nc, 1),
                                 rd(c.tab, 32, rows, 32), rd(c.lost, 2, rows, 2),
@@ -666,7 +756,69 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     c.Wc = (float*)workspace;
     c.Epan[0] = (float*)((char*)workspace + off_e);
     c.Epan[1] = (float*)((char*)workspace + off_e + align256(sizeof(float) * (size_t)(rows * SOB)));
-    const int rc = sweep_pipeline<false>(c, (hipStream_t)stream);
+    const int rc = sweep_pipeline<0>(c, (hipStream_t)stream);
+    if (rc != GPTQ_OK) return rc;
+    return check.finish();
+}
+
+extern "C" int gptq_ladder_q2(const float* W, const uint8_t* dead, int64_t rows, int64_t n,
+                              float* lost, float* tab, void* stream) {
+    if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !dead || !lost || !tab) return GPTQ_EINVAL;
+    if (rows > ((int64_t)1 << 31) - 1) return GPTQ_EINVAL;
+    CheckScope check;
+    check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
+    check_buffer(dead, (size_t)n, "dead");
+    check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
+    check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
+    hipStream_t st = (hipStream_t)stream;
+    {
+        ProfScope ps(FAM_LADDER, st, 0.0, 4.0 * (double)rows * n);
+        GPTQ_LAUNCH(st, "ladder_q2", (ladder_kernel<true><<<(unsigned)rows, 256, 0, st>>>(W, dead, n, lost, tab)),
+                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), wr(lost, 2, rows, 2),
+                    wr(tab, 32, rows, 32));
+    }
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    return check.finish();
+}
+
+extern "C" int gptq_sweep_q2(const float* W, const float* U, const float* hdiag,
+                             const uint8_t* dead, const float* tab, int64_t rows, int64_t n,
+                             uint8_t* plane, uint8_t* rung, float* scale, float* E,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !hdiag || !dead || !tab || !plane ||
+        !rung || !scale || !workspace)
+        return GPTQ_EINVAL;
+    if (rows > ((int64_t)1 << 31) - 64 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
+    size_t off_e = 0;
+    if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
+    CheckScope check;
+    check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
+    check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
+    check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
+    check_buffer(dead, (size_t)n, "dead");
+    check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
+    check_buffer(plane, (size_t)(rows * (n / 4)), "plane");
+    check_buffer(rung, (size_t)(rows * (n / 32)), "rung");
+    check_buffer(scale, sizeof(float) * (size_t)(rows * (n / 32)), "scale");
+    if (E) check_buffer(E, sizeof(float) * (size_t)(rows * n), "E");
+    check_buffer(workspace, workspace_bytes, "workspace");
+    SweepRun c{};
+    c.first = W;
+    c.U = U;
+    c.hdiag = hdiag;
+    c.dead = dead;
+    c.tab = tab;
+    c.lost = nullptr;  // the q2tp rule searches every rung: no nominal rung, no lo / step
+    c.rows = rows;
+    c.n = n;
+    c.nib = plane;
+    c.rung = rung;
+    c.scale = scale;
+    c.E = E;
+    c.Wc = (float*)workspace;
+    c.Epan[0] = (float*)((char*)workspace + off_e);
+    c.Epan[1] = (float*)((char*)workspace + off_e + align256(sizeof(float) * (size_t)(rows * SOB)));
+    const int rc = sweep_pipeline<2>(c, (hipStream_t)stream);
     if (rc != GPTQ_OK) return rc;
     return check.finish();
 }
@@ -802,7 +954,7 @@ extern "C" int gptq_sweep_act_order(const float* W, const float* U, const uint8_
     c.Epan[1] = (float*)(ws + off_e + align256(sizeof(float) * (size_t)(rows * SOB)));
     c.sp = sp;
     c.codes = codes;
-    int rc = sweep_pipeline<true>(c, st);
+    int rc = sweep_pipeline<1>(c, st);
     if (rc != GPTQ_OK) return rc;
     {
         ProfScope ps(FAM_SWEEP_GROUP, st, 0.0, 1.5 * (double)rows * n);

@@ -117,3 +117,16 @@ def test_act_order_schedule(lib, rows, n, want_e):
         st = lib.gptq_sweep_act_order(W, U, dead, perm, tab, lost, rows, n, nib, rung, scale,
                                       E if want_e else None, ws, need, None)
     assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(16, 32), (37, 96), (300, 1056), (5120, 17408)])
+@pytest.mark.parametrize("want_e", [False, True])
+def test_q2_schedule(lib, rows, n, want_e):
+    W, U, hd, dead, tab, lost, plane, rung, scale, E, ws = addrs(11)
+    need = lib.gptq_sweep_workspace_size(rows, n)
+    with pwq.check_mode():
+        st = lib.gptq_ladder_q2(W, dead, rows, n, lost, tab, None)
+        assert st == GPTQ_OK, pwq.check_message()
+        st = lib.gptq_sweep_q2(W, U, hd, dead, tab, rows, n, plane, rung, scale,
+                               E if want_e else None, ws, need, None)
+    assert st == GPTQ_OK, pwq.check_message()
