@@ -307,25 +307,25 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
     }
     if (wave == 0 && lane == 0 && bad) atomicOr(flag, 1u);
     __syncthreads();
-    // Outputs as float4 rows: L (zeros above the diagonal; the upper triangle of A's diagonal
-    // block is never read), MI_k and X's diagonal block (both with zeros above).
+    // Output: MI_k as float4 rows (zeros above the diagonal).  Nothing reads L's diagonal block
+    // after this kernel (the panel solve multiplies by MI_k), so it is not stored; the inverse's
+    // diagonal blocks are copied from MI on the inverse's own stream.
     float* mi = MI + (int64_t)k * NB * NB;
 #pragma unroll 4
     for (int i = 0; i < 16; ++i) {
         const int r = (tid >> 5) + 8 * i, c = (tid & 31) * 4;
-        f32x4 l4, m4;
+        const int I = r >> 5, J = c >> 5;  // the four columns share one 32-block
+        f32x4 m4;
+        if (I == J) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int cc = c + q, I = r >> 5, J = cc >> 5;
-            float m = 0.0f;
-            if (I == J) m = Ts[I][(r & 31) * SLD + (cc & 31)];
-            else if (I > J) m = Ls[(32 * J + (r & 31)) * DLD + 32 * I + (cc & 31)];
-            m4[q] = m;
-            l4[q] = (cc <= r) ? Ls[r * DLD + cc] : 0.0f;
+            for (int q = 0; q < 4; ++q) m4[q] = Ts[I][(r & 31) * SLD + ((c + q) & 31)];
+        } else if (I > J) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m4[q] = Ls[(32 * J + (r & 31)) * DLD + 32 * I + ((c + q) & 31)];
+        } else {
+            m4 = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        *reinterpret_cast<f32x4*>(A + (kb + r) * np + kb + c) = l4;
         *reinterpret_cast<f32x4*>(mi + r * NB + c) = m4;
-        *reinterpret_cast<f32x4*>(X + (kb + r) * np + kb + c) = m4;
     }
 }
 
@@ -375,14 +375,18 @@ static FoldLayout fold_layout(int64_t n) {
     return L;
 }
 
-// Zero the strictly upper 128-blocks of X's w x w diagonal block at kb, and copy the rows
-// multiplied out of place back into X (both small, on the critical stream).
-__global__ __launch_bounds__(256) void fold_zero_upper_kernel(float* __restrict__ X, int64_t np,
-                                                              int64_t kb, int64_t w) {
+// The w x w diagonal block of X at kb before its block forward substitution: the diagonal
+// 128-blocks are the inverses MI of L's diagonal blocks, the blocks above are 0 (the blocks
+// below are written by the substitution).
+__global__ __launch_bounds__(256) void fold_x_diag_kernel(float* __restrict__ X,
+                                                          const float* __restrict__ MI,
+                                                          int64_t np, int64_t kb, int64_t w) {
     const int64_t r = blockIdx.y;                // row within the block
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= w) return;
-    if ((c / NB) > (r / NB)) X[(kb + r) * np + kb + c] = 0.0f;
+    const int64_t I = r / NB, J = c / NB;
+    if (J > I) X[(kb + r) * np + kb + c] = 0.0f;
+    else if (J == I) X[(kb + r) * np + kb + c] = MI[((kb / NB + I) * NB + (r % NB)) * NB + (c % NB)];
 }
 
 __global__ __launch_bounds__(256) void fold_copy_rows_kernel(const float* __restrict__ src,
@@ -491,8 +495,8 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                     ProfScope ps(FAM_FOLD_DIAG, st, 2.0 * NB * NB * NB / 3.0, 0.0);
                     GPTQ_LAUNCH(st, "fold_diag",
                                 (fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)(cb / NB), &state->flag)),
-                                wr(A + cb * np + cb, np, NB, NB), wr(X + cb * np + cb, np, NB, NB),
-                                wr(MI + (cb / NB) * NB * NB, NB, NB, NB), st_rw);
+                                rd(A + cb * np + cb, np, NB, NB), wr(MI + (cb / NB) * NB * NB, NB, NB, NB),
+                                st_rw);
                 }
                 if (rest_c <= 0) continue;
                 const float* mic = MI + (cb / NB) * NB * NB;
@@ -530,11 +534,11 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
             // Inverse of the panel's w x w diagonal block of L, into X[kb:kb+w, kb:kb+w]: the
             // 128-blocks on the diagonal are the MI_c written by the diagonal kernel; block row I
             // is -MI_I (L[I, <I] X[<I, <I]) (block forward substitution).
+            GPTQ_LAUNCH(tx, "fold_x_diag",
+                        (fold_x_diag_kernel<<<dim3((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, tx>>>(
+                            X, MI, np, kb, w)),
+                        rd(MI + (kb / NB) * NB * NB, NB, w, NB), wr(X + kb * np + kb, np, w, w));
             if (R > 1) {
-                GPTQ_LAUNCH(tx, "fold_zero_upper",
-                            (fold_zero_upper_kernel<<<dim3((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, tx>>>(
-                                X, np, kb, w)),
-                            wr(X + kb * np + kb, np, w, w));
                 for (int64_t I = 1; I < R; ++I) {
                     const int64_t ci = kb + I * NB;
                     const GemmBatch t1 = gemm_batch(
