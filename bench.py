@@ -110,6 +110,7 @@ def main():
     ap.add_argument("--no-debias", action="store_true", help="skip the output debias timing")
     ap.add_argument("--no-act-order", action="store_true", help="skip the act-order timing")
     ap.add_argument("--no-q2", action="store_true", help="skip the q2tp sweep timing")
+    ap.add_argument("--no-rounds", action="store_true", help="skip the concurrent-group timings")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size reference for "
                          "hardware traffic counters)")
@@ -262,6 +263,61 @@ def main():
         result["detail"]["gram_frac_fp32_mfma"] = result["detail"]["gram_tflops"] / FP32_MFMA_PEAK_TFLOPS
         result["detail"]["gram_shape"] = f"H[{n},{n}] += X^T X, X[{Xg.shape[0]},{n}]"
         del Xg, Hg
+    # Concurrent groups (the batched round): G independent groups, each folded, laddered and
+    # swept on its own stream from its own host thread, with preallocated outputs and
+    # workspaces; groups/s over whole rounds.
+    def concurrent_round(name, G, rounds):
+        import threading
+        spec_g = workloads.SPECS[name]
+        gs_ = []
+        for kk in range(G):
+            Hg_, Wg_, lam_g = workloads.make(name, k=kk, device=dev)
+            ng_, rg_ = spec_g.n, spec_g.rows
+            bufs = dict(
+                U=torch.empty(ng_, ng_, device=dev), hd=torch.empty(ng_, device=dev),
+                dd=torch.empty(ng_, dtype=torch.uint8, device=dev),
+                lost=torch.empty(rg_, 2, device=dev), tab=torch.empty(rg_, 32, device=dev),
+                nib=torch.empty(rg_, ng_ // 2, dtype=torch.uint8, device=dev),
+                rung=torch.empty(rg_, ng_ // 32, dtype=torch.uint8, device=dev),
+                scale=torch.empty(rg_, ng_ // 32, device=dev),
+                wf=torch.empty(pwq.fold_workspace_size(ng_), dtype=torch.uint8, device=dev),
+                ws=torch.empty(pwq.sweep_workspace_size(rg_, ng_), dtype=torch.uint8, device=dev))
+            gs_.append((Hg_, Wg_, lam_g, bufs, torch.cuda.Stream(device=dev)))
+        torch.cuda.synchronize()
+
+        def one(i):
+            Hg_, Wg_, lam_g, b, st_ = gs_[i]
+            with torch.cuda.stream(st_):
+                pwq.gptq_fold(Hg_, lam_g, workspace=b["wf"], out=(b["U"], b["hd"], b["dd"]))
+                pwq.gptq_ladder(Wg_, b["dd"], out=(b["lost"], b["tab"]))
+                pwq.gptq_sweep(Wg_, b["U"], b["hd"], b["dd"], b["tab"], b["lost"],
+                               workspace=b["ws"], out=(b["nib"], b["rung"], b["scale"], None))
+                st_.synchronize()
+
+        def round_():
+            th = [threading.Thread(target=one, args=(i,)) for i in range(G)]
+            for t in th:
+                t.start()
+            for t in th:
+                t.join()
+            torch.cuda.synchronize()
+
+        round_()
+        t0_ = time.perf_counter()
+        for _ in range(rounds):
+            round_()
+        dt_ = (time.perf_counter() - t0_) / rounds
+        del gs_
+        torch.cuda.empty_cache()
+        return G / dt_, dt_ * 1e3
+
+    if not args.no_rounds:
+        gps, ms = concurrent_round("batch", 11, 3)
+        result["detail"]["batched_round_11x4096_groups_per_s"] = gps
+        result["detail"]["batched_round_11x4096_ms"] = ms
+        gps2, ms2 = concurrent_round("down", 2, 2)
+        result["detail"]["concurrent_2x17408_groups_per_s"] = gps2
+        result["detail"]["concurrent_2x17408_ms_per_pair"] = ms2
     # The q2tp sweep ("placed" rule) on the step's U (a next-step row, not part of the step).
     if not args.no_q2:
         lost_q, tab_q = pwq.gptq_ladder_q2(W, dead)
