@@ -70,7 +70,7 @@ def recorded_traffic():
         return None
 
 
-def cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows, m_fold=7680, rows_sweep=512):
+def cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows, m_fold=8192, rows_sweep=1024):
     """The oracle on a bounded sample: the fold of the trailing m x m block of H and the sweep
     of `rows_sweep` rows at full width against the GPU's U, scaled to one whole group."""
     import numpy as np
