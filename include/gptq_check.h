@@ -17,6 +17,8 @@
 #ifndef GPTQ_MI355X_CHECK_H
 #define GPTQ_MI355X_CHECK_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -27,6 +29,11 @@ const char* gptq_check_message(void);
  * write (GPTQ_ECHECK), 2 the same ordered by an event (GPTQ_OK), 3 a read past the end of
  * its buffer (GPTQ_ECHECK). */
 int gptq_check_selftest(int which);
+/* The tile GEMM's map from workgroup to output tile, on the host: GPTQ_OK when the workgroups
+ * of one launch over an M x N product (lower != 0: the lower tiles of an M x M product, N
+ * ignored) cover every 128 x 128 tile exactly once; GPTQ_ECHECK otherwise; GPTQ_EINVAL for
+ * sizes outside 1 .. 2^20. */
+int gptq_check_tile_order(int64_t M, int64_t N, int lower);
 
 #ifdef __cplusplus
 }

@@ -92,6 +92,8 @@ def load():
     lib.gptq_check_message.restype = ctypes.c_char_p
     lib.gptq_check_selftest.argtypes = [ctypes.c_int]
     lib.gptq_check_selftest.restype = ctypes.c_int
+    lib.gptq_check_tile_order.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    lib.gptq_check_tile_order.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -405,7 +407,12 @@ def check_selftest(which: int) -> int:
     return int(load().gptq_check_selftest(int(which)))
 
 
-__all__ = ["check_mode", "check_message", "check_selftest", "gptq_gram_add", "gptq_debias",
+def check_tile_order(M: int, N: int, lower: bool) -> int:
+    """Status of the host-side check of the tile GEMM's workgroup -> tile map for one shape."""
+    return int(load().gptq_check_tile_order(int(M), int(N), 1 if lower else 0))
+
+
+__all__ = ["check_mode", "check_message", "check_selftest", "check_tile_order", "gptq_gram_add", "gptq_debias",
            "gptq_act_order_perm", "gptq_permute_hessian", "gptq_sweep_act_order",
            "sweep_act_order_workspace_size", "gptq_ladder_q2", "gptq_sweep_q2",
            "debias_workspace_size", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",

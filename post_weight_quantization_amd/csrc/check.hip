@@ -10,6 +10,7 @@
 #include "../../include/gptq_check.h"
 #include "check.hpp"
 #include "common.hpp"
+#include "gemm_mfma.hpp"
 
 namespace gptq {
 
@@ -284,4 +285,24 @@ extern "C" int gptq_check_selftest(int which) {
     }
     g_mode.store(saved);
     return rc;
+}
+
+// The GEMM's workgroup -> tile map (XCD renumbering, then the super-tile order) on the host:
+// every workgroup of a launch must get a distinct tile of the problem's tile set.
+extern "C" int gptq_check_tile_order(int64_t M, int64_t N, int lower) {
+    if (M <= 0 || N <= 0 || M > ((int64_t)1 << 20) || N > ((int64_t)1 << 20)) return GPTQ_EINVAL;
+    const GemmProblem P = lower ? gemm_syrk_lower(nullptr, 32, nullptr, nullptr, M, (int)M, 32, 1.0f, 0)
+                                : gemm_full(nullptr, 32, nullptr, 32, nullptr, nullptr, N, (int)M,
+                                            (int)N, 32, 1.0f, 0);
+    const int TN = P.tiles_n, TM = lower ? P.tiles_n : P.ntiles / P.tiles_n;
+    std::vector<unsigned char> seen((size_t)TM * TN, 0);
+    for (int b = 0; b < P.ntiles; ++b) {
+        int tm = -1, tn = -1;
+        tile_of(P, xcd_order(b, P.ntiles), tm, tn);
+        if (tm < 0 || tm >= TM || tn < 0 || tn >= TN || (lower && tn > tm)) return GPTQ_ECHECK;
+        unsigned char& f = seen[(size_t)tm * TN + tn];
+        if (f) return GPTQ_ECHECK;
+        f = 1;
+    }
+    return GPTQ_OK;
 }

@@ -94,33 +94,43 @@ __global__ void fold_scale_kernel(const float* __restrict__ hdiag, const uint8_t
 }
 
 // A[i][j] (i >= j) = reversed, damped, equilibrated H read from its upper triangle; the
-// padding block is the identity; entries above the diagonal inside diagonal 32x32 tiles are 0.
+// padding block is the identity; entries above the diagonal inside diagonal 64 x 64 tiles are 0.
+// One workgroup per lower 64 x 64 tile (the grid enumerates only those); a row of the tile is
+// one wave, so both the read of H (a row of H, in reverse) and the write of A coalesce.
 __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict__ H, int64_t ldh,
                                                          const float* __restrict__ dinv,
                                                          const uint8_t* __restrict__ dead,
                                                          const FoldState* st, double lam,
                                                          float* __restrict__ A, int64_t n,
                                                          int64_t np) {
-    const int tj = blockIdx.x, ti = blockIdx.y;
-    if (tj > ti) return;
+    const int b = blockIdx.x;
+    int ti = (int)((sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
+    while ((ti + 1) * (ti + 2) / 2 <= b) ++ti;
+    while (ti * (ti + 1) / 2 > b) --ti;
+    const int tj = b - ti * (ti + 1) / 2;
     const double damp = lam * st->base;
-    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
-        const int64_t i = (int64_t)ti * 32 + (e >> 5);
-        const int64_t j = (int64_t)tj * 32 + (e & 31);
+    const int64_t j = (int64_t)tj * 64 + (threadIdx.x & 63);
+    const int64_t bc = n - 1 - j;  // column of H (valid when j < n)
+    const bool jin = j < n;
+    const bool dead_b = jin && dead[bc];
+    const float db = jin ? dinv[bc] : 0.0f;
+#pragma unroll 4
+    for (int q = 0; q < 16; ++q) {
+        const int64_t i = (int64_t)ti * 64 + (threadIdx.x >> 6) + 4 * q;
         float v;
         if (j > i) {
             v = 0.0f;
-        } else if (i >= n || j >= n) {
+        } else if (i >= n || !jin) {
             v = (i == j) ? 1.0f : 0.0f;
         } else {
-            const int64_t a = n - 1 - i, b = n - 1 - j;  // a <= b: upper triangle of H
-            if (dead[a] || dead[b]) {
-                v = (a == b) ? 1.0f : 0.0f;
-            } else if (a == b) {
-                const double di = (double)dinv[a];
+            const int64_t a = n - 1 - i;  // a <= bc: upper triangle of H
+            if (dead[a] || dead_b) {
+                v = (a == bc) ? 1.0f : 0.0f;
+            } else if (a == bc) {
+                const double di = (double)db;
                 v = (float)(((double)H[a * ldh + a] + damp) * di * di);
             } else {
-                v = H[a * ldh + b] * dinv[a] * dinv[b];
+                v = H[a * ldh + bc] * dinv[a] * db;
             }
         }
         A[i * np + j] = v;
@@ -329,16 +339,20 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
     }
 }
 
-// U[j][c] = X[n-1-j][n-1-c] * dinv[c] for c >= j, 0 below the diagonal.
+// U[j][c] = X[n-1-j][n-1-c] * dinv[c] for c >= j, 0 below the diagonal.  One workgroup per
+// 64 x 64 tile of U, a row of the tile per wave; tiles wholly below the diagonal only store 0.
 __global__ __launch_bounds__(256) void fold_make_u_kernel(const float* __restrict__ X,
                                                           const float* __restrict__ dinv,
                                                           float* __restrict__ U, int64_t n,
                                                           int64_t np) {
-    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
-        const int64_t j = (int64_t)blockIdx.y * 32 + (e >> 5);
-        const int64_t c = (int64_t)blockIdx.x * 32 + (e & 31);
+    const int64_t c = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+    const bool below = blockIdx.x < blockIdx.y;
+    const float dc = (!below && c < n) ? dinv[c] : 0.0f;
+#pragma unroll 4
+    for (int q = 0; q < 16; ++q) {
+        const int64_t j = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 6) + 4 * q;
         if (j >= n || c >= n) continue;
-        U[j * n + c] = (c >= j) ? X[(n - 1 - j) * np + (n - 1 - c)] * dinv[c] : 0.0f;
+        U[j * n + c] = (!below && c >= j) ? X[(n - 1 - j) * np + (n - 1 - c)] * dc : 0.0f;
     }
 }
 
@@ -467,7 +481,7 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                             hdiag, dead, state, lam, n, np, dinv)),
                         rd(hdiag, n, 1, n), rd(dead, n, 1, n, 1), st_rw, wr(dinv, np, 1, np));
             GPTQ_LAUNCH(st, "fold_build",
-                        (fold_build_kernel<<<dim3((unsigned)(np / 32), (unsigned)(np / 32)), 256, 0, st>>>(
+                        (fold_build_kernel<<<(unsigned)((np / 64) * (np / 64 + 1) / 2), 256, 0, st>>>(
                             H, ldh, dinv, dead, state, lam, A, n, np)),
                         rd(H, ldh, n, n), rd(dinv, np, 1, np), rd(dead, n, 1, n, 1),
                         rd(state, 1, 1, sizeof(FoldState), 1), wr(A, np, np, np));
@@ -652,7 +666,8 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
         GPTQ_LAUNCH(st, "fold_identity", (fold_identity_kernel<<<g, 256, 0, st>>>(U, n)), wr(U, n, n, n));
     } else {
         ProfScope ps(FAM_FOLD_MAKEU, st, 0.0, 4.0 * (double)n * n);
-        GPTQ_LAUNCH(st, "fold_make_u", (fold_make_u_kernel<<<g, 256, 0, st>>>(X, dinv, U, n, np)),
+        const dim3 g64((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64));
+        GPTQ_LAUNCH(st, "fold_make_u", (fold_make_u_kernel<<<g64, 256, 0, st>>>(X, dinv, U, n, np)),
                     rd(X, np, np, np), rd(dinv, np, 1, np), wr(U, n, n, n));
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;

@@ -58,22 +58,62 @@ struct GemmBatch {
     int total;            // p[0].ntiles + p[1].ntiles
 };
 
-__device__ __forceinline__ void tile_of(const GemmProblem& P, int t, int& tm, int& tn) {
+// Tile order.  Consecutive tile numbers walk super-tiles of GT_S x GT_S tiles (1024 x 1024
+// elements of C), row by row inside a super-tile, so that the workgroups resident on one XCD at
+// a time share the A rows and B columns of one super-tile in that XCD's L2 (about 2 GT_S
+// operand blocks for GT_S^2 tiles, instead of a fresh B block for every tile of a tile row).
+// Full grids: super-rows of GT_S tile rows (the last one may be shorter), each cut into
+// super-tiles of GT_S tile columns (the last one may be narrower).  Lower grids (tn <= tm):
+// super-row R holds R full super-tiles left of the diagonal and the diagonal one, a triangle.
+constexpr int GT_S = 8;
+
+// Tiles in the lower grid's super-rows 0 .. R-1 when those are all GT_S tile rows high.
+__host__ __device__ __forceinline__ int lower_prefix(int R) {
+    return GT_S * GT_S * (R * (R - 1) / 2) + R * (GT_S * (GT_S + 1) / 2);
+}
+
+// Row r and column c of entry u of a lower triangle enumerated row by row (c <= r).
+__host__ __device__ __forceinline__ void tri_of(int u, int& r, int& c) {
+    r = (int)((sqrtf(8.0f * (float)u + 1.0f) - 1.0f) * 0.5f);
+    while ((r + 1) * (r + 2) / 2 <= u) ++r;
+    while (r * (r + 1) / 2 > u) --r;
+    c = u - r * (r + 1) / 2;
+}
+
+__host__ __device__ __forceinline__ void tile_of(const GemmProblem& P, int t, int& tm, int& tn) {
     if (P.lower) {
-        int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-        while ((r + 1) * (r + 2) / 2 <= t) ++r;
-        while (r * (r + 1) / 2 > t) --r;
-        tm = r;
-        tn = t - r * (r + 1) / 2;
+        const int T = P.tiles_n;
+        const int RB = (T + GT_S - 1) / GT_S;
+        int R = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) / (2.0f * GT_S));
+        R = R < 0 ? 0 : (R > RB - 1 ? RB - 1 : R);
+        while (R + 1 <= RB - 1 && lower_prefix(R + 1) <= t) ++R;
+        while (R > 0 && lower_prefix(R) > t) --R;
+        const int u = t - lower_prefix(R);
+        const int m = (T - R * GT_S < GT_S) ? T - R * GT_S : GT_S;  // tile rows in super-row R
+        if (u < R * m * GT_S) {
+            const int C = u / (m * GT_S), v = u - C * m * GT_S;
+            tm = R * GT_S + v / GT_S;
+            tn = C * GT_S + v % GT_S;
+        } else {
+            int r, c;
+            tri_of(u - R * m * GT_S, r, c);
+            tm = R * GT_S + r;
+            tn = R * GT_S + c;
+        }
     } else {
-        tm = t / P.tiles_n;
-        tn = t - tm * P.tiles_n;
+        const int TN = P.tiles_n, TM = P.ntiles / P.tiles_n;
+        const int R = t / (GT_S * TN), u = t - R * GT_S * TN;
+        const int m = (TM - R * GT_S < GT_S) ? TM - R * GT_S : GT_S;
+        const int C = u / (m * GT_S), v = u - C * m * GT_S;
+        const int w = (TN - C * GT_S < GT_S) ? TN - C * GT_S : GT_S;
+        tm = R * GT_S + v / w;
+        tn = C * GT_S + v % w;
     }
 }
 
 // Bijective renumbering: the hardware sends workgroup b to XCD b % 8; give XCD x the
 // contiguous tile range [o_x, o_x + c_x).
-__device__ __forceinline__ int xcd_order(int b, int total) {
+__host__ __device__ __forceinline__ int xcd_order(int b, int total) {
     const int q = total / NUM_XCD, r = total % NUM_XCD;
     const int x = b % NUM_XCD, i = b / NUM_XCD;
     return x * q + (x < r ? x : r) + i;

@@ -24,6 +24,23 @@ def lib():
     return pwq.load()
 
 
+@pytest.mark.parametrize("lower", [False, True])
+def test_gemm_tile_order_is_a_bijection(lib, lower):
+    """Every workgroup of a tile GEMM launch gets a distinct tile and every tile is taken: square
+    and ragged tile grids, grids narrower and wider than a super-tile, and the shapes the fold
+    (lower trailing blocks at n = 17408) and the sweep (5120 rows) launch."""
+    shapes = [(1, 1), (128, 128), (129, 4000), (1000, 100), (1024, 1024), (1152, 1152),
+              (5120, 17408 - 512), (5120, 384), (17408 - 512, 17408 - 512), (17408 - 1024, 512),
+              (3 * 128, 37 * 128), (9 * 128 + 5, 17 * 128 - 3)]
+    shapes += [(m * 128, n * 128) for m in range(1, 20) for n in (1, 7, 8, 9, 23)]
+    for M, N in shapes:
+        assert pwq.check_tile_order(M, N, lower) == GPTQ_OK, (M, N, lower)
+    if lower:
+        for T in range(1, 140):
+            assert pwq.check_tile_order(T * 128, 0 + 1, True) == GPTQ_OK, T
+    assert pwq.check_tile_order(0, 5, lower) != GPTQ_OK
+
+
 def test_checker_selftest(lib):
     assert pwq.check_selftest(0) == GPTQ_OK
     assert pwq.check_selftest(1) == GPTQ_ECHECK
