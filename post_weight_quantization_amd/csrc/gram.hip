@@ -23,7 +23,8 @@ struct GramArgs {
     const float* X;
     int64_t ldh, ldx;
     int n, t;
-    int tiles;   // T (T + 1) / 2 upper tiles, T = ceil(n / 128)
+    int T;       // ceil(n / 128) tile rows
+    int tiles;   // T (T + 1) / 2 upper tiles
 };
 
 // Rows k0 .. k0+31 of X, columns col0 .. col0+127, as 4 float4 per thread (32 threads per
@@ -44,12 +45,16 @@ __device__ __forceinline__ void gram_load(const GramArgs& g, int col0, int k0, i
 __global__ __launch_bounds__(G_THREADS) void gram_kernel(GramArgs g) {
     __shared__ __attribute__((aligned(16))) float As[2 * LDS_TILE];
     __shared__ __attribute__((aligned(16))) float Bs[2 * LDS_TILE];
-    const int b = xcd_order(blockIdx.x, g.tiles);
-    // Upper tile (tm, tn), tn >= tm, from the lower-triangle enumeration (r, c), r >= c.
-    int r = (int)((sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
-    while ((r + 1) * (r + 2) / 2 <= b) ++r;
-    while (r * (r + 1) / 2 > b) --r;
-    const int tm = b - r * (r + 1) / 2, tn = r;
+    // Upper tile (tm, tn), tn >= tm: the transpose of lower tile (r, c), r >= c, taken in the
+    // GEMM's super-tile order (both operands are column blocks of X, shared in L2 by the
+    // workgroups of one super-tile).
+    GemmProblem lp{};
+    lp.lower = 1;
+    lp.tiles_n = g.T;
+    lp.ntiles = g.tiles;
+    int r, c;
+    tile_of(lp, xcd_order(blockIdx.x, g.tiles), r, c);
+    const int tm = c, tn = r;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -153,7 +158,7 @@ extern "C" int gptq_gram_add(float* H, int64_t n, int64_t ldh, const float* X, i
     check_buffer(X, sizeof(float) * (size_t)((t - 1) * ldx + n), "X");
     hipStream_t st = (hipStream_t)stream;
     const int T = (int)((n + GT_M - 1) / GT_M);
-    GramArgs g{H, X, ldh, ldx, (int)n, (int)t, T * (T + 1) / 2};
+    GramArgs g{H, X, ldh, ldx, (int)n, (int)t, T, T * (T + 1) / 2};
     // Reads stay inside t x n of X and n x n of H (loads past the edge are skipped or clamped).
     {
         ProfScope ps(FAM_GRAM, st, (double)n * (n + 1) * (double)t, 0.0);
