@@ -8,8 +8,8 @@
 // checking (the fold's matrices are padded to whole tiles and need none).  One workgroup of
 // 256 threads (4 waves, 2 x 2) computes a 128 x 128 tile; each wave holds a 64 x 64 sub-tile as
 // 2 x 2 accumulators of v_mfma_f32_32x32x2_f32.  K is consumed in chunks of 32 staged through
-// LDS, double buffered (one barrier per chunk); the C tile is fetched into registers before the
-// K loop so its latency hides behind the MFMAs.  A launch carries up to two independent
+// LDS, double buffered (one barrier per chunk); the C tile is fetched into registers during the
+// last chunk so its latency hides behind that chunk's MFMAs.  A launch carries up to two independent
 // problems so that the fold can update the Cholesky trailing matrix and the inverse in one
 // grid.  Workgroups are dealt to the 8 XCDs round-robin by the hardware; tiles are renumbered
 // so that each XCD works on a contiguous range (neighbouring tiles share operand rows in the
@@ -178,11 +178,49 @@ __device__ __forceinline__ void store_b(float* lds, int tid, const f32x4 (&r)[4]
     else store_krows_n(lds, tid, r);
 }
 
-// One 128 x 128 tile of problem P.  Lane l of a wave feeds MFMA row/col (l % 32) and k-half
-// h = l / 32; in step s of a chunk the k index is 16 h + s for both operands, so the two lane
-// halves together cover the chunk's 32 k values over 16 steps.  Output slot v of a 32 x 32
-// accumulator holds row 8 (v / 4) + 4 h + v % 4, column l % 32.
-template <bool TB, bool CHK>
+// The MFMAs of one K chunk staged in LDS (as, bs): lane l of a wave feeds MFMA row/col (l % 32)
+// and k-half h = l / 32; in step s of the chunk the k index is 16 h + s for both operands, so
+// the two lane halves together cover the chunk's 32 k values over 16 steps.
+template <bool TB>
+__device__ __forceinline__ void chunk_mfma(const float* as, const float* bs, int wm, int wn,
+                                           int l32, int h, f32x16 (&acc)[2][2]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f32x4 a4[2], b4[2];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+            a4[bi] = *reinterpret_cast<const f32x4*>(
+                as + (wm * 64 + bi * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
+        if (TB) {
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+                b4[bj] = *reinterpret_cast<const f32x4*>(
+                    bs + (wn * 64 + bj * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
+        } else {
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    b4[bj][q] = bs[(16 * h + 4 * m + q) * LDS_NROW + wn * 64 + bj * 32 + l32];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[bi][q], b4[bj][q],
+                                                                      acc[bi][bj], 0, 0, 0);
+    }
+}
+
+// One 128 x 128 tile of problem P.  K goes through LDS in chunks of 32, NBUF buffers deep: with
+// two, the next chunk is stored into the other buffer while this one feeds the MFMAs (one
+// barrier per chunk); with one, after a second barrier.  The next chunk's global loads are
+// issued before this chunk's MFMAs either way.  The C tile is fetched during the last chunk, so
+// its latency hides behind that chunk's MFMAs and its registers are not held through the loop.
+// Output slot v of a 32 x 32 accumulator holds row 8 (v / 4) + 4 h + v % 4, column l % 32.
+template <bool TB, bool CHK, int NBUF>
 __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, float* As,
                                           float* Bs) {
     const int tid = threadIdx.x;
@@ -199,14 +237,31 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-
-    f32x4 ra[4], rb[4];
-    load_rows_k<CHK>(P.A, P.lda, i0, P.M, 0, tid, ra);
-    load_b<TB, CHK>(P, j0, 0, tid, rb);
-
-    // The C tile, fetched now and consumed after the K loop.
     const bool use_c = P.beta && tn < P.beta0_from_tn;
     const bool diag_tile = P.mask_diag && tm == tn;
+    {
+        f32x4 ra[4], rb[4];
+        load_rows_k<CHK>(P.A, P.lda, i0, P.M, 0, tid, ra);
+        load_b<TB, CHK>(P, j0, 0, tid, rb);
+        store_rows_k(As, tid, ra);
+        store_b<TB>(Bs, tid, rb);
+    }
+    __syncthreads();
+    const int nchunk = P.K / GT_K;
+    int buf = 0;
+    for (int c = 0; c + 1 < nchunk; ++c) {
+        f32x4 ra[4], rb[4];
+        const int k0 = (c + 1) * GT_K;
+        load_rows_k<CHK>(P.A, P.lda, i0, P.M, k0, tid, ra);
+        load_b<TB, CHK>(P, j0, k0, tid, rb);
+        chunk_mfma<TB>(As + buf * LDS_TILE, Bs + buf * LDS_TILE, wm, wn, l32, h, acc);
+        if (NBUF == 1) __syncthreads();
+        const int nb = NBUF == 2 ? (buf ^ 1) : 0;
+        store_rows_k(As + nb * LDS_TILE, tid, ra);
+        store_b<TB>(Bs + nb * LDS_TILE, tid, rb);
+        __syncthreads();
+        buf = nb;
+    }
     float cv[2][2][16];
     if (use_c) {
 #pragma unroll
@@ -224,57 +279,7 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
                     cv[bi][bj][v] = P.Cin[(int64_t)i * P.ldc + j];
                 }
     }
-
-    store_rows_k(As, tid, ra);
-    store_b<TB>(Bs, tid, rb);
-    __syncthreads();
-
-    const int nchunk = P.K / GT_K;
-    for (int c = 0; c < nchunk; ++c) {
-        const int buf = c & 1;
-        const float* as = As + buf * LDS_TILE;
-        const float* bs = Bs + buf * LDS_TILE;
-        const bool more = c + 1 < nchunk;
-        if (more) {
-            const int k0 = (c + 1) * GT_K;
-            load_rows_k<CHK>(P.A, P.lda, i0, P.M, k0, tid, ra);
-            load_b<TB, CHK>(P, j0, k0, tid, rb);
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 a4[2], b4[2];
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-                a4[bi] = *reinterpret_cast<const f32x4*>(
-                    as + (wm * 64 + bi * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
-            if (TB) {
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-                    b4[bj] = *reinterpret_cast<const f32x4*>(
-                        bs + (wn * 64 + bj * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
-            } else {
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        b4[bj][q] = bs[(16 * h + 4 * m + q) * LDS_NROW + wn * 64 + bj * 32 + l32];
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                    for (int bj = 0; bj < 2; ++bj)
-                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[bi][q], b4[bj][q],
-                                                                          acc[bi][bj], 0, 0, 0);
-        }
-        if (more) {
-            store_rows_k(As + (buf ^ 1) * LDS_TILE, tid, ra);
-            store_b<TB>(Bs + (buf ^ 1) * LDS_TILE, tid, rb);
-        }
-        __syncthreads();
-    }
-
+    chunk_mfma<TB>(As + buf * LDS_TILE, Bs + buf * LDS_TILE, wm, wn, l32, h, acc);
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -291,25 +296,37 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
             }
 }
 
+// LDS buffers and waves per SIMD for a launch site.  Every site uses two buffers, so two
+// workgroups share a CU.  With one buffer the bulk updates run about 30% faster per launch,
+// three workgroups to a CU, but the fold's serial chain then waits for free slots and the fold
+// as a whole slows down.
+template <int TAG>
+struct GemmCfg {
+    static constexpr int nbuf = 2;
+    static constexpr int waves = 2;
+};
+
 // TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
 // of problems 0 and 1; CHK: bounds checks on M and N.
 template <int TAG, bool TB0, bool TB1, bool CHK>
-__global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
+__global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(GemmCfg<TAG>::waves, GemmCfg<TAG>::waves)))
+void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
     if (abort_flag && __atomic_load_n(abort_flag, __ATOMIC_RELAXED)) return;
-    __shared__ __attribute__((aligned(16))) float As[2 * LDS_TILE];
-    __shared__ __attribute__((aligned(16))) float Bs[2 * LDS_TILE];
+    constexpr int NBUF = GemmCfg<TAG>::nbuf;
+    __shared__ __attribute__((aligned(16))) float As[NBUF * LDS_TILE];
+    __shared__ __attribute__((aligned(16))) float Bs[NBUF * LDS_TILE];
     int t = xcd_order(blockIdx.x, batch.total);
     if (t < batch.p[0].ntiles) {
         int tm, tn;
         tile_of(batch.p[0], t, tm, tn);
         if (batch.p[0].skip_upper && tn > tm) return;
-        gemm_tile<TB0, CHK>(batch.p[0], tm, tn, As, Bs);
+        gemm_tile<TB0, CHK, NBUF>(batch.p[0], tm, tn, As, Bs);
     } else {
         t -= batch.p[0].ntiles;
         int tm, tn;
         tile_of(batch.p[1], t, tm, tn);
         if (batch.p[1].skip_upper && tn > tm) return;
-        gemm_tile<TB1, CHK>(batch.p[1], tm, tn, As, Bs);
+        gemm_tile<TB1, CHK, NBUF>(batch.p[1], tm, tn, As, Bs);
     }
 }
 
