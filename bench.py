@@ -221,7 +221,7 @@ def main():
                                f"W[{rows},{n}] f32, H=X X^T from X[{n},{spec.T}]",
                    "n": n, "rows": rows, "lambda": lam, "group": 32},
         "roofline": {
-            "kernel": "gemm_kernel<0> (the fold's bulk updates: Cholesky SYRK and inverse update, on two concurrent streams)",
+            "kernel": "gemm_kernel<0> (the fold's bulk updates: Cholesky SYRK, then the inverse update, on one helper stream)",
             "bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / FP32_MFMA_PEAK_TFLOPS,
             "traffic": recorded_traffic(),

@@ -35,7 +35,7 @@ hipEvent_t take_event() {
 
 int helper_acquire(Helper* h) {
     if (dry_run()) {
-        *h = Helper{dry_stream(1), dry_stream(2), dry_event(1), dry_event(2), dry_event(3), -1};
+        *h = Helper{dry_stream(1), dry_stream(2), dry_event(1), dry_event(2), dry_event(3), dry_event(4), -1};
         return GPTQ_OK;
     }
     int dev = 0;
@@ -56,7 +56,8 @@ int helper_acquire(Helper* h) {
         return GPTQ_EHIP;
     if (hipEventCreateWithFlags(&n.ev_a, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&n.ev_b, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.ev_c, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&n.ev_c, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.ev_d, hipEventDisableTiming) != hipSuccess)
         return GPTQ_EHIP;
     *h = n;
     return GPTQ_OK;

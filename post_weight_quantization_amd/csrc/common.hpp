@@ -35,7 +35,7 @@ enum Family {
 // per-process pool for the duration of one call so that independent calls never share one.
 struct Helper {
     hipStream_t stream, stream2;
-    hipEvent_t ev_a, ev_b, ev_c;
+    hipEvent_t ev_a, ev_b, ev_c, ev_d;
     int device;
 };
 int helper_acquire(Helper* h);   // GPTQ_OK or GPTQ_EHIP

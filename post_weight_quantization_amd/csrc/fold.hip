@@ -492,13 +492,18 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
         // Three streams:
         //   st  the Cholesky's serial chain: the panel steps, then the next panel's columns
         //       (look-ahead of one panel);
-        //   ts  the Cholesky's bulk trailing update beyond the next panel, overlapping the next
-        //       panel's chain;
-        //   tx  the inverse X = L^-1, a pipeline of its own: once panel k of L is final it
-        //       inverts the panel's diagonal block, finishes the panel's rows of X and updates
-        //       every row of X below.  Nothing in the Cholesky waits for it.
+        //   ts  the two bulk updates of panel k, one after the other, overlapping the next
+        //       panel's chain: the Cholesky's trailing update beyond the next panel (ev_b, which
+        //       the look-ahead after next waits for), then the inverse's update of every row of X
+        //       below the panel (ev_d);
+        //   tx  the inverse's small steps, once panel k of L is final (ev_a): the inverse of the
+        //       panel's diagonal block and the panel's rows of X (ev_c; those rows need the
+        //       previous panel's update of X, ev_d).  Nothing in the Cholesky waits for them.
+        // One bulk update at a time gets the whole GPU beside the chain; two concurrent ones (the
+        // inverse's update on tx) each ran at about 75% of the per-launch rate and no sooner.
         hipStream_t tx = hp.stream2;
         bool first_bulk = true;
+        bool x_pending = false;  // ev_d holds an update of X that the next rows of X need
         for (int64_t kb = 0; kb < np; kb += L.nb2) {
             const int64_t w = std::min<int64_t>(L.nb2, np - kb);
             const int64_t R = w / NB;
@@ -570,8 +575,10 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             }
             // Rows of X in this panel: X[kb:kb+w, 0:kb] = Minv_w X[kb:kb+w, 0:kb] (out of place,
-            // then copied back: a workgroup tile spans only 128 of the w rows it reads).
+            // then copied back: a workgroup tile spans only 128 of the w rows it reads).  They
+            // need the previous panel's update of X (on ts, ev_d).
             if (kb > 0) {
+                if (x_pending) FOLD_OK(stream_wait(tx, hp.ev_d));
                 const GemmBatch xb = gemm_batch(
                     gemm_full(X + kb * np + kb, np, X + kb * np, np, nullptr, Xt, np, (int)w, (int)kb,
                               (int)w, 1.0f, 0),
@@ -586,28 +593,15 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                             rd(Xt, np, w, kb), wr(X + kb * np, np, w, kb));
                 if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             }
-            // Every row below: X_i,<kb+w -= L_i,k X[kb:kb+w, <kb+w] (X's columns kb..kb+w-1 are
-            // first written here, so those tiles ignore C_in).
-            if (rest > 0) {
-                GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np,
-                                           X + (kb + w) * np, np, (int)rest, (int)(kb + w), (int)w,
-                                           -1.0f, 1);
-                xu.beta0_from_tn = (int)(kb / NB);
-                // Second slot of the bulk kernel (its B layout there is "N": rows of X).
-                const GemmProblem none = gemm_none();
-                ProfScope ps(FAM_FOLD_UPDATE, tx, 2.0 * w * (double)rest * (kb + w), 0.0);
-                FOLD_OK((launch_gemm<0, true, false, false>("fold_x_update", tx, gemm_batch(none, &xu),
-                                                            &state->flag)));
-                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-            }
             if (rest <= 0) continue;
+            FOLD_OK(ev_record(hp.ev_c, tx));  // the panel's rows of X are final
 
             // --- the Cholesky's trailing update ---
             const int64_t nw = std::min<int64_t>(L.nb2, rest);  // width of the next panel
             const int64_t rest2 = rest - nw;
             // Bulk, on ts: A_ij -= P_i P_j^T beyond the next panel.
+            FOLD_OK(stream_wait(ts, hp.ev_a));
             if (rest2 > 0) {
-                FOLD_OK(stream_wait(ts, hp.ev_a));
                 const GemmProblem sy = gemm_syrk_lower(P + nw * np, np,
                                                        A + (kb + w + nw) * np + kb + w + nw,
                                                        A + (kb + w + nw) * np + kb + w + nw, np,
@@ -637,6 +631,24 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
             if (rest2 > 0) {
                 FOLD_OK(ev_record(hp.ev_b, ts));
                 first_bulk = false;
+            }
+            // The inverse's update, on ts after the SYRK: every row below,
+            // X_i,<kb+w -= L_i,k X[kb:kb+w, <kb+w] (X's columns kb..kb+w-1 are first written here,
+            // so those tiles ignore C_in).
+            {
+                FOLD_OK(stream_wait(ts, hp.ev_c));
+                GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np,
+                                           X + (kb + w) * np, np, (int)rest, (int)(kb + w), (int)w,
+                                           -1.0f, 1);
+                xu.beta0_from_tn = (int)(kb / NB);
+                // Second slot of the bulk kernel (its B layout there is "N": rows of X).
+                const GemmProblem none = gemm_none();
+                ProfScope ps(FAM_FOLD_UPDATE, ts, 2.0 * w * (double)rest * (kb + w), 0.0);
+                FOLD_OK((launch_gemm<0, true, false, false>("fold_x_update", ts, gemm_batch(none, &xu),
+                                                            &state->flag)));
+                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+                FOLD_OK(ev_record(hp.ev_d, ts));
+                x_pending = true;
             }
         }
         // Join both helper streams, then read the pivot flag.
