@@ -25,6 +25,8 @@
 // serial diag / panel chain of the next step.
 #include <math.h>
 
+#include <utility>
+
 #include <algorithm>
 
 #include "common.hpp"
@@ -182,6 +184,42 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ int mrow(int v) { return 8 * (v >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (v & 3); }
 __device__ __forceinline__ int mcol() { return threadIdx.x & 31; }
 
+// Step C of the 32 x 32 leaf of the diagonal kernel (the lane layout is described there): the
+// pivot x[C] of lane C is tested and turned into 1 / L_CC; x[C] *= 1 / L_CC makes L_sC final on
+// lane s of the lower half (L_CC = sqrt(pivot) on lane C itself) and T_C,row final in the upper
+// half, (e_row - sum_{k<C} L_Ck T_k,row) / L_CC; then every later x[s] -= x[C] L_sC, with L_sC
+// broadcast from lane s.  C is a template parameter so that every loop below has a constant trip
+// count and x[] stays in registers; the broadcasts go four at a time into separate scalar
+// registers.  Each step's updates are pinned in place so the compiler does not defer them.
+template <int C>
+__device__ __forceinline__ void leaf_step(float (&x)[32], float tau0, int& nbad) {
+    float pv = lane_bcast(x[C], C);
+    const float tau = tau0 + (float)C * 5.9604645e-8f;
+    const bool b = !(pv > tau);
+    nbad += b ? 1 : 0;
+    asm volatile("" : "+v"(nbad));
+    pv = b ? 1.0f : pv;
+    x[C] *= __builtin_amdgcn_rsqf(pv);  // pv is a normal float
+#pragma unroll
+    for (int s0 = (C + 1) & ~3; s0 < 32; s0 += 4) {
+        float L[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (s0 + u > C) L[u] = lane_bcast(x[C], s0 + u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (s0 + u > C) x[s0 + u] -= x[C] * L[u];
+    }
+#pragma unroll
+    for (int s2 = C + 1; s2 < 32; ++s2) asm volatile("" : "+v"(x[s2]));
+}
+
+template <int... C>
+__device__ __forceinline__ void leaf_steps(float (&x)[32], float tau0, int& nbad,
+                                           std::integer_sequence<int, C...>) {
+    (leaf_step<C>(x, tau0, nbad), ...);
+}
+
 __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, float* __restrict__ X,
                                                         float* __restrict__ MI, int64_t np, int k,
                                                         unsigned* flag) {
@@ -212,54 +250,34 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
     for (int p = 0; p < 4; ++p) {
         const int c0 = 32 * p;
         if (wave == 0) {
-            // Factor and invert together: lane r (and r + 32) holds row r of the 32 x 32 block
-            // (a) and column r of its inverse T = L^-1 (t).  Step c makes column c of L final;
-            // its entries L_sc (s > c), broadcast once each with readlane, drive both the
-            // right-looking Cholesky update of the later columns and the right-looking
-            // substitution step c of every column of T.  An opaque copy of the row index keeps
-            // comparisons against it inside the sub-panel (instead of hoisted out of the loop and
-            // spilled), and each step's updates are pinned in place so the compiler does not
-            // defer them.
+            // Factor and invert together: lane r holds row r of the 32 x 32 block (a) and lane
+            // r + 32 column r of its inverse T = L^-1 (t), both in x[].  Step c makes column c
+            // of L final; its entries L_sc (s > c), broadcast from the lower half, drive the
+            // same update x[s] -= x[c] L_sc in both halves: the right-looking Cholesky update of
+            // the later columns of a, and the right-looking substitution step c of every column
+            // of T.  An opaque copy of the row index keeps comparisons against it inside the
+            // sub-panel (instead of hoisted out of the loop and spilled).
             int row = l32;
             asm volatile("" : "+v"(row));
-            float a[32], t[32];
+            const bool tpart = lane >= 32;
+            float x[32];
 #pragma unroll
-            for (int c = 0; c < 32; ++c) a[c] = Ls[(c0 + row) * DLD + c0 + c];
-#pragma unroll
-            for (int q = 0; q < 32; ++q) t[q] = (q == row) ? 1.0f : 0.0f;
+            for (int c = 0; c < 32; ++c) {
+                const float av = Ls[(c0 + row) * DLD + c0 + c];
+                x[c] = tpart ? ((c == row) ? 1.0f : 0.0f) : av;
+            }
             // Pivot test at f32 resolution: the computed Schur complement of a unit-diagonal
             // matrix is exact only up to (i + 1) 2^-24 for pivot index i, so a pivot at or below
             // that bound is not known to be positive.
             const float tau0 = (float)(int)(kb + c0 + 1) * 5.9604645e-8f;
             int nbad = 0;
+            leaf_steps(x, tau0, nbad, std::make_integer_sequence<int, 32>{});
+            if (!tpart) {
 #pragma unroll
-            for (int c = 0; c < 32; ++c) {
-                float pv = lane_bcast(a[c], c);
-                const float tau = tau0 + (float)c * 5.9604645e-8f;
-                const bool b = !(pv > tau);
-                nbad += b ? 1 : 0;
-                asm volatile("" : "+v"(nbad));
-                pv = b ? 1.0f : pv;
-                const float r = __builtin_amdgcn_rsqf(pv);  // 1 / L_cc (pv is a normal float)
-                // On the pivot's own lane a[c] is the pivot, so this is L_cc = sqrt(pv) there.
-                const float l = a[c] * r;
-                a[c] = l;
-                t[c] *= r;  // T_c,row is final: (e_row - sum_{k<c} L_ck T_k,row) / L_cc
+                for (int c = 0; c < 32; ++c) Ls[(c0 + row) * DLD + c0 + c] = (c <= row) ? x[c] : 0.0f;
+            } else {
 #pragma unroll
-                for (int s2 = c + 1; s2 < 32; ++s2) {
-                    const float L_sc = lane_bcast(l, s2);
-                    a[s2] -= l * L_sc;
-                    t[s2] -= L_sc * t[c];
-                }
-#pragma unroll
-                for (int s2 = c + 1; s2 < 32; ++s2) asm volatile("" : "+v"(a[s2]), "+v"(t[s2]));
-            }
-            if (lane < 32) {
-#pragma unroll
-                for (int c = 0; c < 32; ++c) {
-                    Ls[(c0 + row) * DLD + c0 + c] = (c <= row) ? a[c] : 0.0f;
-                    Ts[p][c * SLD + row] = t[c];
-                }
+                for (int c = 0; c < 32; ++c) Ts[p][c * SLD + row] = x[c];
             }
             bad = bad || nbad != 0;
         }
