@@ -254,6 +254,9 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
         const int k0 = (c + 1) * GT_K;
         load_rows_k<CHK>(P.A, P.lda, i0, P.M, k0, tid, ra);
         load_b<TB, CHK>(P, j0, k0, tid, rb);
+        // Keep the loads here, ahead of the chunk's MFMAs: left to itself the scheduler sinks
+        // them to just before the LDS stores that use them, exposing their whole latency.
+        __builtin_amdgcn_sched_barrier(0);
         chunk_mfma<TB>(As + buf * LDS_TILE, Bs + buf * LDS_TILE, wm, wn, l32, h, acc);
         if (NBUF == 1) __syncthreads();
         const int nb = NBUF == 2 ? (buf ^ 1) : 0;

@@ -99,6 +99,8 @@ __global__ __launch_bounds__(G_THREADS) void gram_kernel(GramArgs g) {
             gram_load(g, i0, (c + 1) * GT_K, tid, ra);
             gram_load(g, j0, (c + 1) * GT_K, tid, rb);
         }
+        // Keep the loads ahead of the chunk's MFMAs (the scheduler would sink them to their use).
+        __builtin_amdgcn_sched_barrier(0);
         // Both operands are k-rows in LDS: element (k, col) at k * LDS_NROW + col.  Lane l feeds
         // MFMA row / column l % 32 and k-half h = l / 32; step s uses k = 16 h + s.
 #pragma unroll
