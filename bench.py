@@ -118,7 +118,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the fold and sweep of a Hessian group run on a single "
-              "MI355X in this build; run it with --gpus 1", file=sys.stderr)
+              "MI355X (groups are independent; see the multi-GPU notes in the design); run it "
+              "with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

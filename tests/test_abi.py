@@ -52,3 +52,13 @@ def test_product_path_has_no_cpu_fallback(monkeypatch):
         pytest.skip("a GPU is visible")
     with pytest.raises(RuntimeError):
         pwq.require_native()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with a message before touching one."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and not r.stdout.strip()
