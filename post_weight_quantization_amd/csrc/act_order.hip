@@ -8,7 +8,10 @@
 //   act_rank_kernel    the rank of every channel under that order, by counting (n^2 compares,
 //                      keys staged through LDS); perm[rank[i]] = i, dead[i] = !(H_ii > 0);
 //   act_permute_kernel Hp[a][b] = H[min(pa, pb)][max(pa, pb)] (H read through its upper
-//                      triangle), 32 x 32 output tiles, the full symmetric matrix written.
+//                      triangle): each upper 32 x 32 tile is gathered once and written twice
+//                      (in place and transposed), so the full symmetric matrix is written.
+#include <math.h>
+
 #include "check.hpp"
 #include "common.hpp"
 
@@ -49,22 +52,38 @@ __global__ __launch_bounds__(256) void act_rank_kernel(const float* __restrict__
     }
 }
 
+// One upper 32 x 32 tile (A, B), A <= B, of Hp per workgroup: its elements are gathered once
+// (Hp[a][b] = H[min(pa, pb)][max(pa, pb)]) into LDS, stored in place and, off the diagonal,
+// stored again transposed at (B, A); both stores coalesce.
 __global__ __launch_bounds__(256) void act_permute_kernel(const float* __restrict__ H,
                                                           int64_t ldh,
                                                           const int32_t* __restrict__ perm,
                                                           int64_t n, float* __restrict__ Hp) {
-    const int64_t a0 = (int64_t)blockIdx.y * 32, b0 = (int64_t)blockIdx.x * 32;
+    __shared__ float tile[32][33];
+    const int blk = blockIdx.x;
+    int r = (int)((sqrtf(8.0f * (float)blk + 1.0f) - 1.0f) * 0.5f);
+    while ((r + 1) * (r + 2) / 2 <= blk) ++r;
+    while (r * (r + 1) / 2 > blk) --r;
+    const int64_t a0 = (int64_t)(blk - r * (r + 1) / 2) * 32, b0 = (int64_t)r * 32;  // a0 <= b0
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
     const int64_t b = b0 + tx;
     const int64_t pb = (b < n) ? perm[b] : -1;
-    for (int r = ty; r < 32; r += 8) {
-        const int64_t a = a0 + r;
-        if (a >= n || b >= n) continue;
-        const int64_t pa = perm[a];
+    for (int rr = ty; rr < 32; rr += 8) {
+        const int64_t a = a0 + rr;
         float v = 0.0f;
-        if (pa >= 0 && pa < n && pb >= 0 && pb < n)
-            v = (pa <= pb) ? H[pa * ldh + pb] : H[pb * ldh + pa];
-        Hp[a * n + b] = v;
+        if (a < n && b < n) {
+            const int64_t pa = perm[a];
+            if (pa >= 0 && pa < n && pb >= 0 && pb < n)
+                v = (pa <= pb) ? H[pa * ldh + pb] : H[pb * ldh + pa];
+            Hp[a * n + b] = v;
+        }
+        tile[rr][tx] = v;
+    }
+    if (a0 == b0) return;
+    __syncthreads();
+    for (int rr = ty; rr < 32; rr += 8) {
+        const int64_t row = b0 + rr, col = a0 + tx;  // Hp[row][col] = tile[col - a0][row - b0]
+        if (row < n && col < n) Hp[row * n + col] = tile[tx][rr];
     }
 }
 
@@ -97,7 +116,7 @@ extern "C" int gptq_permute_hessian(const float* H, int64_t n, int64_t ldh, cons
     hipStream_t st = (hipStream_t)stream;
     const unsigned nt = (unsigned)((n + 31) / 32);
     GPTQ_LAUNCH(st, "act_permute",
-                (act_permute_kernel<<<dim3(nt, nt), 256, 0, st>>>(H, ldh, perm, n, Hp)),
+                (act_permute_kernel<<<nt * (nt + 1) / 2, 256, 0, st>>>(H, ldh, perm, n, Hp)),
                 rd(H, ldh, n, n), rd(perm, n, 1, n), wr(Hp, n, n, n));
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     return check.finish();
