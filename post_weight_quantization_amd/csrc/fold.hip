@@ -658,7 +658,7 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np,
                                            X + (kb + w) * np, np, (int)rest, (int)(kb + w), (int)w,
                                            -1.0f, 1);
-                xu.beta0_from_tn = (int)(kb / NB);
+                xu.beta0_col = (int)kb;
                 // Second slot of the bulk kernel (its B layout there is "N": rows of X).
                 const GemmProblem none = gemm_none();
                 ProfScope ps(FAM_FOLD_UPDATE, ts, 2.0 * w * (double)rest * (kb + w), 0.0);

@@ -48,8 +48,8 @@ struct GemmProblem {
     int tiles_n;          // tile columns (full grid) or tile rows = cols (lower)
     int ntiles;
     float alpha;
-    int beta;             // 1: add C_in (tiles with tn < beta0_from_tn), 0: never read C_in
-    int beta0_from_tn;    // tiles with tn >= this ignore C_in
+    int beta;             // 1: add C_in (tiles that start left of beta0_col), 0: never read C_in
+    int beta0_col;        // tiles whose first column is at or right of this ignore C_in
 };
 
 struct GemmBatch {
@@ -237,7 +237,7 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-    const bool use_c = P.beta && tn < P.beta0_from_tn;
+    const bool use_c = P.beta && tn * GT_N < P.beta0_col;
     const bool diag_tile = P.mask_diag && tm == tn;
     {
         f32x4 ra[4], rb[4];
@@ -299,15 +299,166 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
             }
 }
 
-// LDS buffers and waves per SIMD for a launch site.  Every site uses two buffers, so two
-// workgroups share a CU.  With one buffer the bulk updates run about 30% faster per launch,
-// three workgroups to a CU, but the fold's serial chain then waits for free slots and the fold
-// as a whole slows down.
+// A 64 x 64 tile, for the small products on the serial chains: four times the workgroups of
+// the 128 tile for the same product, each with a quarter of the MFMAs, so a launch that fills
+// only part of the GPU finishes sooner.  Each of the 4 waves computes 32 x 32 with one
+// accumulator; K chunks of 32 through LDS as in the 128 tile ("T" operands as k-contiguous rows
+// of stride LDS_KROW, the "N" B as k-rows of stride LDS_NROW64).
+constexpr int LDS_NROW64 = 64 + 4;
+constexpr int LDS_TILE64 = 64 * LDS_KROW;  // >= GT_K * LDS_NROW64
+
+template <bool CHK>
+__device__ __forceinline__ void load_rows_k64(const float* base, int64_t ld, int row0, int nrows,
+                                              int k0, int tid, f32x4 (&r)[2]) {
+    const int kq = (tid & 7) * 4;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int row = (tid >> 3) + 32 * p;
+        if (!CHK || row0 + row < nrows)
+            r[p] = *reinterpret_cast<const f32x4*>(base + (int64_t)(row0 + row) * ld + k0 + kq);
+        else
+            r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+__device__ __forceinline__ void store_rows_k64(float* lds, int tid, const f32x4 (&r)[2]) {
+    const int kq = (tid & 7) * 4;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+        *reinterpret_cast<f32x4*>(lds + ((tid >> 3) + 32 * p) * LDS_KROW + kq) = r[p];
+}
+
+template <bool CHK>
+__device__ __forceinline__ void load_krows_n64(const float* base, int64_t ld, int col0, int ncols,
+                                               int k0, int tid, f32x4 (&r)[2]) {
+    const int jq = (tid & 15) * 4;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int kr = (tid >> 4) + 16 * p;
+        if (!CHK || col0 + jq < ncols)
+            r[p] = *reinterpret_cast<const f32x4*>(base + (int64_t)(k0 + kr) * ld + col0 + jq);
+        else
+            r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+__device__ __forceinline__ void store_krows_n64(float* lds, int tid, const f32x4 (&r)[2]) {
+    const int jq = (tid & 15) * 4;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+        *reinterpret_cast<f32x4*>(lds + ((tid >> 4) + 16 * p) * LDS_NROW64 + jq) = r[p];
+}
+
+template <bool TB, bool CHK>
+__device__ __forceinline__ void load_b64(const GemmProblem& P, int j0, int k0, int tid,
+                                         f32x4 (&r)[2]) {
+    if (TB) load_rows_k64<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
+    else load_krows_n64<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
+}
+
+template <bool TB>
+__device__ __forceinline__ void store_b64(float* lds, int tid, const f32x4 (&r)[2]) {
+    if (TB) store_rows_k64(lds, tid, r);
+    else store_krows_n64(lds, tid, r);
+}
+
+template <bool TB>
+__device__ __forceinline__ void chunk_mfma64(const float* as, const float* bs, int wm, int wn,
+                                             int l32, int h, f32x16& acc) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(as + (wm * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
+        f32x4 b4;
+        if (TB) {
+            b4 = *reinterpret_cast<const f32x4*>(bs + (wn * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b4[q] = bs[(16 * h + 4 * m + q) * LDS_NROW64 + wn * 32 + l32];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[q], b4[q], acc, 0, 0, 0);
+    }
+}
+
+template <bool TB, bool CHK>
+__device__ __forceinline__ void gemm_tile64(const GemmProblem& P, int tm, int tn, float* As,
+                                            float* Bs) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int i0 = tm * 64, j0 = tn * 64;
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    const bool use_c = P.beta && j0 < P.beta0_col;
+    const bool diag_tile = P.mask_diag && tm == tn;
+    {
+        f32x4 ra[2], rb[2];
+        load_rows_k64<CHK>(P.A, P.lda, i0, P.M, 0, tid, ra);
+        load_b64<TB, CHK>(P, j0, 0, tid, rb);
+        store_rows_k64(As, tid, ra);
+        store_b64<TB>(Bs, tid, rb);
+    }
+    __syncthreads();
+    const int nchunk = P.K / GT_K;
+    int buf = 0;
+    for (int c = 0; c + 1 < nchunk; ++c) {
+        f32x4 ra[2], rb[2];
+        const int k0 = (c + 1) * GT_K;
+        load_rows_k64<CHK>(P.A, P.lda, i0, P.M, k0, tid, ra);
+        load_b64<TB, CHK>(P, j0, k0, tid, rb);
+        __builtin_amdgcn_sched_barrier(0);
+        chunk_mfma64<TB>(As + buf * LDS_TILE64, Bs + buf * LDS_TILE64, wm, wn, l32, h, acc);
+        const int nb = buf ^ 1;
+        store_rows_k64(As + nb * LDS_TILE64, tid, ra);
+        store_b64<TB>(Bs + nb * LDS_TILE64, tid, rb);
+        __syncthreads();
+        buf = nb;
+    }
+    float cv[16];
+    if (use_c) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = CHK ? min(i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), P.M - 1)
+                              : i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const int j = CHK ? min(j0 + wn * 32 + l32, P.N - 1) : j0 + wn * 32 + l32;
+            cv[v] = P.Cin[(int64_t)i * P.ldc + j];
+        }
+    }
+    chunk_mfma64<TB>(As + buf * LDS_TILE64, Bs + buf * LDS_TILE64, wm, wn, l32, h, acc);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int lj = wn * 32 + l32;
+        const int i = i0 + li, j = j0 + lj;
+        if ((!CHK || (i < P.M && j < P.N)) && (!diag_tile || li >= lj)) {
+            const float base = use_c ? cv[v] : 0.0f;
+            P.Cout[(int64_t)i * P.ldc + j] = base + P.alpha * acc[v];
+        }
+    }
+}
+
+// LDS buffers, waves per SIMD and tile size for a launch site.  Every site uses two buffers.
+// With one buffer the bulk updates run about 30% faster per launch, three workgroups to a CU,
+// but the fold's serial chain then waits for free slots and the fold as a whole slows down.
+// The products on the serial chains that do not fill the GPU with 128 tiles take 64 tiles:
+// the fold's look-ahead (3) and update inside a panel (4), the inverse's diagonal-block steps
+// (5), the sweep's update inside a panel (6) and look-ahead (7).  The fold's panel solve (1)
+// keeps 128 tiles: it works in place, and a 128-wide tile row is what makes that safe (each
+// workgroup reads all the columns it overwrites).
 template <int TAG>
 struct GemmCfg {
     static constexpr int nbuf = 2;
     static constexpr int waves = 2;
+    static constexpr int tile = 128;
 };
+template <> struct GemmCfg<3> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
+template <> struct GemmCfg<4> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
+template <> struct GemmCfg<5> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
+template <> struct GemmCfg<6> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
+template <> struct GemmCfg<7> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
 
 // TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
 // of problems 0 and 1; CHK: bounds checks on M and N.
@@ -316,20 +467,23 @@ __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(GemmC
 void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
     if (abort_flag && __atomic_load_n(abort_flag, __ATOMIC_RELAXED)) return;
     constexpr int NBUF = GemmCfg<TAG>::nbuf;
-    __shared__ __attribute__((aligned(16))) float As[NBUF * LDS_TILE];
-    __shared__ __attribute__((aligned(16))) float Bs[NBUF * LDS_TILE];
+    constexpr int TILE = GemmCfg<TAG>::tile;
+    constexpr int LT = TILE == 128 ? NBUF * LDS_TILE : 2 * LDS_TILE64;
+    __shared__ __attribute__((aligned(16))) float As[LT];
+    __shared__ __attribute__((aligned(16))) float Bs[LT];
     int t = xcd_order(blockIdx.x, batch.total);
+    int tm, tn;
     if (t < batch.p[0].ntiles) {
-        int tm, tn;
         tile_of(batch.p[0], t, tm, tn);
         if (batch.p[0].skip_upper && tn > tm) return;
-        gemm_tile<TB0, CHK, NBUF>(batch.p[0], tm, tn, As, Bs);
+        if (TILE == 128) gemm_tile<TB0, CHK, NBUF>(batch.p[0], tm, tn, As, Bs);
+        else gemm_tile64<TB0, CHK>(batch.p[0], tm, tn, As, Bs);
     } else {
         t -= batch.p[0].ntiles;
-        int tm, tn;
         tile_of(batch.p[1], t, tm, tn);
         if (batch.p[1].skip_upper && tn > tm) return;
-        gemm_tile<TB1, CHK, NBUF>(batch.p[1], tm, tn, As, Bs);
+        if (TILE == 128) gemm_tile<TB1, CHK, NBUF>(batch.p[1], tm, tn, As, Bs);
+        else gemm_tile64<TB1, CHK>(batch.p[1], tm, tn, As, Bs);
     }
 }
 
@@ -346,7 +500,7 @@ inline GemmProblem gemm_full(const float* A, int64_t lda, const float* B, int64_
     p.skip_upper = 0;
     p.tiles_n = (N + GT_N - 1) / GT_N;
     p.ntiles = ((M + GT_M - 1) / GT_M) * p.tiles_n;
-    p.alpha = alpha; p.beta = beta; p.beta0_from_tn = p.tiles_n;
+    p.alpha = alpha; p.beta = beta; p.beta0_col = N;
     if (M <= 0 || N <= 0) p.ntiles = 0;
     return p;
 }
@@ -360,8 +514,20 @@ inline GemmProblem gemm_syrk_lower(const float* A, int64_t lda, const float* Cin
     p.mask_diag = 1;
     p.tiles_n = T;
     p.ntiles = M > 0 ? T * (T + 1) / 2 : 0;
-    p.beta0_from_tn = T;
     return p;
+}
+
+// The tile grid of a problem for tiles of `tile` x `tile` (the helpers above count 128-tiles).
+inline void retile(GemmProblem& p, int tile) {
+    if (p.ntiles <= 0) return;
+    if (p.lower) {
+        const int T = (p.M + tile - 1) / tile;
+        p.tiles_n = T;
+        p.ntiles = T * (T + 1) / 2;
+    } else {
+        p.tiles_n = (p.N + tile - 1) / tile;
+        p.ntiles = ((p.M + tile - 1) / tile) * p.tiles_n;
+    }
 }
 
 // A problem with no tiles: fills the first slot of a batch whose only problem needs the
@@ -390,7 +556,7 @@ inline GemmBatch gemm_batch(const GemmProblem& a, const GemmProblem* b) {
 // or -1 when a problem breaks the kernel's shape rules (K a multiple of 32; with bounds checks
 // and the "N" layout, N a multiple of 4).
 template <bool TB0, bool TB1, bool CHK>
-inline int gemm_spans(const GemmBatch& b, Span* out) {
+inline int gemm_spans(const GemmBatch& b, Span* out, int tile) {
     int n = 0;
     for (int q = 0; q < b.nprob && q < 2; ++q) {
         const GemmProblem& P = b.p[q];
@@ -399,13 +565,15 @@ inline int gemm_spans(const GemmBatch& b, Span* out) {
         if (P.K <= 0 || P.K % GT_K != 0 || (CHK && !TB && P.N % 4 != 0) || P.tiles_n <= 0)
             return -1;
         const int64_t tm = P.lower ? P.tiles_n : P.ntiles / P.tiles_n;
-        const int64_t rows = CHK ? P.M : tm * GT_M;
-        const int64_t cols = CHK ? P.N : (int64_t)P.tiles_n * GT_N;
+        const int64_t rows = CHK ? P.M : tm * tile;
+        const int64_t cols = CHK ? P.N : (int64_t)P.tiles_n * tile;
         out[n++] = rd(P.A, P.lda, rows, P.K);
         out[n++] = TB ? rd(P.B, P.ldb, cols, P.K) : rd(P.B, P.ldb, P.K, cols);
-        if (P.beta && P.beta0_from_tn > 0)
-            out[n++] = rd(P.Cin, P.ldc, rows,
-                          cols < (int64_t)P.beta0_from_tn * GT_N ? cols : (int64_t)P.beta0_from_tn * GT_N);
+        if (P.beta && P.beta0_col > 0) {
+            // Tiles starting left of beta0_col read C_in over their whole width.
+            const int64_t c_in = ((int64_t)P.beta0_col + tile - 1) / tile * tile;
+            out[n++] = rd(P.Cin, P.ldc, rows, cols < c_in ? cols : c_in);
+        }
         out[n++] = wr(P.Cout, P.ldc, rows, cols);
     }
     return n;
@@ -414,10 +582,14 @@ inline int gemm_spans(const GemmBatch& b, Span* out) {
 // Launch one batch on stream s with `grid` workgroups (normally batch.total), after checking
 // its shape rules (GPTQ_EINVAL) and recording its accesses (check mode).
 template <int TAG, bool TB0, bool TB1, bool CHK>
-inline int launch_gemm(const char* name, hipStream_t s, const GemmBatch& b, const unsigned* flag) {
+inline int launch_gemm(const char* name, hipStream_t s, const GemmBatch& b0, const unsigned* flag) {
+    constexpr int TILE = GemmCfg<TAG>::tile;
+    GemmBatch b = b0;
+    for (int q = 0; q < b.nprob && q < 2; ++q) retile(b.p[q], TILE);
+    b.total = b.p[0].ntiles + (b.nprob > 1 ? b.p[1].ntiles : 0);
     if (b.total <= 0) return GPTQ_OK;
     Span acc[8];
-    const int na = gemm_spans<TB0, TB1, CHK>(b, acc);
+    const int na = gemm_spans<TB0, TB1, CHK>(b, acc, TILE);
     if (na < 0) return GPTQ_EINVAL;
     const int rc = check_launch(name, s, acc, na);
     if (rc != GPTQ_OK) return rc;
