@@ -603,7 +603,7 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                     nullptr);
                 {
                     ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * (double)w * w * kb, 0.0);
-                    FOLD_OK((launch_gemm<1, false, false, false>("fold_x_rows", tx, xb, &state->flag)));
+                    FOLD_OK((launch_gemm<9, false, false, false>("fold_x_rows", tx, xb, &state->flag)));
                 }
                 GPTQ_LAUNCH(tx, "fold_copy_rows",
                             (fold_copy_rows_kernel<<<dim3((unsigned)((kb + 1023) / 1024), (unsigned)w), 256, 0, tx>>>(

@@ -445,7 +445,7 @@ __device__ __forceinline__ void gemm_tile64(const GemmProblem& P, int tm, int tn
 // but the fold's serial chain then waits for free slots and the fold as a whole slows down.
 // The products on the serial chains that do not fill the GPU with 128 tiles take 64 tiles:
 // the fold's look-ahead (3) and update inside a panel (4), the inverse's diagonal-block steps
-// (5), the sweep's update inside a panel (6) and look-ahead (7).  The fold's panel solve (1)
+// (5) and panel rows of X (9), the sweep's update inside a panel (6) and look-ahead (7).  The fold's panel solve (1)
 // keeps 128 tiles: it works in place, and a 128-wide tile row is what makes that safe (each
 // workgroup reads all the columns it overwrites).
 template <int TAG>
@@ -459,6 +459,7 @@ template <> struct GemmCfg<4> { static constexpr int nbuf = 2; static constexpr 
 template <> struct GemmCfg<5> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
 template <> struct GemmCfg<6> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
 template <> struct GemmCfg<7> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
+template <> struct GemmCfg<9> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
 
 // TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
 // of problems 0 and 1; CHK: bounds checks on M and N.
