@@ -349,117 +349,151 @@ __device__ __forceinline__ void store_krows_n64(float* lds, int tid, const f32x4
         *reinterpret_cast<f32x4*>(lds + ((tid >> 4) + 16 * p) * LDS_NROW64 + jq) = r[p];
 }
 
-template <bool TB, bool CHK>
-__device__ __forceinline__ void load_b64(const GemmProblem& P, int j0, int k0, int tid,
-                                         f32x4 (&r)[2]) {
-    if (TB) load_rows_k64<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
-    else load_krows_n64<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
-}
-
-template <bool TB>
-__device__ __forceinline__ void store_b64(float* lds, int tid, const f32x4 (&r)[2]) {
-    if (TB) store_rows_k64(lds, tid, r);
-    else store_krows_n64(lds, tid, r);
-}
-
-template <bool TB>
-__device__ __forceinline__ void chunk_mfma64(const float* as, const float* bs, int wm, int wn,
-                                             int l32, int h, f32x16& acc) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(as + (wm * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
-        f32x4 b4;
-        if (TB) {
-            b4 = *reinterpret_cast<const f32x4*>(bs + (wn * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) b4[q] = bs[(16 * h + 4 * m + q) * LDS_NROW64 + wn * 32 + l32];
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[q], b4[q], acc, 0, 0, 0);
+// B staging of the small tiles: TN = 64 uses the helpers above, TN = 128 those of the 128 tile.
+template <bool TB, bool CHK, int TN>
+__device__ __forceinline__ void load_b_small(const GemmProblem& P, int j0, int k0, int tid,
+                                             f32x4 (&r)[TN / 32]) {
+    if constexpr (TN == 64) {
+        if (TB) load_rows_k64<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
+        else load_krows_n64<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
+    } else {
+        if (TB) load_rows_k<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
+        else load_krows_n<CHK>(P.B, P.ldb, j0, P.N, k0, tid, r);
     }
 }
 
-template <bool TB, bool CHK>
-__device__ __forceinline__ void gemm_tile64(const GemmProblem& P, int tm, int tn, float* As,
-                                            float* Bs) {
+template <bool TB, int TN>
+__device__ __forceinline__ void store_b_small(float* lds, int tid, const f32x4 (&r)[TN / 32]) {
+    if constexpr (TN == 64) {
+        if (TB) store_rows_k64(lds, tid, r);
+        else store_krows_n64(lds, tid, r);
+    } else {
+        if (TB) store_rows_k(lds, tid, r);
+        else store_krows_n(lds, tid, r);
+    }
+}
+
+// Wave (wm, wn) of a 64 x TN tile: rows wm*32 .. +32, columns wn*TN/2 .. +TN/2 as TN/64
+// accumulators of 32 x 32.
+template <bool TB, int TN>
+__device__ __forceinline__ void chunk_mfma_small(const float* as, const float* bs, int wm, int wn,
+                                                 int l32, int h, f32x16 (&acc)[TN / 64]) {
+    constexpr int NA = TN / 64, NROW = TN + 4;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(as + (wm * 32 + l32) * LDS_KROW + 16 * h + 4 * m);
+        f32x4 b4[NA];
+#pragma unroll
+        for (int bj = 0; bj < NA; ++bj) {
+            const int col = wn * (TN / 2) + bj * 32 + l32;
+            if (TB) {
+                b4[bj] = *reinterpret_cast<const f32x4*>(bs + col * LDS_KROW + 16 * h + 4 * m);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) b4[bj][q] = bs[(16 * h + 4 * m + q) * NROW + col];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int bj = 0; bj < NA; ++bj)
+                acc[bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[q], b4[bj][q], acc[bj], 0, 0, 0);
+    }
+}
+
+// A 64 x TN tile (TN = 64 or 128), the same K loop as the 128 tile.
+template <bool TB, bool CHK, int TN>
+__device__ __forceinline__ void gemm_tile_small(const GemmProblem& P, int tm, int tn, float* As,
+                                                float* Bs) {
+    constexpr int NA = TN / 64, NB_ = TN / 32;
+    constexpr int BT = TN == 64 ? LDS_TILE64 : LDS_TILE;  // floats per B buffer
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, h = lane >> 5;
-    const int i0 = tm * 64, j0 = tn * 64;
-    f32x16 acc;
+    const int i0 = tm * 64, j0 = tn * TN;
+    f32x16 acc[NA];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    for (int bj = 0; bj < NA; ++bj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[bj][v] = 0.0f;
     const bool use_c = P.beta && j0 < P.beta0_col;
-    const bool diag_tile = P.mask_diag && tm == tn;
+    const bool diag_tile = P.mask_diag && tm == tn;  // square tiles only (host-checked)
     {
-        f32x4 ra[2], rb[2];
+        f32x4 ra[2], rb[NB_];
         load_rows_k64<CHK>(P.A, P.lda, i0, P.M, 0, tid, ra);
-        load_b64<TB, CHK>(P, j0, 0, tid, rb);
+        load_b_small<TB, CHK, TN>(P, j0, 0, tid, rb);
         store_rows_k64(As, tid, ra);
-        store_b64<TB>(Bs, tid, rb);
+        store_b_small<TB, TN>(Bs, tid, rb);
     }
     __syncthreads();
     const int nchunk = P.K / GT_K;
     int buf = 0;
     for (int c = 0; c + 1 < nchunk; ++c) {
-        f32x4 ra[2], rb[2];
+        f32x4 ra[2], rb[NB_];
         const int k0 = (c + 1) * GT_K;
         load_rows_k64<CHK>(P.A, P.lda, i0, P.M, k0, tid, ra);
-        load_b64<TB, CHK>(P, j0, k0, tid, rb);
+        load_b_small<TB, CHK, TN>(P, j0, k0, tid, rb);
         __builtin_amdgcn_sched_barrier(0);
-        chunk_mfma64<TB>(As + buf * LDS_TILE64, Bs + buf * LDS_TILE64, wm, wn, l32, h, acc);
+        chunk_mfma_small<TB, TN>(As + buf * LDS_TILE64, Bs + buf * BT, wm, wn, l32, h, acc);
         const int nb = buf ^ 1;
         store_rows_k64(As + nb * LDS_TILE64, tid, ra);
-        store_b64<TB>(Bs + nb * LDS_TILE64, tid, rb);
+        store_b_small<TB, TN>(Bs + nb * BT, tid, rb);
         __syncthreads();
         buf = nb;
     }
-    float cv[16];
+    float cv[NA][16];
     if (use_c) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = CHK ? min(i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), P.M - 1)
-                              : i0 + wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int j = CHK ? min(j0 + wn * 32 + l32, P.N - 1) : j0 + wn * 32 + l32;
-            cv[v] = P.Cin[(int64_t)i * P.ldc + j];
-        }
-    }
-    chunk_mfma64<TB>(As + buf * LDS_TILE64, Bs + buf * LDS_TILE64, wm, wn, l32, h, acc);
+        for (int bj = 0; bj < NA; ++bj)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        const int lj = wn * 32 + l32;
-        const int i = i0 + li, j = j0 + lj;
-        if ((!CHK || (i < P.M && j < P.N)) && (!diag_tile || li >= lj)) {
-            const float base = use_c ? cv[v] : 0.0f;
-            P.Cout[(int64_t)i * P.ldc + j] = base + P.alpha * acc[v];
-        }
+            for (int v = 0; v < 16; ++v) {
+                const int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int lj = wn * (TN / 2) + bj * 32 + l32;
+                const int i = CHK ? min(i0 + li, P.M - 1) : i0 + li;
+                const int j = CHK ? min(j0 + lj, P.N - 1) : j0 + lj;
+                cv[bj][v] = P.Cin[(int64_t)i * P.ldc + j];
+            }
     }
+    chunk_mfma_small<TB, TN>(As + buf * LDS_TILE64, Bs + buf * BT, wm, wn, l32, h, acc);
+#pragma unroll
+    for (int bj = 0; bj < NA; ++bj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const int lj = wn * (TN / 2) + bj * 32 + l32;
+            const int i = i0 + li, j = j0 + lj;
+            if ((!CHK || (i < P.M && j < P.N)) && (!diag_tile || li >= lj)) {
+                const float base = use_c ? cv[bj][v] : 0.0f;
+                P.Cout[(int64_t)i * P.ldc + j] = base + P.alpha * acc[bj][v];
+            }
+        }
 }
 
 // LDS buffers, waves per SIMD and tile size for a launch site.  Every site uses two buffers.
 // With one buffer the bulk updates run about 30% faster per launch, three workgroups to a CU,
 // but the fold's serial chain then waits for free slots and the fold as a whole slows down.
-// The products on the serial chains that do not fill the GPU with 128 tiles take 64 tiles:
+// The products on the serial chains that do not fill the GPU with 128 tiles take 64 x 64 tiles:
 // the fold's look-ahead (3) and update inside a panel (4), the inverse's diagonal-block steps
-// (5) and panel rows of X (9), the sweep's update inside a panel (6) and look-ahead (7).  The fold's panel solve (1)
-// keeps 128 tiles: it works in place, and a 128-wide tile row is what makes that safe (each
-// workgroup reads all the columns it overwrites).
+// (5) and panel rows of X (9), the sweep's update inside a panel (6) and look-ahead (7).  The
+// fold's panel solve (1) takes 64 x 128 tiles: it works in place on a 128-column block, and a
+// tile row 128 columns wide is what makes that safe (each workgroup reads all the columns it
+// overwrites before it writes).
 template <int TAG>
 struct GemmCfg {
     static constexpr int nbuf = 2;
     static constexpr int waves = 2;
-    static constexpr int tile = 128;
+    static constexpr int tile = 128;    // tile rows
+    static constexpr int tile_n = 128;  // tile columns
 };
-template <> struct GemmCfg<3> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
-template <> struct GemmCfg<4> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
-template <> struct GemmCfg<5> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
-template <> struct GemmCfg<6> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
-template <> struct GemmCfg<7> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
-template <> struct GemmCfg<9> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; };
+template <> struct GemmCfg<3> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
+template <> struct GemmCfg<4> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
+template <> struct GemmCfg<5> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
+template <> struct GemmCfg<6> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
+template <> struct GemmCfg<7> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
+template <> struct GemmCfg<9> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
+template <> struct GemmCfg<1> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 128; };
 
 // TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
 // of problems 0 and 1; CHK: bounds checks on M and N.
@@ -468,23 +502,26 @@ __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(GemmC
 void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
     if (abort_flag && __atomic_load_n(abort_flag, __ATOMIC_RELAXED)) return;
     constexpr int NBUF = GemmCfg<TAG>::nbuf;
-    constexpr int TILE = GemmCfg<TAG>::tile;
-    constexpr int LT = TILE == 128 ? NBUF * LDS_TILE : 2 * LDS_TILE64;
-    __shared__ __attribute__((aligned(16))) float As[LT];
-    __shared__ __attribute__((aligned(16))) float Bs[LT];
+    constexpr int TILE = GemmCfg<TAG>::tile, TILE_N = GemmCfg<TAG>::tile_n;
+    static_assert(TILE == 128 ? TILE_N == 128 : (TILE == 64 && (TILE_N == 64 || TILE_N == 128)),
+                  "tile shapes: 128 x 128, 64 x 64, 64 x 128");
+    constexpr int LA = TILE == 128 ? NBUF * LDS_TILE : 2 * LDS_TILE64;
+    constexpr int LB = TILE == 128 ? NBUF * LDS_TILE : 2 * (TILE_N == 64 ? LDS_TILE64 : LDS_TILE);
+    __shared__ __attribute__((aligned(16))) float As[LA];
+    __shared__ __attribute__((aligned(16))) float Bs[LB];
     int t = xcd_order(blockIdx.x, batch.total);
     int tm, tn;
     if (t < batch.p[0].ntiles) {
         tile_of(batch.p[0], t, tm, tn);
         if (batch.p[0].skip_upper && tn > tm) return;
         if (TILE == 128) gemm_tile<TB0, CHK, NBUF>(batch.p[0], tm, tn, As, Bs);
-        else gemm_tile64<TB0, CHK>(batch.p[0], tm, tn, As, Bs);
+        else gemm_tile_small<TB0, CHK, TILE_N>(batch.p[0], tm, tn, As, Bs);
     } else {
         t -= batch.p[0].ntiles;
         tile_of(batch.p[1], t, tm, tn);
         if (batch.p[1].skip_upper && tn > tm) return;
         if (TILE == 128) gemm_tile<TB1, CHK, NBUF>(batch.p[1], tm, tn, As, Bs);
-        else gemm_tile64<TB1, CHK>(batch.p[1], tm, tn, As, Bs);
+        else gemm_tile_small<TB1, CHK, TILE_N>(batch.p[1], tm, tn, As, Bs);
     }
 }
 
@@ -518,17 +555,20 @@ inline GemmProblem gemm_syrk_lower(const float* A, int64_t lda, const float* Cin
     return p;
 }
 
-// The tile grid of a problem for tiles of `tile` x `tile` (the helpers above count 128-tiles).
-inline void retile(GemmProblem& p, int tile) {
-    if (p.ntiles <= 0) return;
+// The tile grid of a problem for tiles of tm x tn (the helpers above count 128-tiles).
+// Returns false for a lower grid or a diagonal mask with non-square tiles.
+inline bool retile(GemmProblem& p, int tm, int tn) {
+    if (p.ntiles <= 0) return true;
+    if ((p.lower || p.mask_diag || p.skip_upper) && tm != tn) return false;
     if (p.lower) {
-        const int T = (p.M + tile - 1) / tile;
+        const int T = (p.M + tm - 1) / tm;
         p.tiles_n = T;
         p.ntiles = T * (T + 1) / 2;
     } else {
-        p.tiles_n = (p.N + tile - 1) / tile;
-        p.ntiles = ((p.M + tile - 1) / tile) * p.tiles_n;
+        p.tiles_n = (p.N + tn - 1) / tn;
+        p.ntiles = ((p.M + tm - 1) / tm) * p.tiles_n;
     }
+    return true;
 }
 
 // A problem with no tiles: fills the first slot of a batch whose only problem needs the
@@ -557,7 +597,7 @@ inline GemmBatch gemm_batch(const GemmProblem& a, const GemmProblem* b) {
 // or -1 when a problem breaks the kernel's shape rules (K a multiple of 32; with bounds checks
 // and the "N" layout, N a multiple of 4).
 template <bool TB0, bool TB1, bool CHK>
-inline int gemm_spans(const GemmBatch& b, Span* out, int tile) {
+inline int gemm_spans(const GemmBatch& b, Span* out, int tile, int tile_n) {
     int n = 0;
     for (int q = 0; q < b.nprob && q < 2; ++q) {
         const GemmProblem& P = b.p[q];
@@ -567,12 +607,12 @@ inline int gemm_spans(const GemmBatch& b, Span* out, int tile) {
             return -1;
         const int64_t tm = P.lower ? P.tiles_n : P.ntiles / P.tiles_n;
         const int64_t rows = CHK ? P.M : tm * tile;
-        const int64_t cols = CHK ? P.N : (int64_t)P.tiles_n * tile;
+        const int64_t cols = CHK ? P.N : (int64_t)P.tiles_n * tile_n;
         out[n++] = rd(P.A, P.lda, rows, P.K);
         out[n++] = TB ? rd(P.B, P.ldb, cols, P.K) : rd(P.B, P.ldb, P.K, cols);
         if (P.beta && P.beta0_col > 0) {
             // Tiles starting left of beta0_col read C_in over their whole width.
-            const int64_t c_in = ((int64_t)P.beta0_col + tile - 1) / tile * tile;
+            const int64_t c_in = ((int64_t)P.beta0_col + tile_n - 1) / tile_n * tile_n;
             out[n++] = rd(P.Cin, P.ldc, rows, cols < c_in ? cols : c_in);
         }
         out[n++] = wr(P.Cout, P.ldc, rows, cols);
@@ -584,13 +624,14 @@ inline int gemm_spans(const GemmBatch& b, Span* out, int tile) {
 // its shape rules (GPTQ_EINVAL) and recording its accesses (check mode).
 template <int TAG, bool TB0, bool TB1, bool CHK>
 inline int launch_gemm(const char* name, hipStream_t s, const GemmBatch& b0, const unsigned* flag) {
-    constexpr int TILE = GemmCfg<TAG>::tile;
+    constexpr int TILE = GemmCfg<TAG>::tile, TILE_N = GemmCfg<TAG>::tile_n;
     GemmBatch b = b0;
-    for (int q = 0; q < b.nprob && q < 2; ++q) retile(b.p[q], TILE);
+    for (int q = 0; q < b.nprob && q < 2; ++q)
+        if (!retile(b.p[q], TILE, TILE_N)) return GPTQ_EINVAL;
     b.total = b.p[0].ntiles + (b.nprob > 1 ? b.p[1].ntiles : 0);
     if (b.total <= 0) return GPTQ_OK;
     Span acc[8];
-    const int na = gemm_spans<TB0, TB1, CHK>(b, acc, TILE);
+    const int na = gemm_spans<TB0, TB1, CHK>(b, acc, TILE, TILE_N);
     if (na < 0) return GPTQ_EINVAL;
     const int rc = check_launch(name, s, acc, na);
     if (rc != GPTQ_OK) return rc;
