@@ -52,6 +52,24 @@ def test_ragged_shapes(gpu, n, rows):
     assert_sweep_bar(st)
 
 
+@pytest.mark.parametrize("n,rows", [(1184, 300), (2080, 77)])
+def test_ragged_multi_panel(gpu, n, rows):
+    """Several fold panels and sweep panels with ragged ends: n = 1184 pads to 1280 (outer
+    fold panels of 256, sweep panels 512 + 512 + 160), n = 2080 pads to 2176 (fold panels of
+    512 and a last one of 128; sweep panels 4 x 512 + 32); rows not a multiple of any tile."""
+    say("ragged multi-panel", n, rows)
+    rng = np.random.default_rng(7 * n + rows)
+    X = rng.standard_normal((n, n + 64)) * np.exp(0.8 * rng.standard_normal(n))[:, None]
+    H = (X @ X.T).astype(np.float32)
+    for c in (3, n // 2, n - 1):
+        H[c, :] = 0.0
+        H[:, c] = 0.0
+    W = (rng.standard_normal((rows, n)) * 0.02).astype(np.float32)
+    (U, hdiag, dead, rep), orc, err = check_fold(gpu, _dev(H), 0.01, H_np=H)
+    st, _ = check_sweep_isolated(gpu, _dev(W), U, hdiag, dead)
+    assert_sweep_bar(st)
+
+
 def test_identity_hessian_closed_form_and_rtn(gpu):
     n, rows, lam = 256, 96, 0.01
     say("identity hessian")
