@@ -252,6 +252,7 @@ struct BlockCtx {
     const float* uinv;   // 1 / U_jj (0 where U_jj <= 0), LDS
     const float* hs;     // H_ii of the block's columns, LDS
     const float* tb;     // the row's 32 rung scales
+    const float* ti;     // their reciprocals (0 where the scale is not positive)
     const float* sp;     // static groups: this row's per-column scales from column c0
     uint8_t* codes;      // static groups: this row's codes (one byte each) from column c0
     float lo, st;
@@ -283,7 +284,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
             for (int cand = 1; cand < 32; ++cand) {
                 const float s_c = cx.tb[cand];
                 if (!(s_c > 0.0f)) continue;
-                const float err = group16_sum(pair_err_q2(w[g][0], w[g][1], h0, h1, s_c, 1.0f / s_c));
+                const float err = group16_sum(pair_err_q2(w[g][0], w[g][1], h0, h1, s_c, cx.ti[cand]));
                 if (err < best_e) {
                     best_e = err;
                     best = cand;
@@ -291,7 +292,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
             }
         }
         s = cx.tb[best];
-        inv_s = (s > 0.0f) ? 1.0f / s : 0.0f;
+        inv_s = cx.ti[best];
         if (k == 0) {
             const int64_t gi = r * (n / 32) + (c0 / 32) + g;
             rung[gi] = (uint8_t)best;
@@ -315,7 +316,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         for (int cand = lo_c; cand <= hi_c; ++cand) {
             const float s_c = cx.tb[cand];
             if (s_c <= 0.0f) continue;
-            const float err = group16_sum(pair_err(w[g][0], w[g][1], h0, h1, s_c, 1.0f / s_c));
+            const float err = group16_sum(pair_err(w[g][0], w[g][1], h0, h1, s_c, cx.ti[cand]));
             if (err < best_e) {
                 best_e = err;
                 best = cand;
@@ -323,7 +324,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         }
     }
     s = cx.tb[best];
-    inv_s = (s > 0.0f) ? 1.0f / s : 0.0f;
+    inv_s = cx.ti[best];
     if (k == 0) {
         const int64_t gi = r * (n / 32) + (c0 / 32) + g;
         rung[gi] = (uint8_t)best;
@@ -424,6 +425,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     __shared__ float hs[SB];
     __shared__ float uinv[SB];
     __shared__ float tabs[16 * 32];
+    __shared__ float tinv[16 * 32];
     const int tid = threadIdx.x;
     // The block's U with its entries below the diagonal set to 0 (only the upper triangle of U
     // is read): the feedback of column j then runs unconditionally over every column.
@@ -441,8 +443,13 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
         uinv[tid] = (d > 0.0f) ? 1.0f / d : 0.0f;
     }
     const int64_t r0 = (int64_t)blockIdx.x * 16;
-    for (int e = tid; e < 16 * 32; e += 256)
-        tabs[e] = (r0 + e / 32 < rows) ? tab[(r0 + e / 32) * 32 + (e & 31)] : 1.0f;
+    // The rows' rung scales and their reciprocals (the same IEEE division the search would do
+    // per candidate, done once).
+    for (int e = tid; e < 16 * 32; e += 256) {
+        const float t = (r0 + e / 32 < rows) ? tab[(r0 + e / 32) * 32 + (e & 31)] : 1.0f;
+        tabs[e] = t;
+        tinv[e] = (t > 0.0f) ? 1.0f / t : 0.0f;
+    }
     __syncthreads();
     const int k = tid & 15;
     const int64_t r = r0 + (tid >> 4);
@@ -462,6 +469,7 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     cx.uinv = uinv;
     cx.hs = hs;
     cx.tb = &tabs[(tid >> 4) * 32];
+    cx.ti = &tinv[(tid >> 4) * 32];
     cx.lo = (MODE == 0) ? lost[r * 2] : 0.0f;  // only q4tp's nominal rung reads the ladder's lo / step
     cx.st = (MODE == 0) ? lost[r * 2 + 1] : 0.0f;
     cx.k = k;
