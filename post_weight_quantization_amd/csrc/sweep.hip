@@ -245,6 +245,8 @@ __device__ __forceinline__ float pair_err_q2(float w0, float w1, float h0, float
 #pragma clang fp contract(on)
 
 constexpr int SB = 128;          // columns per block (4 groups)
+constexpr int RPW = 32;          // rows per workgroup of the block kernel (16 lanes each)
+constexpr int BT = 16 * RPW;     // its threads
 constexpr int ULD = SB + 4;      // LDS row stride of the block's U
 
 struct BlockCtx {
@@ -405,14 +407,17 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
     if constexpr (g + 1 < G) block_group<G, g + 1, MODE>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
 }
 
-// One block of up to 4 groups for 16 rows per workgroup, 16 lanes per row.  Lane k of a row
+// One block of up to 4 groups for RPW rows per workgroup, 16 lanes per row.  RPW = 32 (512
+// threads) stages the block's U once for twice the rows of 16, and the 5120 rows of a down_proj
+// layer make 160 workgroups, which find room beside the bulk update's sooner than 320 do; 20,
+// 48 and 64 rows measured slower.  Lane k of a row
 // owns columns 2k and 2k+1 of every group in the block (8 values in registers).  For each group:
 // rung from the group's absmax and the 16-lane sums of the weighted error of each candidate;
 // then the group's 32 columns in order: the column's corrected value is broadcast from its
 // owner, every lane of the row computes the same code and residual, and each lane feeds the
 // residual into its own later columns of the block through row j of U (held in LDS).
 template <int G, int MODE>
-__global__ __launch_bounds__(256) void sweep_block_kernel(
+__global__ __launch_bounds__(BT) void sweep_block_kernel(
     const float* __restrict__ src, int64_t n, int64_t c0, const float* __restrict__ U,
     const float* __restrict__ hdiag, const uint8_t* __restrict__ dead,
     const float* __restrict__ tab, const float* __restrict__ lost, int64_t rows,
@@ -424,12 +429,12 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
     __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
     __shared__ float hs[SB];
     __shared__ float uinv[SB];
-    __shared__ float tabs[16 * 32];
-    __shared__ float tinv[16 * 32];
+    __shared__ float tabs[RPW * 32];
+    __shared__ float tinv[RPW * 32];
     const int tid = threadIdx.x;
     // The block's U with its entries below the diagonal set to 0 (only the upper triangle of U
     // is read): the feedback of column j then runs unconditionally over every column.
-    for (int e = tid; e < NC * (NC / 4); e += 256) {
+    for (int e = tid; e < NC * (NC / 4); e += BT) {
         const int j = e / (NC / 4), t4 = (e % (NC / 4)) * 4;
         f32x4 v = *reinterpret_cast<const f32x4*>(U + (c0 + j) * n + c0 + t4);
 #pragma unroll
@@ -442,10 +447,10 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(
         const float d = U[(c0 + tid) * n + c0 + tid];
         uinv[tid] = (d > 0.0f) ? 1.0f / d : 0.0f;
     }
-    const int64_t r0 = (int64_t)blockIdx.x * 16;
+    const int64_t r0 = (int64_t)blockIdx.x * RPW;
     // The rows' rung scales and their reciprocals (the same IEEE division the search would do
     // per candidate, done once).
-    for (int e = tid; e < 16 * 32; e += 256) {
+    for (int e = tid; e < RPW * 32; e += BT) {
         const float t = (r0 + e / 32 < rows) ? tab[(r0 + e / 32) * 32 + (e & 31)] : 1.0f;
         tabs[e] = t;
         tinv[e] = (t > 0.0f) ? 1.0f / t : 0.0f;
@@ -570,7 +575,7 @@ static void launch_block(unsigned nwg, hipStream_t st, const float* src, int64_t
                          const float* U, const float* hdiag, const uint8_t* dead, const float* tab,
                          const float* lost, int64_t rows, uint8_t* nib, uint8_t* rung, float* scale,
                          float* E, int64_t ldE, const float* sp, uint8_t* codes) {
-    sweep_block_kernel<G, MODE><<<nwg, 256, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows,
+    sweep_block_kernel<G, MODE><<<nwg, BT, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows,
                                                    nib, rung, scale, E, ldE, sp, codes);
 }
 
@@ -599,7 +604,7 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
     const int64_t rows = c.rows, n = c.n;
     const float* U = c.U;
     float* Wc = c.Wc;
-    const unsigned nwg = (unsigned)((rows + 15) / 16);
+    const unsigned nwg = (unsigned)((rows + RPW - 1) / RPW);
 
     Helper hp{};
     if (helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
