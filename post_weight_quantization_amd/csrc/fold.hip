@@ -97,8 +97,11 @@ __global__ void fold_scale_kernel(const float* __restrict__ hdiag, const uint8_t
 
 // A[i][j] (i >= j) = reversed, damped, equilibrated H read from its upper triangle; the
 // padding block is the identity; entries above the diagonal inside diagonal 64 x 64 tiles are 0.
-// One workgroup per lower 64 x 64 tile (the grid enumerates only those); a row of the tile is
-// one wave, so both the read of H (a row of H, in reverse) and the write of A coalesce.
+// One workgroup per lower 64 x 64 tile (the grid enumerates only those).  VEC (n and ldh
+// multiples of 4, H 16-byte aligned): each thread takes 4 adjacent columns of 4 rows, as float4
+// reads of H (4 adjacent columns of H in reverse order) and float4 writes of A; otherwise a
+// row of the tile is one wave of single floats.  Both coalesce.
+template <bool VEC>
 __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict__ H, int64_t ldh,
                                                          const float* __restrict__ dinv,
                                                          const uint8_t* __restrict__ dead,
@@ -111,31 +114,75 @@ __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict
     while (ti * (ti + 1) / 2 > b) --ti;
     const int tj = b - ti * (ti + 1) / 2;
     const double damp = lam * st->base;
-    const int64_t j = (int64_t)tj * 64 + (threadIdx.x & 63);
-    const int64_t bc = n - 1 - j;  // column of H (valid when j < n)
-    const bool jin = j < n;
-    const bool dead_b = jin && dead[bc];
-    const float db = jin ? dinv[bc] : 0.0f;
-#pragma unroll 4
-    for (int q = 0; q < 16; ++q) {
-        const int64_t i = (int64_t)ti * 64 + (threadIdx.x >> 6) + 4 * q;
-        float v;
-        if (j > i) {
-            v = 0.0f;
-        } else if (i >= n || !jin) {
-            v = (i == j) ? 1.0f : 0.0f;
-        } else {
-            const int64_t a = n - 1 - i;  // a <= bc: upper triangle of H
-            if (dead[a] || dead_b) {
-                v = (a == bc) ? 1.0f : 0.0f;
-            } else if (a == bc) {
-                const double di = (double)db;
-                v = (float)(((double)H[a * ldh + a] + damp) * di * di);
-            } else {
-                v = H[a * ldh + bc] * dinv[a] * db;
-            }
+    if constexpr (VEC) {
+        const int64_t j4 = (int64_t)tj * 64 + (threadIdx.x & 15) * 4;
+        const bool jin = j4 < n;  // n % 4 == 0: the 4 columns are all in or all out
+        const int64_t bc4 = n - 4 - j4;  // H columns bc4 .. bc4 + 3 are A's columns j4 + 3 .. j4
+        f32x4 db = {0.f, 0.f, 0.f, 0.f};
+        bool deadb[4] = {false, false, false, false};
+        if (jin) {
+            db = *reinterpret_cast<const f32x4*>(dinv + bc4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) deadb[u] = dead[bc4 + u] != 0;
         }
-        A[i * np + j] = v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t i = (int64_t)ti * 64 + (threadIdx.x >> 4) + 16 * q;
+            f32x4 v;
+            if (i >= n || !jin) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = (i == j4 + u) ? 1.0f : 0.0f;
+            } else {
+                const int64_t a = n - 1 - i;
+                const bool dead_a = dead[a] != 0;
+                const float da = dinv[a];
+                const f32x4 h4 = *reinterpret_cast<const f32x4*>(H + a * ldh + bc4);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t j = j4 + u, bcol = n - 1 - j;  // H column of A's column j
+                    float x;
+                    if (j > i) {
+                        x = 0.0f;
+                    } else if (dead_a || deadb[3 - u]) {
+                        x = (a == bcol) ? 1.0f : 0.0f;
+                    } else if (a == bcol) {
+                        const double di = (double)da;
+                        x = (float)(((double)h4[3 - u] + damp) * di * di);
+                    } else {
+                        x = h4[3 - u] * da * db[3 - u];
+                    }
+                    v[u] = x;
+                }
+            }
+            *reinterpret_cast<f32x4*>(A + i * np + j4) = v;
+        }
+    } else {
+        const int64_t j = (int64_t)tj * 64 + (threadIdx.x & 63);
+        const int64_t bc = n - 1 - j;  // column of H (valid when j < n)
+        const bool jin = j < n;
+        const bool dead_b = jin && dead[bc];
+        const float db = jin ? dinv[bc] : 0.0f;
+#pragma unroll 4
+        for (int q = 0; q < 16; ++q) {
+            const int64_t i = (int64_t)ti * 64 + (threadIdx.x >> 6) + 4 * q;
+            float v;
+            if (j > i) {
+                v = 0.0f;
+            } else if (i >= n || !jin) {
+                v = (i == j) ? 1.0f : 0.0f;
+            } else {
+                const int64_t a = n - 1 - i;  // a <= bc: upper triangle of H
+                if (dead[a] || dead_b) {
+                    v = (a == bc) ? 1.0f : 0.0f;
+                } else if (a == bc) {
+                    const double di = (double)db;
+                    v = (float)(((double)H[a * ldh + a] + damp) * di * di);
+                } else {
+                    v = H[a * ldh + bc] * dinv[a] * db;
+                }
+            }
+            A[i * np + j] = v;
+        }
     }
 }
 
@@ -358,19 +405,42 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
 }
 
 // U[j][c] = X[n-1-j][n-1-c] * dinv[c] for c >= j, 0 below the diagonal.  One workgroup per
-// 64 x 64 tile of U, a row of the tile per wave; tiles wholly below the diagonal only store 0.
+// 64 x 64 tile of U; tiles wholly below the diagonal only store 0.  VEC (n a multiple of 4, U
+// 16-byte aligned): each thread takes 4 adjacent columns of 4 rows, float4 reads of X (4
+// adjacent columns in reverse order) and float4 writes of U; otherwise a row of the tile per
+// wave, single floats.
+template <bool VEC>
 __global__ __launch_bounds__(256) void fold_make_u_kernel(const float* __restrict__ X,
                                                           const float* __restrict__ dinv,
                                                           float* __restrict__ U, int64_t n,
                                                           int64_t np) {
-    const int64_t c = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
     const bool below = blockIdx.x < blockIdx.y;
-    const float dc = (!below && c < n) ? dinv[c] : 0.0f;
+    if constexpr (VEC) {
+        const int64_t c4 = (int64_t)blockIdx.x * 64 + (threadIdx.x & 15) * 4;
+        if (c4 >= n) return;  // n % 4 == 0: the 4 columns are all in or all out
+        const f32x4 d4 = below ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(dinv + c4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t j = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 4) + 16 * q;
+            if (j >= n) continue;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (!below && c4 + 3 >= j) {
+                // X[n-1-j][n-4-c4 .. n-1-c4] holds the columns c4 + 3 .. c4 of U's row j.
+                const f32x4 x4 = *reinterpret_cast<const f32x4*>(X + (n - 1 - j) * np + (n - 4 - c4));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = (c4 + u >= j) ? x4[3 - u] * d4[u] : 0.0f;
+            }
+            *reinterpret_cast<f32x4*>(U + j * n + c4) = v;
+        }
+    } else {
+        const int64_t c = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+        const float dc = (!below && c < n) ? dinv[c] : 0.0f;
 #pragma unroll 4
-    for (int q = 0; q < 16; ++q) {
-        const int64_t j = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 6) + 4 * q;
-        if (j >= n || c >= n) continue;
-        U[j * n + c] = (!below && c >= j) ? X[(n - 1 - j) * np + (n - 1 - c)] * dc : 0.0f;
+        for (int q = 0; q < 16; ++q) {
+            const int64_t j = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 6) + 4 * q;
+            if (j >= n || c >= n) continue;
+            U[j * n + c] = (!below && c >= j) ? X[(n - 1 - j) * np + (n - 1 - c)] * dc : 0.0f;
+        }
     }
 }
 
@@ -498,9 +568,14 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                         (fold_scale_kernel<<<(unsigned)((np + 255) / 256), 256, 0, st>>>(
                             hdiag, dead, state, lam, n, np, dinv)),
                         rd(hdiag, n, 1, n), rd(dead, n, 1, n, 1), st_rw, wr(dinv, np, 1, np));
+            const bool build_vec = n % 4 == 0 && ldh % 4 == 0 && ((uintptr_t)H & 15u) == 0;
+            const unsigned build_grid = (unsigned)((np / 64) * (np / 64 + 1) / 2);
             GPTQ_LAUNCH(st, "fold_build",
-                        (fold_build_kernel<<<(unsigned)((np / 64) * (np / 64 + 1) / 2), 256, 0, st>>>(
-                            H, ldh, dinv, dead, state, lam, A, n, np)),
+                        (build_vec
+                             ? fold_build_kernel<true><<<build_grid, 256, 0, st>>>(
+                                   H, ldh, dinv, dead, state, lam, A, n, np)
+                             : fold_build_kernel<false><<<build_grid, 256, 0, st>>>(
+                                   H, ldh, dinv, dead, state, lam, A, n, np)),
                         rd(H, ldh, n, n), rd(dinv, np, 1, np), rd(dead, n, 1, n, 1),
                         rd(state, 1, 1, sizeof(FoldState), 1), wr(A, np, np, np));
         }
@@ -697,7 +772,10 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
     } else {
         ProfScope ps(FAM_FOLD_MAKEU, st, 0.0, 4.0 * (double)n * n);
         const dim3 g64((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64));
-        GPTQ_LAUNCH(st, "fold_make_u", (fold_make_u_kernel<<<g64, 256, 0, st>>>(X, dinv, U, n, np)),
+        const bool vec = n % 4 == 0 && ((uintptr_t)U & 15u) == 0;
+        GPTQ_LAUNCH(st, "fold_make_u",
+                    (vec ? fold_make_u_kernel<true><<<g64, 256, 0, st>>>(X, dinv, U, n, np)
+                         : fold_make_u_kernel<false><<<g64, 256, 0, st>>>(X, dinv, U, n, np)),
                     rd(X, np, np, np), rd(dinv, np, 1, np), wr(U, n, n, n));
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;

@@ -52,6 +52,19 @@ def test_ragged_shapes(gpu, n, rows):
     assert_sweep_bar(st)
 
 
+@pytest.mark.parametrize("n", [150, 301, 517])
+def test_fold_n_not_multiple_of_4(gpu, n):
+    """The fold for any n (the sweep needs whole 32-column groups): n that is not a multiple of
+    4 takes the single-float build and make-U paths, and pads to the 128 block."""
+    say("fold odd n", n)
+    rng = np.random.default_rng(n)
+    X = rng.standard_normal((n, n + 9)) * np.exp(0.5 * rng.standard_normal(n))[:, None]
+    H = (X @ X.T).astype(np.float32)
+    H[n // 3, :] = 0.0
+    H[:, n // 3] = 0.0
+    check_fold(gpu, _dev(H), 0.01, H_np=H)
+
+
 @pytest.mark.parametrize("n,rows", [(1184, 300), (2080, 77)])
 def test_ragged_multi_panel(gpu, n, rows):
     """Several fold panels and sweep panels with ragged ends: n = 1184 pads to 1280 (outer
