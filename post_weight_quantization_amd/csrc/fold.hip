@@ -54,6 +54,9 @@ __global__ __launch_bounds__(1024) void fold_prep_kernel(const float* __restrict
     const int t = threadIdx.x;
     double s = 0.0;
     int cnt = 0;
+    // Unrolled so that several of the strided diagonal loads are in flight at once (the sums
+    // keep their order).
+#pragma unroll 8
     for (int64_t i = t; i < n; i += 1024) {
         const float d = H[i * ldh + i];
         const bool dd = !(d > 0.0f);
