@@ -6,7 +6,8 @@
 // Hessian; dead channels in the original order).
 //
 //   act_rank_kernel    the rank of every channel under that order, by counting (n^2 compares,
-//                      keys staged through LDS); perm[rank[i]] = i, dead[i] = !(H_ii > 0);
+//                      keys staged through LDS, four threads per channel); perm[rank[i]] = i,
+//                      dead[i] = !(H_ii > 0);
 //   act_permute_kernel Hp[a][b] = H[min(pa, pb)][max(pa, pb)] (H read through its upper
 //                      triangle): each upper 32 x 32 tile is gathered once and written twice
 //                      (in place and transposed), so the full symmetric matrix is written.
@@ -23,15 +24,18 @@ __device__ __forceinline__ int32_t total_key(float x) {
     return b >= 0 ? b : (b ^ 0x7fffffff);
 }
 
+// Four threads per channel i (64 channels per workgroup), each counting the channels j before
+// i in one quarter of every 1024-key chunk; the four counts are summed with lane shuffles.
 __global__ __launch_bounds__(256) void act_rank_kernel(const float* __restrict__ H, int64_t ldh,
                                                        int64_t n, int32_t* __restrict__ perm,
                                                        uint8_t* __restrict__ dead) {
     __shared__ int32_t keys[1024];
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int part = threadIdx.x & 3;
+    const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
     const bool live = i < n;
     const float hi = live ? H[i * ldh + i] : 0.0f;
     const int32_t ki = total_key(hi);
-    int64_t rank = 0;
+    int rank = 0;
     for (int64_t j0 = 0; j0 < n; j0 += 1024) {
         __syncthreads();
         for (int t = threadIdx.x; t < 1024; t += 256) {
@@ -39,14 +43,16 @@ __global__ __launch_bounds__(256) void act_rank_kernel(const float* __restrict__
             keys[t] = (j < n) ? total_key(H[j * ldh + j]) : INT32_MIN;
         }
         __syncthreads();
-        const int64_t m = (n - j0 < 1024) ? n - j0 : 1024;
-        for (int64_t t = 0; t < m; ++t) {
+        const int m = (n - j0 < 1024) ? (int)(n - j0) : 1024;
+        for (int t = part; t < m; t += 4) {
             const int32_t kj = keys[t];
             // j before i: a larger key, or the same key at a smaller index.
             rank += (kj > ki || (kj == ki && j0 + t < i)) ? 1 : 0;
         }
     }
-    if (live) {
+    rank += __shfl_xor(rank, 1);
+    rank += __shfl_xor(rank, 2);
+    if (live && part == 0) {
         perm[rank] = (int32_t)i;
         dead[i] = (hi > 0.0f) ? 0 : 1;
     }
@@ -100,7 +106,7 @@ extern "C" int gptq_act_order_perm(const float* H, int64_t n, int64_t ldh, int32
     check_buffer(dead, (size_t)n, "dead");
     hipStream_t st = (hipStream_t)stream;
     GPTQ_LAUNCH(st, "act_rank",
-                (act_rank_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(H, ldh, n, perm, dead)),
+                (act_rank_kernel<<<(unsigned)((n + 63) / 64), 256, 0, st>>>(H, ldh, n, perm, dead)),
                 rd(H, ldh + 1, n, 1), wr(perm, n, 1, n), wr(dead, n, 1, n, 1));
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     return check.finish();
