@@ -81,9 +81,10 @@ size_t gptq_fold_workspace_size(int64_t n);
  *
  * Steps on the device: diagonal, dead mask and mean (f64) -> per attempt: D_i^-1 =
  * (H_ii + damp)^-1/2 (dead: (1 + damp)^-1/2), the reversed equilibrated matrix
- * A = P D^-1 H_d D^-1 P, blocked Cholesky A = L L^T and, one 512-column panel behind on a
- * helper stream, the blocked right-looking inverse X = L^-1 -> U = P X P D^-1.  The host reads the pivot flag once per attempt
- * (one stream synchronisation); U is still being written when the call returns.
+ * A = P D^-1 H_d D^-1 P, blocked Cholesky A = L L^T and, pipelined on the helper streams one
+ * 512-column panel behind, the blocked right-looking inverse X = L^-1 -> U = P X P D^-1.  The
+ * host reads the pivot flag once per attempt (one stream synchronisation); U is still being
+ * written when the call returns.
  */
 int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, float* U, float* hdiag,
               uint8_t* dead, void* workspace, size_t workspace_bytes, void* stream,
