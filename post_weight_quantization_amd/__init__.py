@@ -122,6 +122,18 @@ def _dev(t: torch.Tensor, dtype, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dev_rows(t: torch.Tensor, dtype, name):
+    """A 2-D device tensor whose rows may be padded: unit column stride, row stride >= width
+    (the row stride is passed as the leading dimension)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+    if t.dim() != 2 or (t.shape[0] > 1 and t.stride(1) != 1) or t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -151,7 +163,7 @@ def gptq_fold(H: torch.Tensor, lam: float, workspace: torch.Tensor | None = None
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     rep = FoldReport()
-    st = lib.gptq_fold(_dev(H, torch.float32, "H"), n, H.stride(0), float(lam),
+    st = lib.gptq_fold(_dev_rows(H, torch.float32, "H"), n, H.stride(0), float(lam),
                        _dev(U, torch.float32, "U"), _dev(hdiag, torch.float32, "hdiag"),
                        _dev(dead, torch.uint8, "dead"), _dev(workspace, torch.uint8, "workspace"),
                        workspace.numel(), _stream(stream), ctypes.byref(rep))
@@ -216,8 +228,8 @@ def gptq_gram_add(H: torch.Tensor, X: torch.Tensor, stream=None):
     n = H.shape[0]
     if X.dim() != 2 or X.shape[1] != n:
         raise ValueError("X must be [t, n] with n = H.shape[0]")
-    st = lib.gptq_gram_add(_dev(H, torch.float32, "H"), n, H.stride(0),
-                           _dev(X, torch.float32, "X"), X.shape[0], X.stride(0), _stream(stream))
+    st = lib.gptq_gram_add(_dev_rows(H, torch.float32, "H"), n, H.stride(0),
+                           _dev_rows(X, torch.float32, "X"), X.shape[0], X.stride(0), _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_gram_add")
     return H

@@ -80,6 +80,26 @@ def test_gram_workload_and_repeatability(gpu):
 
 
 @pytest.mark.gpu
+def test_gram_padded_leading_dimensions(gpu):
+    """H and X with padded rows (ldh = n + 12, ldx = n + 8; the padding is NaN and neither read
+    nor written): the upper triangle matches the contiguous call bitwise."""
+    n, t = 200, 300
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    X = torch.randn(t, n, generator=g, device=dev)
+    H0, _ = run(gpu, n, t, X=X)
+    Xp = torch.full((t, n + 8), float("nan"), device=dev)
+    Xp[:, :n] = X
+    Hp = torch.full((n, n + 12), float("nan"), device=dev)
+    Hp[:, :n] = torch.triu(torch.zeros(n, n, device=dev))
+    gpu.gptq_gram_add(Hp[:, :n], Xp[:, :n])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.triu(Hp[:, :n]), torch.triu(H0))
+    assert torch.isnan(Hp[:, n:]).all()
+
+
+@pytest.mark.gpu
 def test_gram_zero_tokens_and_invalid(gpu):
     import ctypes
     H = torch.ones(64, 64, device="cuda:0")

@@ -65,6 +65,26 @@ def test_fold_n_not_multiple_of_4(gpu, n):
     check_fold(gpu, _dev(H), 0.01, H_np=H)
 
 
+@pytest.mark.parametrize("pad", [3, 4])
+def test_fold_padded_leading_dimension(gpu, pad):
+    """The fold of a row-padded H (ldh = n + pad, the padding NaN and never read) is bitwise the
+    fold of the contiguous H, on the float4 build path (ldh % 4 == 0) and the single-float one."""
+    n, lam = 300, 0.01
+    say("fold ldh", n + pad)
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((n, n + 40)) * np.exp(0.7 * rng.standard_normal(n))[:, None]
+    H = (X @ X.T).astype(np.float32)
+    U0, hd0, dead0, rep0 = gpu.gptq_fold(_dev(H), lam)
+    Hp = torch.full((n, n + pad), float("nan"), dtype=torch.float32, device="cuda")
+    Hp[:, :n] = _dev(H)
+    view = Hp[:, :n]
+    assert view.stride(0) == n + pad
+    U, hd, dead, rep = gpu.gptq_fold(view, lam)
+    torch.cuda.synchronize()
+    assert rep["status"] == gpu.GPTQ_OK and rep0["status"] == gpu.GPTQ_OK
+    assert torch.equal(U, U0) and torch.equal(hd, hd0) and torch.equal(dead, dead0)
+
+
 @pytest.mark.parametrize("n,rows", [(1184, 300), (2080, 77)])
 def test_ragged_multi_panel(gpu, n, rows):
     """Several fold panels and sweep panels with ragged ends: n = 1184 pads to 1280 (outer
