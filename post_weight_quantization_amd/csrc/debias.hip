@@ -182,7 +182,7 @@ extern "C" int gptq_debias(const float* W, const float* H, int64_t ldh, const ui
         const GemmBatch b = gemm_batch(
             gemm_full(W, n, Hs, n, nullptr, Y, n, (int)rows, (int)n, (int)n, 1.0f, 0), nullptr);
         ProfScope ps(FAM_DEBIAS, st, 2.0 * (double)rows * n * n, 0.0);
-        const int rc = launch_gemm<8, true, false, true>("debias_gemm", st, b, nullptr);
+        const int rc = launch_gemm_fit<8, true, false>("debias_gemm", st, b, nullptr);
         if (rc != GPTQ_OK) return rc;
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;

@@ -639,4 +639,18 @@ inline int launch_gemm(const char* name, hipStream_t s, const GemmBatch& b0, con
     return GPTQ_OK;
 }
 
+// For sites whose shapes may be ragged: a batch whose problems all cover whole tiles of the
+// site (M and N multiples of its tile) launches the kernel without bounds checks, which is
+// the same computation with fewer instructions per load and store; any other batch launches
+// the checked kernel.
+template <int TAG, bool TB0, bool TB1>
+inline int launch_gemm_fit(const char* name, hipStream_t s, const GemmBatch& b, const unsigned* flag) {
+    constexpr int TILE = GemmCfg<TAG>::tile, TILE_N = GemmCfg<TAG>::tile_n;
+    bool whole = true;
+    for (int q = 0; q < b.nprob && q < 2; ++q)
+        whole = whole && b.p[q].M % TILE == 0 && b.p[q].N % TILE_N == 0;
+    return whole ? launch_gemm<TAG, TB0, TB1, false>(name, s, b, flag)
+                 : launch_gemm<TAG, TB0, TB1, true>(name, s, b, flag);
+}
+
 }  // namespace gptq

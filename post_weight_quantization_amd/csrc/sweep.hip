@@ -679,7 +679,7 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
                     nullptr);
                 ProfScope ps(FAM_SWEEP_NEXT, st, 2.0 * nc * rows * rest_in,
                              8.0 * rows * rest_in + 4.0 * nc * rest_in + 4.0 * rows * nc);
-                SWEEP_OK((launch_gemm<6, false, false, true>("sweep_in_panel", st, b, nullptr)));
+                SWEEP_OK((launch_gemm_fit<6, false, false>("sweep_in_panel", st, b, nullptr)));
             }
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
@@ -702,7 +702,7 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
                 nullptr);
             ProfScope ps(FAM_SWEEP_TRAIL, ts, 2.0 * w * rows * rest2,
                          8.0 * rows * rest2 + 4.0 * w * rest2 + 4.0 * rows * w);
-            SWEEP_OK((launch_gemm<2, false, false, true>("sweep_bulk", ts, b, nullptr)));
+            SWEEP_OK((launch_gemm_fit<2, false, false>("sweep_bulk", ts, b, nullptr)));
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
         // Look-ahead: the next panel's columns, after the previous panel's bulk update (which
@@ -716,7 +716,7 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
                 nullptr);
             ProfScope ps(FAM_SWEEP_NEXT, st, 2.0 * w * rows * nw,
                          8.0 * rows * nw + 4.0 * w * nw + 4.0 * rows * w);
-            SWEEP_OK((launch_gemm<7, false, false, true>("sweep_look_ahead", st, b, nullptr)));
+            SWEEP_OK((launch_gemm_fit<7, false, false>("sweep_look_ahead", st, b, nullptr)));
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
         if (rest2 > 0) {
