@@ -265,24 +265,47 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
         __syncthreads();
         buf = nb;
     }
+    // C addresses: the tile's corner as one 64-bit offset, each element as a 32-bit offset from
+    // it (the host bounds ldc, so 128 rows of C fit), so no element needs a 64-bit multiply.
+    const int64_t corner = (int64_t)i0 * P.ldc + j0;
+    const int ldc = (int)P.ldc;
     float cv[2][2][16];
     if (use_c) {
+        const float* cin = P.Cin + corner;
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    const int lj = wn * 64 + bj * 32 + l32;
+                    int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    int lj = wn * 64 + bj * 32 + l32;
                     // Unconditional load (clamped inside the matrix); masked values are
                     // never stored.
-                    const int i = CHK ? min(i0 + li, P.M - 1) : i0 + li;
-                    const int j = CHK ? min(j0 + lj, P.N - 1) : j0 + lj;
-                    cv[bi][bj][v] = P.Cin[(int64_t)i * P.ldc + j];
+                    if (CHK) {
+                        li = min(li, P.M - 1 - i0);
+                        lj = min(lj, P.N - 1 - j0);
+                    }
+                    cv[bi][bj][v] = cin[li * ldc + lj];
                 }
     }
     chunk_mfma<TB>(As + buf * LDS_TILE, Bs + buf * LDS_TILE, wm, wn, l32, h, acc);
+    float* cout = P.Cout + corner;
+    if (!CHK && !diag_tile) {
+        // Every element of the tile is stored (the common case): no per-element conditions.
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj) {
+                const int o = (wm * 64 + bi * 32 + 4 * h) * ldc + wn * 64 + bj * 32 + l32;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float base = use_c ? cv[bi][bj][v] : 0.0f;
+                    cout[o + (8 * (v >> 2) + (v & 3)) * ldc] = base + P.alpha * acc[bi][bj][v];
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -291,10 +314,9 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
             for (int v = 0; v < 16; ++v) {
                 const int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
                 const int lj = wn * 64 + bj * 32 + l32;
-                const int i = i0 + li, j = j0 + lj;
-                if ((!CHK || (i < P.M && j < P.N)) && (!diag_tile || li >= lj)) {
+                if ((!CHK || (i0 + li < P.M && j0 + lj < P.N)) && (!diag_tile || li >= lj)) {
                     const float base = use_c ? cv[bi][bj][v] : 0.0f;
-                    P.Cout[(int64_t)i * P.ldc + j] = base + P.alpha * acc[bi][bj][v];
+                    cout[li * ldc + lj] = base + P.alpha * acc[bi][bj][v];
                 }
             }
 }
@@ -443,30 +465,48 @@ __device__ __forceinline__ void gemm_tile_small(const GemmProblem& P, int tm, in
         __syncthreads();
         buf = nb;
     }
+    // C addresses as in the 128 tile: a 64-bit corner and 32-bit element offsets.
+    const int64_t corner = (int64_t)i0 * P.ldc + j0;
+    const int ldc = (int)P.ldc;
     float cv[NA][16];
     if (use_c) {
+        const float* cin = P.Cin + corner;
 #pragma unroll
         for (int bj = 0; bj < NA; ++bj)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                const int lj = wn * (TN / 2) + bj * 32 + l32;
-                const int i = CHK ? min(i0 + li, P.M - 1) : i0 + li;
-                const int j = CHK ? min(j0 + lj, P.N - 1) : j0 + lj;
-                cv[bj][v] = P.Cin[(int64_t)i * P.ldc + j];
+                int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                int lj = wn * (TN / 2) + bj * 32 + l32;
+                if (CHK) {
+                    li = min(li, P.M - 1 - i0);
+                    lj = min(lj, P.N - 1 - j0);
+                }
+                cv[bj][v] = cin[li * ldc + lj];
             }
     }
     chunk_mfma_small<TB, TN>(As + buf * LDS_TILE64, Bs + buf * BT, wm, wn, l32, h, acc);
+    float* cout = P.Cout + corner;
+    if (!CHK && !diag_tile) {
+#pragma unroll
+        for (int bj = 0; bj < NA; ++bj) {
+            const int o = (wm * 32 + 4 * h) * ldc + wn * (TN / 2) + bj * 32 + l32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float base = use_c ? cv[bj][v] : 0.0f;
+                cout[o + (8 * (v >> 2) + (v & 3)) * ldc] = base + P.alpha * acc[bj][v];
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int bj = 0; bj < NA; ++bj)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
             const int lj = wn * (TN / 2) + bj * 32 + l32;
-            const int i = i0 + li, j = j0 + lj;
-            if ((!CHK || (i < P.M && j < P.N)) && (!diag_tile || li >= lj)) {
+            if ((!CHK || (i0 + li < P.M && j0 + lj < P.N)) && (!diag_tile || li >= lj)) {
                 const float base = use_c ? cv[bj][v] : 0.0f;
-                P.Cout[(int64_t)i * P.ldc + j] = base + P.alpha * acc[bj][v];
+                cout[li * ldc + lj] = base + P.alpha * acc[bj][v];
             }
         }
 }
@@ -595,7 +635,7 @@ inline GemmBatch gemm_batch(const GemmProblem& a, const GemmProblem* b) {
 // Memory one batch touches, as spans for the schedule checker: per problem A, B, C_in (when
 // read) and C_out, over whole tiles unless the launch checks bounds.  Returns the span count,
 // or -1 when a problem breaks the kernel's shape rules (K a multiple of 32; with bounds checks
-// and the "N" layout, N a multiple of 4).
+// and the "N" layout, N a multiple of 4; 0 < ldc <= 2^23).
 template <bool TB0, bool TB1, bool CHK>
 inline int gemm_spans(const GemmBatch& b, Span* out, int tile, int tile_n) {
     int n = 0;
@@ -603,7 +643,9 @@ inline int gemm_spans(const GemmBatch& b, Span* out, int tile, int tile_n) {
         const GemmProblem& P = b.p[q];
         if (P.ntiles <= 0) continue;
         const bool TB = (q == 0) ? TB0 : TB1;
-        if (P.K <= 0 || P.K % GT_K != 0 || (CHK && !TB && P.N % 4 != 0) || P.tiles_n <= 0)
+        // ldc is bounded so that an element's offset from its tile's corner fits in 32 bits.
+        if (P.K <= 0 || P.K % GT_K != 0 || (CHK && !TB && P.N % 4 != 0) || P.tiles_n <= 0 ||
+            P.ldc <= 0 || P.ldc > ((int64_t)1 << 23))
             return -1;
         const int64_t tm = P.lower ? P.tiles_n : P.ntiles / P.tiles_n;
         const int64_t rows = CHK ? P.M : tm * tile;
