@@ -275,19 +275,24 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj)
+            for (int bj = 0; bj < 2; ++bj) {
+                const float* cp = cin + (wm * 64 + bi * 32 + 4 * h) * ldc + wn * 64 + bj * 32 + l32;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    int lj = wn * 64 + bj * 32 + l32;
-                    // Unconditional load (clamped inside the matrix); masked values are
-                    // never stored.
                     if (CHK) {
-                        li = min(li, P.M - 1 - i0);
-                        lj = min(lj, P.N - 1 - j0);
+                        // Unconditional load, clamped inside the matrix; masked values are
+                        // never stored.
+                        const int li = min(wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3),
+                                           P.M - 1 - i0);
+                        const int lj = min(wn * 64 + bj * 32 + l32, P.N - 1 - j0);
+                        cv[bi][bj][v] = cin[li * ldc + lj];
+                    } else {
+                        // Rows 0-3, 8-11, 16-19, 24-27 (+ 4h) of the block, by pointer steps.
+                        cv[bi][bj][v] = *cp;
+                        cp += ((v & 3) == 3) ? 5 * ldc : ldc;
                     }
-                    cv[bi][bj][v] = cin[li * ldc + lj];
                 }
+            }
     }
     chunk_mfma<TB>(As + buf * LDS_TILE, Bs + buf * LDS_TILE, wm, wn, l32, h, acc);
     float* cout = P.Cout + corner;
@@ -297,11 +302,13 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) {
-                const int o = (wm * 64 + bi * 32 + 4 * h) * ldc + wn * 64 + bj * 32 + l32;
+                // Walk the block's rows 0-3, 8-11, 16-19, 24-27 (+ 4h) with a pointer.
+                float* cp = cout + (wm * 64 + bi * 32 + 4 * h) * ldc + wn * 64 + bj * 32 + l32;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const float base = use_c ? cv[bi][bj][v] : 0.0f;
-                    cout[o + (8 * (v >> 2) + (v & 3)) * ldc] = base + P.alpha * acc[bi][bj][v];
+                    *cp = base + P.alpha * acc[bi][bj][v];
+                    cp += ((v & 3) == 3) ? 5 * ldc : ldc;
                 }
             }
         return;
@@ -309,16 +316,19 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < 2; ++bj) {
+            const int lj = wn * 64 + bj * 32 + l32;
+            float* cp = cout + (wm * 64 + bi * 32 + 4 * h) * ldc + lj;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                const int lj = wn * 64 + bj * 32 + l32;
                 if ((!CHK || (i0 + li < P.M && j0 + lj < P.N)) && (!diag_tile || li >= lj)) {
                     const float base = use_c ? cv[bi][bj][v] : 0.0f;
-                    cout[li * ldc + lj] = base + P.alpha * acc[bi][bj][v];
+                    *cp = base + P.alpha * acc[bi][bj][v];
                 }
+                cp += ((v & 3) == 3) ? 5 * ldc : ldc;
             }
+        }
 }
 
 // A 64 x 64 tile, for the small products on the serial chains: four times the workgroups of
@@ -472,43 +482,50 @@ __device__ __forceinline__ void gemm_tile_small(const GemmProblem& P, int tm, in
     if (use_c) {
         const float* cin = P.Cin + corner;
 #pragma unroll
-        for (int bj = 0; bj < NA; ++bj)
+        for (int bj = 0; bj < NA; ++bj) {
+            const float* cp = cin + (wm * 32 + 4 * h) * ldc + wn * (TN / 2) + bj * 32 + l32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                int lj = wn * (TN / 2) + bj * 32 + l32;
                 if (CHK) {
-                    li = min(li, P.M - 1 - i0);
-                    lj = min(lj, P.N - 1 - j0);
+                    const int li = min(wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), P.M - 1 - i0);
+                    const int lj = min(wn * (TN / 2) + bj * 32 + l32, P.N - 1 - j0);
+                    cv[bj][v] = cin[li * ldc + lj];
+                } else {
+                    cv[bj][v] = *cp;
+                    cp += ((v & 3) == 3) ? 5 * ldc : ldc;
                 }
-                cv[bj][v] = cin[li * ldc + lj];
             }
+        }
     }
     chunk_mfma_small<TB, TN>(As + buf * LDS_TILE64, Bs + buf * BT, wm, wn, l32, h, acc);
     float* cout = P.Cout + corner;
     if (!CHK && !diag_tile) {
 #pragma unroll
         for (int bj = 0; bj < NA; ++bj) {
-            const int o = (wm * 32 + 4 * h) * ldc + wn * (TN / 2) + bj * 32 + l32;
+            float* cp = cout + (wm * 32 + 4 * h) * ldc + wn * (TN / 2) + bj * 32 + l32;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float base = use_c ? cv[bj][v] : 0.0f;
-                cout[o + (8 * (v >> 2) + (v & 3)) * ldc] = base + P.alpha * acc[bj][v];
+                *cp = base + P.alpha * acc[bj][v];
+                cp += ((v & 3) == 3) ? 5 * ldc : ldc;
             }
         }
         return;
     }
 #pragma unroll
-    for (int bj = 0; bj < NA; ++bj)
+    for (int bj = 0; bj < NA; ++bj) {
+        const int lj = wn * (TN / 2) + bj * 32 + l32;
+        float* cp = cout + (wm * 32 + 4 * h) * ldc + lj;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int lj = wn * (TN / 2) + bj * 32 + l32;
             if ((!CHK || (i0 + li < P.M && j0 + lj < P.N)) && (!diag_tile || li >= lj)) {
                 const float base = use_c ? cv[bj][v] : 0.0f;
-                cout[li * ldc + lj] = base + P.alpha * acc[bj][v];
+                *cp = base + P.alpha * acc[bj][v];
             }
+            cp += ((v & 3) == 3) ? 5 * ldc : ldc;
         }
+    }
 }
 
 // LDS buffers, waves per SIMD and tile size for a launch site.  Every site uses two buffers.
