@@ -28,7 +28,9 @@ hipEvent_t take_event() {
         return e;
     }
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    // Timing only: no system-scope fence when the event is recorded (the cache writeback it
+    // would force lands between the kernels being timed).
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 }  // namespace

@@ -180,3 +180,43 @@ def test_repeat_runs_are_bitwise_identical(gpu):
         outs.append([t.cpu().numpy() for t in (U, nib, rung, scale, E)])
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+def test_profile_counts_the_fold_bulk_updates(gpu):
+    """The event timing behind the benchmark's roofline: at n = 2080 (padded to 2176, outer
+    panels of 512) the fold's bulk family is the Cholesky's trailing update beyond the next panel
+    (3 launches) and the inverse's update of the rows below each panel (4 launches), with the
+    flops of their definitions; every launch is timed."""
+    n, lam = 2080, 0.01
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((n, n + 64))
+    H = (X @ X.T).astype(np.float32)
+    Hd = _dev(H)
+    gpu.gptq_fold(Hd, lam)  # warm
+    torch.cuda.synchronize()
+    gpu.profile_collect()
+    gpu.profile_enable(["fold_update"])
+    try:
+        gpu.gptq_fold(Hd, lam)
+        torch.cuda.synchronize()
+    finally:
+        gpu.profile_enable([])
+    fu = gpu.profile_collect()["fold_update"]
+    np_, nb2 = 2176, 512
+    launches, flops = 0, 0.0
+    for kb in range(0, np_, nb2):
+        w = min(nb2, np_ - kb)
+        rest = np_ - kb - w
+        if rest <= 0:
+            continue
+        rest2 = rest - min(nb2, rest)
+        if rest2 > 0:
+            launches += 1
+            flops += w * rest2 * (rest2 + 1)  # lower triangle of a rank-w update
+        launches += 1
+        flops += 2.0 * w * rest * (kb + w)
+    assert fu["launches"] == launches == 7
+    assert fu["flops"] == pytest.approx(flops, rel=1e-12)
+    tflops = fu["flops"] / (fu["ms"] * 1e-3) / 1e12
+    say(f"fold_update at n={n}: {fu['launches']} launches, {fu['ms']:.3f} ms, {tflops:.1f} TFLOP/s")
+    assert 0.0 < tflops < 157.3
