@@ -690,23 +690,12 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
         const float* Up = U + P0 * n;  // the panel's rows of U
         const int64_t nw = std::min<int64_t>(SOB, rest);
         const int64_t rest2 = rest - nw;
-        // Bulk: every column beyond the next panel, on the helper stream once the panel's
-        // residuals are complete.
-        if (rest2 > 0) {
-            SWEEP_OK(ev_record(hp.ev_a, st));
-            SWEEP_OK(stream_wait(ts, hp.ev_a));
-            const int64_t j0 = P0 + w + nw;
-            const GemmBatch b = gemm_batch(
-                gemm_full(Ep, ldE, Up + j0, n, src + j0, Wc + j0, n, (int)rows, (int)rest2, (int)w,
-                          -1.0f, 1),
-                nullptr);
-            ProfScope ps(FAM_SWEEP_TRAIL, ts, 2.0 * w * rows * rest2,
-                         8.0 * rows * rest2 + 4.0 * w * rest2 + 4.0 * rows * w);
-            SWEEP_OK((launch_gemm_fit<2, false, false>("sweep_bulk", ts, b, nullptr)));
-            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-        }
-        // Look-ahead: the next panel's columns, after the previous panel's bulk update (which
-        // wrote them, and read the residual buffer the next panel's blocks overwrite).
+        // Look-ahead: the next panel's columns, on the chain, after the previous panel's bulk
+        // update (which wrote them, and read the residual buffer the next panel's blocks
+        // overwrite).  Bulk: every column beyond the next panel, on the helper stream.  Both
+        // become ready together; started together, the bulk update takes most of the GPU and
+        // the look-ahead, which the next panel's blocks wait for, crawls (about 140 us instead
+        // of 30).  So the look-ahead goes first and the bulk update waits for it.
         if (!first_bulk) SWEEP_OK(stream_wait(st, hp.ev_b));
         {
             const int64_t j0 = P0 + w;
@@ -720,6 +709,17 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
         if (rest2 > 0) {
+            SWEEP_OK(ev_record(hp.ev_a, st));
+            SWEEP_OK(stream_wait(ts, hp.ev_a));
+            const int64_t j0 = P0 + w + nw;
+            const GemmBatch b = gemm_batch(
+                gemm_full(Ep, ldE, Up + j0, n, src + j0, Wc + j0, n, (int)rows, (int)rest2, (int)w,
+                          -1.0f, 1),
+                nullptr);
+            ProfScope ps(FAM_SWEEP_TRAIL, ts, 2.0 * w * rows * rest2,
+                         8.0 * rows * rest2 + 4.0 * w * rest2 + 4.0 * rows * w);
+            SWEEP_OK((launch_gemm_fit<2, false, false>("sweep_bulk", ts, b, nullptr)));
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             SWEEP_OK(ev_record(hp.ev_b, ts));
             first_bulk = false;
         }
