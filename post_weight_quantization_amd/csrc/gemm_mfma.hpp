@@ -528,9 +528,11 @@ __device__ __forceinline__ void gemm_tile_small(const GemmProblem& P, int tm, in
     }
 }
 
-// LDS buffers, waves per SIMD and tile size for a launch site.  Every site uses two buffers.
-// With one buffer the bulk updates run about 30% faster per launch, three workgroups to a CU,
-// but the fold's serial chain then waits for free slots and the fold as a whole slows down.
+// LDS buffers, waves per SIMD and tile size for a launch site.  The two bulk updates (the fold's,
+// 0, and the sweep's, 2) stage K through one LDS buffer (a second barrier per chunk): their
+// registers already hold them to two workgroups per CU, and the LDS this frees lets the serial
+// chains' kernels run beside them instead of waiting for a workgroup to finish.  Every other
+// site uses two buffers.
 // The products on the serial chains that do not fill the GPU with 128 tiles take 64 x 64 tiles:
 // the fold's look-ahead (3) and update inside a panel (4), the inverse's diagonal-block steps
 // (5) and panel rows of X (9), the sweep's update inside a panel (6) and look-ahead (7).  The
@@ -551,6 +553,8 @@ template <> struct GemmCfg<6> { static constexpr int nbuf = 2; static constexpr 
 template <> struct GemmCfg<7> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
 template <> struct GemmCfg<9> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
 template <> struct GemmCfg<1> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 128; };
+template <> struct GemmCfg<0> { static constexpr int nbuf = 1; static constexpr int waves = 2; static constexpr int tile = 128; static constexpr int tile_n = 128; };
+template <> struct GemmCfg<2> { static constexpr int nbuf = 1; static constexpr int waves = 2; static constexpr int tile = 128; static constexpr int tile_n = 128; };
 
 // TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
 // of problems 0 and 1; CHK: bounds checks on M and N.
