@@ -283,6 +283,8 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
             best = 1;
             float best_e = INFINITY;
             const float h0 = cx.hs[32 * g + 2 * k], h1 = cx.hs[32 * g + 2 * k + 1];
+            // Unrolled so that the candidates' 16-lane reductions overlap.
+#pragma unroll 4
             for (int cand = 1; cand < 32; ++cand) {
                 const float s_c = cx.tb[cand];
                 if (!(s_c > 0.0f)) continue;
@@ -315,6 +317,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         const int lo_c = nominal >= 2 ? nominal - 2 : 0;
         const int hi_c = nominal + 1 < 31 ? nominal + 1 : 31;
         const float h0 = cx.hs[32 * g + 2 * k], h1 = cx.hs[32 * g + 2 * k + 1];
+#pragma unroll 4
         for (int cand = lo_c; cand <= hi_c; ++cand) {
             const float s_c = cx.tb[cand];
             if (s_c <= 0.0f) continue;
