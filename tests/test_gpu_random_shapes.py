@@ -1,0 +1,38 @@
+"""GPU parity on seeded random shapes: n a random multiple of 32 up to 1248, 1-399 rows, Hessians
+from 0.6-3 n tokens (so some are rank-deficient and take the retry path), random dead
+channels, heavy-tailed channel scales, λ in {0, 1e-4, 1e-2, 0.1}, and now and then an all-zero
+row of W.  Every case is held to the fold and sweep bars of the other parity tests."""
+import numpy as np
+import pytest
+import torch
+
+from parity import assert_sweep_bar, check_fold, check_sweep_isolated, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(rng):
+    n = int(rng.integers(1, 40)) * 32
+    rows = int(rng.integers(1, 400))
+    t = int(n * rng.uniform(0.6, 3.0)) + 1
+    X = rng.standard_normal((n, t)) * np.exp(rng.uniform(0, 1.5) * rng.standard_normal(n))[:, None]
+    nd = int(rng.integers(0, max(1, n // 20)))
+    if nd:
+        X[rng.choice(n, size=nd, replace=False), :] = 0.0
+    H = (X @ X.T).astype(np.float32)
+    lam = float(rng.choice([0.0, 1e-4, 1e-2, 0.1]))
+    W = (rng.standard_normal((rows, n)) * rng.uniform(0.005, 0.05)).astype(np.float32)
+    if rng.random() < 0.2:
+        W[rng.integers(0, rows), :] = 0.0
+    return H, W, lam, t, nd
+
+
+@pytest.mark.parametrize("seed", [101, 202, 303])
+def test_random_shapes(gpu, seed):
+    rng = np.random.default_rng(seed)
+    for i in range(12):
+        H, W, lam, t, nd = _case(rng)
+        say(f"seed {seed} case {i}: n={H.shape[0]} rows={W.shape[0]} t={t} dead={nd} lam={lam}")
+        (U, hdiag, dead, rep), orc, err = check_fold(gpu, torch.as_tensor(H).cuda(), lam, H_np=H)
+        st, _ = check_sweep_isolated(gpu, torch.as_tensor(W).cuda(), U, hdiag, dead)
+        assert_sweep_bar(st)
