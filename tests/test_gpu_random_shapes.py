@@ -1,4 +1,5 @@
-"""GPU parity on seeded random shapes: n a random multiple of 32 up to 1248, 1-399 rows, Hessians
+"""GPU parity on seeded random shapes (the fold and sweep; then the q2tp sweep, act order and
+the output debias): n a random multiple of 32 up to 1248, 1-399 rows, Hessians
 from 0.6-3 n tokens (so some are rank-deficient and take the retry path), random dead
 channels, heavy-tailed channel scales, λ in {0, 1e-4, 1e-2, 0.1}, and now and then an all-zero
 row of W.  Every case is held to the fold and sweep bars of the other parity tests."""
@@ -36,3 +37,24 @@ def test_random_shapes(gpu, seed):
         (U, hdiag, dead, rep), orc, err = check_fold(gpu, torch.as_tensor(H).cuda(), lam, H_np=H)
         st, _ = check_sweep_isolated(gpu, torch.as_tensor(W).cuda(), U, hdiag, dead)
         assert_sweep_bar(st)
+
+
+@pytest.mark.parametrize("seed", [404, 505])
+def test_random_shapes_next_rows(gpu, seed):
+    """The same generator for the q2tp sweep, act order and the output debias, each against its
+    own checker (the bars of its parity tests)."""
+    from test_gpu_act_order import check_order, check_sweep, run_gpu
+    from test_gpu_debias import check as check_debias
+    from test_gpu_q2 import check_q2
+    rng = np.random.default_rng(seed)
+    for i in range(6):
+        H, W, lam, t, nd = _case(rng)
+        say(f"seed {seed} case {i}: n={H.shape[0]} rows={W.shape[0]} t={t} dead={nd} lam={lam}")
+        Hd, Wd = torch.as_tensor(H).cuda(), torch.as_tensor(W).cuda()
+        (U, hdiag, dead, rep), _, _ = check_fold(gpu, Hd, lam, H_np=H)
+        check_q2(gpu, Wd, U, hdiag, dead)
+        perm, dead_a, Hp = run_gpu(gpu, Hd, Wd, lam)
+        p_o = check_order(perm, dead_a, Hp, H)
+        (Up, _, _, _), _, _ = check_fold(gpu, Hp, lam)
+        check_sweep(gpu, Wd, Up, dead_a, perm, p_o)
+        check_debias(gpu, Hd, Wd, lam, label=f"random n={H.shape[0]}")
