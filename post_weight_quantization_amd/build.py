@@ -15,7 +15,7 @@ SOURCES = ["fold.hip", "sweep.hip", "gram.hip", "debias.hip", "act_order.hip", "
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-ffp-contract=fast", "-fno-gpu-rdc"]
+         "-ffp-contract=fast-honor-pragmas", "-fno-gpu-rdc"]
 
 
 def _compile(src: str) -> str:

@@ -123,7 +123,7 @@ __device__ __forceinline__ int nominal_rung(float amax, float lo, float st) {
     r = fmin(fmax(r, 0.0), 31.0);
     return (int)r;
 }
-#pragma clang fp contract(on)
+#pragma clang fp contract(fast)
 
 // Cross-lane moves inside the 16-lane rows of a wave, as DPP operand modifiers (a VALU move,
 // no LDS round trip).  C is the DPP control: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
@@ -242,7 +242,7 @@ __device__ __forceinline__ float pair_err_q2(float w0, float w1, float h0, float
     const float f0 = e0 * d0, f1 = e1 * d1;
     return f0 + f1;
 }
-#pragma clang fp contract(on)
+#pragma clang fp contract(fast)
 
 constexpr int SB = 128;          // columns per block (4 groups)
 constexpr int RPW = 32;          // rows per workgroup of the block kernel (16 lanes each)

@@ -58,3 +58,24 @@ def test_random_shapes_next_rows(gpu, seed):
         (Up, _, _, _), _, _ = check_fold(gpu, Hp, lam)
         check_sweep(gpu, Wd, Up, dead_a, perm, p_o)
         check_debias(gpu, Hd, Wd, lam, label=f"random n={H.shape[0]}")
+
+
+def test_near_tie_rungs_decided_like_the_oracle(gpu):
+    """Regression: the 215th case of seed 7 (n = 32, 211 rows) has rows whose candidate rungs'
+    f32 errors lie within an ulp of each other.  The rung decisions are taken in f32 with every
+    product and sum rounded separately; when the build fused them into multiply-adds, the
+    act-order static rungs differed from the oracle's here.  They must now agree exactly."""
+    from test_gpu_act_order import check_order, check_sweep, run_gpu
+    rng = np.random.default_rng(7)
+    for _ in range(215):
+        H, W, lam, t, nd = _case(rng)
+    assert H.shape == (32, 32) and W.shape == (211, 32)
+    Hd, Wd = torch.as_tensor(H).cuda(), torch.as_tensor(W).cuda()
+    (U, hdiag, dead, rep), _, _ = check_fold(gpu, Hd, lam, H_np=H)
+    st, _ = check_sweep_isolated(gpu, Wd, U, hdiag, dead)
+    assert_sweep_bar(st)
+    assert st["rung_hard"] == 0 and st["rung_ties"] == 0, st
+    perm, dead_a, Hp = run_gpu(gpu, Hd, Wd, lam)
+    p_o = check_order(perm, dead_a, Hp, H)
+    (Up, _, _, _), _, _ = check_fold(gpu, Hp, lam)
+    check_sweep(gpu, Wd, Up, dead_a, perm, p_o)
