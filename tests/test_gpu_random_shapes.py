@@ -79,3 +79,28 @@ def test_near_tie_rungs_decided_like_the_oracle(gpu):
     p_o = check_order(perm, dead_a, Hp, H)
     (Up, _, _, _), _, _ = check_fold(gpu, Hp, lam)
     check_sweep(gpu, Wd, Up, dead_a, perm, p_o)
+
+
+def test_random_larger_shapes(gpu):
+    """Three seeded cases at n = 1280-4096 (several 512-column panels; H formed on the GPU), 64
+    sampled rows each, with and without the residual output."""
+    rng = np.random.default_rng(11)
+    for i in range(3):
+        n = int(rng.integers(40, 129)) * 32
+        rows = int(rng.integers(64, 600))
+        t = int(n * rng.uniform(0.8, 2.5)) + 1
+        X = rng.standard_normal((n, t)).astype(np.float32)
+        X *= np.exp(rng.uniform(0, 1.5) * rng.standard_normal(n)).astype(np.float32)[:, None]
+        nd = int(rng.integers(0, max(1, n // 50)))
+        if nd:
+            X[rng.choice(n, size=nd, replace=False), :] = 0.0
+        Xd = torch.as_tensor(X).cuda()
+        Hd = (Xd @ Xd.T).contiguous()
+        lam = float(rng.choice([0.0, 1e-4, 1e-2]))
+        W = (rng.standard_normal((rows, n)) * rng.uniform(0.005, 0.05)).astype(np.float32)
+        say(f"larger case {i}: n={n} rows={rows} t={t} dead={nd} lam={lam}")
+        (U, hdiag, dead, rep), _, _ = check_fold(gpu, Hd, lam, H_np=Hd.cpu().numpy())
+        sel = np.sort(rng.choice(rows, size=64, replace=False))
+        st, _ = check_sweep_isolated(gpu, torch.as_tensor(W).cuda(), U, hdiag, dead, rows_sel=sel,
+                                     want_E=(i % 2 == 0))
+        assert_sweep_bar(st)
