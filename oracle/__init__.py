@@ -7,7 +7,8 @@ it, and this package imports nothing from the product package.
 What each function follows (docs.rs source pages of the cortiq project):
 
 * :func:`fold` -- "cortiq-cli 0.8.45 src/gptq.rs", ``gptq_fold_operator_par``: dead channels,
-  damping ``lambda * mean(diag)``, the x10 retry, ``U`` = upper Cholesky factor of ``H_d^-1``.
+  damping ``lambda * mean(diag)``, the x10 retry, ``U`` = upper Cholesky factor of ``H_d^-1``,
+  computed from that definition as ``J chol(J H_d J)^-1 J`` (see the C source).
 * :func:`ladder` -- the per-row rung ladder; the pages take it from a converter whose rule is
   not printed, so the rule here is a stated reading (see the C source).
 * :func:`sweep` -- "cortiq-cli 0.8.45 src/gptq.rs", ``gptq_quantize_q4tp``, and
@@ -104,8 +105,9 @@ def threads(nt=None) -> int:
 def fold(H, lam, retry=True, route=0, nt=None):
     """Fold ``H`` (f32, ``n x ldh``; the upper triangle is read) at starting damping ``lam``.
 
-    ``route`` 0 is the pages' host route (the oracle's definition); 1 and 2 are the reversed
-    and reversed-equilibrated cross-check routes.  Returns a dict with ``U`` (f64, upper),
+    ``route`` 0 computes U = J chol(J H_d J)^-1 J (J the order reversal), the definition
+    solved for U; route 1 does the same on the equilibrated matrix (a cross-check with other
+    rounding).  Returns a dict with ``U`` (f64, upper),
     ``hdiag`` (f32), ``dead`` (bool), ``lam``, ``base``, ``damp``, ``attempts``, ``status``.
     """
     H = np.ascontiguousarray(H, dtype=np.float32)

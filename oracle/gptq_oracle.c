@@ -6,9 +6,11 @@
  * code, header, table or constant with the HIP library.
  *
  * Sources it follows (docs.rs source pages of the cortiq project):
- *   [gptq.rs]      "cortiq-cli 0.8.45 src/gptq.rs": gptq_fold_operator_par (the f64 fold),
- *                  cholesky_lower / cholesky_lower_rows (the factor), gptq_quantize_q4tp
- *                  (rung rule, per-column rounding, full-row error feedback).
+ *   [gptq.rs]      "cortiq-cli 0.8.45 src/gptq.rs": gptq_fold_operator_par (what the fold
+ *                  computes: dead channels, damping, the retry schedule, U = the upper Cholesky
+ *                  factor of H_d^-1; computed here from that definition, not by the page's
+ *                  route), gptq_quantize_q4tp (rung rule, per-column rounding, full-row error
+ *                  feedback).
  *   [gptq_dev.rs]  "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs": module documentation
  *                  (steps 1-5 of the method) and the q4tp_group kernel (the same rung rule).
  *
@@ -52,12 +54,13 @@ static double dot(const double* a, const double* b, int64_t len) {
     return s;
 }
 
-/* In-place lower Cholesky A = L L^T of a dense row-major n x n f64 matrix (lower triangle
- * read, upper triangle zeroed on success).  Textbook entry formula
- *     l_ij = (a_ij - sum_{k<j} l_ik l_jk) / l_jj,      l_jj = sqrt(a_jj - sum_{k<j} l_jk^2),
- * failing when a pivot is not positive or not finite ([gptq.rs] cholesky_lower_rows: the
- * pivot test).  Columns are visited in blocks so that row prefixes stay in cache; the rows
- * below a block are independent and run in parallel. */
+/* In-place lower Cholesky factor A = C C^T of a dense row-major n x n f64 matrix (lower
+ * triangle read, upper triangle zeroed on success), by the textbook entry formula
+ *     c_jj = sqrt(a_jj - sum_{k<j} c_jk^2),     c_ij = (a_ij - sum_{k<j} c_ik c_jk) / c_jj  (i > j)
+ * (Golub and Van Loan, "Matrix Computations", the Cholesky algorithm), failing when a pivot is
+ * not positive or not finite: the pivot rule of the host fold ([gptq.rs]).  Columns are visited
+ * in blocks of BLK so that the rows of a block stay in cache; the rows below a block are
+ * independent given the block and run in parallel. */
 static int chol_lower(double* a, int64_t n, int nt) {
     for (int64_t jb = 0; jb < n; jb += BLK) {
         int64_t je = imin(jb + BLK, n);
@@ -82,38 +85,24 @@ static int chol_lower(double* a, int64_t n, int nt) {
     return 1;
 }
 
-/* Columns of L^-1 by forward substitution, stored as rows: lt[j][i] = (L^-1)_ij for i >= j,
- *     (L^-1)_jj = 1 / l_jj,    (L^-1)_ij = -(sum_{k=j}^{i-1} l_ik (L^-1)_kj) / l_ii.
- * Each column is independent; a block of BLK columns walks the rows of L once. */
-static void lower_inverse_cols(const double* l, double* lt, int64_t n, int nt) {
+/* The inverse of a lower triangular C by triangular solves: column j of C^-1 is the solution y
+ * of C y = e_j, by forward substitution
+ *     y_i = 0 (i < j),   y_j = 1 / c_jj,   y_i = -(sum_{k=j}^{i-1} c_ik y_k) / c_ii  (i > j).
+ * Column j is stored as row j of yt (yt[j][i] = (C^-1)_ij), so each sum is a contiguous dot
+ * product.  The columns are independent; a block of BLK of them walks the rows of C once. */
+static void lower_inverse_cols(const double* c, double* yt, int64_t n, int nt) {
     int64_t nblk = (n + BLK - 1) / BLK;
 #pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
     for (int64_t b = 0; b < nblk; ++b) {
         int64_t c0 = b * BLK, c1 = imin(c0 + BLK, n);
-        for (int64_t j = c0; j < c1; ++j) memset(lt + j * n, 0, sizeof(double) * (size_t)n);
+        for (int64_t j = c0; j < c1; ++j) memset(yt + j * n, 0, sizeof(double) * (size_t)n);
         for (int64_t i = c0; i < n; ++i) {
-            const double* li = l + i * n;
+            const double* ci = c + i * n;
             for (int64_t j = c0; j < c1 && j <= i; ++j) {
-                double* x = lt + j * n;
-                x[i] = (i == j) ? 1.0 / li[i] : -dot(li + j, x + j, i - j) / li[i];
+                double* y = yt + j * n;
+                y[i] = (i == j) ? 1.0 / ci[i] : -dot(ci + j, y + j, i - j) / ci[i];
             }
         }
-    }
-}
-
-/* Fold status of one attempt sequence.  h is the symmetric f64 Hessian after the dead-channel
- * treatment; returns 1 and the factor in a when a damped copy factors. */
-static int damped_cholesky(const double* h, double* a, int64_t n, double base, double* lam,
-                           int retry, int* attempts, int nt) {
-    for (;;) {
-        ++*attempts;
-        memcpy(a, h, sizeof(double) * (size_t)(n * n));
-        for (int64_t i = 0; i < n; ++i) a[i * n + i] += *lam * base;
-        if (chol_lower(a, n, nt)) return 1;
-        if (!retry) return 0;
-        /* [gptq.rs] gptq_fold_operator_par: 0 -> 1e-4, otherwise x10; past 10 give up. */
-        *lam = (*lam == 0.0) ? 1e-4 : *lam * 10.0;
-        if (*lam > 10.0) return -1;
     }
 }
 
@@ -123,27 +112,36 @@ static void set_identity(double* u, int64_t n) {
 }
 
 /*
- * The fold ([gptq.rs] gptq_fold_operator_par; [gptq_dev.rs] module documentation, step 1):
+ * The fold: U, the upper triangular factor with a positive diagonal of H_d^-1 = U^T U
+ * ([gptq.rs] gptq_fold_operator_par; [gptq_dev.rs] module documentation, steps 1-4).
+ *
+ * Decision rules fixed by the method:
  *   1. h = H in f64, symmetric, read from the UPPER triangle of H (ldh = row stride).
  *   2. hdiag_i = H_ii (raw f32); dead_i = !(H_ii > 0) (so NaN is dead).
- *   3. dead channel: row and column zeroed, diagonal 1.
- *   4. base = max(mean_i h_ii, 1e-12);  damp = lam * base.
- *   5. lam = max(lambda, 0); factor h + damp I; on failure lam -> 1e-4 (from 0) or x10 and
- *      refactor; past 10 the result is U = I with status DEGENERATE.
- *   6. route 0 (the pages' host route): L = chol(H_d), L^-1, H_d^-1 = L^-T L^-1,
- *      M = chol(H_d^-1), U = M^T (upper Cholesky factor of H_d^-1).
- *      route 1 (cross-check): U = P chol(P H_d P)^-1 P with P the order reversal;
- *      route 2 (cross-check): the same on the equilibrated D^-1 H_d D^-1, then U = ... D^-1
- *      (the device route of [gptq_dev.rs], steps 1-4, here in f64).
+ *   3. a dead channel's row and column are zeroed and its diagonal set to 1.
+ *   4. base = max(mean_i h_ii, 1e-12);  damp = lam * base;  H_d = h + damp I.
+ *   5. lam = max(lambda, 0); a factorization that meets a pivot that is not positive or not
+ *      finite is redone at lam -> 1e-4 (from 0) or 10 lam; past 10 the result is U = I with
+ *      status DEGENERATE.  With retry == 0 the first failure returns FAILED.
+ *
+ * How U is computed (from the definition; the factor is unique):  with J the order reversal,
+ * let J H_d J = C C^T (lower Cholesky).  Then H_d = (J C J)(J C J)^T, where R = J C J is upper
+ * triangular with a positive diagonal, so H_d^-1 = R^-T R^-1 and U = R^-1 = J C^-1 J:
+ *     U[j][k] = (C^-1)[n-1-j][n-1-k]  for k >= j, 0 below.
+ *   route 0: exactly that.
+ *   route 1: the same on the equilibrated matrix, J D^-1 H_d D^-1 J = C~ C~^T with
+ *            D = sqrt(diag H_d), then U = J C~^-1 J D^-1 (the device's arrangement in f64;
+ *            different rounding, the same U).  Used to cross-check route 0.
  * info[0] = lam used, info[1] = base, info[2] = damp, info[3] = attempts.
  * Returns ORC_OK, ORC_FAILED (retry == 0 and the factor failed) or ORC_DEGENERATE.
  */
 int orc_fold(const float* H, int64_t n, int64_t ldh, double lambda, int retry, int route,
              double* U, float* hdiag, uint8_t* dead, double* info, int nt) {
-    if (n <= 0) return ORC_FAILED;
+    if (n <= 0 || route < 0 || route > 1) return ORC_FAILED;
     size_t nn = (size_t)(n * n);
     double* h = (double*)malloc(sizeof(double) * nn);
     double* a = (double*)malloc(sizeof(double) * nn);
+    double* dsc = (double*)malloc(sizeof(double) * (size_t)n);
     for (int64_t i = 0; i < n; ++i) {
         float d = H[i * ldh + i];
         hdiag[i] = d;
@@ -166,72 +164,40 @@ int orc_fold(const float* H, int64_t n, int64_t ldh, double lambda, int retry, i
     double lam = lambda > 0.0 ? lambda : 0.0;
     int attempts = 0;
     int status = ORC_OK;
-
-    if (route == 0) {
-        int ok = damped_cholesky(h, a, n, base, &lam, retry, &attempts, nt);
-        if (ok <= 0) {
-            status = ok == 0 ? ORC_FAILED : ORC_DEGENERATE;
-            set_identity(U, n);
-        } else {
-            double* lt = h; /* h is no longer needed */
-            lower_inverse_cols(a, lt, n, nt);
-            /* H_d^-1 (lower part): (H^-1)_ik = sum_{m >= i} (L^-1)_mi (L^-1)_mk, k <= i. */
-            int64_t nblk = (n + BLK - 1) / BLK;
-#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
-            for (int64_t b = 0; b < nblk; ++b) {
-                int64_t i0 = b * BLK, i1 = imin(i0 + BLK, n);
-                for (int64_t k = 0; k < i1; ++k)
-                    for (int64_t i = (i0 > k ? i0 : k); i < i1; ++i)
-                        a[i * n + k] = dot(lt + i * n + i, lt + k * n + i, n - i);
+    int ok;
+    for (;;) {
+        double damp = lam * base;
+        for (int64_t i = 0; i < n; ++i) dsc[i] = (route == 1) ? sqrt(h[i * n + i] + damp) : 1.0;
+        /* a = J (D^-1) H_d (D^-1) J, lower triangle (the factorization reads no more) */
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t j = 0; j <= i; ++j) {
+                int64_t ii = n - 1 - i, jj = n - 1 - j;
+                double v = h[ii * n + jj] + (ii == jj ? damp : 0.0);
+                a[i * n + j] = v / (dsc[ii] * dsc[jj]);
             }
-            if (!chol_lower(a, n, nt)) {
-                status = ORC_DEGENERATE;
-                set_identity(U, n);
-            } else {
-                for (int64_t j = 0; j < n; ++j)
-                    for (int64_t c = 0; c < n; ++c) U[c * n + j] = (c <= j) ? a[j * n + c] : 0.0;
-            }
-        }
+        ++attempts;
+        ok = chol_lower(a, n, nt);
+        if (ok > 0) break;
+        if (!retry) { ok = 0; break; }
+        lam = (lam == 0.0) ? 1e-4 : lam * 10.0;
+        if (lam > 10.0) { ok = -1; break; }
+    }
+    if (ok <= 0) {
+        status = ok == 0 ? ORC_FAILED : ORC_DEGENERATE;
+        set_identity(U, n);
     } else {
-        /* Reversed (and optionally equilibrated) route, used only to cross-check route 0. */
-        double* dsc = (double*)malloc(sizeof(double) * (size_t)n);
-        double* hr = (double*)malloc(sizeof(double) * nn);
-        int ok;
-        for (;;) {
-            double damp = lam * base;
-            for (int64_t i = 0; i < n; ++i)
-                dsc[i] = (route == 2) ? sqrt(h[i * n + i] + damp) : 1.0;
-            for (int64_t i = 0; i < n; ++i)
-                for (int64_t j = 0; j < n; ++j) {
-                    int64_t ii = n - 1 - i, jj = n - 1 - j;
-                    double v = h[ii * n + jj] + (ii == jj ? damp : 0.0);
-                    hr[i * n + j] = v / (dsc[ii] * dsc[jj]);
-                }
-            ++attempts;
-            memcpy(a, hr, sizeof(double) * nn);
-            ok = chol_lower(a, n, nt);
-            if (ok > 0) break;
-            if (!retry) { ok = 0; break; }
-            lam = (lam == 0.0) ? 1e-4 : lam * 10.0;
-            if (lam > 10.0) { ok = -1; break; }
-        }
-        if (ok <= 0) {
-            status = ok == 0 ? ORC_FAILED : ORC_DEGENERATE;
-            set_identity(U, n);
-        } else {
-            lower_inverse_cols(a, hr, n, nt); /* hr[j][i] = (L^-1)_ij */
-            /* U_jk = (L^-1)_{n-1-j, n-1-k} / d_k for k >= j. */
-            for (int64_t j = 0; j < n; ++j)
-                for (int64_t k = 0; k < n; ++k)
-                    U[j * n + k] = (k >= j) ? hr[(n - 1 - k) * n + (n - 1 - j)] / dsc[k] : 0.0;
-        }
-        free(hr);
-        free(dsc);
+        double* yt = h; /* h is no longer needed: yt[j][i] = (C^-1)_ij */
+        lower_inverse_cols(a, yt, n, nt);
+#pragma omp parallel for num_threads(nt) schedule(static)
+        for (int64_t j = 0; j < n; ++j)
+            for (int64_t k = 0; k < n; ++k)
+                U[j * n + k] = (k >= j) ? yt[(n - 1 - k) * n + (n - 1 - j)] / dsc[k] : 0.0;
     }
     info[0] = lam;
     info[1] = base;
     info[2] = lam * base;
     info[3] = (double)attempts;
+    free(dsc);
     free(h);
     free(a);
     return status;

@@ -115,27 +115,62 @@ def test_first_row_is_scaled_inverse_row():
     np.testing.assert_allclose(r["U"][0], hinv[0] / np.sqrt(hinv[0, 0]), rtol=1e-9, atol=1e-14)
 
 
+def _inverse_identity_residual(H, r):
+    """max |D (U^T U H_d - I) D^-1|, the equilibrated residual of U^T U H_d = I."""
+    hd = _hd(H, r)
+    d = np.sqrt(np.diag(hd))
+    res = (r["U"].T @ r["U"] @ hd - np.eye(len(hd))) * d[:, None] / d[None, :]
+    return float(np.abs(res).max())
+
+
 def test_inverse_identity_on_tiny_workload():
     H, W, lam = workloads.make("tiny")
     H = H.numpy()
     r = oracle.fold(H, lam)
     assert r["status"] == oracle.OK and r["attempts"] == 1
-    hd = _hd(H, r)
-    d = np.sqrt(np.diag(hd))
-    res = (r["U"].T @ r["U"] @ hd - np.eye(len(hd))) * d[:, None] / d[None, :]
-    assert np.abs(res).max() < 1e-10, np.abs(res).max()
+    res = _inverse_identity_residual(H, r)
+    assert res < 1e-10, res
 
 
-def test_three_routes_agree():
-    """The factor is unique, so the host route, the reversed route and the reversed
-    equilibrated route give the same U up to rounding."""
+@pytest.mark.slow
+def test_inverse_identity_on_attention_workload():
+    """U^T U H_d = I to 1e-10 (equilibrated) at the attention-projection size, n = 4096 with
+    its lognormal channels and dead channels."""
+    H, W, lam = workloads.make("attn")
+    H = H.numpy()
+    r = oracle.fold(H, lam)
+    assert r["status"] == oracle.OK and r["attempts"] == 1 and r["dead"].sum() == 20
+    res = _inverse_identity_residual(H, r)
+    assert res < 1e-10, res
+
+
+def test_two_routes_agree():
+    """The factor is unique, so the reversed route and the reversed equilibrated route (other
+    rounding) give the same U up to rounding."""
     for H in (_spd(77, 7), workloads.make("tiny")[0].numpy(), workloads.fixture()[0].numpy()):
         ref = oracle.fold(H, 0.01, route=0)
-        for route in (1, 2):
-            r = oracle.fold(H, 0.01, route=route)
-            assert r["status"] == oracle.OK and r["lam"] == ref["lam"]
-            err = np.linalg.norm(r["U"] - ref["U"]) / np.linalg.norm(ref["U"])
-            assert err < 1e-12, (route, err)
+        r = oracle.fold(H, 0.01, route=1)
+        assert r["status"] == oracle.OK and r["lam"] == ref["lam"]
+        err = np.linalg.norm(r["U"] - ref["U"]) / np.linalg.norm(ref["U"])
+        assert err < 1e-12, err
+
+
+def test_every_row_is_the_obs_row_of_its_trailing_hessian():
+    """Row j of U is the first row of the inverse of H_d's trailing principal block F = {j..n-1},
+    divided by the square root of its first entry (the pages' OBS reading of the operator: the
+    feedback of column j reaches only the columns not yet quantized).  Each row is checked
+    against its own LAPACK inverse, so a wrong index anywhere in the factor or its inverse
+    fails it; the entries left of the diagonal are exactly 0."""
+    for n, seed, lam in [(9, 21, 0.0), (40, 22, 0.01), (73, 23, 1e-4)]:
+        H = _spd(n, seed)
+        H[5, :] = H[:, 5] = 0.0
+        r = oracle.fold(H, lam)
+        assert r["status"] == oracle.OK
+        hd = _hd(H, r)
+        for j in range(n):
+            g = np.linalg.inv(hd[j:, j:])[0]
+            np.testing.assert_allclose(r["U"][j, j:], g / np.sqrt(g[0]), rtol=1e-9, atol=1e-12)
+            assert np.all(r["U"][j, :j] == 0.0)
 
 
 def test_reads_upper_triangle_only():
