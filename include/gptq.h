@@ -51,41 +51,67 @@ typedef struct {
                            first schedule value past 10 */
     double base;        /* max(mean of the diagonal with dead entries counted as 1, 1e-12) */
     double damp;        /* lambda_used * base, added to the diagonal */
-    int32_t attempts;   /* factorizations tried (1 when the starting lambda factors) */
+    int32_t attempts;   /* factorizations tried, f32 and f64 (1 when the first one factors) */
     int32_t n_dead;     /* channels with !(H_ii > 0) */
     int32_t degenerate; /* 1 when U = I was written */
-    int32_t reserved;
+    int32_t precision;  /* 32 or 64: the arithmetic of the factorization U comes from */
+    double min_pivot;   /* smallest pivot of that factorization (of the unit-diagonal
+                           equilibrated matrix, so in (0, 1]); 0 on GPTQ_DEGENERATE */
 } gptq_fold_report;
 
-/* Bytes of device workspace gptq_fold needs for size n: two padded n_p x n_p f32 matrices
- * (n_p = n rounded up to 128) plus O(n_p * 128).  0 for n <= 0. */
+/* Arithmetic of the fold (gptq_fold_ex).
+ *   GPTQ_FOLD_AUTO  each damping value is factored in f32 first; if a pivot of the equilibrated
+ *                   matrix is at or below 1e-3 (the f32 factor's error in U D grows as 6e-8 /
+ *                   smallest pivot) or fails, that damping value is factored again in f64, and
+ *                   every later one too.  The pivot rule is then the f64 host's, so the damping
+ *                   reached equals the f64 host fold's.
+ *   GPTQ_FOLD_F32   f32 only, the pages' device rule (a pivot that is not > 0, or NaN, raises
+ *                   lambda).  Accurate to about 6e-8 / min_pivot.
+ *   GPTQ_FOLD_F64   f64 only (f64 MFMA), the host's rule (not > 0 or not finite). */
+enum { GPTQ_FOLD_AUTO = 0, GPTQ_FOLD_F32 = 1, GPTQ_FOLD_F64 = 2 };
+
+/* Bytes of device workspace gptq_fold_ex needs for size n and a precision, with
+ * n_p = n rounded up to 128: GPTQ_FOLD_F32 two n_p x n_p f32 matrices plus O(n_p * 512);
+ * GPTQ_FOLD_AUTO and GPTQ_FOLD_F64 two n_p x n_p f64 matrices plus O(n_p * 512).
+ * 0 for n <= 0, n > 2^20 or an unknown precision. */
+size_t gptq_fold_workspace_size_ex(int64_t n, int precision);
+/* gptq_fold_workspace_size_ex(n, GPTQ_FOLD_AUTO): what gptq_fold needs. */
 size_t gptq_fold_workspace_size(int64_t n);
 
 /*
- * gptq_fold -- the damped, equilibrated fold of one Hessian.
+ * gptq_fold_ex -- the damped, equilibrated fold of one Hessian.
  *
  *   H        [n, ldh] f32, device.  Only the UPPER triangle (j >= i) is read; the lower one
  *            may hold anything.  Non-finite entries are allowed: a non-finite or non-positive
  *            diagonal marks the channel dead, anything else fails pivots and raises lambda.
- *   n        channels, >= 1.  ldh >= n.
- *   lambda   starting relative damping (negative or NaN is treated as 0).  A pivot that is
- *            not positive (or NaN) in the f32 factorization restarts it with lambda -> 1e-4
- *            (from 0) or lambda * 10; past 10 the call writes U = I and returns
- *            GPTQ_DEGENERATE (the round-to-nearest operator of the host fold).
+ *   n        channels, 1 <= n <= 2^20.  ldh >= n.
+ *   lambda   starting relative damping (negative or NaN is treated as 0).  A pivot that fails
+ *            (see the precisions above) restarts the factorization with lambda -> 1e-4 (from
+ *            0) or lambda * 10; past 10 the call writes U = I and returns GPTQ_DEGENERATE (the
+ *            round-to-nearest operator of the host fold).
+ *   precision  GPTQ_FOLD_AUTO, GPTQ_FOLD_F32 or GPTQ_FOLD_F64.
  *   U        [n, n] f32 out, device: U[j][k] for k >= j, zeros below the diagonal.
  *   hdiag    [n] f32 out, device: the raw H_ii (the sweep's rung-search weights).
  *   dead     [n] u8 out, device: 1 where !(H_ii > 0).
- *   workspace / workspace_bytes: device scratch of at least gptq_fold_workspace_size(n).
+ *   workspace / workspace_bytes: device scratch of at least
+ *            gptq_fold_workspace_size_ex(n, precision).
  *   stream   hipStream_t.
  *   report   host pointer (may be NULL).
  *
  * Steps on the device: diagonal, dead mask and mean (f64) -> per attempt: D_i^-1 =
  * (H_ii + damp)^-1/2 (dead: (1 + damp)^-1/2), the reversed equilibrated matrix
- * A = P D^-1 H_d D^-1 P, blocked Cholesky A = L L^T and, pipelined on the helper streams one
- * 512-column panel behind, the blocked right-looking inverse X = L^-1 -> U = P X P D^-1.  The
- * host reads the pivot flag once per attempt (one stream synchronisation); U is still being
- * written when the call returns.
+ * A = P D^-1 H_d D^-1 P, blocked Cholesky A = L L^T and the blocked right-looking inverse
+ * X = L^-1 (in f32 pipelined on the helper streams one 512-column panel behind; in f64
+ * trailing each 256-column panel) -> U = P X P D^-1.  The host reads the pivot flag once per
+ * attempt (one stream synchronisation); U is still being written when the call returns.
+ * Sources: page "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs", module documentation steps
+ * 1-4 and the driver `fold`; page "cortiq-cli 0.8.45 src/gptq.rs", gptq_fold_operator_par.
  */
+int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambda, int precision, float* U,
+                 float* hdiag, uint8_t* dead, void* workspace, size_t workspace_bytes,
+                 void* stream, gptq_fold_report* report);
+
+/* gptq_fold_ex with precision GPTQ_FOLD_AUTO. */
 int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, float* U, float* hdiag,
               uint8_t* dead, void* workspace, size_t workspace_bytes, void* stream,
               gptq_fold_report* report);

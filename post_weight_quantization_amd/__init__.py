@@ -33,10 +33,14 @@ class FoldReport(ctypes.Structure):
     _fields_ = [("lambda_used", ctypes.c_double), ("base", ctypes.c_double),
                 ("damp", ctypes.c_double), ("attempts", ctypes.c_int32),
                 ("n_dead", ctypes.c_int32), ("degenerate", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("precision", ctypes.c_int32), ("min_pivot", ctypes.c_double)]
 
     def as_dict(self):
-        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+# Arithmetic of the fold (include/gptq.h, GPTQ_FOLD_*).
+FOLD_PRECISION = {"auto": 0, "f32": 1, "f64": 2}
 
 
 def load():
@@ -51,9 +55,14 @@ def load():
     P, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     lib.gptq_fold_workspace_size.argtypes = [i64]
     lib.gptq_fold_workspace_size.restype = sz
+    lib.gptq_fold_workspace_size_ex.argtypes = [i64, ctypes.c_int]
+    lib.gptq_fold_workspace_size_ex.restype = sz
     lib.gptq_fold.argtypes = [P, i64, i64, ctypes.c_double, P, P, P, P, sz, P,
                               ctypes.POINTER(FoldReport)]
     lib.gptq_fold.restype = ctypes.c_int
+    lib.gptq_fold_ex.argtypes = [P, i64, i64, ctypes.c_double, ctypes.c_int, P, P, P, P, sz, P,
+                                 ctypes.POINTER(FoldReport)]
+    lib.gptq_fold_ex.restype = ctypes.c_int
     lib.gptq_ladder.argtypes = [P, P, i64, i64, P, P, P]
     lib.gptq_ladder.restype = ctypes.c_int
     lib.gptq_sweep_workspace_size.argtypes = [i64, i64]
@@ -112,13 +121,21 @@ def status_string(status: int) -> str:
         return "unknown"
 
 
-def _dev(t: torch.Tensor, dtype, name):
-    if not t.is_cuda:
+def _dev(t: torch.Tensor, dtype, name, shape=None, align=1, device=None):
+    """A contiguous device tensor's pointer, after checking its dtype, shape, device and the
+    alignment (bytes) of its first element."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's tensors on {device}")
+    if align > 1 and t.data_ptr() % align:
+        raise ValueError(f"{name} must be {align}-byte aligned")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -139,8 +156,25 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def fold_workspace_size(n: int) -> int:
-    return int(load().gptq_fold_workspace_size(int(n)))
+def _on(stream, device):
+    """The stream a call is enqueued on, as a context for the tensors it allocates: PyTorch's
+    caching allocator then reuses their memory only in that stream's order, after the call's
+    kernels, never while they may still run."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return torch.cuda.stream(s)
+
+
+def _workspace(workspace, need, device, name="workspace"):
+    if workspace is None:
+        return torch.empty(max(int(need), 1), dtype=torch.uint8, device=device)
+    _dev(workspace, torch.uint8, name, align=256, device=device)
+    if workspace.numel() < need:
+        raise ValueError(f"{name} has {workspace.numel()} bytes, the call needs {need}")
+    return workspace
+
+
+def fold_workspace_size(n: int, precision: str = "auto") -> int:
+    return int(load().gptq_fold_workspace_size_ex(int(n), FOLD_PRECISION[precision]))
 
 
 def sweep_workspace_size(rows: int, n: int) -> int:
@@ -148,25 +182,32 @@ def sweep_workspace_size(rows: int, n: int) -> int:
 
 
 def gptq_fold(H: torch.Tensor, lam: float, workspace: torch.Tensor | None = None, stream=None,
-              out=None, check=True):
-    """Fold H (f32 [n, n], upper triangle read).  Returns (U, hdiag, dead, report dict)."""
+              out=None, check=True, precision: str = "auto"):
+    """Fold H (f32 [n, n], upper triangle read; rows may be padded).  ``precision`` is "auto"
+    (f32, repeated in f64 where a pivot is at or below 1e-3), "f32" or "f64".  Returns
+    (U, hdiag, dead, report dict)."""
     lib = load()
+    if H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise ValueError("H must be [n, n]")
     n = H.shape[0]
     dev = H.device
-    if out is None:
-        U = torch.empty(n, n, dtype=torch.float32, device=dev)
-        hdiag = torch.empty(n, dtype=torch.float32, device=dev)
-        dead = torch.empty(n, dtype=torch.uint8, device=dev)
-    else:
-        U, hdiag, dead = out
-    need = lib.gptq_fold_workspace_size(n)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    prec = FOLD_PRECISION[precision]
+    need = int(lib.gptq_fold_workspace_size_ex(n, prec))
+    with _on(stream, dev):
+        if out is None:
+            U = torch.empty(n, n, dtype=torch.float32, device=dev)
+            hdiag = torch.empty(n, dtype=torch.float32, device=dev)
+            dead = torch.empty(n, dtype=torch.uint8, device=dev)
+        else:
+            U, hdiag, dead = out
+        workspace = _workspace(workspace, need, dev)
     rep = FoldReport()
-    st = lib.gptq_fold(_dev_rows(H, torch.float32, "H"), n, H.stride(0), float(lam),
-                       _dev(U, torch.float32, "U"), _dev(hdiag, torch.float32, "hdiag"),
-                       _dev(dead, torch.uint8, "dead"), _dev(workspace, torch.uint8, "workspace"),
-                       workspace.numel(), _stream(stream), ctypes.byref(rep))
+    st = lib.gptq_fold_ex(_dev_rows(H, torch.float32, "H"), n, H.stride(0), float(lam), prec,
+                          _dev(U, torch.float32, "U", (n, n), device=dev),
+                          _dev(hdiag, torch.float32, "hdiag", (n,), device=dev),
+                          _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                          ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                          _stream(stream), ctypes.byref(rep))
     if check and st not in (GPTQ_OK, GPTQ_DEGENERATE):
         raise GptqError(st, "gptq_fold")
     r = rep.as_dict()
@@ -178,14 +219,16 @@ def gptq_ladder(W: torch.Tensor, dead: torch.Tensor, stream=None, out=None):
     """Per-row (lo, step) and the 32 rung scales of the dead-zeroed W."""
     lib = load()
     rows, n = W.shape
-    if out is None:
-        lost = torch.empty(rows, 2, dtype=torch.float32, device=W.device)
-        tab = torch.empty(rows, 32, dtype=torch.float32, device=W.device)
-    else:
-        lost, tab = out
-    st = lib.gptq_ladder(_dev(W, torch.float32, "W"), _dev(dead, torch.uint8, "dead"), rows, n,
-                         _dev(lost, torch.float32, "lost"), _dev(tab, torch.float32, "tab"),
-                         _stream(stream))
+    dev = W.device
+    with _on(stream, dev):
+        if out is None:
+            lost = torch.empty(rows, 2, dtype=torch.float32, device=dev)
+            tab = torch.empty(rows, 32, dtype=torch.float32, device=dev)
+        else:
+            lost, tab = out
+    st = lib.gptq_ladder(_dev(W, torch.float32, "W", align=16), _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                         rows, n, _dev(lost, torch.float32, "lost", (rows, 2), device=dev),
+                         _dev(tab, torch.float32, "tab", (rows, 32), device=dev), _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_ladder")
     return lost, tab
@@ -198,23 +241,27 @@ def gptq_sweep(W, U, hdiag, dead, tab, lost, want_E=False, workspace=None, strea
     lib = load()
     rows, n = W.shape
     dev = W.device
-    if out is None:
-        nib = torch.empty(rows, n // 2, dtype=torch.uint8, device=dev)
-        rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
-        scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
-        E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
-    else:
-        nib, rung, scale, E = out
-    if workspace is None:
-        workspace = torch.empty(lib.gptq_sweep_workspace_size(rows, n), dtype=torch.uint8,
-                                device=dev)
-    st = lib.gptq_sweep(_dev(W, torch.float32, "W"), _dev(U, torch.float32, "U"),
-                        _dev(hdiag, torch.float32, "hdiag"), _dev(dead, torch.uint8, "dead"),
-                        _dev(tab, torch.float32, "tab"), _dev(lost, torch.float32, "lost"),
-                        rows, n, _dev(nib, torch.uint8, "nib"), _dev(rung, torch.uint8, "rung"),
-                        _dev(scale, torch.float32, "scale"),
-                        None if E is None else _dev(E, torch.float32, "E"),
-                        _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+    need = int(lib.gptq_sweep_workspace_size(rows, n))
+    with _on(stream, dev):
+        if out is None:
+            nib = torch.empty(rows, n // 2, dtype=torch.uint8, device=dev)
+            rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+            scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+            E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
+        else:
+            nib, rung, scale, E = out
+        workspace = _workspace(workspace, need, dev)
+    st = lib.gptq_sweep(_dev(W, torch.float32, "W", align=16),
+                        _dev(U, torch.float32, "U", (n, n), 16, dev),
+                        _dev(hdiag, torch.float32, "hdiag", (n,), device=dev),
+                        _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                        _dev(tab, torch.float32, "tab", (rows, 32), 16, dev),
+                        _dev(lost, torch.float32, "lost", (rows, 2), 8, dev),
+                        rows, n, _dev(nib, torch.uint8, "nib", (rows, n // 2), 16, dev),
+                        _dev(rung, torch.uint8, "rung", (rows, n // 32), device=dev),
+                        _dev(scale, torch.float32, "scale", (rows, n // 32), device=dev),
+                        None if E is None else _dev(E, torch.float32, "E", (rows, n), 16, dev),
+                        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                         _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_sweep")
@@ -226,8 +273,12 @@ def gptq_gram_add(H: torch.Tensor, X: torch.Tensor, stream=None):
     Returns H."""
     lib = load()
     n = H.shape[0]
+    if H.dim() != 2 or H.shape[1] != n:
+        raise ValueError("H must be [n, n]")
     if X.dim() != 2 or X.shape[1] != n:
         raise ValueError("X must be [t, n] with n = H.shape[0]")
+    if X.device != H.device:
+        raise ValueError("X and H must be on one device")
     st = lib.gptq_gram_add(_dev_rows(H, torch.float32, "H"), n, H.stride(0),
                            _dev_rows(X, torch.float32, "X"), X.shape[0], X.stride(0), _stream(stream))
     if st != GPTQ_OK:
@@ -246,20 +297,22 @@ def gptq_debias(W, H, dead, nib, rung, lost, scale, want_tab=True, want_slope=Tr
     lib = load()
     rows, n = W.shape
     dev = W.device
-    tab = torch.empty(rows, 32, dtype=torch.float32, device=dev) if want_tab else None
-    slope = torch.empty(rows, dtype=torch.float64, device=dev) if want_slope else None
-    if workspace is None:
-        workspace = torch.empty(lib.gptq_debias_workspace_size(rows, n), dtype=torch.uint8,
-                                device=dev)
-    if H.stride(1) != 1:
-        raise ValueError("H must be row-major")
-    st = lib.gptq_debias(_dev(W, torch.float32, "W"), ctypes.c_void_p(H.data_ptr()), H.stride(0),
-                         _dev(dead, torch.uint8, "dead"), _dev(nib, torch.uint8, "nib"),
-                         _dev(rung, torch.uint8, "rung"), _dev(lost, torch.float32, "lost"),
-                         None if tab is None else _dev(tab, torch.float32, "tab"),
-                         _dev(scale, torch.float32, "scale"),
-                         None if slope is None else _dev(slope, torch.float64, "slope"),
-                         rows, n, _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+    if H.dim() != 2 or H.shape[0] != n or H.shape[1] != n or H.stride(1) != 1:
+        raise ValueError("H must be a row-major [n, n] matrix")
+    need = int(lib.gptq_debias_workspace_size(rows, n))
+    with _on(stream, dev):
+        tab = torch.empty(rows, 32, dtype=torch.float32, device=dev) if want_tab else None
+        slope = torch.empty(rows, dtype=torch.float64, device=dev) if want_slope else None
+        workspace = _workspace(workspace, need, dev)
+    st = lib.gptq_debias(_dev(W, torch.float32, "W", align=16), _dev_rows(H, torch.float32, "H"),
+                         H.stride(0), _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                         _dev(nib, torch.uint8, "nib", (rows, n // 2), 16, dev),
+                         _dev(rung, torch.uint8, "rung", (rows, n // 32), device=dev),
+                         _dev(lost, torch.float32, "lost", (rows, 2), 8, dev),
+                         None if tab is None else _dev(tab, torch.float32, "tab", (rows, 32), 16, dev),
+                         _dev(scale, torch.float32, "scale", (rows, n // 32), device=dev),
+                         None if slope is None else _dev(slope, torch.float64, "slope", (rows,), device=dev),
+                         rows, n, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                          _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_debias")
@@ -270,9 +323,12 @@ def gptq_ladder_q2(W, dead, stream=None):
     """The q2tp ladder: (lost [rows, 2], tab [rows, 32]) with TAB[0] = 0."""
     lib = load()
     rows, n = W.shape
-    lost = torch.empty(rows, 2, dtype=torch.float32, device=W.device)
-    tab = torch.empty(rows, 32, dtype=torch.float32, device=W.device)
-    st = lib.gptq_ladder_q2(_dev(W, torch.float32, "W"), _dev(dead, torch.uint8, "dead"), rows, n,
+    dev = W.device
+    with _on(stream, dev):
+        lost = torch.empty(rows, 2, dtype=torch.float32, device=dev)
+        tab = torch.empty(rows, 32, dtype=torch.float32, device=dev)
+    st = lib.gptq_ladder_q2(_dev(W, torch.float32, "W", align=16),
+                            _dev(dead, torch.uint8, "dead", (n,), device=dev), rows, n,
                             _dev(lost, torch.float32, "lost"), _dev(tab, torch.float32, "tab"),
                             _stream(stream))
     if st != GPTQ_OK:
@@ -285,20 +341,22 @@ def gptq_sweep_q2(W, U, hdiag, dead, tab, want_E=False, workspace=None, stream=N
     lib = load()
     rows, n = W.shape
     dev = W.device
-    plane = torch.empty(rows, n // 4, dtype=torch.uint8, device=dev)
-    rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
-    scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
-    E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
-    if workspace is None:
-        workspace = torch.empty(lib.gptq_sweep_workspace_size(rows, n), dtype=torch.uint8,
-                                device=dev)
-    st = lib.gptq_sweep_q2(_dev(W, torch.float32, "W"), _dev(U, torch.float32, "U"),
-                           _dev(hdiag, torch.float32, "hdiag"), _dev(dead, torch.uint8, "dead"),
-                           _dev(tab, torch.float32, "tab"), rows, n,
+    need = int(lib.gptq_sweep_workspace_size(rows, n))
+    with _on(stream, dev):
+        plane = torch.empty(rows, n // 4, dtype=torch.uint8, device=dev)
+        rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+        scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+        E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
+        workspace = _workspace(workspace, need, dev)
+    st = lib.gptq_sweep_q2(_dev(W, torch.float32, "W", align=16),
+                           _dev(U, torch.float32, "U", (n, n), 16, dev),
+                           _dev(hdiag, torch.float32, "hdiag", (n,), device=dev),
+                           _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                           _dev(tab, torch.float32, "tab", (rows, 32), 16, dev), rows, n,
                            _dev(plane, torch.uint8, "plane"), _dev(rung, torch.uint8, "rung"),
                            _dev(scale, torch.float32, "scale"),
                            None if E is None else _dev(E, torch.float32, "E"),
-                           _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                            _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_sweep_q2")
@@ -313,11 +371,13 @@ def gptq_act_order_perm(H, stream=None):
     """(perm i32 [n], dead u8 [n]) of act-order GPTQ from H's diagonal."""
     lib = load()
     n = H.shape[0]
-    perm = torch.empty(n, dtype=torch.int32, device=H.device)
-    dead = torch.empty(n, dtype=torch.uint8, device=H.device)
-    if H.stride(1) != 1:
-        raise ValueError("H must be row-major")
-    st = lib.gptq_act_order_perm(ctypes.c_void_p(H.data_ptr()), n, H.stride(0),
+    dev = H.device
+    if H.dim() != 2 or H.shape[1] != n or H.stride(1) != 1:
+        raise ValueError("H must be a row-major [n, n] matrix")
+    with _on(stream, dev):
+        perm = torch.empty(n, dtype=torch.int32, device=dev)
+        dead = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = lib.gptq_act_order_perm(_dev_rows(H, torch.float32, "H"), n, H.stride(0),
                                  _dev(perm, torch.int32, "perm"), _dev(dead, torch.uint8, "dead"),
                                  _stream(stream))
     if st != GPTQ_OK:
@@ -329,10 +389,14 @@ def gptq_permute_hessian(H, perm, stream=None):
     """H[perm][perm] (f32 [n, n], full symmetric) from H's upper triangle."""
     lib = load()
     n = H.shape[0]
-    Hp = torch.empty(n, n, dtype=torch.float32, device=H.device)
-    st = lib.gptq_permute_hessian(ctypes.c_void_p(H.data_ptr()), n, H.stride(0),
-                                  _dev(perm, torch.int32, "perm"), _dev(Hp, torch.float32, "Hp"),
-                                  _stream(stream))
+    dev = H.device
+    if H.dim() != 2 or H.shape[1] != n or H.stride(1) != 1:
+        raise ValueError("H must be a row-major [n, n] matrix")
+    with _on(stream, dev):
+        Hp = torch.empty(n, n, dtype=torch.float32, device=dev)
+    st = lib.gptq_permute_hessian(_dev_rows(H, torch.float32, "H"), n, H.stride(0),
+                                  _dev(perm, torch.int32, "perm", (n,), device=dev),
+                                  _dev(Hp, torch.float32, "Hp"), _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_permute_hessian")
     return Hp
@@ -343,20 +407,23 @@ def gptq_sweep_act_order(W, U, dead, perm, tab, lost, want_E=False, workspace=No
     lib = load()
     rows, n = W.shape
     dev = W.device
-    nib = torch.empty(rows, n // 2, dtype=torch.uint8, device=dev)
-    rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
-    scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
-    E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
-    if workspace is None:
-        workspace = torch.empty(lib.gptq_sweep_act_order_workspace_size(rows, n),
-                                dtype=torch.uint8, device=dev)
-    st = lib.gptq_sweep_act_order(_dev(W, torch.float32, "W"), _dev(U, torch.float32, "U"),
-                                  _dev(dead, torch.uint8, "dead"), _dev(perm, torch.int32, "perm"),
-                                  _dev(tab, torch.float32, "tab"), _dev(lost, torch.float32, "lost"),
+    need = int(lib.gptq_sweep_act_order_workspace_size(rows, n))
+    with _on(stream, dev):
+        nib = torch.empty(rows, n // 2, dtype=torch.uint8, device=dev)
+        rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+        scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+        E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
+        workspace = _workspace(workspace, need, dev)
+    st = lib.gptq_sweep_act_order(_dev(W, torch.float32, "W", align=16),
+                                  _dev(U, torch.float32, "U", (n, n), 16, dev),
+                                  _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                                  _dev(perm, torch.int32, "perm", (n,), device=dev),
+                                  _dev(tab, torch.float32, "tab", (rows, 32), 16, dev),
+                                  _dev(lost, torch.float32, "lost", (rows, 2), 8, dev),
                                   rows, n, _dev(nib, torch.uint8, "nib"),
                                   _dev(rung, torch.uint8, "rung"), _dev(scale, torch.float32, "scale"),
                                   None if E is None else _dev(E, torch.float32, "E"),
-                                  _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                  ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                   _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_sweep_act_order")
@@ -427,6 +494,6 @@ def check_tile_order(M: int, N: int, lower: bool) -> int:
 __all__ = ["check_mode", "check_message", "check_selftest", "check_tile_order", "gptq_gram_add", "gptq_debias",
            "gptq_act_order_perm", "gptq_permute_hessian", "gptq_sweep_act_order",
            "sweep_act_order_workspace_size", "gptq_ladder_q2", "gptq_sweep_q2",
-           "debias_workspace_size", "gptq_fold", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
+           "debias_workspace_size", "gptq_fold", "FOLD_PRECISION", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
            "profile_collect", "LIB_PATH"]

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
-SOURCES = ["fold.hip", "sweep.hip", "gram.hip", "debias.hip", "act_order.hip", "api.hip",
+SOURCES = ["fold.hip", "fold64.hip", "sweep.hip", "gram.hip", "debias.hip", "act_order.hip", "api.hip",
            "check.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

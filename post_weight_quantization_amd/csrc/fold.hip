@@ -24,24 +24,17 @@
 // panel) runs on the caller's stream, and the bulk runs on a helper stream, overlapping the
 // serial diag / panel chain of the next step.
 #include <math.h>
+#include <string.h>
 
 #include <utility>
 
 #include <algorithm>
 
 #include "common.hpp"
+#include "fold.hpp"
 #include "gemm_mfma.hpp"
 
 namespace gptq {
-
-constexpr int NB = 128;
-
-struct FoldState {
-    double base;
-    unsigned flag;
-    int n_dead;
-    double pad[6];
-};
 
 // Diagonal, dead mask, mean of the diagonal with dead channels counted as 1 (f64, fixed
 // reduction order).
@@ -87,7 +80,10 @@ __global__ void fold_scale_kernel(const float* __restrict__ hdiag, const uint8_t
                                   FoldState* st, double lam, int64_t n, int64_t np,
                                   float* __restrict__ dinv) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i == 0) __atomic_store_n(&st->flag, 0u, __ATOMIC_RELAXED);
+    if (i == 0) {
+        __atomic_store_n(&st->flag, 0u, __ATOMIC_RELAXED);
+        __atomic_store_n(&st->minp32, 0x7F800000u, __ATOMIC_RELAXED);  // +inf
+    }
     if (i >= np) return;
     if (i >= n) {
         dinv[i] = 1.0f;
@@ -198,8 +194,9 @@ __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict
 //           32 x 32 x 32 product on v_mfma_f32_32x32x2_f32;
 // then the off-diagonal blocks of L^-1 by block forward substitution down each block column,
 //   M_IJ = -T_I sum_{J <= Q < I} L_IQ M_QJ   (waves 0..2 take block columns 0..2).
-// A pivot that is not above its own f32 rounding bound (in particular one that is not > 0, or
-// NaN) sets the flag and is replaced by 1.
+// A pivot that is not > 0 (or NaN) sets flag bit 0 and is replaced by 1; a positive pivot at or
+// below tau (the accuracy floor of the "auto" precision, 0 otherwise) sets flag bit 1.  The
+// smallest accepted pivot goes to *minp.
 constexpr int DLD = NB + 1;  // row stride of the block in LDS (odd: column reads spread banks)
 constexpr int SLD = 33;      // row stride of 32 x 32 blocks in LDS
 
@@ -242,14 +239,18 @@ __device__ __forceinline__ int mcol() { return threadIdx.x & 31; }
 // count and x[] stays in registers; the broadcasts go four at a time into separate scalar
 // registers.  Each step's updates are pinned in place so the compiler does not defer them.
 template <int C>
-__device__ __forceinline__ void leaf_step(float (&x)[32], float tau0, int& nbad) {
+__device__ __forceinline__ void leaf_step(float (&x)[32], float tau, int& nsmall, int& nfail,
+                                          float& pmin) {
     float pv = lane_bcast(x[C], C);
-    const float tau = tau0 + (float)C * 5.9604645e-8f;
-    const bool b = !(pv > tau);
-    nbad += b ? 1 : 0;
-    asm volatile("" : "+v"(nbad));
-    pv = b ? 1.0f : pv;
-    x[C] *= __builtin_amdgcn_rsqf(pv);  // pv is a normal float
+    const bool fail = !(pv > 0.0f);  // not positive, or NaN: the attempt fails
+    const bool small = !(pv > tau);  // at or below the accuracy floor (tau = 0: same as fail)
+    nsmall += small ? 1 : 0;
+    nfail += fail ? 1 : 0;
+    pmin = fail ? pmin : fminf(pmin, pv);
+    asm volatile("" : "+v"(nsmall), "+v"(nfail), "+v"(pmin));
+    pv = fail ? 1.0f : pv;
+    // rsq needs a normal input; a positive subnormal pivot takes the IEEE route.
+    x[C] *= (pv >= 1.17549435e-38f) ? __builtin_amdgcn_rsqf(pv) : 1.0f / sqrtf(pv);
 #pragma unroll
     for (int s0 = (C + 1) & ~3; s0 < 32; s0 += 4) {
         float L[4];
@@ -265,14 +266,14 @@ __device__ __forceinline__ void leaf_step(float (&x)[32], float tau0, int& nbad)
 }
 
 template <int... C>
-__device__ __forceinline__ void leaf_steps(float (&x)[32], float tau0, int& nbad,
-                                           std::integer_sequence<int, C...>) {
-    (leaf_step<C>(x, tau0, nbad), ...);
+__device__ __forceinline__ void leaf_steps(float (&x)[32], float tau, int& nsmall, int& nfail,
+                                           float& pmin, std::integer_sequence<int, C...>) {
+    (leaf_step<C>(x, tau, nsmall, nfail, pmin), ...);
 }
 
 __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, float* __restrict__ X,
                                                         float* __restrict__ MI, int64_t np, int k,
-                                                        unsigned* flag) {
+                                                        unsigned* flag, unsigned* minp, float tau) {
     if (__atomic_load_n(flag, __ATOMIC_RELAXED)) return;
     // 81 KB of LDS, so that the kernel fits on a CU beside one GEMM workgroup.  The off-diagonal
     // 32-blocks M_IJ (I > J) of L^-1 live in the unused upper triangle of Ls, at block (J, I).
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
         }
     }
     __syncthreads();
-    bool bad = false;
+    bool small = false, fail = false;
+    float pmin_all = INFINITY;
     for (int p = 0; p < 4; ++p) {
         const int c0 = 32 * p;
         if (wave == 0) {
@@ -316,12 +318,9 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
                 const float av = Ls[(c0 + row) * DLD + c0 + c];
                 x[c] = tpart ? ((c == row) ? 1.0f : 0.0f) : av;
             }
-            // Pivot test at f32 resolution: the computed Schur complement of a unit-diagonal
-            // matrix is exact only up to (i + 1) 2^-24 for pivot index i, so a pivot at or below
-            // that bound is not known to be positive.
-            const float tau0 = (float)(int)(kb + c0 + 1) * 5.9604645e-8f;
-            int nbad = 0;
-            leaf_steps(x, tau0, nbad, std::make_integer_sequence<int, 32>{});
+            int nsmall = 0, nfail = 0;
+            float pmin = INFINITY;
+            leaf_steps(x, tau, nsmall, nfail, pmin, std::make_integer_sequence<int, 32>{});
             if (!tpart) {
 #pragma unroll
                 for (int c = 0; c < 32; ++c) Ls[(c0 + row) * DLD + c0 + c] = (c <= row) ? x[c] : 0.0f;
@@ -329,7 +328,9 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
 #pragma unroll
                 for (int c = 0; c < 32; ++c) Ts[p][c * SLD + row] = x[c];
             }
-            bad = bad || nbad != 0;
+            small = small || nsmall != 0;
+            fail = fail || nfail != 0;
+            pmin_all = fminf(pmin_all, pmin);
         }
         __syncthreads();
         // Panel: rows below, L_rb = A_rb T_p^T.
@@ -383,7 +384,11 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
-    if (wave == 0 && lane == 0 && bad) atomicOr(flag, 1u);
+    if (wave == 0 && lane == 0) {
+        if (fail) atomicOr(flag, 1u);
+        else if (small) atomicOr(flag, 2u);
+        atomicMin(minp, __float_as_uint(pmin_all));
+    }
     __syncthreads();
     // Output: MI_k as float4 rows (zeros above the diagonal).  Nothing reads L's diagonal block
     // after this kernel (the panel solve multiplies by MI_k), so it is not stored; the inverse's
@@ -455,31 +460,6 @@ __global__ __launch_bounds__(256) void fold_identity_kernel(float* __restrict__ 
     }
 }
 
-// Outer panel width (columns per bulk trailing update, its K) for a padded size n_p.
-static int64_t outer_width(int64_t np) { return np >= 2048 ? 4 * NB : (np >= 512 ? 2 * NB : NB); }
-
-struct FoldLayout {
-    int64_t np, nbk, nb2;
-    size_t off_state, off_dinv, off_mi, off_t, off_xt, off_a, off_x, total;
-};
-
-static FoldLayout fold_layout(int64_t n) {
-    FoldLayout L{};
-    L.np = round_up(n, NB);
-    L.nbk = L.np / NB;
-    L.nb2 = outer_width(L.np);
-    size_t o = 0;
-    L.off_state = o; o += align256(sizeof(FoldState));
-    L.off_dinv = o; o += align256(sizeof(float) * (size_t)L.np);
-    L.off_mi = o; o += align256(sizeof(float) * (size_t)(L.nbk * NB * NB));
-    L.off_t = o; o += align256(sizeof(float) * (size_t)(NB * L.nb2));
-    L.off_xt = o; o += align256(sizeof(float) * (size_t)(L.nb2 * L.np));
-    L.off_a = o; o += align256(sizeof(float) * (size_t)(L.np * L.np));
-    L.off_x = o; o += align256(sizeof(float) * (size_t)(L.np * L.np));
-    L.total = o;
-    return L;
-}
-
 // The w x w diagonal block of X at kb before its block forward substitution: the diagonal
 // 128-blocks are the inverses MI of L's diagonal blocks, the blocks above are 0 (the blocks
 // below are written by the substitution).
@@ -509,18 +489,38 @@ __global__ __launch_bounds__(256) void fold_copy_rows_kernel(const float* __rest
 
 using namespace gptq;
 
+// The "auto" precision's accuracy floor on the f32 pivots.  The pivots are those of the
+// unit-diagonal equilibrated matrix; the f32 factor's error in U D grows as u32 / (smallest
+// pivot), so an attempt whose smallest pivot is at or below this floor is repeated in f64.
+static constexpr float kF32PivotFloor = 1.0e-2f;
+
+extern "C" size_t gptq_fold_workspace_size_ex(int64_t n, int precision) {
+    if (n <= 0 || n > ((int64_t)1 << 20)) return 0;
+    if (precision != GPTQ_FOLD_AUTO && precision != GPTQ_FOLD_F32 && precision != GPTQ_FOLD_F64) return 0;
+    const FoldLayout L = fold_layout(n);
+    return precision == GPTQ_FOLD_F32 ? L.total_f32 : L.total;
+}
+
 extern "C" size_t gptq_fold_workspace_size(int64_t n) {
-    if (n <= 0) return 0;
-    return fold_layout(n).total;
+    return gptq_fold_workspace_size_ex(n, GPTQ_FOLD_AUTO);
 }
 
 extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, float* U,
                          float* hdiag, uint8_t* dead, void* workspace, size_t workspace_bytes,
                          void* stream, gptq_fold_report* report) {
+    return gptq_fold_ex(H, n, ldh, lambda, GPTQ_FOLD_AUTO, U, hdiag, dead, workspace,
+                        workspace_bytes, stream, report);
+}
+
+extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambda, int precision,
+                            float* U, float* hdiag, uint8_t* dead, void* workspace,
+                            size_t workspace_bytes, void* stream, gptq_fold_report* report) {
     if (n <= 0 || ldh < n || !H || !U || !hdiag || !dead || !workspace) return GPTQ_EINVAL;
     if (n > (int64_t)1 << 20) return GPTQ_EINVAL;
+    if (precision != GPTQ_FOLD_AUTO && precision != GPTQ_FOLD_F32 && precision != GPTQ_FOLD_F64)
+        return GPTQ_EINVAL;
     const FoldLayout L = fold_layout(n);
-    if (workspace_bytes < L.total) return GPTQ_EWORKSPACE;
+    if (workspace_bytes < (precision == GPTQ_FOLD_F32 ? L.total_f32 : L.total)) return GPTQ_EWORKSPACE;
     CheckScope check;
     check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
     check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
@@ -563,8 +563,15 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
     int attempts = 0;
     FoldState host{};
     bool degenerate = false;
+    // f64 from the start, or once an f32 attempt of the "auto" precision met a pivot at or below
+    // the floor (then for the rest of the damping schedule).
+    bool use64 = precision == GPTQ_FOLD_F64;
+    const float tau = precision == GPTQ_FOLD_AUTO ? kF32PivotFloor : 0.0f;
     for (;;) {
         ++attempts;
+        if (use64) {
+            FOLD_OK(fold64_attempt(H, n, ldh, hdiag, dead, state, lam, ws, L, st));
+        } else {
         {
             ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 4.0 * (double)n * n + 4.0 * (double)np * np / 2);
             GPTQ_LAUNCH(st, "fold_scale",
@@ -609,7 +616,8 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
                 {
                     ProfScope ps(FAM_FOLD_DIAG, st, 2.0 * NB * NB * NB / 3.0, 0.0);
                     GPTQ_LAUNCH(st, "fold_diag",
-                                (fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)(cb / NB), &state->flag)),
+                                (fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)(cb / NB), &state->flag,
+                                                                     &state->minp32, tau)),
                                 rd(A + cb * np + cb, np, NB, NB), wr(MI + (cb / NB) * NB * NB, NB, NB, NB),
                                 st_rw);
                 }
@@ -752,6 +760,7 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
         FOLD_OK(stream_wait(st, hp.ev_c));
         FOLD_OK(ev_record(hp.ev_b, ts));
         FOLD_OK(stream_wait(st, hp.ev_b));
+        }
         if (dry_run()) {
             host_sync_record(st);
             host.flag = 0u;
@@ -762,6 +771,10 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
             GPTQ_HIP(hipStreamSynchronize(st));
         }
         if (host.flag == 0u) break;
+        if (!use64 && precision == GPTQ_FOLD_AUTO) {
+            use64 = true;  // the same damping again, in f64
+            continue;
+        }
         lam = (lam == 0.0) ? 1e-4 : lam * 10.0;
         if (lam > 10.0) {
             degenerate = true;
@@ -772,6 +785,9 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
     const dim3 g((unsigned)((n + 31) / 32), (unsigned)((n + 31) / 32));
     if (degenerate) {
         GPTQ_LAUNCH(st, "fold_identity", (fold_identity_kernel<<<g, 256, 0, st>>>(U, n)), wr(U, n, n, n));
+    } else if (use64) {
+        const int rc = fold64_make_u(U, n, ws, L, st);
+        if (rc != GPTQ_OK) return rc;
     } else {
         ProfScope ps(FAM_FOLD_MAKEU, st, 0.0, 4.0 * (double)n * n);
         const dim3 g64((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64));
@@ -793,7 +809,18 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
         report->attempts = attempts;
         report->n_dead = host.n_dead;
         report->degenerate = degenerate ? 1 : 0;
-        report->reserved = 0;
+        report->precision = use64 ? 64 : 32;
+        double pm = 0.0;
+        if (!degenerate) {
+            if (use64) {
+                memcpy(&pm, &host.minp64, sizeof(pm));
+            } else {
+                float p32;
+                memcpy(&p32, &host.minp32, sizeof(p32));
+                pm = p32;
+            }
+        }
+        report->min_pivot = pm;
     }
     return degenerate ? GPTQ_DEGENERATE : GPTQ_OK;
 }

@@ -80,7 +80,9 @@ __host__ __device__ __forceinline__ void tri_of(int u, int& r, int& c) {
     c = u - r * (r + 1) / 2;
 }
 
-__host__ __device__ __forceinline__ void tile_of(const GemmProblem& P, int t, int& tm, int& tn) {
+// PROB is any problem type with the fields lower, tiles_n and ntiles (the f32 and f64 GEMMs).
+template <class PROB>
+__host__ __device__ __forceinline__ void tile_of(const PROB& P, int t, int& tm, int& tn) {
     if (P.lower) {
         const int T = P.tiles_n;
         const int RB = (T + GT_S - 1) / GT_S;

@@ -123,10 +123,16 @@ def test_identity_hessian_closed_form_and_rtn(gpu):
 
 def test_retry_and_degenerate_cases(gpu):
     say("retry cases")
-    # [[1,1],[1,1]]: singular at 0; f32 needs at least the f64 damping.
+    # [[1,1],[1,1]]: singular at 0.  The f32 attempt fails, the same damping fails in f64, and
+    # 1e-4 factors in f64: the damping the f64 host fold reaches.
     U, hd, dd, rep = gpu.gptq_fold(_dev(np.array([[1, 1], [1, 1]], np.float32)), 0.0)
     orc = oracle.fold(np.array([[1, 1], [1, 1]], np.float32), 0.0)
-    assert rep["status"] == 0 and rep["lambda_used"] >= orc["lam"] and rep["attempts"] >= 2
+    assert orc["lam"] == 1e-4
+    assert rep["status"] == 0 and rep["lambda_used"] == orc["lam"], rep
+    assert rep["attempts"] == 3 and rep["precision"] == 64, rep
+    # The pages' f32 device rule alone reaches the same damping here.
+    U, hd, dd, rep = gpu.gptq_fold(_dev(np.array([[1, 1], [1, 1]], np.float32)), 0.0, precision="f32")
+    assert rep["status"] == 0 and rep["lambda_used"] == 1e-4 and rep["precision"] == 32, rep
     # [[1,20],[20,1]] cannot be damped into a factor below 10: U = I, DEGENERATE.
     U, hd, dd, rep = gpu.gptq_fold(_dev(np.array([[1, 20], [20, 1]], np.float32)), 0.01)
     assert rep["status"] == 4 and rep["degenerate"] == 1
@@ -149,6 +155,26 @@ def test_retry_and_degenerate_cases(gpu):
     assert rep["n_dead"] == 3
 
 
+@pytest.mark.parametrize("precision", ["auto", "f64"])
+def test_fold_reads_only_the_upper_triangle(gpu, precision):
+    """Garbage below H's diagonal (NaN, inf, huge values) changes nothing: U is bit-identical to
+    the fold of the symmetric matrix, in both arithmetics."""
+    say(f"upper triangle only ({precision})")
+    rng = np.random.default_rng(5)
+    n = 300
+    X = rng.standard_normal((n, 500)) * np.exp(rng.standard_normal(n))[:, None]
+    H = (X @ X.T).astype(np.float32)
+    Hg = H.copy()
+    il = np.tril_indices(n, -1)
+    junk = rng.choice(np.array([np.nan, np.inf, -np.inf, 1e30, -7.0], np.float32), size=il[0].size)
+    Hg[il] = junk
+    U0, hd0, dd0, r0 = gpu.gptq_fold(_dev(H), 0.01, precision=precision)
+    U1, hd1, dd1, r1 = gpu.gptq_fold(_dev(Hg), 0.01, precision=precision)
+    torch.cuda.synchronize()
+    assert r0["status"] == r1["status"] == 0
+    assert torch.equal(U0, U1) and torch.equal(hd0, hd1) and torch.equal(dd0, dd1)
+
+
 def test_invalid_arguments_write_nothing(gpu):
     say("invalid arguments")
     lib = gpu.load()
@@ -158,10 +184,18 @@ def test_invalid_arguments_write_nothing(gpu):
     hd = torch.zeros(64, device="cuda")
     dd = torch.zeros(64, dtype=torch.uint8, device="cuda")
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
-    with pytest.raises(gpu.GptqError) as e:
+    with pytest.raises(ValueError):  # the binding checks the size first
         gpu.gptq_fold(H, 0.01, workspace=ws, out=(U, hd, dd))
-    assert e.value.status == 2
+    import ctypes
+    P = ctypes.c_void_p
+    rep = gpu.FoldReport()
+    st = lib.gptq_fold(P(H.data_ptr()), 64, 64, 0.01, P(U.data_ptr()), P(hd.data_ptr()),
+                       P(dd.data_ptr()), P(ws.data_ptr()), ws.numel(), None, ctypes.byref(rep))
+    torch.cuda.synchronize()
+    assert st == gpu.GPTQ_EWORKSPACE
     assert torch.all(U == 7.0)
+    with pytest.raises(ValueError):  # U of the wrong shape never reaches the library
+        gpu.gptq_fold(H, 0.01, out=(torch.empty(64, 63, device="cuda"), hd, dd))
     W = torch.zeros(4, 48, device="cuda")  # n % 32 != 0
     with pytest.raises(gpu.GptqError):
         gpu.gptq_ladder(W, torch.zeros(48, dtype=torch.uint8, device="cuda"))
@@ -184,7 +218,7 @@ def test_repeat_runs_are_bitwise_identical(gpu):
 
 def test_profile_counts_the_fold_bulk_updates(gpu):
     """The event timing behind the benchmark's roofline: at n = 2080 (padded to 2176, outer
-    panels of 512) the fold's bulk family is the Cholesky's trailing update beyond the next panel
+    panels of 512) the f32 fold's bulk family is the Cholesky's trailing update beyond the next panel
     (3 launches) and the inverse's update of the rows below each panel (4 launches), with the
     flops of their definitions; every launch is timed."""
     n, lam = 2080, 0.01
@@ -192,12 +226,12 @@ def test_profile_counts_the_fold_bulk_updates(gpu):
     X = rng.standard_normal((n, n + 64))
     H = (X @ X.T).astype(np.float32)
     Hd = _dev(H)
-    gpu.gptq_fold(Hd, lam)  # warm
+    gpu.gptq_fold(Hd, lam, precision="f32")  # warm
     torch.cuda.synchronize()
     gpu.profile_collect()
     gpu.profile_enable(["fold_update"])
     try:
-        gpu.gptq_fold(Hd, lam)
+        gpu.gptq_fold(Hd, lam, precision="f32")
         torch.cuda.synchronize()
     finally:
         gpu.profile_enable([])

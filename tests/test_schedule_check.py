@@ -51,14 +51,36 @@ def test_checker_selftest(lib):
 
 
 @pytest.mark.parametrize("n", [8, 96, 128, 256, 600, 1024, 2048, 2080, 4096, 8192, 17408])
-def test_fold_schedule(lib, n):
+@pytest.mark.parametrize("precision", ["auto", "f32", "f64"])
+def test_fold_schedule(lib, n, precision):
+    """Each precision's schedule with the workspace its size query asks for (the f32 one is
+    smaller: the f64 one overlays the f32 matrices and adds an f64 inverse)."""
     H, U, hd, dead, ws = addrs(5)
-    need = lib.gptq_fold_workspace_size(n)
+    prec = pwq.FOLD_PRECISION[precision]
+    need = lib.gptq_fold_workspace_size_ex(n, prec)
     rep = pwq.FoldReport()
     with pwq.check_mode():
-        st = lib.gptq_fold(H, n, n, 0.01, U, hd, dead, ws, need, None, ctypes.byref(rep))
+        st = lib.gptq_fold_ex(H, n, n, 0.01, prec, U, hd, dead, ws, need, None, ctypes.byref(rep))
     assert st == GPTQ_OK, pwq.check_message()
     assert pwq.check_message() == ""
+    assert rep.precision == (64 if precision == "f64" else 32)
+    if precision == "f32":
+        assert need < lib.gptq_fold_workspace_size(n)
+    else:
+        assert need == lib.gptq_fold_workspace_size(n)
+        with pwq.check_mode():
+            st = lib.gptq_fold_ex(H, n, n, 0.01, prec, U, hd, dead, ws,
+                                  lib.gptq_fold_workspace_size_ex(n, 1), None, ctypes.byref(rep))
+        assert st == pwq.GPTQ_EWORKSPACE
+
+
+def test_fold_rejects_unknown_precision(lib):
+    H, U, hd, dead, ws = addrs(5)
+    rep = pwq.FoldReport()
+    assert lib.gptq_fold_workspace_size_ex(64, 3) == 0
+    with pwq.check_mode():
+        st = lib.gptq_fold_ex(H, 64, 64, 0.01, 3, U, hd, dead, ws, 1 << 30, None, ctypes.byref(rep))
+    assert st == pwq.GPTQ_EINVAL
 
 
 def test_fold_schedule_padded_rows_of_h(lib):
