@@ -24,6 +24,8 @@
  *     (default priority, two per concurrent call) that wait on `stream` and are joined back
  *     into it before the call returns, so `stream` orders everything the call does.
  *   - Return value: a GPTQ_* status.  On GPTQ_EINVAL or GPTQ_EWORKSPACE nothing is written.
+ *   - Workspaces and the matrices a call reads or writes in rows (W, U, E) must be 16-byte
+ *     aligned (GPTQ_EINVAL otherwise); device allocations are.
  *   - Calls on different streams may run concurrently if their buffers are disjoint.
  */
 #ifndef GPTQ_MI355X_H
@@ -161,6 +163,27 @@ int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t
                const float* tab, const float* lost, int64_t rows, int64_t n, uint8_t* nib,
                uint8_t* rung, float* scale, float* E, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/* Bytes of device workspace gptq_sweep_inplace needs without E: two rows x 512 f32 panel
+ * buffers of residuals.  (With E it needs none.) */
+size_t gptq_sweep_inplace_workspace_size(int64_t rows, int64_t n);
+
+/*
+ * gptq_sweep_inplace -- gptq_sweep with W as its own working copy: the same codes, rungs,
+ * scales and residuals, bit for bit, without the rows x n copy (356 MB at 5120 x 17408).
+ *
+ *   W      [rows, n] f32, device, IN/OUT: read as gptq_sweep reads it, then overwritten by the
+ *          sweep's partially corrected weights (no meaning to the caller; keep a copy of W if it
+ *          is still needed).
+ *   E      [rows, n] f32 out or NULL.  With E the residuals are written straight into it and
+ *          workspace may be NULL (workspace_bytes 0); without E the workspace holds them,
+ *          at least gptq_sweep_inplace_workspace_size(rows, n) bytes.
+ *   Every other argument as gptq_sweep.  Asynchronous.
+ */
+int gptq_sweep_inplace(float* W, const float* U, const float* hdiag, const uint8_t* dead,
+                       const float* tab, const float* lost, int64_t rows, int64_t n, uint8_t* nib,
+                       uint8_t* rung, float* scale, float* E, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * gptq_gram_add -- accumulate one batch of layer inputs into the device Hessian.

@@ -69,6 +69,10 @@ def load():
     lib.gptq_sweep_workspace_size.restype = sz
     lib.gptq_sweep.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
     lib.gptq_sweep.restype = ctypes.c_int
+    lib.gptq_sweep_inplace_workspace_size.argtypes = [i64, i64]
+    lib.gptq_sweep_inplace_workspace_size.restype = sz
+    lib.gptq_sweep_inplace.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
+    lib.gptq_sweep_inplace.restype = ctypes.c_int
     lib.gptq_gram_add.argtypes = [P, i64, i64, P, i64, i64, P]
     lib.gptq_gram_add.restype = ctypes.c_int
     lib.gptq_debias_workspace_size.argtypes = [i64, i64]
@@ -265,6 +269,42 @@ def gptq_sweep(W, U, hdiag, dead, tab, lost, want_E=False, workspace=None, strea
                         _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_sweep")
+    return nib, rung, scale, E
+
+
+def gptq_sweep_inplace(W, U, hdiag, dead, tab, lost, want_E=False, workspace=None, stream=None,
+                       out=None):
+    """The q4tp sweep with W as its own working copy (W is overwritten).  Returns (nib, rung,
+    scale, E or None), the same as :func:`gptq_sweep` on the original W."""
+    lib = load()
+    rows, n = W.shape
+    dev = W.device
+    with _on(stream, dev):
+        if out is None:
+            nib = torch.empty(rows, n // 2, dtype=torch.uint8, device=dev)
+            rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+            scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+            E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
+        else:
+            nib, rung, scale, E = out
+        need = 0 if E is not None else int(lib.gptq_sweep_inplace_workspace_size(rows, n))
+        if need:
+            workspace = _workspace(workspace, need, dev)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if (need and workspace is not None) else None
+    st = lib.gptq_sweep_inplace(_dev(W, torch.float32, "W", align=16),
+                                _dev(U, torch.float32, "U", (n, n), 16, dev),
+                                _dev(hdiag, torch.float32, "hdiag", (n,), device=dev),
+                                _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                                _dev(tab, torch.float32, "tab", (rows, 32), 16, dev),
+                                _dev(lost, torch.float32, "lost", (rows, 2), 8, dev),
+                                rows, n, _dev(nib, torch.uint8, "nib", (rows, n // 2), device=dev),
+                                _dev(rung, torch.uint8, "rung", (rows, n // 32), device=dev),
+                                _dev(scale, torch.float32, "scale", (rows, n // 32), device=dev),
+                                None if E is None else _dev(E, torch.float32, "E", (rows, n), 16, dev),
+                                ws_ptr, workspace.numel() if ws_ptr is not None else 0,
+                                _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_sweep_inplace")
     return nib, rung, scale, E
 
 
@@ -494,6 +534,6 @@ def check_tile_order(M: int, N: int, lower: bool) -> int:
 __all__ = ["check_mode", "check_message", "check_selftest", "check_tile_order", "gptq_gram_add", "gptq_debias",
            "gptq_act_order_perm", "gptq_permute_hessian", "gptq_sweep_act_order",
            "sweep_act_order_workspace_size", "gptq_ladder_q2", "gptq_sweep_q2",
-           "debias_workspace_size", "gptq_fold", "FOLD_PRECISION", "gptq_ladder", "gptq_sweep", "fold_workspace_size",
+           "debias_workspace_size", "gptq_fold", "FOLD_PRECISION", "gptq_ladder", "gptq_sweep", "gptq_sweep_inplace", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
            "profile_collect", "LIB_PATH"]

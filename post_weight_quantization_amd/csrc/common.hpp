@@ -53,6 +53,9 @@ struct ProfScope {
 };
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+// 16-byte alignment, which every pointer the kernels read or write as float4 / double2 needs
+// (NULL counts as aligned: optional outputs).
+inline bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace gptq

@@ -154,6 +154,7 @@ extern "C" int gptq_debias(const float* W, const float* H, int64_t ldh, const ui
         !lost || !scale || !workspace)
         return GPTQ_EINVAL;
     if (rows > ((int64_t)1 << 31) - 1 || n > ((int64_t)1 << 20)) return GPTQ_EINVAL;
+    if (!al16(W) || !al16(workspace)) return GPTQ_EINVAL;  // W and the workspace are read as float4
     size_t off_y = 0;
     if (workspace_bytes < debias_ws(rows, n, &off_y)) return GPTQ_EWORKSPACE;
     CheckScope check;

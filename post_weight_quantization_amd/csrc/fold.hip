@@ -519,6 +519,7 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
     if (n > (int64_t)1 << 20) return GPTQ_EINVAL;
     if (precision != GPTQ_FOLD_AUTO && precision != GPTQ_FOLD_F32 && precision != GPTQ_FOLD_F64)
         return GPTQ_EINVAL;
+    if (!al16(workspace)) return GPTQ_EINVAL;  // its matrices are read as float4 / double2
     const FoldLayout L = fold_layout(n);
     if (workspace_bytes < (precision == GPTQ_FOLD_F32 ? L.total_f32 : L.total)) return GPTQ_EWORKSPACE;
     CheckScope check;

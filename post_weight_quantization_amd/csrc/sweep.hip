@@ -540,7 +540,7 @@ using namespace gptq;
 extern "C" int gptq_ladder(const float* W, const uint8_t* dead, int64_t rows, int64_t n,
                            float* lost, float* tab, void* stream) {
     if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !dead || !lost || !tab) return GPTQ_EINVAL;
-    if (rows > ((int64_t)1 << 31) - 1) return GPTQ_EINVAL;
+    if (rows > ((int64_t)1 << 31) - 1 || !al16(W)) return GPTQ_EINVAL;  // rows read as float4
     CheckScope check;
     check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
     check_buffer(dead, (size_t)n, "dead");
@@ -734,17 +734,24 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
     return GPTQ_OK;
 }
 
-extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
+// Argument rules shared by the q4tp sweep entry points (GPTQ_EINVAL otherwise): sizes, the
+// required pointers, and 16-byte alignment of W, U and E (read and written as float4 / float2
+// rows; n % 32 == 0 keeps every row aligned).
+static bool sweep_args_ok(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
                           const float* tab, const float* lost, int64_t rows, int64_t n,
-                          uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          const uint8_t* nib, const uint8_t* rung, const float* scale,
+                          const float* E) {
     if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !hdiag || !dead || !tab || !lost ||
-        !nib || !rung || !scale || !workspace)
-        return GPTQ_EINVAL;
-    if (rows > ((int64_t)1 << 31) - 64 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
-    size_t off_e = 0;
-    if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
-    CheckScope check;
+        !nib || !rung || !scale)
+        return false;
+    if (rows > ((int64_t)1 << 31) - 64 || n > ((int64_t)1 << 24)) return false;
+    return al16(W) && al16(U) && al16(E);
+}
+
+static void sweep_check_buffers(const float* W, const float* U, const float* hdiag,
+                                const uint8_t* dead, const float* tab, const float* lost,
+                                int64_t rows, int64_t n, const uint8_t* nib, const uint8_t* rung,
+                                const float* scale, const float* E) {
     check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
     check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
     check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
@@ -755,9 +762,14 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     check_buffer(rung, (size_t)(rows * (n / 32)), "rung");
     check_buffer(scale, sizeof(float) * (size_t)(rows * (n / 32)), "scale");
     if (E) check_buffer(E, sizeof(float) * (size_t)(rows * n), "E");
-    check_buffer(workspace, workspace_bytes, "workspace");
+}
+
+static SweepRun q4_run(const float* first, float* Wc, const float* U, const float* hdiag,
+                       const uint8_t* dead, const float* tab, const float* lost, int64_t rows,
+                       int64_t n, uint8_t* nib, uint8_t* rung, float* scale, float* E,
+                       float* pan0, float* pan1) {
     SweepRun c{};
-    c.first = W;
+    c.first = first;
     c.U = U;
     c.hdiag = hdiag;
     c.dead = dead;
@@ -769,9 +781,63 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     c.rung = rung;
     c.scale = scale;
     c.E = E;
-    c.Wc = (float*)workspace;
-    c.Epan[0] = (float*)((char*)workspace + off_e);
-    c.Epan[1] = (float*)((char*)workspace + off_e + align256(sizeof(float) * (size_t)(rows * SOB)));
+    c.Wc = Wc;
+    c.Epan[0] = pan0;
+    c.Epan[1] = pan1;
+    return c;
+}
+
+extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
+                          const float* tab, const float* lost, int64_t rows, int64_t n,
+                          uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!sweep_args_ok(W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E) || !workspace ||
+        !al16(workspace))
+        return GPTQ_EINVAL;
+    size_t off_e = 0;
+    if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
+    CheckScope check;
+    sweep_check_buffers(W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E);
+    check_buffer(workspace, workspace_bytes, "workspace");
+    char* ws = (char*)workspace;
+    const SweepRun c = q4_run(W, (float*)ws, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale,
+                              E, (float*)(ws + off_e),
+                              (float*)(ws + off_e + align256(sizeof(float) * (size_t)(rows * SOB))));
+    const int rc = sweep_pipeline<0>(c, (hipStream_t)stream);
+    if (rc != GPTQ_OK) return rc;
+    return check.finish();
+}
+
+// In place: W is its own working copy, so the workspace holds only the two residual panels, and
+// nothing at all when the residuals go to E.
+static size_t sweep_panels_ws(int64_t rows) {
+    return 2 * align256(sizeof(float) * (size_t)(rows * SOB));
+}
+
+extern "C" size_t gptq_sweep_inplace_workspace_size(int64_t rows, int64_t n) {
+    if (rows <= 0 || n <= 0) return 0;
+    return sweep_panels_ws(rows);
+}
+
+extern "C" int gptq_sweep_inplace(float* W, const float* U, const float* hdiag,
+                                  const uint8_t* dead, const float* tab, const float* lost,
+                                  int64_t rows, int64_t n, uint8_t* nib, uint8_t* rung,
+                                  float* scale, float* E, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (!sweep_args_ok(W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E) ||
+        !al16(workspace) || (!E && !workspace))
+        return GPTQ_EINVAL;
+    if (!E && workspace_bytes < sweep_panels_ws(rows)) return GPTQ_EWORKSPACE;
+    CheckScope check;
+    sweep_check_buffers(W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E);
+    float* pan0 = nullptr;
+    float* pan1 = nullptr;
+    if (!E) {
+        check_buffer(workspace, workspace_bytes, "workspace");
+        pan0 = (float*)workspace;
+        pan1 = (float*)((char*)workspace + align256(sizeof(float) * (size_t)(rows * SOB)));
+    }
+    const SweepRun c = q4_run(W, W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E, pan0, pan1);
     const int rc = sweep_pipeline<0>(c, (hipStream_t)stream);
     if (rc != GPTQ_OK) return rc;
     return check.finish();
@@ -780,7 +846,7 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
 extern "C" int gptq_ladder_q2(const float* W, const uint8_t* dead, int64_t rows, int64_t n,
                               float* lost, float* tab, void* stream) {
     if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !dead || !lost || !tab) return GPTQ_EINVAL;
-    if (rows > ((int64_t)1 << 31) - 1) return GPTQ_EINVAL;
+    if (rows > ((int64_t)1 << 31) - 1 || !al16(W)) return GPTQ_EINVAL;  // rows read as float4
     CheckScope check;
     check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
     check_buffer(dead, (size_t)n, "dead");
@@ -805,6 +871,7 @@ extern "C" int gptq_sweep_q2(const float* W, const float* U, const float* hdiag,
         !rung || !scale || !workspace)
         return GPTQ_EINVAL;
     if (rows > ((int64_t)1 << 31) - 64 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
+    if (!al16(W) || !al16(U) || !al16(E) || !al16(workspace)) return GPTQ_EINVAL;
     size_t off_e = 0;
     if (workspace_bytes < sweep_ws(rows, n, &off_e)) return GPTQ_EWORKSPACE;
     CheckScope check;
@@ -910,6 +977,7 @@ extern "C" int gptq_sweep_act_order(const float* W, const float* U, const uint8_
         !nib || !rung || !scale || !workspace)
         return GPTQ_EINVAL;
     if (rows > 65535 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;  // rows index grid.y
+    if (!al16(U) || !al16(E) || !al16(workspace)) return GPTQ_EINVAL;
     size_t off_e = 0, off_sp = 0, off_codes = 0, off_inv = 0;
     if (workspace_bytes < act_ws(rows, n, &off_e, &off_sp, &off_codes, &off_inv))
         return GPTQ_EWORKSPACE;

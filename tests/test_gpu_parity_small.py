@@ -254,3 +254,70 @@ def test_profile_counts_the_fold_bulk_updates(gpu):
     tflops = fu["flops"] / (fu["ms"] * 1e-3) / 1e12
     say(f"fold_update at n={n}: {fu['launches']} launches, {fu['ms']:.3f} ms, {tflops:.1f} TFLOP/s")
     assert 0.0 < tflops < 157.3
+
+
+@pytest.mark.parametrize("n,rows,want_e", [(256, 512, False), (256, 512, True), (1184, 300, False),
+                                           (2080, 77, True)])
+def test_sweep_inplace_matches_sweep(gpu, n, rows, want_e):
+    """The in-place sweep gives gptq_sweep's codes, rungs, scales and residuals bit for bit
+    (several 512-column panels and ragged rows included)."""
+    say("sweep in place", n, rows, want_e)
+    rng = np.random.default_rng(n + rows)
+    X = rng.standard_normal((n, 2 * n)) * np.exp(rng.standard_normal(n))[:, None]
+    H = (X @ X.T).astype(np.float32)
+    W = (rng.standard_normal((rows, n)) * 0.02).astype(np.float32)
+    U, hd, dd, rep = gpu.gptq_fold(_dev(H), 0.01)
+    Wd = _dev(W)
+    lost, tab = gpu.gptq_ladder(Wd, dd)
+    a = gpu.gptq_sweep(Wd, U, hd, dd, tab, lost, want_E=want_e)
+    Wi = Wd.clone()
+    b = gpu.gptq_sweep_inplace(Wi, U, hd, dd, tab, lost, want_E=want_e)
+    torch.cuda.synchronize()
+    assert torch.equal(Wd, _dev(W))  # gptq_sweep leaves W alone
+    for x, y in zip(a, b):
+        if x is not None:
+            assert torch.equal(x, y)
+
+
+def test_misaligned_pointers_are_rejected(gpu):
+    """Pointers the kernels read or write as float4 rows must be 16-byte aligned: a W, U, E or
+    workspace four bytes off is refused with GPTQ_EINVAL before anything is written."""
+    import ctypes
+    lib = gpu.load()
+    P = ctypes.c_void_p
+    rows, n = 8, 64
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((n, 2 * n))
+    Hd = _dev((X @ X.T).astype(np.float32))
+    U, hd, dd, rep = gpu.gptq_fold(Hd, 0.01)
+    Wbuf = _dev(np.concatenate([[0.0], (rng.standard_normal(rows * n) * 0.02)]).astype(np.float32))
+    W_off = P(Wbuf.data_ptr() + 4)           # rows of W four bytes off
+    W_ok = Wbuf[1:].clone()
+    lost, tab = gpu.gptq_ladder(W_ok.view(rows, n), dd)
+    nib = torch.full((rows, n // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    rung = torch.full((rows, n // 32), 0xCD, dtype=torch.uint8, device="cuda")
+    scale = torch.full((rows, n // 32), 3.0, device="cuda")
+    ws = torch.empty(lib.gptq_sweep_workspace_size(rows, n) + 64, dtype=torch.uint8, device="cuda")
+    Ubuf = torch.empty(n * n + 4, device="cuda")
+    Ubuf[1:n * n + 1].copy_(U.flatten())
+    p = lambda t: P(t.data_ptr())
+    args = lambda w, u, wsp: (w, u, p(hd), p(dd), p(tab), p(lost), rows, n, p(nib), p(rung),
+                              p(scale), None, wsp, ws.numel() - 64, None)
+    assert lib.gptq_sweep(*args(W_off, p(U), p(ws))) == gpu.GPTQ_EINVAL
+    assert lib.gptq_sweep(*args(p(W_ok), P(Ubuf.data_ptr() + 4), p(ws))) == gpu.GPTQ_EINVAL
+    assert lib.gptq_sweep(*args(p(W_ok), p(U), P(ws.data_ptr() + 4))) == gpu.GPTQ_EINVAL
+    assert lib.gptq_sweep_inplace(*args(W_off, p(U), p(ws))) == gpu.GPTQ_EINVAL
+    assert lib.gptq_sweep_q2(W_off, p(U), p(hd), p(dd), p(tab), rows, n, p(nib), p(rung), p(scale),
+                             None, p(ws), ws.numel() - 64, None) == gpu.GPTQ_EINVAL
+    assert lib.gptq_ladder(W_off, p(dd), rows, n, p(lost), p(tab), None) == gpu.GPTQ_EINVAL
+    rep = gpu.FoldReport()
+    wsf = torch.empty(gpu.fold_workspace_size(n) + 64, dtype=torch.uint8, device="cuda")
+    Uo = torch.full((n, n), 7.0, device="cuda")
+    assert lib.gptq_fold(p(Hd), n, n, 0.01, p(Uo), p(hd), p(dd), P(wsf.data_ptr() + 4),
+                         wsf.numel() - 64, None, ctypes.byref(rep)) == gpu.GPTQ_EINVAL
+    torch.cuda.synchronize()
+    assert torch.all(nib == 0xAB) and torch.all(rung == 0xCD) and torch.all(scale == 3.0)
+    assert torch.all(Uo == 7.0)
+    # The same call with aligned pointers runs.
+    assert lib.gptq_sweep(*args(p(W_ok), p(U), p(ws))) == gpu.GPTQ_OK
+    torch.cuda.synchronize()

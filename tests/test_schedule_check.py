@@ -169,3 +169,18 @@ def test_q2_schedule(lib, rows, n, want_e):
         st = lib.gptq_sweep_q2(W, U, hd, dead, tab, rows, n, plane, rung, scale,
                                E if want_e else None, ws, need, None)
     assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(16, 32), (37, 96), (300, 1056), (4096, 4096), (5120, 17408)])
+@pytest.mark.parametrize("want_e", [False, True])
+def test_sweep_inplace_schedule(lib, rows, n, want_e):
+    """W is its own working copy: every launch stays inside W, the outputs and the panel
+    workspace (none with E), and the helper stream's updates never race the chain's."""
+    W, U, hd, dead, tab, lost, nib, rung, scale, E, ws = addrs(11)
+    need = lib.gptq_sweep_inplace_workspace_size(rows, n)
+    assert need < lib.gptq_sweep_workspace_size(rows, n)
+    with pwq.check_mode():
+        st = lib.gptq_sweep_inplace(W, U, hd, dead, tab, lost, rows, n, nib, rung, scale,
+                                    E if want_e else None, None if want_e else ws,
+                                    0 if want_e else need, None)
+    assert st == GPTQ_OK, pwq.check_message()
