@@ -44,7 +44,8 @@ enum {
     GPTQ_EWORKSPACE = 2,  /* workspace smaller than the matching *_workspace_size() */
     GPTQ_EHIP = 3,        /* a HIP runtime call failed */
     GPTQ_DEGENERATE = 4,  /* the damping passed 10 without a factor: U = I was written */
-    GPTQ_ECHECK = 5       /* check mode only (gptq_check.h): the schedule failed its check */
+    GPTQ_ECHECK = 5,      /* check mode only (gptq_check.h): the schedule failed its check */
+    GPTQ_ETOOBIG = 6      /* larger than the static scratch of gptq_sweep_inplace_noalloc */
 };
 
 /* Host-side record of one fold. */
@@ -184,6 +185,22 @@ int gptq_sweep_inplace(float* W, const float* U, const float* hdiag, const uint8
                        const float* tab, const float* lost, int64_t rows, int64_t n, uint8_t* nib,
                        uint8_t* rung, float* scale, float* E, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * gptq_sweep_inplace_noalloc -- gptq_sweep_inplace for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid allocation).
+ * It allocates nothing and creates no stream or event: the residual panels live in a static
+ * device array of the library, 2 x 8192 x 512 f32 = 32 MiB on each GPU it runs on (held until
+ * the process ends), and every launch goes on `stream`.
+ *   Arguments as gptq_sweep_inplace, without the workspace.  Without E, rows <= 8192, else
+ *   GPTQ_ETOOBIG (nothing written); with E the static array is not used and rows is free.
+ *   Results equal gptq_sweep_inplace's bit for bit.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on different
+ *   streams, or from several threads) race.  Asynchronous.
+ */
+int gptq_sweep_inplace_noalloc(float* W, const float* U, const float* hdiag, const uint8_t* dead,
+                               const float* tab, const float* lost, int64_t rows, int64_t n,
+                               uint8_t* nib, uint8_t* rung, float* scale, float* E, void* stream);
 
 /*
  * gptq_gram_add -- accumulate one batch of layer inputs into the device Hessian.

@@ -18,7 +18,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgptq_mi355x.so")
 
-GPTQ_OK, GPTQ_EINVAL, GPTQ_EWORKSPACE, GPTQ_EHIP, GPTQ_DEGENERATE, GPTQ_ECHECK = 0, 1, 2, 3, 4, 5
+GPTQ_OK, GPTQ_EINVAL, GPTQ_EWORKSPACE, GPTQ_EHIP, GPTQ_DEGENERATE, GPTQ_ECHECK, GPTQ_ETOOBIG = 0, 1, 2, 3, 4, 5, 6
 
 _lib = None
 
@@ -73,6 +73,8 @@ def load():
     lib.gptq_sweep_inplace_workspace_size.restype = sz
     lib.gptq_sweep_inplace.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
     lib.gptq_sweep_inplace.restype = ctypes.c_int
+    lib.gptq_sweep_inplace_noalloc.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P]
+    lib.gptq_sweep_inplace_noalloc.restype = ctypes.c_int
     lib.gptq_gram_add.argtypes = [P, i64, i64, P, i64, i64, P]
     lib.gptq_gram_add.restype = ctypes.c_int
     lib.gptq_debias_workspace_size.argtypes = [i64, i64]

@@ -107,6 +107,7 @@ extern "C" const char* gptq_status_string(int status) {
         case GPTQ_EHIP: return "HIP runtime error";
         case GPTQ_DEGENERATE: return "damping passed 10 without a factor; U = I";
         case GPTQ_ECHECK: return "schedule check failed (check mode)";
+        case GPTQ_ETOOBIG: return "more rows than the no-allocation sweep's static scratch holds (8192)";
         default: return "unknown status";
     }
 }

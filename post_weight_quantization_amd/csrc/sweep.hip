@@ -25,6 +25,9 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "common.hpp"
 #include "gemm_mfma.hpp"
@@ -602,20 +605,26 @@ struct SweepRun {
     uint8_t* codes;      // static groups: codes [rows, n] (elimination order)
 };
 
+// single: every launch on the caller's stream, in the order the two-stream pipeline's events
+// impose (so each column receives the same updates in the same order: the same results, bit
+// for bit); no helper stream or event is taken.
 template <int MODE>
-static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
+static int sweep_pipeline(const SweepRun& c, hipStream_t st, bool single = false) {
     const int64_t rows = c.rows, n = c.n;
     const float* U = c.U;
     float* Wc = c.Wc;
     const unsigned nwg = (unsigned)((rows + RPW - 1) / RPW);
 
     Helper hp{};
-    if (helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
-    hipStream_t ts = hp.stream;
+    if (!single && helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
+    hipStream_t ts = single ? st : hp.stream;
     struct Release {
         const Helper& h;
-        ~Release() { helper_release(h); }
-    } release{hp};
+        bool on;
+        ~Release() {
+            if (on) helper_release(h);
+        }
+    } release{hp, !single};
 #define SWEEP_OK(call)                          \
     do {                                        \
         const int rc_ = (call);                 \
@@ -699,7 +708,7 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
         // become ready together; started together, the bulk update takes most of the GPU and
         // the look-ahead, which the next panel's blocks wait for, crawls (about 140 us instead
         // of 30).  So the look-ahead goes first and the bulk update waits for it.
-        if (!first_bulk) SWEEP_OK(stream_wait(st, hp.ev_b));
+        if (!first_bulk && !single) SWEEP_OK(stream_wait(st, hp.ev_b));
         {
             const int64_t j0 = P0 + w;
             const GemmBatch b = gemm_batch(
@@ -712,8 +721,10 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
         if (rest2 > 0) {
-            SWEEP_OK(ev_record(hp.ev_a, st));
-            SWEEP_OK(stream_wait(ts, hp.ev_a));
+            if (!single) {
+                SWEEP_OK(ev_record(hp.ev_a, st));
+                SWEEP_OK(stream_wait(ts, hp.ev_a));
+            }
             const int64_t j0 = P0 + w + nw;
             const GemmBatch b = gemm_batch(
                 gemm_full(Ep, ldE, Up + j0, n, src + j0, Wc + j0, n, (int)rows, (int)rest2, (int)w,
@@ -723,13 +734,15 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st) {
                          8.0 * rows * rest2 + 4.0 * w * rest2 + 4.0 * rows * w);
             SWEEP_OK((launch_gemm_fit<2, false, false>("sweep_bulk", ts, b, nullptr)));
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-            SWEEP_OK(ev_record(hp.ev_b, ts));
+            if (!single) SWEEP_OK(ev_record(hp.ev_b, ts));
             first_bulk = false;
         }
     }
     // Join the helper stream.
-    SWEEP_OK(ev_record(hp.ev_b, ts));
-    SWEEP_OK(stream_wait(st, hp.ev_b));
+    if (!single) {
+        SWEEP_OK(ev_record(hp.ev_b, ts));
+        SWEEP_OK(stream_wait(st, hp.ev_b));
+    }
 #undef SWEEP_OK
     return GPTQ_OK;
 }
@@ -839,6 +852,59 @@ extern "C" int gptq_sweep_inplace(float* W, const float* U, const float* hdiag,
     }
     const SweepRun c = q4_run(W, W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E, pan0, pan1);
     const int rc = sweep_pipeline<0>(c, (hipStream_t)stream);
+    if (rc != GPTQ_OK) return rc;
+    return check.finish();
+}
+
+// ---------------------------------------------------------------------------------------------
+// For callers that cannot allocate device memory: the residual panels of the in-place sweep in
+// a static device buffer of the library, 2 x kScratchRows x 512 f32 = 32 MiB on each GPU it
+// runs on, held until the process ends.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in): each device's copy is located once, with that device
+// current, by hipGetSymbolAddress, and that address is what the kernels get.
+constexpr int64_t kScratchRows = 8192;
+static __device__ __align__(256) float scratch[2 * kScratchRows * SOB];
+
+static int scratch_address(float** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GPTQ_EHIP;
+    static std::mutex mu;
+    static std::vector<std::pair<int, float*>> known;  // (device, its copy of scratch)
+    std::lock_guard<std::mutex> lk(mu);
+    for (const auto& k : known)
+        if (k.first == dev) {
+            *out = k.second;
+            return GPTQ_OK;
+        }
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GPTQ_EHIP;
+    known.emplace_back(dev, (float*)p);
+    *out = (float*)p;
+    return GPTQ_OK;
+}
+
+extern "C" int gptq_sweep_inplace_noalloc(float* W, const float* U, const float* hdiag,
+                                          const uint8_t* dead, const float* tab, const float* lost,
+                                          int64_t rows, int64_t n, uint8_t* nib, uint8_t* rung,
+                                          float* scale, float* E, void* stream) {
+    if (!sweep_args_ok(W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E))
+        return GPTQ_EINVAL;
+    if (!E && rows > kScratchRows) return GPTQ_ETOOBIG;
+    CheckScope check;
+    float* pan = nullptr;
+    if (!E) {
+        if (dry_run()) {
+            pan = reinterpret_cast<float*>((uintptr_t)1 << 46);  // a stand-in for the schedule check
+        } else {
+            const int rc = scratch_address(&pan);
+            if (rc != GPTQ_OK) return rc;
+        }
+    }
+    sweep_check_buffers(W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E);
+    if (pan) check_buffer(pan, sizeof(float) * (size_t)(2 * kScratchRows * SOB), "scratch");
+    const SweepRun c = q4_run(W, W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E, pan,
+                              pan ? pan + kScratchRows * SOB : nullptr);
+    const int rc = sweep_pipeline<0>(c, (hipStream_t)stream, /*single=*/true);
     if (rc != GPTQ_OK) return rc;
     return check.finish();
 }

@@ -184,3 +184,19 @@ def test_sweep_inplace_schedule(lib, rows, n, want_e):
                                     E if want_e else None, None if want_e else ws,
                                     0 if want_e else need, None)
     assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(16, 32), (300, 1056), (5120, 17408), (8192, 4096)])
+@pytest.mark.parametrize("want_e", [False, True])
+def test_sweep_inplace_noalloc_schedule(lib, rows, n, want_e):
+    """The no-allocation sweep: one stream, the residual panels in the static scratch (a
+    stand-in address in a dry run), every launch inside the call's buffers."""
+    W, U, hd, dead, tab, lost, nib, rung, scale, E = addrs(10)
+    with pwq.check_mode():
+        st = lib.gptq_sweep_inplace_noalloc(W, U, hd, dead, tab, lost, rows, n, nib, rung, scale,
+                                            E if want_e else None, None)
+    assert st == GPTQ_OK, pwq.check_message()
+    with pwq.check_mode():
+        st = lib.gptq_sweep_inplace_noalloc(W, U, hd, dead, tab, lost, 8193, n, nib, rung, scale,
+                                            None, None)
+    assert st == pwq.GPTQ_ETOOBIG
