@@ -28,6 +28,11 @@ What each function follows (docs.rs source pages of the cortiq project):
   rungs chosen up front from the original tiles, columns eliminated in ``perm`` order.  The
   converter's rung choice is not printed; the reading is the sweep's rung rule on the
   dead-zeroed original tile with unit weights.
+* :func:`static_rungs_q2` and :func:`sweep_act_order` with ``two_bit`` -- act order for q2tp
+  ("cortiq-cli 0.8.45 src/gptq.rs", ``gptq_quantize_q2tp`` with ``perm``): the rungs fixed up
+  front, 2-bit levels in elimination order.  The placement helper that fixes them is not
+  printed; the reading is the sweep's full rung search on the dead-zeroed original tile with the
+  clipped ``H_ii`` weights.  :func:`debias` with ``two_bit`` is ``q2tp_debias_hessian``.
 * :func:`ladder_q2`, :func:`sweep_q2` -- the q2tp sweep with the "placed" rule ("cortiq-engine
   0.8.41 src/gpu_wgpu/gptq_dev.rs", ``q2tp_group``; "cortiq-cli 0.8.45 src/gptq.rs",
   ``sweep_q2tp``, ``gptq_quantize_q2tp``): 2-bit levels, a full search over rungs 1..31 by the
@@ -77,7 +82,8 @@ def _load():
     lib.orc_fold.restype = ctypes.c_int
     lib.orc_ladder.argtypes = [P, P, i64, i64, i64, P, P]
     lib.orc_ladder.restype = None
-    lib.orc_sweep_static.argtypes = [P, i64, i64, P, P, P, P, P, ctypes.c_double, P, ctypes.c_int]
+    lib.orc_sweep_static.argtypes = [P, i64, i64, P, P, ctypes.c_int, P, P, P, ctypes.c_double, P,
+                                     ctypes.c_int]
     lib.orc_sweep_static.restype = ctypes.c_int
     lib.orc_ladder_q2.argtypes = [P, P, i64, i64, i64, P, P]
     lib.orc_ladder_q2.restype = None
@@ -227,17 +233,20 @@ def symmetric_from_upper(H, dead=None):
     return Hs
 
 
-def debias(W0, H, dead, code, rung, lost, scale, gs=32, rows=None):
-    """Output debias in f64.  ``code`` [rows, n] (0..15), ``rung`` [rows, n/gs], ``lost``
-    [rows, 2] (lo, step), ``scale`` [rows, n/gs] the scales the codes were made with.  ``rows``
-    restricts the work to those row indices.  Returns dict(num, den, b, v = lo - log2 b before
-    rounding (nan where lo is kept), lo, tab [rows, 32], scale)."""
+def debias(W0, H, dead, code, rung, lost, scale, gs=32, rows=None, two_bit=False):
+    """Output debias in f64.  ``code`` [rows, n] (0..15; with ``two_bit`` the q2tp levels 0..3),
+    ``rung`` [rows, n/gs], ``lost`` [rows, 2] (lo, step), ``scale`` [rows, n/gs] the scales the
+    codes were made with.  ``rows`` restricts the work to those row indices.  The new ladder is
+    TAB[c] = 2^(lo + c step) (4-bit) or TAB[0] = 0, TAB[c] = 2^(lo + (c - 1) step) (2-bit, the
+    q2tp ladder).  Returns dict(num, den, b, v = lo - log2 b before rounding (nan where lo is
+    kept), lo, tab [rows, 32], scale)."""
     W0 = np.asarray(W0, dtype=np.float32)
     sel = np.arange(W0.shape[0]) if rows is None else np.asarray(rows)
     d = np.asarray(dead, dtype=bool)
     Wd = W0[sel].astype(np.float64)
     Wd[:, d] = 0.0
-    What = dequant(np.asarray(code)[sel], np.asarray(scale)[sel], gs)
+    dq = dequant_q2 if two_bit else dequant
+    What = dq(np.asarray(code)[sel], np.asarray(scale)[sel], gs)
     Y = Wd @ symmetric_from_upper(H, d)          # H w for each row (H symmetric)
     num = np.sum(What * Y, axis=1)
     den = np.sum(Wd * Y, axis=1)
@@ -252,7 +261,11 @@ def debias(W0, H, dead, code, rung, lost, scale, gs=32, rows=None):
             lo2 = f16_round(v[k])
             if np.isfinite(lo2):
                 lo[k] = lo2
-    tab = np.float32(np.exp2(lo[:, None] + np.arange(32)[None, :] * st[:, None]))
+    if two_bit:
+        tab = np.float32(np.exp2(lo[:, None] + (np.arange(32)[None, :] - 1) * st[:, None]))
+        tab[:, 0] = 0.0
+    else:
+        tab = np.float32(np.exp2(lo[:, None] + np.arange(32)[None, :] * st[:, None]))
     rg = np.asarray(rung)[sel].astype(np.int64) & 31
     new_scale = np.take_along_axis(tab, rg, axis=1)
     return dict(num=num, den=den, b=b, v=v, lo=lo, tab=tab, scale=new_scale)
@@ -294,18 +307,32 @@ def static_rungs(W0, dead, tab, lost, gs=32):
     return r["rung"], r["scale"]
 
 
+def static_rungs_q2(W0, dead, tab, hdiag, gs=32):
+    """The q2tp rung of every (row, group) chosen up front from the dead-zeroed original tile:
+    the sweep's full search over rungs 1..31 by the max(H_ii, 0)-weighted error, with no error
+    feedback (U = I); rung 0 for an all-zero tile."""
+    n = np.asarray(W0).shape[1]
+    r = sweep_q2(W0, np.eye(n), hdiag, dead, tab, gs=gs, want_E=False)
+    return r["rung"], r["scale"]
+
+
 def sweep_act_order(W0, Up, dead, perm, tab, lost, gs=32, rung=None, force_code=None,
-                    tie_band=1e-3, want_E=True, nt=None):
-    """Act-order q4tp sweep.  ``Up`` is the fold operator of H[perm][perm]; ``dead`` is in
-    original channel order.  Returns code (rows x n, original order, q + 8), rung and scale
-    (static), E (elimination order) and the tie statistics of a forced replay (force_code in
-    original order)."""
+                    tie_band=1e-3, want_E=True, nt=None, two_bit=False, hdiag=None):
+    """Act-order sweep with static groups.  ``Up`` is the fold operator of H[perm][perm];
+    ``dead`` (and ``hdiag``) are in original channel order.  4-bit (q4tp) by default: static
+    rungs from :func:`static_rungs`, code = q + 8; ``two_bit``: q2tp, static rungs from
+    :func:`static_rungs_q2` (needs ``hdiag``), code = the level 0..3.  Returns code (rows x n,
+    original order), rung and scale (static), E (elimination order) and the tie statistics of a
+    forced replay (force_code in original order)."""
     W0 = np.asarray(W0, dtype=np.float32)
     rows, n = W0.shape
     d = np.asarray(dead, dtype=bool)
     p = np.asarray(perm, dtype=np.int64)
     if rung is None:
-        rung, scale = static_rungs(W0, d, tab, lost, gs)
+        if two_bit:
+            rung, scale = static_rungs_q2(W0, d, tab, hdiag, gs)
+        else:
+            rung, scale = static_rungs(W0, d, tab, lost, gs)
     else:
         rung = np.asarray(rung, dtype=np.uint8)
         scale = np.take_along_axis(np.asarray(tab, np.float32), rung.astype(np.int64) & 31, 1)
@@ -318,8 +345,9 @@ def sweep_act_order(W0, Up, dead, perm, tab, lost, gs=32, rung=None, force_code=
     E = np.empty((rows, n), dtype=np.float64) if want_E else None
     fc = None if force_code is None else np.ascontiguousarray(np.asarray(force_code)[:, p], dtype=np.uint8)
     stats = np.zeros(2, dtype=np.int64)
-    _load().orc_sweep_static(_ptr(Wp), rows, n, _ptr(Upc), _ptr(sp), _ptr(code_p), _ptr(E),
-                             _ptr(fc), float(tie_band), _ptr(stats), threads(nt))
+    _load().orc_sweep_static(_ptr(Wp), rows, n, _ptr(Upc), _ptr(sp), int(bool(two_bit)),
+                             _ptr(code_p), _ptr(E), _ptr(fc), float(tie_band), _ptr(stats),
+                             threads(nt))
     code = np.empty_like(code_p)
     code[:, p] = code_p
     return dict(code=code, rung=rung, scale=scale, E=E,

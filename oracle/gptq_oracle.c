@@ -436,17 +436,23 @@ int orc_sweep(const float* W0, int64_t rows, int64_t n, int64_t gs, const double
 }
 
 /*
- * Act-order sweep with static groups ([gptq.rs] gptq_quantize_q4tp_act_order): the columns of
- * Wp (rows x n, already in elimination order and dead-zeroed) are eliminated in order with the
- * fold operator Up of the permuted Hessian, each column a with its own fixed scale sp[r][a]
- * (the rung of its original group, chosen up front):
- *   q = (s > 0) ? clamp(rne(f32(w_a) / s), -8, 7) : 0,  code = q + 8,
- *   e_a = (Up_aa > 0) ? (w_a - q s) / Up_aa : 0,  w_t -= e_a Up_at for every t > a.
- * code_p and E are in elimination order.  force_code: tie-forced replay as in orc_sweep.
+ * Act-order sweep with static groups ([gptq.rs] gptq_quantize_q4tp_act_order; for 2-bit codes,
+ * gptq_quantize_q2tp with a permutation): the columns of Wp (rows x n, already in elimination
+ * order and dead-zeroed) are eliminated in order with the fold operator Up of the permuted
+ * Hessian, each column a with its own fixed scale sp[r][a] (the rung of its original group,
+ * chosen up front):
+ *   4-bit: q = (s > 0) ? clamp(rne(f32(w_a) / s), -8, 7) : 0,  code = q + 8,  level q;
+ *   2-bit: q = (s > 0) ? q2_level(f32(w_a) / s + 1.5) : 0,      code = q,      level q - 1.5;
+ *   e_a = (Up_aa > 0) ? (w_a - level s) / Up_aa : 0,  w_t -= e_a Up_at for every t > a.
+ * code_p and E are in elimination order.  force_code: tie-forced replay as in orc_sweep (for
+ * 2-bit codes a tie is a difference of one where f32(w_a)/s + 1.5 lies within tie_band of a
+ * half-integer).
  */
+static float q2_level(float x);
+
 int orc_sweep_static(const float* Wp, int64_t rows, int64_t n, const double* Up, const float* sp,
-                     uint8_t* code_p, double* E, const uint8_t* force_code, double tie_band,
-                     int64_t* stats, int nt) {
+                     int two_bit, uint8_t* code_p, double* E, const uint8_t* force_code,
+                     double tie_band, int64_t* stats, int nt) {
     const int64_t RB = 16;
     int64_t ct = 0, ch = 0;
 #pragma omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(+ : ct, ch)
@@ -462,19 +468,28 @@ int orc_sweep_static(const float* Wp, int64_t rows, int64_t n, const double* Up,
                 int64_t r = r0 + k;
                 double wa = w[k * n + a];
                 float s = sp[r * n + a];
-                float q = 0.0f;
-                if (s > 0.0f) q = clampf(rne_f32((float)wa / s), -8.0f, 7.0f);
+                float q = 0.0f, x = 0.0f;
+                if (s > 0.0f) {
+                    if (two_bit) {
+                        x = (float)wa / s + 1.5f;
+                        q = q2_level(x);
+                    } else {
+                        x = (float)wa / s;
+                        q = clampf(rne_f32(x), -8.0f, 7.0f);
+                    }
+                }
                 if (force_code) {
-                    float fq = (float)force_code[r * n + a] - 8.0f;
+                    float fq = (float)force_code[r * n + a] - (two_bit ? 0.0f : 8.0f);
                     if (fq != q) {
-                        double x = fabs((double)((float)wa / s));
-                        double fr = x - floor(x);
+                        double ax = two_bit ? (double)x : fabs((double)x);
+                        double fr = ax - floor(ax);
                         if (fabsf(fq - q) == 1.0f && fabs(fr - 0.5) < tie_band) ++ct; else ++ch;
                         q = fq;
                     }
                 }
-                code_p[r * n + a] = (uint8_t)(q + 8.0f);
-                e[k] = (uaa > 0.0) ? (wa - (double)q * (double)s) / uaa : 0.0;
+                code_p[r * n + a] = (uint8_t)(two_bit ? q : q + 8.0f);
+                double lev = two_bit ? (double)q - 1.5 : (double)q;
+                e[k] = (uaa > 0.0) ? (wa - lev * (double)s) / uaa : 0.0;
                 if (E) E[r * n + a] = e[k];
             }
             const double* urow = Up + a * n;
