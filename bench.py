@@ -332,6 +332,22 @@ def main():
         e1.record(stream)
         e1.synchronize()
         result["detail"]["q2_sweep_ms"] = e0.elapsed_time(e1) / reps
+        # ... and the 2-bit output debias of those codes.
+        if not args.no_debias:
+            ws_dq = torch.empty(pwq.debias_workspace_size(rows, n), dtype=torch.uint8, device=dev)
+            plane_q, rung_q, scale_q, _ = out_q
+            lost_dq, scale_dq = lost_q.clone(), scale_q.clone()
+            pwq.gptq_debias_q2(W, H, dead, plane_q, rung_q, lost_dq, scale_dq, workspace=ws_dq)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                lost_dq.copy_(lost_q)
+                scale_dq.copy_(scale_q)
+                pwq.gptq_debias_q2(W, H, dead, plane_q, rung_q, lost_dq, scale_dq, workspace=ws_dq)
+            e1.record(stream)
+            e1.synchronize()
+            result["detail"]["debias_q2_ms"] = e0.elapsed_time(e1) / reps
+            del ws_dq, lost_dq, scale_dq
         del out_q
     # Act-order GPTQ on the same layer (a next-step row, not part of the step): channel order,
     # permuted Hessian, fold of it, ladder and the static-group sweep, timed as one group.
@@ -339,27 +355,32 @@ def main():
         ws_a = torch.empty(pwq.sweep_act_order_workspace_size(rows, n), dtype=torch.uint8,
                            device=dev)
 
-        def ao_step():
+        def ao_step(two_bit):
             perm_a, dead_a = pwq.gptq_act_order_perm(H)
             Hp_a = pwq.gptq_permute_hessian(H, perm_a)
-            Ua, _, _, rep_a = pwq.gptq_fold(Hp_a, lam, workspace=ws_f)
+            Ua, hd_a, _, rep_a = pwq.gptq_fold(Hp_a, lam, workspace=ws_f)
             del Hp_a
-            lost_a, tab_a = pwq.gptq_ladder(W, dead_a)
-            pwq.gptq_sweep_act_order(W, Ua, dead_a, perm_a, tab_a, lost_a, workspace=ws_a)
+            if two_bit:
+                _, tab_a = pwq.gptq_ladder_q2(W, dead_a)
+                pwq.gptq_sweep_act_order_q2(W, Ua, dead_a, hd_a, perm_a, tab_a, workspace=ws_a)
+            else:
+                lost_a, tab_a = pwq.gptq_ladder(W, dead_a)
+                pwq.gptq_sweep_act_order(W, Ua, dead_a, perm_a, tab_a, lost_a, workspace=ws_a)
             return rep_a
 
-        ao_step()
-        torch.cuda.synchronize()
-        reps = 2
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            rep_a = ao_step()
-        e1.record(stream)
-        e1.synchronize()
-        result["detail"]["act_order_ms"] = e0.elapsed_time(e1) / reps
-        result["detail"]["act_order_groups_per_s"] = 1e3 / result["detail"]["act_order_ms"]
-        result["detail"]["act_order_lambda_used"] = rep_a["lambda_used"]
+        for two_bit, key in ((False, "act_order"), (True, "act_order_q2")):
+            ao_step(two_bit)
+            torch.cuda.synchronize()
+            reps = 2
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                rep_a = ao_step(two_bit)
+            e1.record(stream)
+            e1.synchronize()
+            result["detail"][f"{key}_ms"] = e0.elapsed_time(e1) / reps
+            result["detail"][f"{key}_groups_per_s"] = 1e3 / result["detail"][f"{key}_ms"]
+            result["detail"][f"{key}_lambda_used"] = rep_a["lambda_used"]
         del ws_a
     # The output debias on the step's codes (a next-step row of the path, not part of the step):
     # symmetrised H, the product W H and the per-row slopes, timed alone on the stream.

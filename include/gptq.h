@@ -302,6 +302,43 @@ int gptq_sweep_act_order(const float* W, const float* U, const uint8_t* dead, co
                          size_t workspace_bytes, void* stream);
 
 /*
+ * gptq_sweep_act_order_q2 -- act order with 2-bit (q2tp) codes.  Source: page "cortiq-cli 0.8.45
+ * src/gptq.rs", gptq_quantize_q2tp with a permutation (the sweep's perm branch: columns in perm
+ * order, each group's rung fixed up front).  The pages fix the rungs with a placement helper
+ * that is handed the clipped H_ii weights and is not printed; the rule implemented (a stated
+ * reading) is the q2tp sweep's own search on the dead-zeroed original tile: rung 0 for an
+ * all-zero tile, else the best of rungs 1..31 (TAB > 0) by sum_t max(H_tt, 0) (w_t - (q_t - 1.5)
+ * s)^2 in f32, summed in column order, a strictly smaller error replacing the current best.
+ *
+ *   W [rows, n] f32 (original order, 16-byte aligned), read only.  U and hdiag: gptq_fold of
+ *   gptq_permute_hessian(H, perm) (hdiag [n] is H_ii in elimination order, hdiag[a] =
+ *   H[perm[a]][perm[a]]).  dead [n] in original order (gptq_act_order_perm's).  perm [n] i32.
+ *   tab: gptq_ladder_q2(W, dead).
+ *   plane [rows, n/4] u8 out (column 4m + i in bits 2i of byte m, original order), rung / scale
+ *   [rows, n/32] out (the static choice), E [rows, n] f32 out (elimination order) or NULL.
+ *   Per column a of the elimination order: q = clamp(rne(clamp(w_a / s_a + 1.5, -1, 4)), 0, 3),
+ *   e_a = (w_a - (q - 1.5) s_a) / U_aa, w_t -= e_a U_at for t > a.
+ *   rows <= 65535, n % 32 == 0.  Workspace: gptq_sweep_act_order_workspace_size(rows, n).
+ */
+int gptq_sweep_act_order_q2(const float* W, const float* U, const uint8_t* dead,
+                            const float* hdiag, const int32_t* perm, const float* tab,
+                            int64_t rows, int64_t n, uint8_t* plane, uint8_t* rung, float* scale,
+                            float* E, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gptq_debias_q2 -- gptq_debias for 2-bit codes.  Source: page "cortiq-cli 0.8.45 src/gptq.rs",
+ * q2tp_debias_hessian / q2tp_debias_gemm (the pages' primary use of the debias: the MSE-optimal
+ * 2-bit rounding shrinks every output).  As gptq_debias with plane [rows, n/4] (gptq_sweep_q2's
+ * layout) in place of the nibbles, W^ = (q - 1.5) scale, and the q2 ladder for the new scales:
+ * TAB[0] = 0, TAB[c] = f32(2^(lo + (c - 1) step)) (f64).  lo <- f16(lo - log2 b) as there.
+ * Workspace: gptq_debias_workspace_size(rows, n).
+ */
+int gptq_debias_q2(const float* W, const float* H, int64_t ldh, const uint8_t* dead,
+                   const uint8_t* plane, const uint8_t* rung, float* lost, float* tab,
+                   float* scale, double* slope, int64_t rows, int64_t n, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
  * q2tp, the "placed" rule.  Source: page "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs",
  * q2tp_group; page "cortiq-cli 0.8.45 src/gptq.rs", sweep_q2tp / gptq_quantize_q2tp_dev.
  *

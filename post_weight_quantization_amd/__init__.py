@@ -89,6 +89,10 @@ def load():
     lib.gptq_sweep_act_order_workspace_size.restype = sz
     lib.gptq_sweep_act_order.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
     lib.gptq_sweep_act_order.restype = ctypes.c_int
+    lib.gptq_sweep_act_order_q2.argtypes = [P, P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
+    lib.gptq_sweep_act_order_q2.restype = ctypes.c_int
+    lib.gptq_debias_q2.argtypes = [P, P, i64, P, P, P, P, P, P, P, i64, i64, P, sz, P]
+    lib.gptq_debias_q2.restype = ctypes.c_int
     lib.gptq_ladder_q2.argtypes = [P, P, i64, i64, P, P, P]
     lib.gptq_ladder_q2.restype = ctypes.c_int
     lib.gptq_sweep_q2.argtypes = [P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
@@ -361,6 +365,66 @@ def gptq_debias(W, H, dead, nib, rung, lost, scale, want_tab=True, want_slope=Tr
     return lost, tab, scale, slope
 
 
+def gptq_debias_q2(W, H, dead, plane, rung, lost, scale, want_tab=True, want_slope=True,
+                   workspace=None, stream=None):
+    """Output debias of 2-bit codes in place on (lost, scale).  Returns (lost, tab or None,
+    scale, slope f64 [rows] or None)."""
+    lib = load()
+    rows, n = W.shape
+    dev = W.device
+    if H.dim() != 2 or H.shape[0] != n or H.shape[1] != n or H.stride(1) != 1:
+        raise ValueError("H must be a row-major [n, n] matrix")
+    need = int(lib.gptq_debias_workspace_size(rows, n))
+    with _on(stream, dev):
+        tab = torch.empty(rows, 32, dtype=torch.float32, device=dev) if want_tab else None
+        slope = torch.empty(rows, dtype=torch.float64, device=dev) if want_slope else None
+        workspace = _workspace(workspace, need, dev)
+    st = lib.gptq_debias_q2(_dev(W, torch.float32, "W", align=16), _dev_rows(H, torch.float32, "H"),
+                            H.stride(0), _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                            _dev(plane, torch.uint8, "plane", (rows, n // 4), device=dev),
+                            _dev(rung, torch.uint8, "rung", (rows, n // 32), device=dev),
+                            _dev(lost, torch.float32, "lost", (rows, 2), 8, dev),
+                            None if tab is None else _dev(tab, torch.float32, "tab", (rows, 32), 16, dev),
+                            _dev(scale, torch.float32, "scale", (rows, n // 32), device=dev),
+                            None if slope is None else _dev(slope, torch.float64, "slope", (rows,), device=dev),
+                            rows, n, ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                            _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_debias_q2")
+    return lost, tab, scale, slope
+
+
+def gptq_sweep_act_order_q2(W, U, dead, hdiag, perm, tab, want_E=False, workspace=None,
+                            stream=None):
+    """Act-order q2tp sweep.  ``U`` and ``hdiag`` come from the fold of H[perm][perm] (hdiag
+    in elimination order); ``dead`` in original order.  Returns (plane [rows, n/4], rung,
+    scale, E or None); E in elimination order."""
+    lib = load()
+    rows, n = W.shape
+    dev = W.device
+    need = int(lib.gptq_sweep_act_order_workspace_size(rows, n))
+    with _on(stream, dev):
+        plane = torch.empty(rows, n // 4, dtype=torch.uint8, device=dev)
+        rung = torch.empty(rows, n // 32, dtype=torch.uint8, device=dev)
+        scale = torch.empty(rows, n // 32, dtype=torch.float32, device=dev)
+        E = torch.empty(rows, n, dtype=torch.float32, device=dev) if want_E else None
+        workspace = _workspace(workspace, need, dev)
+    st = lib.gptq_sweep_act_order_q2(_dev(W, torch.float32, "W", align=16),
+                                     _dev(U, torch.float32, "U", (n, n), 16, dev),
+                                     _dev(dead, torch.uint8, "dead", (n,), device=dev),
+                                     _dev(hdiag, torch.float32, "hdiag", (n,), device=dev),
+                                     _dev(perm, torch.int32, "perm", (n,), device=dev),
+                                     _dev(tab, torch.float32, "tab", (rows, 32), 16, dev),
+                                     rows, n, _dev(plane, torch.uint8, "plane"),
+                                     _dev(rung, torch.uint8, "rung"), _dev(scale, torch.float32, "scale"),
+                                     None if E is None else _dev(E, torch.float32, "E"),
+                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                     _stream(stream))
+    if st != GPTQ_OK:
+        raise GptqError(st, "gptq_sweep_act_order_q2")
+    return plane, rung, scale, E
+
+
 def gptq_ladder_q2(W, dead, stream=None):
     """The q2tp ladder: (lost [rows, 2], tab [rows, 32]) with TAB[0] = 0."""
     lib = load()
@@ -536,6 +600,7 @@ def check_tile_order(M: int, N: int, lower: bool) -> int:
 __all__ = ["check_mode", "check_message", "check_selftest", "check_tile_order", "gptq_gram_add", "gptq_debias",
            "gptq_act_order_perm", "gptq_permute_hessian", "gptq_sweep_act_order",
            "sweep_act_order_workspace_size", "gptq_ladder_q2", "gptq_sweep_q2",
+           "gptq_sweep_act_order_q2", "gptq_debias_q2",
            "debias_workspace_size", "gptq_fold", "FOLD_PRECISION", "gptq_ladder", "gptq_sweep", "gptq_sweep_inplace", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
            "profile_collect", "LIB_PATH"]

@@ -9,6 +9,9 @@
 // products in f64.  The helper that applies b to lo is not printed on the pages; the reading
 // here is lo <- f16(lo - log2 b), left unchanged unless num and den are positive and finite.
 //
+// The same for 2-bit codes (q2tp: "MSE-optimal 2-bit rounding shrinks every output"; the pages
+// run it by default there and make the 4-bit form opt-in): gptq_debias_q2.
+//
 // Three kernels:
 //   debias_sym_kernel   H_s = H read through its upper triangle (H_s[i][j] = H[min][max]) with
 //                       dead channels' rows and columns zeroed, into the workspace (32 x 32
@@ -71,6 +74,10 @@ __device__ __forceinline__ double f16_round(double x) {
     return copysign(ldexp(r, qe), x);
 }
 
+// TWO_BIT: the codes are q2tp levels (2-bit plane [rows, n/4], W^ = (q - 1.5) s) and the
+// row's ladder is the q2tp one, TAB[0] = 0, TAB[c] = 2^(lo + (c - 1) step); otherwise 4-bit
+// nibbles [rows, n/2], W^ = (q - 8) s, TAB[c] = 2^(lo + c step).
+template <bool TWO_BIT>
 __global__ __launch_bounds__(256) void debias_row_kernel(
     const float* __restrict__ W, const uint8_t* __restrict__ dead, const float* __restrict__ Y,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ rung, float* __restrict__ lost,
@@ -86,9 +93,18 @@ __global__ __launch_bounds__(256) void debias_row_kernel(
         const f32x4 w = *reinterpret_cast<const f32x4*>(W + r * n + c);
         const f32x4 y = *reinterpret_cast<const f32x4*>(Y + r * n + c);
         const float s = scale[r * ng + c / 32];
-        const uint8_t b0 = nib[r * (n / 2) + c / 2], b1 = nib[r * (n / 2) + c / 2 + 1];
-        const float q[4] = {(float)(b0 & 15) - 8.0f, (float)(b0 >> 4) - 8.0f,
-                            (float)(b1 & 15) - 8.0f, (float)(b1 >> 4) - 8.0f};
+        float q[4];
+        if constexpr (TWO_BIT) {
+            const uint8_t b = nib[r * (n / 4) + c / 4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = (float)((b >> (2 * u)) & 3) - 1.5f;
+        } else {
+            const uint8_t b0 = nib[r * (n / 2) + c / 2], b1 = nib[r * (n / 2) + c / 2 + 1];
+            q[0] = (float)(b0 & 15) - 8.0f;
+            q[1] = (float)(b0 >> 4) - 8.0f;
+            q[2] = (float)(b1 & 15) - 8.0f;
+            q[3] = (float)(b1 >> 4) - 8.0f;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const float wq = q[u] * s;
@@ -123,7 +139,8 @@ __global__ __launch_bounds__(256) void debias_row_kernel(
     // The row's ladder with the new lo (an all-zero row keeps TAB = 1: step 0 and lo 0 there).
     __shared__ float stab[32];
     if (t < 32) {
-        const float v = (float)exp2(s_lo + (double)t * s_st);
+        const float v = TWO_BIT ? (t == 0 ? 0.0f : (float)exp2(s_lo + (double)(t - 1) * s_st))
+                                : (float)exp2(s_lo + (double)t * s_st);
         stab[t] = v;
         if (tab) tab[r * 32 + t] = v;
     }
@@ -146,10 +163,10 @@ extern "C" size_t gptq_debias_workspace_size(int64_t rows, int64_t n) {
     return debias_ws(rows, n, nullptr);
 }
 
-extern "C" int gptq_debias(const float* W, const float* H, int64_t ldh, const uint8_t* dead,
-                           const uint8_t* nib, const uint8_t* rung, float* lost, float* tab,
-                           float* scale, double* slope, int64_t rows, int64_t n,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+static int debias_impl(const float* W, const float* H, int64_t ldh, const uint8_t* dead,
+                       const uint8_t* nib, const uint8_t* rung, float* lost, float* tab,
+                       float* scale, double* slope, int64_t rows, int64_t n, void* workspace,
+                       size_t workspace_bytes, void* stream, bool two_bit) {
     if (rows <= 0 || n < 32 || n % 32 != 0 || ldh < n || !W || !H || !dead || !nib || !rung ||
         !lost || !scale || !workspace)
         return GPTQ_EINVAL;
@@ -161,7 +178,8 @@ extern "C" int gptq_debias(const float* W, const float* H, int64_t ldh, const ui
     check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
     check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
     check_buffer(dead, (size_t)n, "dead");
-    check_buffer(nib, (size_t)(rows * (n / 2)), "nib");
+    const int64_t cb = two_bit ? n / 4 : n / 2;  // code bytes per row
+    check_buffer(nib, (size_t)(rows * cb), "codes");
     check_buffer(rung, (size_t)(rows * (n / 32)), "rung");
     check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
     if (tab) check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
@@ -190,14 +208,32 @@ extern "C" int gptq_debias(const float* W, const float* H, int64_t ldh, const ui
     {
         ProfScope ps(FAM_DEBIAS, st, 0.0, 12.0 * (double)rows * n);
         GPTQ_LAUNCH(st, "debias_rows",
-                    (debias_row_kernel<<<(unsigned)rows, 256, 0, st>>>(W, dead, Y, nib, rung, lost,
-                                                                       tab, scale, slope, n)),
+                    (two_bit ? debias_row_kernel<true><<<(unsigned)rows, 256, 0, st>>>(
+                                   W, dead, Y, nib, rung, lost, tab, scale, slope, n)
+                             : debias_row_kernel<false><<<(unsigned)rows, 256, 0, st>>>(
+                                   W, dead, Y, nib, rung, lost, tab, scale, slope, n)),
                     rd(W, n, rows, n), rd(dead, n, 1, n, 1), rd(Y, n, rows, n),
-                    rd(nib, n / 2, rows, n / 2, 1), rd(rung, n / 32, rows, n / 32, 1),
+                    rd(nib, cb, rows, cb, 1), rd(rung, n / 32, rows, n / 32, 1),
                     wr(lost, 2, rows, 2), wr(scale, n / 32, rows, n / 32),
                     wr(tab ? (const void*)tab : (const void*)lost, tab ? 32 : 2, tab ? rows : 0, tab ? 32 : 0),
                     wr(slope ? (const void*)slope : (const void*)lost, 1, slope ? 1 : 0, slope ? rows : 0, 8));
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     return check.finish();
+}
+
+extern "C" int gptq_debias(const float* W, const float* H, int64_t ldh, const uint8_t* dead,
+                           const uint8_t* nib, const uint8_t* rung, float* lost, float* tab,
+                           float* scale, double* slope, int64_t rows, int64_t n,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    return debias_impl(W, H, ldh, dead, nib, rung, lost, tab, scale, slope, rows, n, workspace,
+                       workspace_bytes, stream, false);
+}
+
+extern "C" int gptq_debias_q2(const float* W, const float* H, int64_t ldh, const uint8_t* dead,
+                              const uint8_t* plane, const uint8_t* rung, float* lost, float* tab,
+                              float* scale, double* slope, int64_t rows, int64_t n,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return debias_impl(W, H, ldh, dead, plane, rung, lost, tab, scale, slope, rows, n, workspace,
+                       workspace_bytes, stream, true);
 }

@@ -245,6 +245,24 @@ __device__ __forceinline__ float pair_err_q2(float w0, float w1, float h0, float
     const float f0 = e0 * d0, f1 = e1 * d1;
     return f0 + f1;
 }
+
+// Clipped-H_ii-weighted q2tp rounding error of a 32-column tile at scale s, summed in column
+// order with every product and sum rounded separately (the static q2 groups' rung choice).
+__device__ __forceinline__ float q2_tile_err(const float (&w)[32], const float (&h)[32], float s,
+                                             float inv_s) {
+    float err = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const float q = q2_level_quot(w[t], s, inv_s);
+        const float l = q - 1.5f;
+        const float qs = l * s;
+        const float d = w[t] - qs;
+        const float e = h[t] * d;
+        const float f = e * d;
+        err = err + f;
+    }
+    return err;
+}
 #pragma clang fp contract(fast)
 
 constexpr int SB = 128;          // columns per block (4 groups)
@@ -269,17 +287,19 @@ struct BlockCtx {
 // MODE 0: q4tp.  MODE 1 (static groups, act order): no rung search; every column carries its
 // own scale, read from cx.sp and broadcast from its owner like the weight, and the codes go to
 // cx.codes as bytes.  MODE 2: q2tp ("placed"): the full search over rungs 1..31 (rung 0 for an
-// all-zero group), 2-bit levels (q - 1.5) s, codes packed four to a byte.
+// all-zero group), 2-bit levels (q - 1.5) s, codes packed four to a byte.  MODE 3: static groups
+// with 2-bit levels (q2tp act order): the scales of MODE 1, the levels of MODE 2, the level q
+// (0..3) to cx.codes.
 template <int G, int g, int MODE>
 __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx, int64_t r,
                                             int64_t n, int64_t c0, uint8_t* __restrict__ nib,
                                             uint8_t* __restrict__ rung, float* __restrict__ scale,
                                             float* __restrict__ E, int64_t ldE) {
-    constexpr bool ST = MODE == 1, Q2 = MODE == 2;
+    constexpr bool ST = MODE == 1 || MODE == 3, Q2 = MODE == 2 || MODE == 3;
     const int k = cx.k;
     float s = 0.0f, inv_s = 0.0f;
     float s_own[2] = {0.0f, 0.0f}, inv_own[2] = {0.0f, 0.0f};
-    if constexpr (Q2) {
+    if constexpr (Q2 && !ST) {
         const float amax = group16_max(fmaxf(fabsf(w[g][0]), fabsf(w[g][1])));
         int best = 0;
         if (amax > 0.0f) {
@@ -383,7 +403,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         w[g][0] -= e * uo.x;
         w[g][1] -= e * uo.y;
         if (k == owner) {
-            if constexpr (ST) byte |= ((uint32_t)((int)q + 8) & 255u) << (8 * slot);
+            if constexpr (ST) byte |= ((uint32_t)((int)q + (Q2 ? 0 : 8)) & 255u) << (8 * slot);
             else if constexpr (Q2) byte |= ((uint32_t)(int)q & 3u) << (2 * slot);
             else byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
             w[g][slot] = e;
@@ -431,7 +451,7 @@ __global__ __launch_bounds__(BT) void sweep_block_kernel(
     float* __restrict__ E, int64_t ldE, const float* __restrict__ sp,
     uint8_t* __restrict__ codes) {
     constexpr int NC = 32 * G;
-    constexpr bool ST = MODE == 1;
+    constexpr bool ST = MODE == 1 || MODE == 3;
     __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
     __shared__ float hs[SB];
     __shared__ float uinv[SB];
@@ -526,6 +546,57 @@ __global__ __launch_bounds__(256) void static_rung_kernel(const float* __restric
             const float s_c = tb[cand];
             if (s_c <= 0.0f) continue;
             const float err = unit_tile_err(w, s_c, 1.0f / s_c);
+            if (err < best_e) {
+                best_e = err;
+                best = cand;
+            }
+        }
+    }
+    rung[r * ng + g] = (uint8_t)best;
+    scale[r * ng + g] = tb[best];
+}
+
+// Static groups of q2tp, step 1: the rung of every (row, group) chosen up front from the
+// dead-zeroed original tile by the q2tp sweep's own search: rung 0 for an all-zero tile, else
+// the best of rungs 1..31 (TAB > 0) by the max(H_ii, 0)-weighted f32 error summed in column
+// order, a strictly smaller error replacing the current best.  One thread per (row, group).
+// hdiag_p holds H_ii in elimination order (the fold of H[perm][perm]); channel c's weight is
+// hdiag_p[inv[c]] (0 for a channel perm does not name).
+__global__ __launch_bounds__(256) void static_rung_q2_kernel(const float* __restrict__ W,
+                                                             const uint8_t* __restrict__ dead,
+                                                             const float* __restrict__ hdiag_p,
+                                                             const int32_t* __restrict__ inv,
+                                                             const float* __restrict__ tab,
+                                                             int64_t rows, int64_t n,
+                                                             uint8_t* __restrict__ rung,
+                                                             float* __restrict__ scale) {
+    const int64_t ng = n / 32;
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= rows * ng) return;
+    const int64_t r = id / ng, g = id % ng;
+    float w[32], h[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 32; t += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(W + r * n + 32 * g + t);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t c = 32 * g + t + u;
+            const int32_t a = inv[c];
+            w[t + u] = dead[c] ? 0.0f : v[u];
+            h[t + u] = (a >= 0 && a < n) ? fmaxf(hdiag_p[a], 0.0f) : 0.0f;
+            amax = fmaxf(amax, fabsf(w[t + u]));
+        }
+    }
+    const float* tb = tab + r * 32;
+    int best = 0;
+    if (amax > 0.0f) {
+        best = 1;
+        float best_e = INFINITY;
+        for (int cand = 1; cand < 32; ++cand) {
+            const float s_c = tb[cand];
+            if (!(s_c > 0.0f)) continue;
+            const float err = q2_tile_err(w, h, s_c, 1.0f / s_c);
             if (err < best_e) {
                 best_e = err;
                 best = cand;
@@ -646,12 +717,12 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st, bool single = false
                 ProfScope ps(FAM_SWEEP_GROUP, st, 51.0 * nc * rows + (double)rows * nc * nc,
                              4.0 * rows * nc * 2 + 4.0 * nc * nc);
 #define BLOCK_ARGS nwg, st, src, n, c0, U, c.hdiag, c.dead, c.tab, c.lost, rows, c.nib, c.rung, c.scale, Eo, ldE, c.sp, c.codes
-                if constexpr (MODE == 1) {
+                if constexpr (MODE == 1 || MODE == 3) {
                     GPTQ_LAUNCH(st, "sweep_block_static",
-                                (G == 4   ? launch_block<4, 1>(BLOCK_ARGS)
-                                 : G == 3 ? launch_block<3, 1>(BLOCK_ARGS)
-                                 : G == 2 ? launch_block<2, 1>(BLOCK_ARGS)
-                                          : launch_block<1, 1>(BLOCK_ARGS)),
+                                (G == 4   ? launch_block<4, MODE>(BLOCK_ARGS)
+                                 : G == 3 ? launch_block<3, MODE>(BLOCK_ARGS)
+                                 : G == 2 ? launch_block<2, MODE>(BLOCK_ARGS)
+                                          : launch_block<1, MODE>(BLOCK_ARGS)),
                                 rd(src + c0, n, rows, nc), rd(U + c0 * n + c0, n, nc, nc),
                                 rd(c.sp + c0, n, rows, nc), wr(c.codes + c0, n, rows, nc, 1),
                                 wr(Eo, ldE, rows, nc));
@@ -1017,6 +1088,24 @@ __global__ __launch_bounds__(256) void act_pack_kernel(const uint8_t* __restrict
     nib[r * (n / 2) + m] = (uint8_t)((c0 & 15u) | ((c1 & 15u) << 4));
 }
 
+// The 2-bit plane from the levels in elimination order: column 4m + i in bits 2i of byte m (a
+// channel no entry of perm names gets level 0).
+__global__ __launch_bounds__(256) void act_pack_q2_kernel(const uint8_t* __restrict__ codes,
+                                                          const int32_t* __restrict__ inv,
+                                                          int64_t n, uint8_t* __restrict__ plane) {
+    const int64_t r = blockIdx.y;
+    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (m >= n / 4) return;
+    uint32_t b = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t a = inv[4 * m + i];
+        const uint32_t q = (a >= 0 && a < n) ? (codes[r * n + a] & 3u) : 0u;
+        b |= q << (2 * i);
+    }
+    plane[r * (n / 4) + m] = (uint8_t)b;
+}
+
 static size_t act_ws(int64_t rows, int64_t n, size_t* off_e, size_t* off_sp, size_t* off_codes,
                      size_t* off_inv) {
     size_t o = sweep_ws(rows, n, off_e);
@@ -1034,27 +1123,32 @@ extern "C" size_t gptq_sweep_act_order_workspace_size(int64_t rows, int64_t n) {
     return act_ws(rows, n, nullptr, nullptr, nullptr, nullptr);
 }
 
-extern "C" int gptq_sweep_act_order(const float* W, const float* U, const uint8_t* dead,
-                                    const int32_t* perm, const float* tab, const float* lost,
-                                    int64_t rows, int64_t n, uint8_t* nib, uint8_t* rung,
-                                    float* scale, float* E, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
-    if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !dead || !perm || !tab || !lost ||
-        !nib || !rung || !scale || !workspace)
+// The act-order sweep with static groups, 4-bit (q4tp: the static rung from the ladder's nominal
+// window with unit weights; lost is read) or 2-bit (q2tp: the static rung from the full search
+// with max(H_ii, 0) weights; hdiag, in elimination order, is read).  out is the nibble plane or
+// the 2-bit plane.
+static int act_order_impl(const float* W, const float* U, const uint8_t* dead, const int32_t* perm,
+                          const float* tab, const float* lost, const float* hdiag, bool two_bit,
+                          int64_t rows, int64_t n, uint8_t* out, uint8_t* rung, float* scale,
+                          float* E, void* workspace, size_t workspace_bytes, void* stream) {
+    if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !dead || !perm || !tab ||
+        (two_bit ? !hdiag : !lost) || !out || !rung || !scale || !workspace)
         return GPTQ_EINVAL;
     if (rows > 65535 || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;  // rows index grid.y
-    if (!al16(U) || !al16(E) || !al16(workspace)) return GPTQ_EINVAL;
+    if (!al16(W) || !al16(U) || !al16(E) || !al16(workspace)) return GPTQ_EINVAL;
     size_t off_e = 0, off_sp = 0, off_codes = 0, off_inv = 0;
     if (workspace_bytes < act_ws(rows, n, &off_e, &off_sp, &off_codes, &off_inv))
         return GPTQ_EWORKSPACE;
     CheckScope check;
+    const int64_t obytes = two_bit ? n / 4 : n / 2;  // output plane bytes per row
     check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
     check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
     check_buffer(dead, (size_t)n, "dead");
     check_buffer(perm, sizeof(int32_t) * (size_t)n, "perm");
     check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
-    check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
-    check_buffer(nib, (size_t)(rows * (n / 2)), "nib");
+    if (two_bit) check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
+    else check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
+    check_buffer(out, (size_t)(rows * obytes), "plane");
     check_buffer(rung, (size_t)(rows * (n / 32)), "rung");
     check_buffer(scale, sizeof(float) * (size_t)(rows * (n / 32)), "scale");
     if (E) check_buffer(E, sizeof(float) * (size_t)(rows * n), "E");
@@ -1068,22 +1162,30 @@ extern "C" int gptq_sweep_act_order(const float* W, const float* U, const uint8_
     const int64_t ng = n / 32;
     {
         ProfScope ps(FAM_SWEEP_GROUP, st, 0.0, 4.0 * (double)rows * n);
-        GPTQ_LAUNCH(st, "static_rungs",
-                    (static_rung_kernel<<<(unsigned)((rows * ng + 255) / 256), 256, 0, st>>>(
-                        W, dead, tab, lost, rows, n, rung, scale)),
-                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), rd(tab, 32, rows, 32),
-                    rd(lost, 2, rows, 2), wr(rung, ng, rows, ng, 1), wr(scale, ng, rows, ng));
-        GPTQ_LAUNCH(st, "act_gather",
-                    (act_gather_kernel<<<dim3((unsigned)((n + 255) / 256), (unsigned)rows), 256, 0, st>>>(
-                        W, dead, perm, scale, n, Wc, sp)),
-                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), rd(perm, n, 1, n),
-                    rd(scale, ng, rows, ng), wr(Wc, n, rows, n), wr(sp, n, rows, n));
+        const unsigned grid = (unsigned)((rows * ng + 255) / 256);
         GPTQ_LAUNCH(st, "act_inverse_clear",
                     (act_inverse_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, n, inv, 0)),
                     wr(inv, n, 1, n));
         GPTQ_LAUNCH(st, "act_inverse",
                     (act_inverse_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(perm, n, inv, 1)),
                     rd(perm, n, 1, n), wr(inv, n, 1, n));
+        if (two_bit) {
+            GPTQ_LAUNCH(st, "static_rungs_q2",
+                        (static_rung_q2_kernel<<<grid, 256, 0, st>>>(W, dead, hdiag, inv, tab, rows, n,
+                                                                     rung, scale)),
+                        rd(W, n, rows, n), rd(dead, n, 1, n, 1), rd(hdiag, n, 1, n), rd(inv, n, 1, n),
+                        rd(tab, 32, rows, 32), wr(rung, ng, rows, ng, 1), wr(scale, ng, rows, ng));
+        } else {
+            GPTQ_LAUNCH(st, "static_rungs",
+                        (static_rung_kernel<<<grid, 256, 0, st>>>(W, dead, tab, lost, rows, n, rung, scale)),
+                        rd(W, n, rows, n), rd(dead, n, 1, n, 1), rd(tab, 32, rows, 32),
+                        rd(lost, 2, rows, 2), wr(rung, ng, rows, ng, 1), wr(scale, ng, rows, ng));
+        }
+        GPTQ_LAUNCH(st, "act_gather",
+                    (act_gather_kernel<<<dim3((unsigned)((n + 255) / 256), (unsigned)rows), 256, 0, st>>>(
+                        W, dead, perm, scale, n, Wc, sp)),
+                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), rd(perm, n, 1, n),
+                    rd(scale, ng, rows, ng), wr(Wc, n, rows, n), wr(sp, n, rows, n));
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     SweepRun c{};
@@ -1095,7 +1197,7 @@ extern "C" int gptq_sweep_act_order(const float* W, const float* U, const uint8_
     c.lost = lost;
     c.rows = rows;
     c.n = n;
-    c.nib = nib;
+    c.nib = out;
     c.rung = rung;
     c.scale = scale;
     c.E = E;
@@ -1104,15 +1206,40 @@ extern "C" int gptq_sweep_act_order(const float* W, const float* U, const uint8_
     c.Epan[1] = (float*)(ws + off_e + align256(sizeof(float) * (size_t)(rows * SOB)));
     c.sp = sp;
     c.codes = codes;
-    int rc = sweep_pipeline<1>(c, st);
+    int rc = two_bit ? sweep_pipeline<3>(c, st) : sweep_pipeline<1>(c, st);
     if (rc != GPTQ_OK) return rc;
     {
         ProfScope ps(FAM_SWEEP_GROUP, st, 0.0, 1.5 * (double)rows * n);
-        GPTQ_LAUNCH(st, "act_pack",
-                    (act_pack_kernel<<<dim3((unsigned)((n / 2 + 255) / 256), (unsigned)rows), 256, 0, st>>>(
-                        codes, inv, n, nib)),
-                    rd(codes, n, rows, n, 1), rd(inv, n, 1, n), wr(nib, n / 2, rows, n / 2, 1));
+        if (two_bit) {
+            GPTQ_LAUNCH(st, "act_pack_q2",
+                        (act_pack_q2_kernel<<<dim3((unsigned)((n / 4 + 255) / 256), (unsigned)rows), 256, 0, st>>>(
+                            codes, inv, n, out)),
+                        rd(codes, n, rows, n, 1), rd(inv, n, 1, n), wr(out, n / 4, rows, n / 4, 1));
+        } else {
+            GPTQ_LAUNCH(st, "act_pack",
+                        (act_pack_kernel<<<dim3((unsigned)((n / 2 + 255) / 256), (unsigned)rows), 256, 0, st>>>(
+                            codes, inv, n, out)),
+                        rd(codes, n, rows, n, 1), rd(inv, n, 1, n), wr(out, n / 2, rows, n / 2, 1));
+        }
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     return check.finish();
+}
+
+extern "C" int gptq_sweep_act_order(const float* W, const float* U, const uint8_t* dead,
+                                    const int32_t* perm, const float* tab, const float* lost,
+                                    int64_t rows, int64_t n, uint8_t* nib, uint8_t* rung,
+                                    float* scale, float* E, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return act_order_impl(W, U, dead, perm, tab, lost, nullptr, false, rows, n, nib, rung, scale,
+                          E, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gptq_sweep_act_order_q2(const float* W, const float* U, const uint8_t* dead,
+                                       const float* hdiag, const int32_t* perm, const float* tab,
+                                       int64_t rows, int64_t n, uint8_t* plane, uint8_t* rung,
+                                       float* scale, float* E, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    return act_order_impl(W, U, dead, perm, tab, nullptr, hdiag, true, rows, n, plane, rung, scale,
+                          E, workspace, workspace_bytes, stream);
 }

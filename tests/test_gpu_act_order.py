@@ -131,3 +131,94 @@ def test_act_order_down_proj_sampled(gpu):
     torch.cuda.synchronize()
     sel = np.sort(np.random.default_rng(5).choice(W.shape[0], 24, replace=False))
     check_sweep(gpu, W, U, dead, perm, p_o, rows_sel=sel, want_E=False)
+
+
+# --- act order with 2-bit codes (q2tp) ---------------------------------------------------------
+
+def check_sweep_q2(gpu, W, Up, hdiag_p, dead, perm, p_o, rows_sel=None, want_E=True):
+    """The q2tp act-order sweep: the q2 ladder bit for bit, the static rungs exactly (both sides
+    sum the clipped-H_ii-weighted error in f32 in column order), the levels in a tie-forced
+    replay of the oracle's static q2 sweep on the GPU's U (0 hard, >= 99.9% identical)."""
+    lost, tab = gpu.gptq_ladder_q2(W, dead)
+    plane, rung, scale, E = gpu.gptq_sweep_act_order_q2(W, Up, dead, hdiag_p, perm, tab, want_E=want_E)
+    torch.cuda.synchronize()
+    Wn = W.cpu().numpy()
+    n = Wn.shape[1]
+    d = dead.cpu().numpy().astype(bool)
+    lost_o, tab_o = oracle.ladder_q2(Wn, d)
+    assert np.array_equal(lost.cpu().numpy(), lost_o) and np.array_equal(tab.cpu().numpy(), tab_o)
+    hd = np.empty(n, np.float32)
+    hd[p_o] = hdiag_p.cpu().numpy()  # back to the original channel order
+    sel = np.arange(Wn.shape[0]) if rows_sel is None else np.asarray(rows_sel)
+    rung_o, scale_o = oracle.static_rungs_q2(Wn[sel], d, tab_o[sel], hd)
+    assert np.array_equal(rung.cpu().numpy()[sel], rung_o), "static q2 rungs differ"
+    assert np.array_equal(scale.cpu().numpy()[sel], scale_o)
+    code_g = oracle.unpack_q2(plane.cpu().numpy()[sel])
+    Ud = Up.cpu().numpy().astype(np.float64)
+    free = oracle.sweep_act_order(Wn[sel], Ud, d, p_o, tab_o[sel], lost_o[sel], rung=rung_o, two_bit=True)
+    rep = oracle.sweep_act_order(Wn[sel], Ud, d, p_o, tab_o[sel], lost_o[sel], rung=rung_o,
+                                 force_code=code_g, tie_band=TIE_BAND, two_bit=True)
+    total = code_g.size
+    st = dict(rep["stats"], code_agree=float((free["code"] == code_g).mean()),
+              replay_agree=1.0 - (rep["stats"]["code_ties"] + rep["stats"]["code_hard"]) / total)
+    if want_E:
+        Eg = E.cpu().numpy()[sel].astype(np.float64)
+        st["E_relF"] = float(np.linalg.norm(Eg - rep["E"]) / max(np.linalg.norm(rep["E"]), 1e-300))
+        assert st["E_relF"] <= 1e-3, st
+    say(f"act-order q2 sweep rows={len(sel)} {st}")
+    assert st["code_hard"] == 0, st
+    assert st["replay_agree"] >= CODE_AGREE, st
+    return plane, scale, st
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", ["tiny", "fixture"])
+def test_act_order_q2_small_workloads(gpu, name):
+    H, W, lam = workloads.make(name, device="cuda:0")
+    H_np = H.cpu().numpy()
+    perm, dead, Hp = run_gpu(gpu, H, W, lam)
+    p_o = check_order(perm, dead, Hp, H_np)
+    (Up, hdiag_p, dead_p, rep), orc, err = check_fold(gpu, Hp, lam)
+    plane, scale, st = check_sweep_q2(gpu, W, Up, hdiag_p, dead, perm, p_o)
+    # End to end against the free-running oracle (its own fold of the permuted Hessian).
+    Wn = W.cpu().numpy()
+    d = dead.cpu().numpy().astype(bool)
+    f_o = oracle.fold(oracle.permute_sym(H_np, p_o).astype(np.float32), lam)
+    lost_o, tab_o = oracle.ladder_q2(Wn, d)
+    ao = oracle.sweep_act_order(Wn, f_o["U"], d, p_o, tab_o, lost_o, two_bit=True,
+                                hdiag=np.diag(H_np).astype(np.float32))
+
+    def t(code, sc):
+        Wz = Wn.astype(np.float64)
+        Wz[:, d] = 0.0
+        dW = Wz - oracle.dequant_q2(code, sc)
+        dW[:, d] = 0.0
+        return float(np.einsum("ij,jk,ik->", dW, oracle.symmetric_from_upper(H_np), dW))
+
+    t_o = t(ao["code"], ao["scale"])
+    t_g = t(oracle.unpack_q2(plane.cpu().numpy()), scale.cpu().numpy())
+    say(f"act-order q2 {name}: tr(dW H dW^T) gpu {t_g:.6e} oracle {t_o:.6e}")
+    assert abs(t_g - t_o) <= 0.01 * t_o
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,rows", [(96, 37), (288, 130)])
+def test_act_order_q2_ragged(gpu, n, rows):
+    H, W, lam = workloads.make("attn", device="cuda:0", n=n, rows=rows, T=1024)
+    H_np = H.cpu().numpy()
+    perm, dead, Hp = run_gpu(gpu, H, W, lam)
+    p_o = check_order(perm, dead, Hp, H_np)
+    (Up, hdiag_p, _, _), _, _ = check_fold(gpu, Hp, lam)
+    check_sweep_q2(gpu, W, Up, hdiag_p, dead, perm, p_o)
+
+
+@pytest.mark.gpu
+def test_act_order_q2_down_proj_sampled(gpu):
+    H, W, lam = workloads.make("down", device="cuda:0")
+    perm, dead, Hp = run_gpu(gpu, H, W, lam)
+    p_o = oracle.act_order_perm(np.diag(H.cpu().numpy()).astype(np.float32))
+    assert np.array_equal(perm.cpu().numpy().astype(np.int64), p_o)
+    U, hdiag_p, dead_p, rep = gpu.gptq_fold(Hp, lam)
+    torch.cuda.synchronize()
+    sel = np.sort(np.random.default_rng(6).choice(W.shape[0], 24, replace=False))
+    check_sweep_q2(gpu, W, U, hdiag_p, dead, perm, p_o, rows_sel=sel, want_E=False)

@@ -41,9 +41,9 @@ def test_random_shapes(gpu, seed):
 
 @pytest.mark.parametrize("seed", [404, 505])
 def test_random_shapes_next_rows(gpu, seed):
-    """The same generator for the q2tp sweep, act order and the output debias, each against its
-    own checker (the bars of its parity tests)."""
-    from test_gpu_act_order import check_order, check_sweep, run_gpu
+    """The same generator for the q2tp sweep, act order (4- and 2-bit) and the output debias
+    (4- and 2-bit), each against its own checker (the bars of its parity tests)."""
+    from test_gpu_act_order import check_order, check_sweep, check_sweep_q2, run_gpu
     from test_gpu_debias import check as check_debias
     from test_gpu_q2 import check_q2
     rng = np.random.default_rng(seed)
@@ -55,9 +55,11 @@ def test_random_shapes_next_rows(gpu, seed):
         check_q2(gpu, Wd, U, hdiag, dead)
         perm, dead_a, Hp = run_gpu(gpu, Hd, Wd, lam)
         p_o = check_order(perm, dead_a, Hp, H)
-        (Up, _, _, _), _, _ = check_fold(gpu, Hp, lam)
+        (Up, hdiag_p, _, _), _, _ = check_fold(gpu, Hp, lam)
         check_sweep(gpu, Wd, Up, dead_a, perm, p_o)
+        check_sweep_q2(gpu, Wd, Up, hdiag_p, dead_a, perm, p_o)
         check_debias(gpu, Hd, Wd, lam, label=f"random n={H.shape[0]}")
+        check_debias(gpu, Hd, Wd, lam, label=f"random q2 n={H.shape[0]}", two_bit=True)
 
 
 def test_near_tie_rungs_decided_like_the_oracle(gpu):

@@ -200,3 +200,24 @@ def test_sweep_inplace_noalloc_schedule(lib, rows, n, want_e):
         st = lib.gptq_sweep_inplace_noalloc(W, U, hd, dead, tab, lost, 8193, n, nib, rung, scale,
                                             None, None)
     assert st == pwq.GPTQ_ETOOBIG
+
+
+@pytest.mark.parametrize("rows,n", [(1, 32), (37, 96), (300, 1056), (5120, 17408)])
+@pytest.mark.parametrize("want_e", [False, True])
+def test_act_order_q2_schedule(lib, rows, n, want_e):
+    W, U, dead, hd, perm, tab, plane, rung, scale, E, ws = addrs(11)
+    need = lib.gptq_sweep_act_order_workspace_size(rows, n)
+    with pwq.check_mode():
+        st = lib.gptq_sweep_act_order_q2(W, U, dead, hd, perm, tab, rows, n, plane, rung, scale,
+                                         E if want_e else None, ws, need, None)
+    assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(1, 32), (70, 160), (5120, 17408)])
+def test_debias_q2_schedule(lib, rows, n):
+    W, H, dead, plane, rung, lost, tab, scale, slope, ws = addrs(10)
+    need = lib.gptq_debias_workspace_size(rows, n)
+    with pwq.check_mode():
+        st = lib.gptq_debias_q2(W, H, n, dead, plane, rung, lost, tab, scale, slope, rows, n, ws,
+                                need, None)
+    assert st == GPTQ_OK, pwq.check_message()
