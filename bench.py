@@ -23,6 +23,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
+FP64_MFMA_PEAK_TFLOPS = 78.6    # MI355X dense FP64 matrix peak
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 
 
@@ -44,6 +45,18 @@ def sweep_bytes_k32(rows: int, n: int) -> float:
 
 def sweep_flops(rows: int, n: int) -> float:
     return rows * (n * n - 32.0 * n) + 51.0 * rows * n
+
+
+def recorded_sweep_dram_bytes():
+    """DRAM bytes of one sweep at n = 17408 from the committed counter summary (its sentence
+    "Per sweep this is X GB of DRAM traffic"), or None."""
+    import re
+    try:
+        txt = open(os.path.join(ROOT, "profiles", "sweep_hbm_traffic_n17408.md")).read()
+    except OSError:
+        return None
+    m = re.search(r"Per sweep this is ([0-9.]+) GB of DRAM traffic", txt)
+    return float(m.group(1)) * 1e9 if m else None
 
 
 def recorded_traffic():
@@ -99,6 +112,182 @@ def cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows, m_fold=8192, rows_swe
     }
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def all_configs(pwq, torch, dev):
+    """One record per workload of the method's configurations: GPU fold / sweep times, the
+    fold's damping, attempts and precision, parity figures against the oracle, and the oracle's
+    own times on the host cores.  Printed as one JSON line ({"configs": [...]}) plus a table on
+    stderr; the numbers behind the per-configuration table of the design notes."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import fold_rel_err, hd_diag, output_error
+
+    nt = oracle.threads()
+    recs = []
+
+    def gpu_step_times(H, W, lam, reps):
+        n, rows = H.shape[0], W.shape[0]
+        ws_f = torch.empty(pwq.fold_workspace_size(n), dtype=torch.uint8, device=dev)
+        ws_s = torch.empty(pwq.sweep_workspace_size(rows, n), dtype=torch.uint8, device=dev)
+        U = torch.empty(n, n, device=dev)
+        hd = torch.empty(n, device=dev)
+        dd = torch.empty(n, dtype=torch.uint8, device=dev)
+        lost = torch.empty(rows, 2, device=dev)
+        tab = torch.empty(rows, 32, device=dev)
+        out = (torch.empty(rows, n // 2, dtype=torch.uint8, device=dev),
+               torch.empty(rows, n // 32, dtype=torch.uint8, device=dev),
+               torch.empty(rows, n // 32, device=dev), None)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        tf, tsw = [], []
+        for i in range(reps + 2):
+            ev[0].record()
+            _, _, _, rep = pwq.gptq_fold(H, lam, workspace=ws_f, out=(U, hd, dd))
+            ev[1].record()
+            pwq.gptq_ladder(W, dd, out=(lost, tab))
+            pwq.gptq_sweep(W, U, hd, dd, tab, lost, workspace=ws_s, out=out)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                tf.append(ev[0].elapsed_time(ev[1]))
+                tsw.append(ev[1].elapsed_time(ev[2]))
+        return float(np.median(tf)), float(np.median(tsw)), rep, (U, hd, dd, lost, tab) + out[:3]
+
+    for name in ("tiny", "attn", "down", "stress"):
+        spec = workloads.SPECS[name]
+        H, W, lam = workloads.make(name, device=dev)
+        torch.cuda.synchronize()
+        n, rows = spec.n, spec.rows
+        log(f"config {name}: n={n} rows={rows}")
+        t_fold, t_sweep, rep, (U, hd, dd, lost, tab, nib, rung, scale) = gpu_step_times(
+            H, W, lam, 3 if name == "down" else 5)
+        rec = dict(workload=name, n=n, rows=rows, lambda_start=lam, lambda_used=rep["lambda_used"],
+                   attempts=rep["attempts"], precision=rep["precision"], min_pivot=rep["min_pivot"],
+                   gpu_fold_ms=t_fold, gpu_sweep_ms=t_sweep,
+                   gpu_groups_per_s=1e3 / (t_fold + t_sweep),
+                   fold_tflops=2.0 * n ** 3 / 3.0 / (t_fold * 1e-3) / 1e12)
+        rec["fold_frac_peak"] = rec["fold_tflops"] / (FP32_MFMA_PEAK_TFLOPS if rep["precision"] == 32
+                                                      else FP64_MFMA_PEAK_TFLOPS)
+        rec["sweep_tflops"] = sweep_flops(rows, n) / (t_sweep * 1e-3) / 1e12
+        Hn, Wn = H.cpu().numpy(), W.cpu().numpy()
+        if name != "down":
+            # Parity and the oracle's own time on the whole workload.
+            t0 = time.perf_counter()
+            of = oracle.fold(Hn, lam, nt=nt)
+            t_ofold = time.perf_counter() - t0
+            Ug = U.cpu().numpy()
+            og = of if of["lam"] == rep["lambda_used"] else oracle.fold(Hn, rep["lambda_used"], retry=False, nt=nt)
+            rec["fold_relF"] = fold_rel_err(Ug, og["U"], np.sqrt(hd_diag(Hn, og["dead"], og["damp"])))
+            rec["oracle_lambda"] = of["lam"]
+            lo, tb = oracle.ladder(Wn, of["dead"])
+            t0 = time.perf_counter()
+            os_ = oracle.sweep(Wn, of["U"], of["hdiag"], of["dead"], tb, lo, want_E=False, nt=nt)
+            t_osweep = time.perf_counter() - t0
+            code_g = oracle.unpack_nibbles(nib.cpu().numpy())
+            rp = oracle.sweep(Wn, Ug.astype(np.float64), hd.cpu().numpy(), dd.cpu().numpy().astype(bool),
+                              tab.cpu().numpy(), lost.cpu().numpy(), force_code=code_g,
+                              force_rung=rung.cpu().numpy(), want_E=False, nt=nt)
+            st_ = rp["stats"]
+            rec["sweep_hard"] = st_["code_hard"] + st_["rung_hard"]
+            rec["sweep_replay_agree"] = 1.0 - (st_["code_ties"] + st_["code_hard"]) / code_g.size
+            t_o = oracle.output_error(Wn, of["dead"], os_["code"], os_["scale"], Hn)
+            t_g = output_error(Wn, of["dead"], nib.cpu().numpy(), scale.cpu().numpy(), Hn)
+            rec["output_error_rel"] = (t_g - t_o) / t_o
+            rec.update(oracle_fold_s=t_ofold, oracle_sweep_s=t_osweep,
+                       oracle_groups_per_s=1.0 / (t_ofold + t_osweep), oracle_threads=nt)
+            if name == "tiny":
+                t0 = time.perf_counter()
+                of1 = oracle.fold(Hn, lam, nt=1)
+                oracle.sweep(Wn, of1["U"], of1["hdiag"], of1["dead"], tb, lo, want_E=False, nt=1)
+                rec["oracle_1thread_s"] = time.perf_counter() - t0
+        else:
+            cb = cpu_baseline(H, U, hd, dd, W, lost, tab, n, rows)
+            rec.update(oracle_groups_per_s=cb["value"], oracle_threads=nt, oracle_sample=cb["sample"],
+                       parity="whole-layer parity: tests/test_gpu_parity_large.py::test_down_proj_full_size")
+        rec["speedup_vs_oracle"] = rec["gpu_groups_per_s"] / rec["oracle_groups_per_s"]
+        recs.append(rec)
+        del H, W, U
+        torch.cuda.empty_cache()
+    # Config 4: 11 groups of the attention shape.  GPU: one stream and host thread per group.
+    # Oracle: the groups concurrently with the host threads split between them, as the pages'
+    # host round runs them.
+    import threading
+    spec = workloads.SPECS["batch"]
+    groups = [workloads.make("batch", k=k, device=dev) for k in range(11)]
+    torch.cuda.synchronize()
+    bufs = []
+    for H, W, lam in groups:
+        n, rows = spec.n, spec.rows
+        bufs.append(dict(wf=torch.empty(pwq.fold_workspace_size(n), dtype=torch.uint8, device=dev),
+                         ws=torch.empty(pwq.sweep_workspace_size(rows, n), dtype=torch.uint8, device=dev),
+                         U=torch.empty(n, n, device=dev), hd=torch.empty(n, device=dev),
+                         dd=torch.empty(n, dtype=torch.uint8, device=dev),
+                         lost=torch.empty(rows, 2, device=dev), tab=torch.empty(rows, 32, device=dev),
+                         out=(torch.empty(rows, n // 2, dtype=torch.uint8, device=dev),
+                              torch.empty(rows, n // 32, dtype=torch.uint8, device=dev),
+                              torch.empty(rows, n // 32, device=dev), None),
+                         st=torch.cuda.Stream(device=dev)))
+
+    def one(i):
+        (H, W, lam), b = groups[i], bufs[i]
+        with torch.cuda.stream(b["st"]):
+            pwq.gptq_fold(H, lam, workspace=b["wf"], out=(b["U"], b["hd"], b["dd"]))
+            pwq.gptq_ladder(W, b["dd"], out=(b["lost"], b["tab"]))
+            pwq.gptq_sweep(W, b["U"], b["hd"], b["dd"], b["tab"], b["lost"], workspace=b["ws"], out=b["out"])
+            b["st"].synchronize()
+
+    def round_():
+        th = [threading.Thread(target=one, args=(i,)) for i in range(11)]
+        for x in th:
+            x.start()
+        for x in th:
+            x.join()
+        torch.cuda.synchronize()
+
+    round_()
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        round_()
+        ts.append(time.perf_counter() - t0)
+    t_round = float(np.median(ts))
+    conc = 4
+    per = max(nt // conc, 1)
+    host = [(H.cpu().numpy(), W.cpu().numpy(), lam) for H, W, lam in groups]
+
+    def orc_group(k):
+        Hn, Wn, lam = host[k]
+        of = oracle.fold(Hn, lam, nt=per)
+        lo, tb = oracle.ladder(Wn, of["dead"])
+        oracle.sweep(Wn, of["U"], of["hdiag"], of["dead"], tb, lo, want_E=False, nt=per)
+
+    import concurrent.futures as cf
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(conc) as ex:
+        list(ex.map(orc_group, range(11)))
+    t_orc = time.perf_counter() - t0
+    recs.append(dict(workload="batch", n=spec.n, rows=spec.rows, groups=11,
+                     gpu_round_ms=t_round * 1e3, gpu_groups_per_s=11 / t_round,
+                     oracle_round_s=t_orc, oracle_groups_per_s=11 / t_orc,
+                     oracle_threads=nt, oracle_concurrency=f"{conc} groups at a time, {per} threads each",
+                     speedup_vs_oracle=(11 / t_round) / (11 / t_orc)))
+    out = {"cpu_model": cpu_model(), "host_threads": nt, "configs": recs}
+    for r in recs:
+        log(json.dumps(r))
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +300,9 @@ def main():
     ap.add_argument("--no-act-order", action="store_true", help="skip the act-order timing")
     ap.add_argument("--no-q2", action="store_true", help="skip the q2tp sweep timing")
     ap.add_argument("--no-rounds", action="store_true", help="skip the concurrent-group timings")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the benchmark line: one record per configuration of the "
+                         "method (GPU times, damping, parity, oracle times)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size reference for "
                          "hardware traffic counters)")
@@ -130,6 +322,9 @@ def main():
     pwq.require_native()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.all_configs:
+        all_configs(pwq, torch, dev)
+        return
     spec = workloads.SPECS[args.workload]
     n, rows = spec.n, spec.rows
     log(f"generating workload {args.workload}: n={n} rows={rows} T={spec.T}")
@@ -235,13 +430,31 @@ def main():
             "fold_ms": fold_ms, "ladder_ms": ladder_ms, "sweep_ms": sweep_ms,
             "fold_tflops": fold_flops / (fold_ms * 1e-3) / 1e12,
             "fold_frac_fp32_mfma": fold_flops / (fold_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
-            "sweep_gbps_k32_equivalent": sweep_bytes_k32(rows, n) / (sweep_ms * 1e-3) / 1e9,
+            "sweep_k32_equivalent_rate_gbps": sweep_bytes_k32(rows, n) / (sweep_ms * 1e-3) / 1e9,
+            "sweep_k32_equivalent_note": "not a bandwidth: the bytes a per-group (K = 32) sweep "
+                                         "would move, over the time of this blocked (K = 512) "
+                                         "sweep, which moves about 8x fewer; see sweep_roofline",
             "sweep_tflops": sweep_flops(rows, n) / (sweep_ms * 1e-3) / 1e12,
             "sweep_frac_fp32_mfma": sweep_flops(rows, n) / (sweep_ms * 1e-3) / 1e12
                                     / FP32_MFMA_PEAK_TFLOPS,
             "lambda_used": rep["lambda_used"], "attempts": rep["attempts"],
-            "n_dead": rep["n_dead"],
+            "n_dead": rep["n_dead"], "fold_precision": rep["precision"],
+            "fold_min_pivot": rep["min_pivot"],
         },
+    }
+    # The sweep's own roofline.  Reassociated into 512-column panels its trailing updates are
+    # K = 512 products (MFMA-bound); the HBM target of a per-group sweep does not describe it.
+    sweep_tf = sweep_flops(rows, n) / (sweep_ms * 1e-3) / 1e12
+    dram = recorded_sweep_dram_bytes() if n == 17408 and rows == 5120 else None
+    result["sweep_roofline"] = {
+        "bound": "mfma", "achieved": sweep_tf, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": sweep_tf / FP32_MFMA_PEAK_TFLOPS,
+        "flops": sweep_flops(rows, n),
+        "dram_bytes_counters": dram,
+        "dram_gbps": dram / (sweep_ms * 1e-3) / 1e9 if dram else None,
+        "dram_frac_hbm": dram / (sweep_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS if dram else None,
+        "note": "flops rows (n^2 - 32 n) + 51 rows n over the whole sweep; DRAM bytes from the "
+                "committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary at this workload",
     }
     # The device Hessian accumulation (a next-step row of the path, not part of the step):
     # H += X^T X for X [T, n] tokens x channels at the same shape, timed alone on the stream.

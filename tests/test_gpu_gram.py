@@ -143,3 +143,37 @@ def test_gram_down_proj_shape_sampled(gpu):
     assert worst <= 1.0, f"sampled error {worst:.3f} x bound"
     low = torch.tril(torch.ones(64, 64, dtype=torch.bool, device="cuda:0"), -1)
     assert not H[:64, :64][low].any()
+
+
+@pytest.mark.gpu
+def test_gram_bit_exact_at_down_proj_shape(gpu):
+    """n = 17408 channels, t = 32768 tokens with integer activations in -2..2 and power-of-two
+    channel scales: every product and partial sum of an entry is exact in f32 (the entry is
+    2^(e_i + e_j) times an integer of magnitude at most 4 t < 2^24), so whatever the summation
+    order the result is the definition h_ij = sum_r x_ri x_rj exactly.  Checked bit for bit
+    against the f64 definition on whole 512 x 512 tiles: the first and last diagonal tiles, the
+    corner tile, the edge tiles of the last tile row and column, and interior tiles."""
+    n, t = 17408, 32768
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1717)
+    Xi = torch.randint(-2, 3, (t, n), generator=g, device=dev, dtype=torch.int32).float()
+    e = torch.randint(-6, 7, (n,), generator=g, device=dev, dtype=torch.int32).float()
+    X = Xi * torch.exp2(e)[None, :]
+    del Xi
+    H = torch.zeros(n, n, device=dev)
+    gpu.gptq_gram_add(H, X)
+    torch.cuda.synchronize()
+    T = 512
+    last = n - T
+    tiles = [(0, 0), (last, last), (0, last), (T * 13, last), (T * 7, T * 21), (T * 16, T * 16),
+             (T * 3, T * 30)]
+    for i0, j0 in tiles:
+        xi = X[:, i0:i0 + T].cpu().numpy().astype(np.float64)
+        xj = X[:, j0:j0 + T].cpu().numpy().astype(np.float64)
+        ref = xi.T @ xj
+        got = H[i0:i0 + T, j0:j0 + T].cpu().numpy().astype(np.float64)
+        up = np.add.outer(np.arange(i0, i0 + T), -np.arange(j0, j0 + T)) <= 0  # j >= i
+        assert np.array_equal(got[up], ref[up]), f"tile ({i0}, {j0}) differs"
+        if i0 != j0:
+            assert up.all()
