@@ -17,7 +17,8 @@
 //   Tb [64][256], Xt [256][n_p]   staging for the inverse's small steps
 //
 // Per outer panel of w = 256 columns (four 64-wide steps), all on the caller's stream:
-//   step   : diag (L_cc, MI_c = L_cc^-1 in LDS), panel solve L_ic = A_ic MI_c^T (in place),
+//   step   : diag (L_cc, MI_c = L_cc^-1, one wave in registers), panel solve L_ic = A_ic MI_c^T
+//            (in place),
 //            the rest of the panel's columns A -= L_ic L_jc^T;
 //   inverse: the panel's w x w diagonal block of X by block forward substitution from the MI,
 //            its rows of X, X[kb:kb+w, <kb] = X_ww X[kb:kb+w, <kb] (staged, copied back);
@@ -25,12 +26,12 @@
 //            inverse's update X[kb+w:, <kb+w] -= P X[kb:kb+w, <kb+w], P = L[kb+w:, kb:kb+w].
 #include <math.h>
 
+#include <utility>
+
 #include "fold.hpp"
 #include "gemm64.hpp"
 
 namespace gptq {
-
-constexpr int DL64 = NB64 + 1;  // LDS row stride of the diagonal block (doubles)
 
 // Per attempt: f64 inverse equilibration scales; the flag and the smallest-pivot record reset.
 __global__ void fold64_scale_kernel(const float* __restrict__ hdiag, const uint8_t* __restrict__ dead,
@@ -87,55 +88,82 @@ __global__ __launch_bounds__(256) void fold64_build_kernel(const float* __restri
     }
 }
 
-// Diagonal block at cb: L_cc = chol(A_cc) in LDS (right-looking, 256 threads), then
-// MI = L_cc^-1 by one wave (lane c holds column c in registers: substitution step k makes
-// x[k] final and removes it from every later row).  A pivot that is not positive and finite
-// sets flag bit 0 and is replaced by 1 so the arithmetic stays finite; the smallest accepted
-// pivot goes to minp64.
-__global__ __launch_bounds__(256) void fold64_diag_kernel(const double* __restrict__ A,
-                                                          double* __restrict__ MI, int64_t np,
-                                                          int64_t cb, FoldState* st) {
-    if (__atomic_load_n(&st->flag, __ATOMIC_RELAXED)) return;
-    __shared__ double Ls[NB64 * DL64];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < NB64 * NB64; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        Ls[r * DL64 + c] = (c <= r) ? A[(cb + r) * np + cb + c] : 0.0;
+// Diagonal block at cb: L_cc = chol(A_cc) and MI = L_cc^-1, 64 x 64, by one wave in registers.
+// Lane i holds row i of the block (x[], becoming row i of L) and column i of the inverse (t[],
+// starting as e_i).  Step c: the pivot x[c] of lane c is tested and turned into 1 / L_cc; x[c]
+// scaled by it makes L_ic final on every lane (L_cc on lane c), t[c] scaled by it makes
+// T_c,i final; then for every s > c the entry L_sc, broadcast from lane s, drives the same
+// update in both halves: the Cholesky update x[s] -= L_ic L_sc of the later columns and the
+// substitution step t[s] -= T_c,i L_sc.  Entries above the diagonal of x carry values nothing
+// reads.  A pivot that is not positive and finite sets flag bit 0 and is replaced by 1 so the
+// arithmetic stays finite; the smallest accepted pivot goes to minp64.
+__device__ __forceinline__ double bcast_f64(double v, int src) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), src);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), src);
+    return __hiloint2double(hi, lo);
+}
+
+template <int C>
+__device__ __forceinline__ void leaf64_step(double (&x)[NB64], double (&t)[NB64], bool& bad,
+                                            double& pmin) {
+    double p = bcast_f64(x[C], C);
+    const bool b = !(p > 0.0) || !isfinite(p);
+    bad = bad || b;
+    pmin = b ? pmin : fmin(pmin, p);
+    p = b ? 1.0 : p;
+    const double rl = 1.0 / sqrt(p);
+    x[C] *= rl;
+    t[C] *= rl;
+    // Four broadcasts at a time, each group fenced off from the next (an empty asm that
+    // "rewrites" x[C]), so the scalar registers they occupy stay few instead of every broadcast
+    // of the step being hoisted together and spilled.
+#pragma unroll
+    for (int s0 = (C + 1) & ~3; s0 < NB64; s0 += 4) {
+        double ls[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (s0 + u > C) ls[u] = bcast_f64(x[C], s0 + u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (s0 + u > C) {
+                x[s0 + u] -= x[C] * ls[u];
+                t[s0 + u] -= t[C] * ls[u];
+            }
+        asm volatile("" : "+v"(x[C]));
     }
-    __syncthreads();
-    const int c = tid & 63, rg = tid >> 6;
+#pragma unroll
+    for (int s2 = C + 1; s2 < NB64; ++s2) asm volatile("" : "+v"(x[s2]), "+v"(t[s2]));
+}
+
+template <int... C>
+__device__ __forceinline__ void leaf64_steps(double (&x)[NB64], double (&t)[NB64], bool& bad,
+                                             double& pmin, std::integer_sequence<int, C...>) {
+    (leaf64_step<C>(x, t, bad, pmin), ...);
+}
+
+__global__ __launch_bounds__(64) void fold64_diag_kernel(const double* __restrict__ A,
+                                                         double* __restrict__ MI, int64_t np,
+                                                         int64_t cb, FoldState* st) {
+    if (__atomic_load_n(&st->flag, __ATOMIC_RELAXED)) return;
+    const int lane = threadIdx.x;
+    double x[NB64], t[NB64];
+    const double* arow = A + (cb + lane) * np + cb;
+#pragma unroll
+    for (int k = 0; k < NB64; k += 2) {
+        const f64x2 v = *reinterpret_cast<const f64x2*>(arow + k);
+        x[k] = (k <= lane) ? v[0] : 0.0;
+        x[k + 1] = (k + 1 <= lane) ? v[1] : 0.0;
+        t[k] = (k == lane) ? 1.0 : 0.0;
+        t[k + 1] = (k + 1 == lane) ? 1.0 : 0.0;
+    }
     bool bad = false;
     double pmin = INFINITY;
-    for (int j = 0; j < NB64; ++j) {
-        double p = Ls[j * DL64 + j];
-        const bool b = !(p > 0.0) || !isfinite(p);
-        bad = bad || b;
-        if (!b) pmin = fmin(pmin, p);
-        p = b ? 1.0 : p;
-        const double l = sqrt(p), rl = 1.0 / l;
-        __syncthreads();  // every thread has read the pivot
-        if (tid == j) Ls[j * DL64 + j] = l;
-        if (tid > j && tid < NB64) Ls[tid * DL64 + j] *= rl;
-        __syncthreads();
-        for (int r = j + 1 + rg; r < NB64; r += 4)
-            if (c > j && c <= r) Ls[r * DL64 + c] -= Ls[r * DL64 + j] * Ls[c * DL64 + j];
-        __syncthreads();
-    }
-    if (tid < 64) {
-        double x[NB64];
+    leaf64_steps(x, t, bad, pmin, std::make_integer_sequence<int, NB64>{});
+    // MI[i][lane] = T_i,lane: row i of MI is written by the 64 lanes together.
+    double* mi = MI + (cb / NB64) * NB64 * NB64;
 #pragma unroll
-        for (int i = 0; i < NB64; ++i) x[i] = (i == c) ? 1.0 : 0.0;
-#pragma unroll
-        for (int k = 0; k < NB64; ++k) {
-            x[k] = x[k] / Ls[k * DL64 + k];
-#pragma unroll
-            for (int i = k + 1; i < NB64; ++i) x[i] -= Ls[i * DL64 + k] * x[k];
-        }
-        double* mi = MI + (cb / NB64) * NB64 * NB64;
-#pragma unroll
-        for (int i = 0; i < NB64; ++i) mi[i * NB64 + c] = x[i];
-    }
-    if (tid == 0) {
+    for (int i = 0; i < NB64; ++i) mi[i * NB64 + lane] = t[i];
+    if (lane == 0) {
         if (bad) atomicOr(&st->flag, 1u);
         atomicMin(&st->minp64, (unsigned long long)__double_as_longlong(pmin));
     }
@@ -223,7 +251,7 @@ int fold64_attempt(const float* H, int64_t n, int64_t ldh, const float* hdiag, c
             {
                 ProfScope ps(FAM_FOLD_DIAG, st, 2.0 * NB64 * NB64 * NB64 / 3.0, 0.0);
                 GPTQ_LAUNCH(st, "fold64_diag",
-                            (fold64_diag_kernel<<<1, 256, 0, st>>>(A, MI, np, cb, state)),
+                            (fold64_diag_kernel<<<1, 64, 0, st>>>(A, MI, np, cb, state)),
                             rd(A + cb * np + cb, np, NB64, NB64, 8),
                             wr(MI + (cb / NB64) * NB64 * NB64, NB64, NB64, NB64, 8), st_rw);
             }
@@ -305,7 +333,7 @@ int fold64_attempt(const float* H, int64_t n, int64_t ldh, const float* hdiag, c
         {
             ProfScope ps(FAM_FOLD_UPDATE, st,
                          (double)w * rest * (rest + 1) + 2.0 * w * (double)rest * (kb + w), 0.0);
-            F64_OK((launch_gemm64<128, 128, true, false>("fold64_bulk", st, sy, &xu, flag)));
+            F64_OK((launch_gemm64<64, 64, true, false>("fold64_bulk", st, sy, &xu, flag)));
         }
         if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     }
