@@ -194,9 +194,10 @@ __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict
 //           32 x 32 x 32 product on v_mfma_f32_32x32x2_f32;
 // then the off-diagonal blocks of L^-1 by block forward substitution down each block column,
 //   M_IJ = -T_I sum_{J <= Q < I} L_IQ M_QJ   (waves 0..2 take block columns 0..2).
-// A pivot that is not > 0 (or NaN) sets flag bit 0 and is replaced by 1; a positive pivot at or
-// below tau (the accuracy floor of the "auto" precision, 0 otherwise) sets flag bit 1.  The
-// smallest accepted pivot goes to *minp.
+// A pivot that is not above tau (the accuracy floor of the "auto" precision, 0 for "f32"), or
+// NaN, is replaced by 1 (if not positive) and sets flag bit 1 under "auto" (the damping is then
+// factored in f64) or bit 0 under "f32" (the attempt failed).  The smallest pivot of the block,
+// as the square of L's smallest diagonal entry, goes to *minp.
 constexpr int DLD = NB + 1;  // row stride of the block in LDS (odd: column reads spread banks)
 constexpr int SLD = 33;      // row stride of 32 x 32 blocks in LDS
 
@@ -239,18 +240,17 @@ __device__ __forceinline__ int mcol() { return threadIdx.x & 31; }
 // count and x[] stays in registers; the broadcasts go four at a time into separate scalar
 // registers.  Each step's updates are pinned in place so the compiler does not defer them.
 template <int C>
-__device__ __forceinline__ void leaf_step(float (&x)[32], float tau, int& nsmall, int& nfail,
-                                          float& pmin) {
+__device__ __forceinline__ void leaf_step(float (&x)[32], float tau, int& nbad) {
     float pv = lane_bcast(x[C], C);
-    const bool fail = !(pv > 0.0f);  // not positive, or NaN: the attempt fails
-    const bool small = !(pv > tau);  // at or below the accuracy floor (tau = 0: same as fail)
-    nsmall += small ? 1 : 0;
-    nfail += fail ? 1 : 0;
-    pmin = fail ? pmin : fminf(pmin, pv);
-    asm volatile("" : "+v"(nsmall), "+v"(nfail), "+v"(pmin));
-    pv = fail ? 1.0f : pv;
-    // rsq needs a normal input; a positive subnormal pivot takes the IEEE route.
-    x[C] *= (pv >= 1.17549435e-38f) ? __builtin_amdgcn_rsqf(pv) : 1.0f / sqrtf(pv);
+    nbad += !(pv > tau) ? 1 : 0;  // not above the floor (tau = 0: not positive), or NaN
+    asm volatile("" : "+v"(nbad));
+    pv = (pv > 0.0f) ? pv : 1.0f;
+    // rsq needs a normal input; a positive subnormal pivot takes the IEEE route (pv is uniform,
+    // so this is a scalar branch off the common path).
+    float rs;
+    if (__builtin_expect(pv < 1.17549435e-38f, 0)) rs = 1.0f / sqrtf(pv);
+    else rs = __builtin_amdgcn_rsqf(pv);
+    x[C] *= rs;
 #pragma unroll
     for (int s0 = (C + 1) & ~3; s0 < 32; s0 += 4) {
         float L[4];
@@ -266,9 +266,9 @@ __device__ __forceinline__ void leaf_step(float (&x)[32], float tau, int& nsmall
 }
 
 template <int... C>
-__device__ __forceinline__ void leaf_steps(float (&x)[32], float tau, int& nsmall, int& nfail,
-                                           float& pmin, std::integer_sequence<int, C...>) {
-    (leaf_step<C>(x, tau, nsmall, nfail, pmin), ...);
+__device__ __forceinline__ void leaf_steps(float (&x)[32], float tau, int& nbad,
+                                           std::integer_sequence<int, C...>) {
+    (leaf_step<C>(x, tau, nbad), ...);
 }
 
 __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, float* __restrict__ X,
@@ -297,8 +297,8 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
         }
     }
     __syncthreads();
-    bool small = false, fail = false;
-    float pmin_all = INFINITY;
+    bool bad = false;
+    float pmin = INFINITY;  // lanes 0..31 of wave 0: the smallest L_cc^2 of their rows
     for (int p = 0; p < 4; ++p) {
         const int c0 = 32 * p;
         if (wave == 0) {
@@ -318,19 +318,18 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
                 const float av = Ls[(c0 + row) * DLD + c0 + c];
                 x[c] = tpart ? ((c == row) ? 1.0f : 0.0f) : av;
             }
-            int nsmall = 0, nfail = 0;
-            float pmin = INFINITY;
-            leaf_steps(x, tau, nsmall, nfail, pmin, std::make_integer_sequence<int, 32>{});
+            int nbad = 0;
+            leaf_steps(x, tau, nbad, std::make_integer_sequence<int, 32>{});
             if (!tpart) {
 #pragma unroll
                 for (int c = 0; c < 32; ++c) Ls[(c0 + row) * DLD + c0 + c] = (c <= row) ? x[c] : 0.0f;
+                const float lcc = Ls[(c0 + row) * DLD + c0 + row];  // written by this lane
+                pmin = fminf(pmin, lcc * lcc);
             } else {
 #pragma unroll
                 for (int c = 0; c < 32; ++c) Ts[p][c * SLD + row] = x[c];
             }
-            small = small || nsmall != 0;
-            fail = fail || nfail != 0;
-            pmin_all = fminf(pmin_all, pmin);
+            bad = bad || nbad != 0;
         }
         __syncthreads();
         // Panel: rows below, L_rb = A_rb T_p^T.
@@ -384,10 +383,14 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
-    if (wave == 0 && lane == 0) {
-        if (fail) atomicOr(flag, 1u);
-        else if (small) atomicOr(flag, 2u);
-        atomicMin(minp, __float_as_uint(pmin_all));
+    if (wave == 0) {
+        // The smallest pivot of the block, as the square of L's smallest diagonal entry.
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) pmin = fminf(pmin, __shfl_xor(pmin, off, 32));
+        if (lane == 0) {
+            if (bad) atomicOr(flag, tau > 0.0f ? 2u : 1u);
+            atomicMin(minp, __float_as_uint(pmin));
+        }
     }
     __syncthreads();
     // Output: MI_k as float4 rows (zeros above the diagonal).  Nothing reads L's diagonal block

@@ -13,8 +13,8 @@ constexpr int W64 = 256;    // f64: outer panel (the K of its bulk updates)
 
 // Device-side record of one fold call.
 //   flag  bit 0: a pivot that is not positive (or not finite); the attempt failed.
-//         bit 1: an f32 pivot at or below the f32 accuracy floor (precision "auto" only): the
-//                attempt is abandoned and repeated in f64 at the same damping.
+//         bit 1: an f32 pivot at or below the f32 accuracy floor, or one that failed (precision
+//                "auto" only): the attempt is abandoned and repeated in f64 at the same damping.
 //   minp32 / minp64: the smallest accepted pivot of the attempt, as the bits of a positive f32
 //         / f64 (their integer order is their value order).
 struct FoldState {
