@@ -296,6 +296,8 @@ def main():
     ap.add_argument("--workload", default="down")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gram", action="store_true", help="skip the Hessian accumulation timing")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="skip the timing of the fold from a packed Hessian")
     ap.add_argument("--no-debias", action="store_true", help="skip the output debias timing")
     ap.add_argument("--no-act-order", action="store_true", help="skip the act-order timing")
     ap.add_argument("--no-q2", action="store_true", help="skip the q2tp sweep timing")
@@ -476,7 +478,33 @@ def main():
         result["detail"]["gram_tflops"] = gram_flops / (gram_ms * 1e-3) / 1e12
         result["detail"]["gram_frac_fp32_mfma"] = result["detail"]["gram_tflops"] / FP32_MFMA_PEAK_TFLOPS
         result["detail"]["gram_shape"] = f"H[{n},{n}] += X^T X, X[{Xg.shape[0]},{n}]"
-        del Xg, Hg
+        del Hg
+        # The same accumulation into the packed upper triangle (half the bytes of H).
+        Hpk = torch.zeros(n * (n + 1) // 2, dtype=torch.float32, device=dev)
+        pwq.gptq_gram_add(Hpk, Xg)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            pwq.gptq_gram_add(Hpk, Xg)
+        e1.record(stream)
+        e1.synchronize()
+        result["detail"]["gram_packed_ms"] = e0.elapsed_time(e1) / reps
+        del Xg, Hpk
+    # The fold of the same Hessian handed over as its packed upper triangle.
+    if not args.no_packed:
+        iu = torch.triu_indices(n, n, device=dev)
+        Hpk = H[iu[0], iu[1]].contiguous()
+        del iu
+        pwq.gptq_fold(Hpk, lam, workspace=ws_f, out=(U, hdiag, dead))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(2):
+            pwq.gptq_fold(Hpk, lam, workspace=ws_f, out=(U, hdiag, dead))
+        e1.record(stream)
+        e1.synchronize()
+        result["detail"]["fold_packed_ms"] = e0.elapsed_time(e1) / 2
+        del Hpk
     # Concurrent groups (the batched round): G independent groups, each folded, laddered and
     # swept on its own stream from its own host thread, with preallocated outputs and
     # workspaces; groups/s over whole rounds.

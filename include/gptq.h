@@ -27,6 +27,12 @@
  *   - Workspaces and the matrices a call reads or writes in rows (W, U, E) must be 16-byte
  *     aligned (GPTQ_EINVAL otherwise); device allocations are.
  *   - Calls on different streams may run concurrently if their buffers are disjoint.
+ *   - A Hessian H comes with a leading dimension ldh.  ldh >= n: a dense row-major [n, ldh]
+ *     matrix of which only the upper triangle (with the diagonal) is read or written.
+ *     ldh = GPTQ_PACKED_UPPER: the upper triangle packed row by row, as the pages' device
+ *     Hessian (page "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs", poff): element (i, j >= i)
+ *     at i (2n - i + 1) / 2 + (j - i), n (n + 1) / 2 floats in all, half the dense bytes.
+ *     Both layouts give the same results bit for bit.
  */
 #ifndef GPTQ_MI355X_H
 #define GPTQ_MI355X_H
@@ -47,6 +53,9 @@ enum {
     GPTQ_ECHECK = 5,      /* check mode only (gptq_check.h): the schedule failed its check */
     GPTQ_ETOOBIG = 6      /* larger than the static scratch of gptq_sweep_inplace_noalloc */
 };
+
+/* ldh of a Hessian stored as its packed upper triangle (conventions above). */
+#define GPTQ_PACKED_UPPER ((int64_t)-1)
 
 /* Host-side record of one fold. */
 typedef struct {
@@ -84,10 +93,11 @@ size_t gptq_fold_workspace_size(int64_t n);
 /*
  * gptq_fold_ex -- the damped, equilibrated fold of one Hessian.
  *
- *   H        [n, ldh] f32, device.  Only the UPPER triangle (j >= i) is read; the lower one
- *            may hold anything.  Non-finite entries are allowed: a non-finite or non-positive
- *            diagonal marks the channel dead, anything else fails pivots and raises lambda.
- *   n        channels, 1 <= n <= 2^20.  ldh >= n.
+ *   H        [n, ldh] f32, device, or packed (ldh = GPTQ_PACKED_UPPER).  Only the UPPER
+ *            triangle (j >= i) is read; a dense lower one may hold anything.  Non-finite
+ *            entries are allowed: a non-finite or non-positive diagonal marks the channel dead,
+ *            anything else fails pivots and raises lambda.
+ *   n        channels, 1 <= n <= 2^20.  ldh >= n or GPTQ_PACKED_UPPER.
  *   lambda   starting relative damping (negative or NaN is treated as 0).  A pivot that fails
  *            (see the precisions above) restarts the factorization with lambda -> 1e-4 (from
  *            0) or lambda * 10; past 10 the call writes U = I and returns GPTQ_DEGENERATE (the
@@ -209,10 +219,11 @@ int gptq_sweep_inplace_noalloc(float* W, const float* U, const float* hdiag, con
  * h[i][j] += x[r][i] x[r][j] over the rows of x [t, n]); the fold reads the upper triangle.
  *
  *   H      [n, ldh] f32, device, in/out: H[i][j] += sum_{k < t} X[k][i] X[k][j] for j >= i
- *          (the upper triangle with the diagonal, which gptq_fold reads).  The lower triangle
- *          is neither read nor written.  f32 products, f32 MFMA accumulation (the pages'
- *          device Hessian is f32).
- *   n      channels: 4 <= n, n % 4 == 0, ldh >= n.
+ *          (the upper triangle with the diagonal, which gptq_fold reads).  A dense lower
+ *          triangle is neither read nor written.  ldh = GPTQ_PACKED_UPPER accumulates into the
+ *          packed upper triangle, the pages' device layout, with the same values bit for bit.
+ *          f32 products, f32 MFMA accumulation (the pages' device Hessian is f32).
+ *   n      channels: 4 <= n, n % 4 == 0, ldh >= n or GPTQ_PACKED_UPPER.
  *   X      [t, ldx] f32, device, row-major: one row per token, column i = input channel i;
  *          16-byte aligned, ldx >= n, ldx % 4 == 0.  Read only.
  *   t      tokens in this batch, >= 0 (0: nothing is done and X may be NULL).  Any t: the
@@ -235,8 +246,9 @@ size_t gptq_debias_workspace_size(int64_t rows, int64_t n);
  * nearest even), kept when num or den is not positive and finite.
  *
  *   W      [rows, n] f32, device: the original weights (dead columns read as 0).
- *   H      [n, ldh] f32, device: the raw Hessian, upper triangle read (as gptq_fold).  Dead
- *          channels (dead[i] != 0) count as zero rows and columns.
+ *   H      [n, ldh] f32, device, or packed (ldh = GPTQ_PACKED_UPPER): the raw Hessian, upper
+ *          triangle read (as gptq_fold).  Dead channels (dead[i] != 0) count as zero rows and
+ *          columns.
  *   dead   [n] u8, device (gptq_fold's output).
  *   nib, rung   gptq_sweep's codes: nibble plane [rows, n/2] and rungs [rows, n/32].
  *   lost   [rows, 2] f32, device, in/out: (lo, step); lo is replaced.
@@ -262,15 +274,15 @@ int gptq_debias(const float* W, const float* H, int64_t ldh, const uint8_t* dead
  *
  * gptq_act_order_perm: perm [n] i32 out, the channels by descending H_ii compared in the f32
  *   total order (-NaN < -inf < ... < -0 < +0 < ... < +inf < +NaN), ties by ascending index;
- *   dead [n] u8 out, 1 where !(H_ii > 0) (original order).  H [n, ldh] f32, only its diagonal
- *   is read.
+ *   dead [n] u8 out, 1 where !(H_ii > 0) (original order).  H [n, ldh] f32 or packed
+ *   (ldh = GPTQ_PACKED_UPPER), only its diagonal is read.
  */
 int gptq_act_order_perm(const float* H, int64_t n, int64_t ldh, int32_t* perm, uint8_t* dead,
                         void* stream);
 
-/* gptq_permute_hessian: Hp [n, n] f32 out (full, symmetric) = H[perm][perm], H read through its
- * upper triangle (H[min][max]).  perm must be a permutation of 0..n-1; an entry outside that
- * range gives zero rows and columns. */
+/* gptq_permute_hessian: Hp [n, n] f32 out (full, symmetric, dense) = H[perm][perm], H (dense or
+ * packed) read through its upper triangle (H[min][max]).  perm must be a permutation of
+ * 0..n-1; an entry outside that range gives zero rows and columns. */
 int gptq_permute_hessian(const float* H, int64_t n, int64_t ldh, const int32_t* perm, float* Hp,
                          void* stream);
 

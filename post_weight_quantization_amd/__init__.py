@@ -11,6 +11,7 @@ raise.  Names follow the C ABI in ``include/gptq.h``:
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -19,6 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgptq_mi355x.so")
 
 GPTQ_OK, GPTQ_EINVAL, GPTQ_EWORKSPACE, GPTQ_EHIP, GPTQ_DEGENERATE, GPTQ_ECHECK, GPTQ_ETOOBIG = 0, 1, 2, 3, 4, 5, 6
+GPTQ_PACKED_UPPER = -1  # ldh of a Hessian stored as its packed upper triangle
 
 _lib = None
 
@@ -161,6 +163,23 @@ def _dev_rows(t: torch.Tensor, dtype, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _hessian(H: torch.Tensor, device=None):
+    """(pointer, n, ldh) of a Hessian: a 2-D [n, n] tensor (rows may be padded) is passed as
+    dense rows; a 1-D tensor of n (n + 1) / 2 floats as the packed upper triangle, row by row
+    (ldh = GPTQ_PACKED_UPPER)."""
+    if isinstance(H, torch.Tensor) and H.dim() == 1:
+        P = H.numel()
+        n = (math.isqrt(8 * P + 1) - 1) // 2
+        if n < 1 or n * (n + 1) // 2 != P:
+            raise ValueError("a packed H must hold n (n + 1) / 2 floats")
+        return _dev(H, torch.float32, "H", device=device), n, GPTQ_PACKED_UPPER
+    if not isinstance(H, torch.Tensor) or H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise ValueError("H must be [n, n], or its packed upper triangle (1-D)")
+    if device is not None and H.device != device:
+        raise ValueError(f"H is on {H.device}, the call's tensors on {device}")
+    return _dev_rows(H, torch.float32, "H"), H.shape[0], H.stride(0)
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -193,14 +212,12 @@ def sweep_workspace_size(rows: int, n: int) -> int:
 
 def gptq_fold(H: torch.Tensor, lam: float, workspace: torch.Tensor | None = None, stream=None,
               out=None, check=True, precision: str = "auto"):
-    """Fold H (f32 [n, n], upper triangle read; rows may be padded).  ``precision`` is "auto"
-    (f32, repeated in f64 where a pivot is at or below 1e-3), "f32" or "f64".  Returns
-    (U, hdiag, dead, report dict)."""
+    """Fold H (f32 [n, n], upper triangle read, rows may be padded; or its packed upper
+    triangle, 1-D).  ``precision`` is "auto" (f32, repeated in f64 where a pivot is at or below
+    1e-2), "f32" or "f64".  Returns (U, hdiag, dead, report dict)."""
     lib = load()
-    if H.dim() != 2 or H.shape[0] != H.shape[1]:
-        raise ValueError("H must be [n, n]")
-    n = H.shape[0]
     dev = H.device
+    h_ptr, n, ldh = _hessian(H)
     prec = FOLD_PRECISION[precision]
     need = int(lib.gptq_fold_workspace_size_ex(n, prec))
     with _on(stream, dev):
@@ -212,7 +229,7 @@ def gptq_fold(H: torch.Tensor, lam: float, workspace: torch.Tensor | None = None
             U, hdiag, dead = out
         workspace = _workspace(workspace, need, dev)
     rep = FoldReport()
-    st = lib.gptq_fold_ex(_dev_rows(H, torch.float32, "H"), n, H.stride(0), float(lam), prec,
+    st = lib.gptq_fold_ex(h_ptr, n, ldh, float(lam), prec,
                           _dev(U, torch.float32, "U", (n, n), device=dev),
                           _dev(hdiag, torch.float32, "hdiag", (n,), device=dev),
                           _dev(dead, torch.uint8, "dead", (n,), device=dev),
@@ -315,17 +332,15 @@ def gptq_sweep_inplace(W, U, hdiag, dead, tab, lost, want_E=False, workspace=Non
 
 
 def gptq_gram_add(H: torch.Tensor, X: torch.Tensor, stream=None):
-    """H (f32 [n, n], device) += X^T X on its upper triangle, X f32 [t, n] (tokens x channels).
-    Returns H."""
+    """H (f32 [n, n], device; or its packed upper triangle, 1-D) += X^T X on its upper
+    triangle, X f32 [t, n] (tokens x channels).  Returns H."""
     lib = load()
-    n = H.shape[0]
-    if H.dim() != 2 or H.shape[1] != n:
-        raise ValueError("H must be [n, n]")
+    h_ptr, n, ldh = _hessian(H)
     if X.dim() != 2 or X.shape[1] != n:
         raise ValueError("X must be [t, n] with n = H.shape[0]")
     if X.device != H.device:
         raise ValueError("X and H must be on one device")
-    st = lib.gptq_gram_add(_dev_rows(H, torch.float32, "H"), n, H.stride(0),
+    st = lib.gptq_gram_add(h_ptr, n, ldh,
                            _dev_rows(X, torch.float32, "X"), X.shape[0], X.stride(0), _stream(stream))
     if st != GPTQ_OK:
         raise GptqError(st, "gptq_gram_add")
@@ -343,15 +358,16 @@ def gptq_debias(W, H, dead, nib, rung, lost, scale, want_tab=True, want_slope=Tr
     lib = load()
     rows, n = W.shape
     dev = W.device
-    if H.dim() != 2 or H.shape[0] != n or H.shape[1] != n or H.stride(1) != 1:
-        raise ValueError("H must be a row-major [n, n] matrix")
+    h_ptr, hn, ldh = _hessian(H, dev)
+    if hn != n:
+        raise ValueError(f"H has {hn} channels, W {n}")
     need = int(lib.gptq_debias_workspace_size(rows, n))
     with _on(stream, dev):
         tab = torch.empty(rows, 32, dtype=torch.float32, device=dev) if want_tab else None
         slope = torch.empty(rows, dtype=torch.float64, device=dev) if want_slope else None
         workspace = _workspace(workspace, need, dev)
-    st = lib.gptq_debias(_dev(W, torch.float32, "W", align=16), _dev_rows(H, torch.float32, "H"),
-                         H.stride(0), _dev(dead, torch.uint8, "dead", (n,), device=dev),
+    st = lib.gptq_debias(_dev(W, torch.float32, "W", align=16), h_ptr,
+                         ldh, _dev(dead, torch.uint8, "dead", (n,), device=dev),
                          _dev(nib, torch.uint8, "nib", (rows, n // 2), 16, dev),
                          _dev(rung, torch.uint8, "rung", (rows, n // 32), device=dev),
                          _dev(lost, torch.float32, "lost", (rows, 2), 8, dev),
@@ -372,15 +388,16 @@ def gptq_debias_q2(W, H, dead, plane, rung, lost, scale, want_tab=True, want_slo
     lib = load()
     rows, n = W.shape
     dev = W.device
-    if H.dim() != 2 or H.shape[0] != n or H.shape[1] != n or H.stride(1) != 1:
-        raise ValueError("H must be a row-major [n, n] matrix")
+    h_ptr, hn, ldh = _hessian(H, dev)
+    if hn != n:
+        raise ValueError(f"H has {hn} channels, W {n}")
     need = int(lib.gptq_debias_workspace_size(rows, n))
     with _on(stream, dev):
         tab = torch.empty(rows, 32, dtype=torch.float32, device=dev) if want_tab else None
         slope = torch.empty(rows, dtype=torch.float64, device=dev) if want_slope else None
         workspace = _workspace(workspace, need, dev)
-    st = lib.gptq_debias_q2(_dev(W, torch.float32, "W", align=16), _dev_rows(H, torch.float32, "H"),
-                            H.stride(0), _dev(dead, torch.uint8, "dead", (n,), device=dev),
+    st = lib.gptq_debias_q2(_dev(W, torch.float32, "W", align=16), h_ptr,
+                            ldh, _dev(dead, torch.uint8, "dead", (n,), device=dev),
                             _dev(plane, torch.uint8, "plane", (rows, n // 4), device=dev),
                             _dev(rung, torch.uint8, "rung", (rows, n // 32), device=dev),
                             _dev(lost, torch.float32, "lost", (rows, 2), 8, dev),
@@ -474,16 +491,14 @@ def sweep_act_order_workspace_size(rows: int, n: int) -> int:
 
 
 def gptq_act_order_perm(H, stream=None):
-    """(perm i32 [n], dead u8 [n]) of act-order GPTQ from H's diagonal."""
+    """(perm i32 [n], dead u8 [n]) of act-order GPTQ from H's diagonal (H dense or packed)."""
     lib = load()
-    n = H.shape[0]
     dev = H.device
-    if H.dim() != 2 or H.shape[1] != n or H.stride(1) != 1:
-        raise ValueError("H must be a row-major [n, n] matrix")
+    h_ptr, n, ldh = _hessian(H)
     with _on(stream, dev):
         perm = torch.empty(n, dtype=torch.int32, device=dev)
         dead = torch.empty(n, dtype=torch.uint8, device=dev)
-    st = lib.gptq_act_order_perm(_dev_rows(H, torch.float32, "H"), n, H.stride(0),
+    st = lib.gptq_act_order_perm(h_ptr, n, ldh,
                                  _dev(perm, torch.int32, "perm"), _dev(dead, torch.uint8, "dead"),
                                  _stream(stream))
     if st != GPTQ_OK:
@@ -492,15 +507,14 @@ def gptq_act_order_perm(H, stream=None):
 
 
 def gptq_permute_hessian(H, perm, stream=None):
-    """H[perm][perm] (f32 [n, n], full symmetric) from H's upper triangle."""
+    """H[perm][perm] (f32 [n, n], full symmetric) from H's upper triangle (H dense or
+    packed)."""
     lib = load()
-    n = H.shape[0]
     dev = H.device
-    if H.dim() != 2 or H.shape[1] != n or H.stride(1) != 1:
-        raise ValueError("H must be a row-major [n, n] matrix")
+    h_ptr, n, ldh = _hessian(H)
     with _on(stream, dev):
         Hp = torch.empty(n, n, dtype=torch.float32, device=dev)
-    st = lib.gptq_permute_hessian(_dev_rows(H, torch.float32, "H"), n, H.stride(0),
+    st = lib.gptq_permute_hessian(h_ptr, n, ldh,
                                   _dev(perm, torch.int32, "perm", (n,), device=dev),
                                   _dev(Hp, torch.float32, "Hp"), _stream(stream))
     if st != GPTQ_OK:

@@ -26,21 +26,21 @@ __device__ __forceinline__ int32_t total_key(float x) {
 
 // Four threads per channel i (64 channels per workgroup), each counting the channels j before
 // i in one quarter of every 1024-key chunk; the four counts are summed with lane shuffles.
-__global__ __launch_bounds__(256) void act_rank_kernel(const float* __restrict__ H, int64_t ldh,
+__global__ __launch_bounds__(256) void act_rank_kernel(const float* __restrict__ H, HLayout hl,
                                                        int64_t n, int32_t* __restrict__ perm,
                                                        uint8_t* __restrict__ dead) {
     __shared__ int32_t keys[1024];
     const int part = threadIdx.x & 3;
     const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
     const bool live = i < n;
-    const float hi = live ? H[i * ldh + i] : 0.0f;
+    const float hi = live ? H[hl.at(i, i)] : 0.0f;
     const int32_t ki = total_key(hi);
     int rank = 0;
     for (int64_t j0 = 0; j0 < n; j0 += 1024) {
         __syncthreads();
         for (int t = threadIdx.x; t < 1024; t += 256) {
             const int64_t j = j0 + t;
-            keys[t] = (j < n) ? total_key(H[j * ldh + j]) : INT32_MIN;
+            keys[t] = (j < n) ? total_key(H[hl.at(j, j)]) : INT32_MIN;
         }
         __syncthreads();
         const int m = (n - j0 < 1024) ? (int)(n - j0) : 1024;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void act_rank_kernel(const float* __restrict__
 // (Hp[a][b] = H[min(pa, pb)][max(pa, pb)]) into LDS, stored in place and, off the diagonal,
 // stored again transposed at (B, A); both stores coalesce.
 __global__ __launch_bounds__(256) void act_permute_kernel(const float* __restrict__ H,
-                                                          int64_t ldh,
+                                                          HLayout hl,
                                                           const int32_t* __restrict__ perm,
                                                           int64_t n, float* __restrict__ Hp) {
     __shared__ float tile[32][33];
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void act_permute_kernel(const float* __restric
         if (a < n && b < n) {
             const int64_t pa = perm[a];
             if (pa >= 0 && pa < n && pb >= 0 && pb < n)
-                v = (pa <= pb) ? H[pa * ldh + pb] : H[pb * ldh + pa];
+                v = (pa <= pb) ? H[hl.at(pa, pb)] : H[hl.at(pb, pa)];
             Hp[a * n + b] = v;
         }
         tile[rr][tx] = v;
@@ -99,31 +99,35 @@ using namespace gptq;
 
 extern "C" int gptq_act_order_perm(const float* H, int64_t n, int64_t ldh, int32_t* perm,
                                    uint8_t* dead, void* stream) {
-    if (!H || !perm || !dead || n <= 0 || ldh < n || n > ((int64_t)1 << 24)) return GPTQ_EINVAL;
+    if (!H || !perm || !dead || n <= 0 || !hessian_ld_ok(n, ldh) || n > ((int64_t)1 << 24))
+        return GPTQ_EINVAL;
     CheckScope check;
-    check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
+    check_buffer(H, sizeof(float) * (size_t)hessian_elems(n, ldh), "H");
     check_buffer(perm, sizeof(int32_t) * (size_t)n, "perm");
     check_buffer(dead, (size_t)n, "dead");
     hipStream_t st = (hipStream_t)stream;
     GPTQ_LAUNCH(st, "act_rank",
-                (act_rank_kernel<<<(unsigned)((n + 63) / 64), 256, 0, st>>>(H, ldh, n, perm, dead)),
-                rd(H, ldh + 1, n, 1), wr(perm, n, 1, n), wr(dead, n, 1, n, 1));
+                (act_rank_kernel<<<(unsigned)((n + 63) / 64), 256, 0, st>>>(H, HLayout{n, ldh}, n, perm,
+                                                                             dead)),
+                hessian_span(H, n, ldh, false), wr(perm, n, 1, n), wr(dead, n, 1, n, 1));
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     return check.finish();
 }
 
 extern "C" int gptq_permute_hessian(const float* H, int64_t n, int64_t ldh, const int32_t* perm,
                                     float* Hp, void* stream) {
-    if (!H || !perm || !Hp || n <= 0 || ldh < n || n > ((int64_t)1 << 20)) return GPTQ_EINVAL;
+    if (!H || !perm || !Hp || n <= 0 || !hessian_ld_ok(n, ldh) || n > ((int64_t)1 << 20))
+        return GPTQ_EINVAL;
     CheckScope check;
-    check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
+    check_buffer(H, sizeof(float) * (size_t)hessian_elems(n, ldh), "H");
     check_buffer(perm, sizeof(int32_t) * (size_t)n, "perm");
     check_buffer(Hp, sizeof(float) * (size_t)(n * n), "Hp");
     hipStream_t st = (hipStream_t)stream;
     const unsigned nt = (unsigned)((n + 31) / 32);
     GPTQ_LAUNCH(st, "act_permute",
-                (act_permute_kernel<<<nt * (nt + 1) / 2, 256, 0, st>>>(H, ldh, perm, n, Hp)),
-                rd(H, ldh, n, n), rd(perm, n, 1, n), wr(Hp, n, n, n));
+                (act_permute_kernel<<<nt * (nt + 1) / 2, 256, 0, st>>>(H, HLayout{n, ldh}, perm, n,
+                                                                         Hp)),
+                hessian_span(H, n, ldh, false), rd(perm, n, 1, n), wr(Hp, n, n, n));
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     return check.finish();
 }

@@ -30,6 +30,15 @@ inline Span rd(const void* p, int64_t ld, int64_t rows, int64_t cols, int esize 
 inline Span wr(const void* p, int64_t ld, int64_t rows, int64_t cols, int esize = 4) {
     return Span{p, ld, rows, cols, esize, true};
 }
+// The whole of a Hessian (f32) of either layout: its n x n rows when dense, its n (n + 1) / 2
+// floats when packed (ldh < 0).
+inline Span hessian_span(const void* H, int64_t n, int64_t ldh, bool write) {
+    if (ldh < 0) {
+        const int64_t P = n * (n + 1) / 2;
+        return Span{H, P, 1, P, 4, write};
+    }
+    return Span{H, ldh, n, n, 4, write};
+}
 
 // True while the calling thread runs an entry point in check mode.
 bool dry_run();

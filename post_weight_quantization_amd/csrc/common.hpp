@@ -52,6 +52,25 @@ struct ProfScope {
     ~ProfScope();
 };
 
+// Storage of a Hessian (ldh >= n: dense rows; ldh = GPTQ_PACKED_UPPER: the upper triangle
+// packed by rows, element (i, j >= i) at i (2n - i + 1) / 2 + j - i).  The upper part of row i
+// is contiguous in both, so element (i, j >= i) is at row(i) + j; in the packed layout row(i)
+// is i (2n - i - 1) / 2, the packed offset of row i less i.  Any (i, j) inside n x n maps
+// inside the buffer (for j < i to some other element of the triangle), so clamped reads that
+// are never used stay in bounds.
+struct HLayout {
+    int64_t n, ldh;
+    __host__ __device__ int64_t row(int64_t i) const {
+        return ldh >= 0 ? i * ldh : (i * (2 * n - i - 1)) >> 1;
+    }
+    __host__ __device__ int64_t at(int64_t i, int64_t j) const { return row(i) + j; }
+};
+inline bool hessian_ld_ok(int64_t n, int64_t ldh) { return ldh == GPTQ_PACKED_UPPER || ldh >= n; }
+// Floats a Hessian of the layout spans (n >= 1).
+inline int64_t hessian_elems(int64_t n, int64_t ldh) {
+    return ldh < 0 ? n * (n + 1) / 2 : (n - 1) * ldh + n;
+}
+
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // 16-byte alignment, which every pointer the kernels read or write as float4 / double2 needs
 // (NULL counts as aligned: optional outputs).

@@ -29,7 +29,7 @@
 
 namespace gptq {
 
-__global__ __launch_bounds__(256) void debias_sym_kernel(const float* __restrict__ H, int64_t ldh,
+__global__ __launch_bounds__(256) void debias_sym_kernel(const float* __restrict__ H, HLayout hl,
                                                          const uint8_t* __restrict__ dead,
                                                          float* __restrict__ Hs, int64_t n) {
     __shared__ float tile[32][33];
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void debias_sym_kernel(const float* __restrict
         for (int r = ty; r < 32; r += 8) {
             const int64_t i = bi * 32 + r, j = bj * 32 + tx;
             if (i < n && j < n) {
-                float v = (j >= i) ? H[i * ldh + j] : H[j * ldh + i];
+                float v = (j >= i) ? H[hl.at(i, j)] : H[hl.at(j, i)];
                 if (dead[i] || dead[j]) v = 0.0f;
                 Hs[i * n + j] = v;
             }
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void debias_sym_kernel(const float* __restrict
         // Below: the transpose of tile (bj, bi) of H's upper triangle, staged through LDS.
         for (int r = ty; r < 32; r += 8) {
             const int64_t i = bj * 32 + r, j = bi * 32 + tx;  // element of H, j > i
-            tile[r][tx] = (i < n && j < n) ? H[i * ldh + j] : 0.0f;
+            tile[r][tx] = (i < n && j < n) ? H[hl.at(i, j)] : 0.0f;
         }
         __syncthreads();
         for (int r = ty; r < 32; r += 8) {
@@ -167,7 +167,7 @@ static int debias_impl(const float* W, const float* H, int64_t ldh, const uint8_
                        const uint8_t* nib, const uint8_t* rung, float* lost, float* tab,
                        float* scale, double* slope, int64_t rows, int64_t n, void* workspace,
                        size_t workspace_bytes, void* stream, bool two_bit) {
-    if (rows <= 0 || n < 32 || n % 32 != 0 || ldh < n || !W || !H || !dead || !nib || !rung ||
+    if (rows <= 0 || n < 32 || n % 32 != 0 || !hessian_ld_ok(n, ldh) || !W || !H || !dead || !nib || !rung ||
         !lost || !scale || !workspace)
         return GPTQ_EINVAL;
     if (rows > ((int64_t)1 << 31) - 1 || n > ((int64_t)1 << 20)) return GPTQ_EINVAL;
@@ -176,7 +176,7 @@ static int debias_impl(const float* W, const float* H, int64_t ldh, const uint8_
     if (workspace_bytes < debias_ws(rows, n, &off_y)) return GPTQ_EWORKSPACE;
     CheckScope check;
     check_buffer(W, sizeof(float) * (size_t)(rows * n), "W");
-    check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
+    check_buffer(H, sizeof(float) * (size_t)hessian_elems(n, ldh), "H");
     check_buffer(dead, (size_t)n, "dead");
     const int64_t cb = two_bit ? n / 4 : n / 2;  // code bytes per row
     check_buffer(nib, (size_t)(rows * cb), "codes");
@@ -192,8 +192,8 @@ static int debias_impl(const float* W, const float* H, int64_t ldh, const uint8_
     {
         const unsigned nt = (unsigned)((n + 31) / 32);
         ProfScope ps(FAM_DEBIAS, st, 0.0, 4.0 * (double)n * n * 1.5);
-        GPTQ_LAUNCH(st, "debias_sym", (debias_sym_kernel<<<dim3(nt, nt), 256, 0, st>>>(H, ldh, dead, Hs, n)),
-                    rd(H, ldh, n, n), rd(dead, n, 1, n, 1), wr(Hs, n, n, n));
+        GPTQ_LAUNCH(st, "debias_sym", (debias_sym_kernel<<<dim3(nt, nt), 256, 0, st>>>(H, HLayout{n, ldh}, dead, Hs, n)),
+                    hessian_span(H, n, ldh, false), rd(dead, n, 1, n, 1), wr(Hs, n, n, n));
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     {

@@ -39,7 +39,7 @@ namespace gptq {
 // Diagonal, dead mask, mean of the diagonal with dead channels counted as 1 (f64, fixed
 // reduction order).
 __global__ __launch_bounds__(1024) void fold_prep_kernel(const float* __restrict__ H, int64_t n,
-                                                          int64_t ldh, float* __restrict__ hdiag,
+                                                          HLayout hl, float* __restrict__ hdiag,
                                                           uint8_t* __restrict__ dead,
                                                           FoldState* st) {
     __shared__ double ssum[1024];
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(1024) void fold_prep_kernel(const float* __restrict
     // keep their order).
 #pragma unroll 8
     for (int64_t i = t; i < n; i += 1024) {
-        const float d = H[i * ldh + i];
+        const float d = H[hl.at(i, i)];
         const bool dd = !(d > 0.0f);
         hdiag[i] = d;
         dead[i] = dd ? 1 : 0;
@@ -96,12 +96,13 @@ __global__ void fold_scale_kernel(const float* __restrict__ hdiag, const uint8_t
 
 // A[i][j] (i >= j) = reversed, damped, equilibrated H read from its upper triangle; the
 // padding block is the identity; entries above the diagonal inside diagonal 64 x 64 tiles are 0.
-// One workgroup per lower 64 x 64 tile (the grid enumerates only those).  VEC (n and ldh
-// multiples of 4, H 16-byte aligned): each thread takes 4 adjacent columns of 4 rows, as float4
-// reads of H (4 adjacent columns of H in reverse order) and float4 writes of A; otherwise a
-// row of the tile is one wave of single floats.  Both coalesce.
+// One workgroup per lower 64 x 64 tile (the grid enumerates only those).  VEC (dense H, n and
+// ldh multiples of 4, H 16-byte aligned): each thread takes 4 adjacent columns of 4 rows, as
+// float4 reads of H (4 adjacent columns of H in reverse order) and float4 writes of A;
+// otherwise (also for the packed layout, whose rows start at any float) a row of the tile is
+// one wave of single floats.  Both coalesce.
 template <bool VEC>
-__global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict__ H, int64_t ldh,
+__global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict__ H, HLayout hl,
                                                          const float* __restrict__ dinv,
                                                          const uint8_t* __restrict__ dead,
                                                          const FoldState* st, double lam,
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict
                 const int64_t a = n - 1 - i;
                 const bool dead_a = dead[a] != 0;
                 const float da = dinv[a];
-                const f32x4 h4 = *reinterpret_cast<const f32x4*>(H + a * ldh + bc4);
+                const f32x4 h4 = *reinterpret_cast<const f32x4*>(H + hl.at(a, bc4));
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int64_t j = j4 + u, bcol = n - 1 - j;  // H column of A's column j
@@ -175,9 +176,9 @@ __global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict
                     v = (a == bc) ? 1.0f : 0.0f;
                 } else if (a == bc) {
                     const double di = (double)db;
-                    v = (float)(((double)H[a * ldh + a] + damp) * di * di);
+                    v = (float)(((double)H[hl.at(a, a)] + damp) * di * di);
                 } else {
-                    v = H[a * ldh + bc] * dinv[a] * db;
+                    v = H[hl.at(a, bc)] * dinv[a] * db;
                 }
             }
             A[i * np + j] = v;
@@ -518,7 +519,8 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
 extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambda, int precision,
                             float* U, float* hdiag, uint8_t* dead, void* workspace,
                             size_t workspace_bytes, void* stream, gptq_fold_report* report) {
-    if (n <= 0 || ldh < n || !H || !U || !hdiag || !dead || !workspace) return GPTQ_EINVAL;
+    if (n <= 0 || !hessian_ld_ok(n, ldh) || !H || !U || !hdiag || !dead || !workspace)
+        return GPTQ_EINVAL;
     if (n > (int64_t)1 << 20) return GPTQ_EINVAL;
     if (precision != GPTQ_FOLD_AUTO && precision != GPTQ_FOLD_F32 && precision != GPTQ_FOLD_F64)
         return GPTQ_EINVAL;
@@ -526,7 +528,7 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
     const FoldLayout L = fold_layout(n);
     if (workspace_bytes < (precision == GPTQ_FOLD_F32 ? L.total_f32 : L.total)) return GPTQ_EWORKSPACE;
     CheckScope check;
-    check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
+    check_buffer(H, sizeof(float) * (size_t)hessian_elems(n, ldh), "H");
     check_buffer(U, sizeof(float) * (size_t)(n * n), "U");
     check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
     check_buffer(dead, (size_t)n, "dead");
@@ -542,11 +544,12 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
     float* Xt = (float*)(ws + L.off_xt);
     const int64_t np = L.np;
     const Span st_rw = wr(state, 1, 1, sizeof(FoldState), 1);
+    const HLayout hl{n, ldh};
 
     {
         ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 8.0 * n);
-        GPTQ_LAUNCH(st, "fold_prep", (fold_prep_kernel<<<1, 1024, 0, st>>>(H, n, ldh, hdiag, dead, state)),
-                    rd(H, ldh + 1, n, 1), wr(hdiag, n, 1, n), wr(dead, n, 1, n, 1), st_rw);
+        GPTQ_LAUNCH(st, "fold_prep", (fold_prep_kernel<<<1, 1024, 0, st>>>(H, n, hl, hdiag, dead, state)),
+                    hessian_span(H, n, ldh, false), wr(hdiag, n, 1, n), wr(dead, n, 1, n, 1), st_rw);
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
 
@@ -574,7 +577,7 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
     for (;;) {
         ++attempts;
         if (use64) {
-            FOLD_OK(fold64_attempt(H, n, ldh, hdiag, dead, state, lam, ws, L, st));
+            FOLD_OK(fold64_attempt(H, hl, hdiag, dead, state, lam, ws, L, st));
         } else {
         {
             ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 4.0 * (double)n * n + 4.0 * (double)np * np / 2);
@@ -582,15 +585,15 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
                         (fold_scale_kernel<<<(unsigned)((np + 255) / 256), 256, 0, st>>>(
                             hdiag, dead, state, lam, n, np, dinv)),
                         rd(hdiag, n, 1, n), rd(dead, n, 1, n, 1), st_rw, wr(dinv, np, 1, np));
-            const bool build_vec = n % 4 == 0 && ldh % 4 == 0 && ((uintptr_t)H & 15u) == 0;
+            const bool build_vec = ldh >= 0 && n % 4 == 0 && ldh % 4 == 0 && al16(H);
             const unsigned build_grid = (unsigned)((np / 64) * (np / 64 + 1) / 2);
             GPTQ_LAUNCH(st, "fold_build",
                         (build_vec
                              ? fold_build_kernel<true><<<build_grid, 256, 0, st>>>(
-                                   H, ldh, dinv, dead, state, lam, A, n, np)
+                                   H, hl, dinv, dead, state, lam, A, n, np)
                              : fold_build_kernel<false><<<build_grid, 256, 0, st>>>(
-                                   H, ldh, dinv, dead, state, lam, A, n, np)),
-                        rd(H, ldh, n, n), rd(dinv, np, 1, np), rd(dead, n, 1, n, 1),
+                                   H, hl, dinv, dead, state, lam, A, n, np)),
+                        hessian_span(H, n, ldh, false), rd(dinv, np, 1, np), rd(dead, n, 1, n, 1),
                         rd(state, 1, 1, sizeof(FoldState), 1), wr(A, np, np, np));
         }
         if (launch_status() != GPTQ_OK) return GPTQ_EHIP;

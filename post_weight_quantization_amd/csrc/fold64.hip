@@ -56,7 +56,7 @@ __global__ void fold64_scale_kernel(const float* __restrict__ hdiag, const uint8
 // f64; the padding block is the identity and the entries above the diagonal inside diagonal
 // tiles are 0.  One workgroup per lower 64 x 64 tile; a wave covers one row of the tile, so the
 // reads of H (its columns in reverse order) and the writes of A coalesce.
-__global__ __launch_bounds__(256) void fold64_build_kernel(const float* __restrict__ H, int64_t ldh,
+__global__ __launch_bounds__(256) void fold64_build_kernel(const float* __restrict__ H, HLayout hl,
                                                            const double* __restrict__ dinv,
                                                            const uint8_t* __restrict__ dead,
                                                            const FoldState* st, double lam,
@@ -81,8 +81,8 @@ __global__ __launch_bounds__(256) void fold64_build_kernel(const float* __restri
         } else {
             const int64_t a = n - 1 - i;  // a <= bc: the upper triangle of H
             if (dead[a] || dead_b) v = (a == bc) ? 1.0 : 0.0;
-            else if (a == bc) v = ((double)H[a * ldh + a] + damp) * db * db;
-            else v = (double)H[a * ldh + bc] * dinv[a] * db;
+            else if (a == bc) v = ((double)H[hl.at(a, a)] + damp) * db * db;
+            else v = (double)H[hl.at(a, bc)] * dinv[a] * db;
         }
         A[i * np + j] = v;
     }
@@ -218,9 +218,9 @@ __global__ __launch_bounds__(256) void fold64_make_u_kernel(const double* __rest
         if (rc_ != GPTQ_OK) return rc_; \
     } while (0)
 
-int fold64_attempt(const float* H, int64_t n, int64_t ldh, const float* hdiag, const uint8_t* dead,
+int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t* dead,
                    FoldState* state, double lam, char* ws, const FoldLayout& L, hipStream_t st) {
-    const int64_t np = L.np;
+    const int64_t n = hl.n, np = L.np;
     double* A = (double*)(ws + L.off_a);
     double* X = (double*)(ws + L.off_x64);
     double* MI = (double*)(ws + L.off_mi64);
@@ -237,8 +237,8 @@ int fold64_attempt(const float* H, int64_t n, int64_t ldh, const float* hdiag, c
                     rd(hdiag, n, 1, n), rd(dead, n, 1, n, 1), st_rw, wr(dinv, np, 1, np, 8));
         const unsigned grid = (unsigned)((np / 64) * (np / 64 + 1) / 2);
         GPTQ_LAUNCH(st, "fold64_build",
-                    (fold64_build_kernel<<<grid, 256, 0, st>>>(H, ldh, dinv, dead, state, lam, A, n, np)),
-                    rd(H, ldh, n, n), rd(dinv, np, 1, np, 8), rd(dead, n, 1, n, 1),
+                    (fold64_build_kernel<<<grid, 256, 0, st>>>(H, hl, dinv, dead, state, lam, A, n, np)),
+                    hessian_span(H, n, hl.ldh, false), rd(dinv, np, 1, np, 8), rd(dead, n, 1, n, 1),
                     rd(state, 1, 1, sizeof(FoldState), 1), wr(A, np, np, np, 8));
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;

@@ -10,8 +10,9 @@
 // the product come from rows of X: A(i, k) = X[k][i], B(k, j) = X[k][j].  Each workgroup owns a
 // 128 x 128 tile of H on or above the diagonal (diagonal tiles store j >= i only); the token axis
 // is the K of the product, consumed 32 rows of X at a time through LDS (double buffered), with
-// the last chunk zero-filled past t.  MFMA v_mfma_f32_32x32x2_f32, 4 waves of 64 x 64 per tile,
-// the same register and lane layout as the GEMM of the fold.
+// the last chunk zero-filled past t.  MFMA v_mfma_f32_32x32x2_f32, 4 waves of 64 x 64 per
+// tile, the same register and lane layout as the GEMM of the fold.  H is dense or packed
+// (HLayout): only the addressing of its tile differs, so both layouts receive the same sums.
 #include "check.hpp"
 #include "common.hpp"
 #include "gemm_mfma.hpp"
@@ -21,7 +22,8 @@ namespace gptq {
 struct GramArgs {
     float* H;
     const float* X;
-    int64_t ldh, ldx;
+    HLayout hl;
+    int64_t ldx;
     int n, t;
     int T;       // ceil(n / 128) tile rows
     int tiles;   // T (T + 1) / 2 upper tiles
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(G_THREADS) void gram_kernel(GramArgs g) {
             for (int v = 0; v < 16; ++v) {
                 const int i = min(i0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3), g.n - 1);
                 const int j = min(j0 + wn * 64 + bj * 32 + l32, g.n - 1);
-                cv[bi][bj][v] = g.H[(int64_t)i * g.ldh + j];
+                cv[bi][bj][v] = g.H[g.hl.at(i, j)];
             }
     store_krows_n(As, tid, ra);
     store_krows_n(Bs, tid, rb);
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(G_THREADS) void gram_kernel(GramArgs g) {
                 const int lj = wn * 64 + bj * 32 + l32;
                 const int i = i0 + li, j = j0 + lj;
                 if (i < g.n && j < g.n && (!diag || lj >= li))
-                    g.H[(int64_t)i * g.ldh + j] = cv[bi][bj][v] + acc[bi][bj][v];
+                    g.H[g.hl.at(i, j)] = cv[bi][bj][v] + acc[bi][bj][v];
             }
 }
 
@@ -151,21 +153,21 @@ using namespace gptq;
 
 extern "C" int gptq_gram_add(float* H, int64_t n, int64_t ldh, const float* X, int64_t t,
                              int64_t ldx, void* stream) {
-    if (!H || n <= 0 || t < 0 || ldh < n || ldx < n || n % 4 != 0) return GPTQ_EINVAL;
+    if (!H || n <= 0 || t < 0 || !hessian_ld_ok(n, ldh) || ldx < n || n % 4 != 0) return GPTQ_EINVAL;
     if (n > ((int64_t)1 << 20) || t > ((int64_t)1 << 30)) return GPTQ_EINVAL;
     if (t == 0) return GPTQ_OK;  // X may be NULL
     if (!X || ldx % 4 != 0 || ((uintptr_t)X & 15u) != 0) return GPTQ_EINVAL;
     CheckScope check;
-    check_buffer(H, sizeof(float) * (size_t)((n - 1) * ldh + n), "H");
+    check_buffer(H, sizeof(float) * (size_t)hessian_elems(n, ldh), "H");
     check_buffer(X, sizeof(float) * (size_t)((t - 1) * ldx + n), "X");
     hipStream_t st = (hipStream_t)stream;
     const int T = (int)((n + GT_M - 1) / GT_M);
-    GramArgs g{H, X, ldh, ldx, (int)n, (int)t, T, T * (T + 1) / 2};
+    GramArgs g{H, X, HLayout{n, ldh}, ldx, (int)n, (int)t, T, T * (T + 1) / 2};
     // Reads stay inside t x n of X and n x n of H (loads past the edge are skipped or clamped).
     {
         ProfScope ps(FAM_GRAM, st, (double)n * (n + 1) * (double)t, 0.0);
         GPTQ_LAUNCH(st, "gram_add", (gram_kernel<<<(unsigned)g.tiles, G_THREADS, 0, st>>>(g)),
-                    rd(X, ldx, t, n), rd(H, ldh, n, n), wr(H, ldh, n, n));
+                    rd(X, ldx, t, n), hessian_span(H, n, ldh, false), hessian_span(H, n, ldh, true));
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     return check.finish();

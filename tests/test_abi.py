@@ -62,3 +62,29 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and not r.stdout.strip()
+
+
+def test_packed_layout_is_the_pages_poff():
+    """The packed Hessian layout: element (i, j >= i) at poff(i) + (j - i) with
+    poff(r) = r (2n - r + 1) / 2 (page "cortiq-engine 0.8.41 src/gpu_wgpu/gptq_dev.rs", poff),
+    n (n + 1) / 2 floats; the tests' packing helper produces exactly that order, and the
+    header's marker value is the binding's."""
+    import re
+
+    import torch
+
+    from packing import pack_upper, unpack_upper
+    for n in (1, 2, 5, 17, 64):
+        H = torch.arange(n * n, dtype=torch.float64).reshape(n, n)
+        Hp = pack_upper(H)
+        assert Hp.numel() == n * (n + 1) // 2
+        for i in range(n):
+            poff = i * (2 * n - i + 1) // 2
+            for j in range(i, n):
+                assert Hp[poff + j - i] == H[i, j]
+        assert torch.equal(unpack_upper(Hp, n), torch.triu(H))
+    hdr = open(os.path.join(ROOT, "include", "gptq.h")).read()
+    m = re.search(r"#define GPTQ_PACKED_UPPER \(\(int64_t\)(-?\d+)\)", hdr)
+    assert m and int(m.group(1)) == pwq.GPTQ_PACKED_UPPER
+    with pytest.raises(ValueError):
+        pwq._hessian(torch.zeros(11))  # 11 is not n (n + 1) / 2

@@ -221,3 +221,61 @@ def test_debias_q2_schedule(lib, rows, n):
         st = lib.gptq_debias_q2(W, H, n, dead, plane, rung, lost, tab, scale, slope, rows, n, ws,
                                 need, None)
     assert st == GPTQ_OK, pwq.check_message()
+
+
+PACKED = pwq.GPTQ_PACKED_UPPER
+
+
+@pytest.mark.parametrize("n", [1, 8, 301, 4096, 17408])
+@pytest.mark.parametrize("precision", ["auto", "f32", "f64"])
+def test_fold_schedule_packed_hessian(lib, n, precision):
+    """H as its packed upper triangle (n (n + 1) / 2 floats): every read of H lies inside it."""
+    H, U, hd, dead, ws = addrs(5)
+    prec = pwq.FOLD_PRECISION[precision]
+    rep = pwq.FoldReport()
+    with pwq.check_mode():
+        st = lib.gptq_fold_ex(H, n, PACKED, 0.01, prec, U, hd, dead, ws,
+                              lib.gptq_fold_workspace_size_ex(n, prec), None, ctypes.byref(rep))
+    assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("n,t", [(4, 1), (200, 777), (17408, 32768)])
+def test_gram_schedule_packed(lib, n, t):
+    H, X = addrs(2)
+    with pwq.check_mode():
+        st = lib.gptq_gram_add(H, n, PACKED, X, t, n, None)
+    assert st == GPTQ_OK, pwq.check_message()
+
+
+@pytest.mark.parametrize("rows,n", [(1, 32), (5120, 17408)])
+def test_debias_and_act_order_schedules_packed(lib, rows, n):
+    W, H, dead, nib, rung, lost, tab, scale, slope, ws, perm, Hp = addrs(12)
+    need = lib.gptq_debias_workspace_size(rows, n)
+    with pwq.check_mode():
+        st = lib.gptq_debias(W, H, PACKED, dead, nib, rung, lost, tab, scale, slope, rows, n, ws,
+                             need, None)
+    assert st == GPTQ_OK, pwq.check_message()
+    with pwq.check_mode():
+        st = lib.gptq_debias_q2(W, H, PACKED, dead, nib, rung, lost, tab, scale, slope, rows, n,
+                                ws, need, None)
+    assert st == GPTQ_OK, pwq.check_message()
+    with pwq.check_mode():
+        st = lib.gptq_act_order_perm(H, n, PACKED, perm, dead, None)
+    assert st == GPTQ_OK, pwq.check_message()
+    with pwq.check_mode():
+        st = lib.gptq_permute_hessian(H, n, PACKED, perm, Hp, None)
+    assert st == GPTQ_OK, pwq.check_message()
+
+
+def test_hessian_leading_dimension_is_checked(lib):
+    """ldh below n, or negative other than the packed marker, is refused before anything runs."""
+    H, U, hd, dead, ws, X, perm, Hp = addrs(8)
+    n = 64
+    rep = pwq.FoldReport()
+    for ldh in (n - 1, -2, 0):
+        with pwq.check_mode():
+            assert lib.gptq_fold(H, n, ldh, 0.01, U, hd, dead, ws, lib.gptq_fold_workspace_size(n),
+                                 None, ctypes.byref(rep)) == pwq.GPTQ_EINVAL
+            assert lib.gptq_gram_add(H, n, ldh, X, 16, n, None) == pwq.GPTQ_EINVAL
+            assert lib.gptq_act_order_perm(H, n, ldh, perm, dead, None) == pwq.GPTQ_EINVAL
+            assert lib.gptq_permute_hessian(H, n, ldh, perm, Hp, None) == pwq.GPTQ_EINVAL
