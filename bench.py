@@ -219,49 +219,24 @@ def all_configs(pwq, torch, dev):
         recs.append(rec)
         del H, W, U
         torch.cuda.empty_cache()
-    # Config 4: 11 groups of the attention shape.  GPU: one stream and host thread per group.
+    # Config 4: 11 groups of the attention shape.  GPU: the library's round (gptq_round).
     # Oracle: the groups concurrently with the host threads split between them, as the pages'
     # host round runs them.
-    import threading
     spec = workloads.SPECS["batch"]
     groups = [workloads.make("batch", k=k, device=dev) for k in range(11)]
+    rnd = pwq.Round([{"H": H, "lam": lam, "members": [W]} for H, W, lam in groups])
     torch.cuda.synchronize()
-    bufs = []
-    for H, W, lam in groups:
-        n, rows = spec.n, spec.rows
-        bufs.append(dict(wf=torch.empty(pwq.fold_workspace_size(n), dtype=torch.uint8, device=dev),
-                         ws=torch.empty(pwq.sweep_workspace_size(rows, n), dtype=torch.uint8, device=dev),
-                         U=torch.empty(n, n, device=dev), hd=torch.empty(n, device=dev),
-                         dd=torch.empty(n, dtype=torch.uint8, device=dev),
-                         lost=torch.empty(rows, 2, device=dev), tab=torch.empty(rows, 32, device=dev),
-                         out=(torch.empty(rows, n // 2, dtype=torch.uint8, device=dev),
-                              torch.empty(rows, n // 32, dtype=torch.uint8, device=dev),
-                              torch.empty(rows, n // 32, device=dev), None),
-                         st=torch.cuda.Stream(device=dev)))
-
-    def one(i):
-        (H, W, lam), b = groups[i], bufs[i]
-        with torch.cuda.stream(b["st"]):
-            pwq.gptq_fold(H, lam, workspace=b["wf"], out=(b["U"], b["hd"], b["dd"]))
-            pwq.gptq_ladder(W, b["dd"], out=(b["lost"], b["tab"]))
-            pwq.gptq_sweep(W, b["U"], b["hd"], b["dd"], b["tab"], b["lost"], workspace=b["ws"], out=b["out"])
-            b["st"].synchronize()
-
-    def round_():
-        th = [threading.Thread(target=one, args=(i,)) for i in range(11)]
-        for x in th:
-            x.start()
-        for x in th:
-            x.join()
-        torch.cuda.synchronize()
-
-    round_()
+    rnd.run()
+    torch.cuda.synchronize()
     ts = []
     for _ in range(3):
         t0 = time.perf_counter()
-        round_()
+        rnd.run()
+        torch.cuda.synchronize()
         ts.append(time.perf_counter() - t0)
     t_round = float(np.median(ts))
+    gpu_conc = rnd.plan()[1]
+    del rnd
     conc = 4
     per = max(nt // conc, 1)
     host = [(H.cpu().numpy(), W.cpu().numpy(), lam) for H, W, lam in groups]
@@ -279,6 +254,7 @@ def all_configs(pwq, torch, dev):
     t_orc = time.perf_counter() - t0
     recs.append(dict(workload="batch", n=spec.n, rows=spec.rows, groups=11,
                      gpu_round_ms=t_round * 1e3, gpu_groups_per_s=11 / t_round,
+                     gpu_concurrency=gpu_conc,
                      oracle_round_s=t_orc, oracle_groups_per_s=11 / t_orc,
                      oracle_threads=nt, oracle_concurrency=f"{conc} groups at a time, {per} threads each",
                      speedup_vs_oracle=(11 / t_round) / (11 / t_orc)))
@@ -505,59 +481,36 @@ def main():
         e1.synchronize()
         result["detail"]["fold_packed_ms"] = e0.elapsed_time(e1) / 2
         del Hpk
-    # Concurrent groups (the batched round): G independent groups, each folded, laddered and
-    # swept on its own stream from its own host thread, with preallocated outputs and
-    # workspaces; groups/s over whole rounds.
+    # Concurrent groups (the batched round): G independent groups through the library's round
+    # (gptq_round: widest first, one host thread and stream per slot, the default concurrency),
+    # outputs and workspace allocated once; groups/s over whole rounds.
     def concurrent_round(name, G, rounds):
-        import threading
-        spec_g = workloads.SPECS[name]
-        gs_ = []
+        groups_ = []
         for kk in range(G):
             Hg_, Wg_, lam_g = workloads.make(name, k=kk, device=dev)
-            ng_, rg_ = spec_g.n, spec_g.rows
-            bufs = dict(
-                U=torch.empty(ng_, ng_, device=dev), hd=torch.empty(ng_, device=dev),
-                dd=torch.empty(ng_, dtype=torch.uint8, device=dev),
-                lost=torch.empty(rg_, 2, device=dev), tab=torch.empty(rg_, 32, device=dev),
-                nib=torch.empty(rg_, ng_ // 2, dtype=torch.uint8, device=dev),
-                rung=torch.empty(rg_, ng_ // 32, dtype=torch.uint8, device=dev),
-                scale=torch.empty(rg_, ng_ // 32, device=dev),
-                wf=torch.empty(pwq.fold_workspace_size(ng_), dtype=torch.uint8, device=dev),
-                ws=torch.empty(pwq.sweep_workspace_size(rg_, ng_), dtype=torch.uint8, device=dev))
-            gs_.append((Hg_, Wg_, lam_g, bufs, torch.cuda.Stream(device=dev)))
+            groups_.append({"H": Hg_, "lam": lam_g, "members": [Wg_]})
+        rnd = pwq.Round(groups_)
         torch.cuda.synchronize()
-
-        def one(i):
-            Hg_, Wg_, lam_g, b, st_ = gs_[i]
-            with torch.cuda.stream(st_):
-                pwq.gptq_fold(Hg_, lam_g, workspace=b["wf"], out=(b["U"], b["hd"], b["dd"]))
-                pwq.gptq_ladder(Wg_, b["dd"], out=(b["lost"], b["tab"]))
-                pwq.gptq_sweep(Wg_, b["U"], b["hd"], b["dd"], b["tab"], b["lost"],
-                               workspace=b["ws"], out=(b["nib"], b["rung"], b["scale"], None))
-                st_.synchronize()
-
-        def round_():
-            th = [threading.Thread(target=one, args=(i,)) for i in range(G)]
-            for t in th:
-                t.start()
-            for t in th:
-                t.join()
-            torch.cuda.synchronize()
-
-        round_()
+        st_ = rnd.run()
+        torch.cuda.synchronize()
+        if st_ != pwq.GPTQ_OK:
+            raise pwq.GptqError(st_, "gptq_round")
         t0_ = time.perf_counter()
         for _ in range(rounds):
-            round_()
+            rnd.run()
+            torch.cuda.synchronize()
         dt_ = (time.perf_counter() - t0_) / rounds
-        del gs_
+        conc_ = rnd.plan()[1]
+        del rnd, groups_
         torch.cuda.empty_cache()
-        return G / dt_, dt_ * 1e3
+        return G / dt_, dt_ * 1e3, conc_
 
     if not args.no_rounds:
-        gps, ms = concurrent_round("batch", 11, 3)
+        gps, ms, conc = concurrent_round("batch", 11, 3)
         result["detail"]["batched_round_11x4096_groups_per_s"] = gps
         result["detail"]["batched_round_11x4096_ms"] = ms
-        gps2, ms2 = concurrent_round("down", 2, 2)
+        result["detail"]["batched_round_concurrency"] = conc
+        gps2, ms2, _ = concurrent_round("down", 2, 2)
         result["detail"]["concurrent_2x17408_groups_per_s"] = gps2
         result["detail"]["concurrent_2x17408_ms_per_pair"] = ms2
     # The q2tp sweep ("placed" rule) on the step's U (a next-step row, not part of the step).

@@ -377,6 +377,78 @@ int gptq_sweep_q2(const float* W, const float* U, const float* hdiag, const uint
                   const float* tab, int64_t rows, int64_t n, uint8_t* plane, uint8_t* rung,
                   float* scale, float* E, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The batched round: many Hessian groups on one GPU.  A group is one Hessian and the weight
+ * matrices that share it (its members); the round folds each group once and ladders and sweeps
+ * every member against that fold.  Source: page "cortiq-cli 0.8.45 src/gptq.rs",
+ * run_quantize_gptq_tiled (workers take whole groups, widest Hessian first -- the
+ * longest-processing-time order, which changes no result -- and sweep every member of a group
+ * against the group's fold) and fold_concurrency (as many groups at once as the memory budget
+ * holds over one group's peak, at least one).  Here the budget is the caller's workspace and a
+ * group's peak is one slot (gptq_round_slot_size).
+ */
+enum { GPTQ_CODEC_Q4TP = 0, GPTQ_CODEC_Q2TP = 1 };
+
+typedef struct {
+    const float* W;  /* [rows, n] f32, device, 16-byte aligned; read only */
+    int64_t rows;    /* >= 1 */
+    int32_t codec;   /* GPTQ_CODEC_Q4TP (gptq_ladder, gptq_sweep) or GPTQ_CODEC_Q2TP
+                        (gptq_ladder_q2, gptq_sweep_q2) */
+    int32_t pad;
+    float* lost;     /* [rows, 2] f32 out: (lo, step) */
+    float* tab;      /* [rows, 32] f32 out: the rung scales */
+    uint8_t* codes;  /* out: the nibble plane [rows, n/2] (q4tp) or the 2-bit plane [rows, n/4] */
+    uint8_t* rung;   /* [rows, n/32] out */
+    float* scale;    /* [rows, n/32] f32 out */
+} gptq_member;
+
+typedef struct {
+    const float* H;           /* the group's Hessian, device: dense [n, ldh] or packed */
+    int64_t n;                /* 1 <= n <= 2^20; n % 32 == 0 when the group has members */
+    int64_t ldh;              /* >= n, or GPTQ_PACKED_UPPER */
+    double lambda;            /* starting damping, as gptq_fold_ex */
+    int32_t precision;        /* GPTQ_FOLD_* */
+    int32_t members;          /* >= 0 */
+    const gptq_member* member; /* host array of `members` entries */
+    float* hdiag;             /* [n] f32 out, device, or NULL */
+    uint8_t* dead;            /* [n] u8 out, device, or NULL */
+    gptq_fold_report report;  /* out: the group's fold */
+    int32_t status;           /* out: GPTQ_OK, GPTQ_DEGENERATE (U = I; the members are swept
+                                 against it), or the status of the group's first failing call */
+    int32_t pad;
+} gptq_group;
+
+/* Bytes of device workspace one group occupies while it runs (a slot): U, hdiag and dead, plus
+ * the larger of the fold's workspace (at the group's precision) and its members' largest sweep
+ * workspace, which share memory because the sweeps follow the fold on one stream; each part
+ * 256-byte aligned.  The maximum over the groups; 0 when a group is invalid or count <= 0. */
+size_t gptq_round_slot_size(const gptq_group* groups, int32_t count);
+
+/* The round's schedule, on the host only.  order [count] i32 out: the groups widest first
+ * (larger n, then more member rows, then the lower index).  *concurrency out: the groups run
+ * at once, min(max_concurrency, count, workspace_bytes / slot size) -- max_concurrency <= 0
+ * means the library's default, 4.  GPTQ_EINVAL for an invalid group or count <= 0,
+ * GPTQ_EWORKSPACE when the workspace holds no slot; nothing is written then. */
+int gptq_round_plan(const gptq_group* groups, int32_t count, size_t workspace_bytes,
+                    int32_t max_concurrency, int32_t* order, int32_t* concurrency);
+
+/*
+ * gptq_round -- run the round.  groups: host array; each entry's report and status are
+ * written.  workspace: device, 256-byte aligned, cut into slots of gptq_round_slot_size bytes.
+ * One host thread and one stream (the library's own, default priority) per slot: a thread
+ * takes the next group of the plan's order, folds it (the host reads the pivot flag once per
+ * attempt), then ladders and sweeps each member on the slot's stream (with more than one slot,
+ * every launch of the group on that stream, no helper streams).  The slot streams start after `stream`, and `stream` waits for
+ * all of them, so the round is ordered on `stream`; the last sweeps may still run when the call
+ * returns.  Every result is bit for bit that of the separate calls (gptq_fold_ex, gptq_ladder
+ * or gptq_ladder_q2, gptq_sweep or gptq_sweep_q2).  Returns GPTQ_OK when every group ended
+ * GPTQ_OK or GPTQ_DEGENERATE, else the first failing group's status in the groups' order; after
+ * a GPTQ_EHIP no group is started any more and those not started report GPTQ_EHIP.  The
+ * buffers of different groups must be disjoint.
+ */
+int gptq_round(gptq_group* groups, int32_t count, void* workspace, size_t workspace_bytes,
+               int32_t max_concurrency, void* stream);
+
 /* Static string for a GPTQ_* status. */
 const char* gptq_status_string(int status);
 

@@ -43,6 +43,24 @@ class FoldReport(ctypes.Structure):
 
 # Arithmetic of the fold (include/gptq.h, GPTQ_FOLD_*).
 FOLD_PRECISION = {"auto": 0, "f32": 1, "f64": 2}
+# Codecs of a round's members (GPTQ_CODEC_*).
+CODEC = {"q4tp": 0, "q2tp": 1}
+
+
+class RoundMember(ctypes.Structure):
+    """gptq_member of include/gptq.h."""
+    _fields_ = [("W", ctypes.c_void_p), ("rows", ctypes.c_int64), ("codec", ctypes.c_int32),
+                ("pad", ctypes.c_int32), ("lost", ctypes.c_void_p), ("tab", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("rung", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class RoundGroup(ctypes.Structure):
+    """gptq_group of include/gptq.h."""
+    _fields_ = [("H", ctypes.c_void_p), ("n", ctypes.c_int64), ("ldh", ctypes.c_int64),
+                ("lam", ctypes.c_double), ("precision", ctypes.c_int32),
+                ("members", ctypes.c_int32), ("member", ctypes.POINTER(RoundMember)),
+                ("hdiag", ctypes.c_void_p), ("dead", ctypes.c_void_p), ("report", FoldReport),
+                ("status", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 def load():
@@ -99,6 +117,13 @@ def load():
     lib.gptq_ladder_q2.restype = ctypes.c_int
     lib.gptq_sweep_q2.argtypes = [P, P, P, P, P, i64, i64, P, P, P, P, P, sz, P]
     lib.gptq_sweep_q2.restype = ctypes.c_int
+    lib.gptq_round_slot_size.argtypes = [ctypes.POINTER(RoundGroup), ctypes.c_int32]
+    lib.gptq_round_slot_size.restype = sz
+    lib.gptq_round_plan.argtypes = [ctypes.POINTER(RoundGroup), ctypes.c_int32, sz, ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.gptq_round_plan.restype = ctypes.c_int
+    lib.gptq_round.argtypes = [ctypes.POINTER(RoundGroup), ctypes.c_int32, P, sz, ctypes.c_int32, P]
+    lib.gptq_round.restype = ctypes.c_int
     lib.gptq_status_string.argtypes = [ctypes.c_int]
     lib.gptq_status_string.restype = ctypes.c_char_p
     lib.gptq_profile_enable.argtypes = [ctypes.c_uint]
@@ -584,6 +609,88 @@ def profile_collect():
             for f in range(nf)}
 
 
+class Round:
+    """A batched round (include/gptq.h, gptq_round) with its outputs and workspace allocated
+    once, so that run() can be repeated.  ``groups``: a sequence of dicts with "H" (f32 [n, n],
+    rows may be padded, or its packed upper triangle, 1-D), "lam", optionally "precision"
+    ("auto", "f32", "f64"), and "members": W [rows, n] tensors, or (W, codec) pairs with codec
+    "q4tp" or "q2tp".  Without a workspace, min(groups, max_concurrency or 4) slots are
+    allocated.  ``results``: per group a dict with hdiag, dead and, per member, (lost, tab,
+    codes, rung, scale); run() adds the group's status and fold report."""
+
+    def __init__(self, groups, max_concurrency: int = 0, workspace=None, stream=None):
+        lib = load()
+        if not groups:
+            raise ValueError("a round needs at least one group")
+        dev = groups[0]["H"].device
+        G = len(groups)
+        self.arr = (RoundGroup * G)()
+        self.keep, self.results = [], []
+        with _on(stream, dev):
+            for i, g in enumerate(groups):
+                h_ptr, n, ldh = _hessian(g["H"], dev)
+                mem = list(g.get("members", ()))
+                ms = (RoundMember * max(len(mem), 1))()
+                outs = []
+                for k, m in enumerate(mem):
+                    W, codec = m if isinstance(m, tuple) else (m, "q4tp")
+                    if W.dim() != 2 or W.shape[1] != n:
+                        raise ValueError(f"group {i} member {k}: W must be [rows, {n}]")
+                    rows = W.shape[0]
+                    cb = n // 2 if codec == "q4tp" else n // 4
+                    o = (torch.empty(rows, 2, dtype=torch.float32, device=dev),
+                         torch.empty(rows, 32, dtype=torch.float32, device=dev),
+                         torch.empty(rows, cb, dtype=torch.uint8, device=dev),
+                         torch.empty(rows, n // 32, dtype=torch.uint8, device=dev),
+                         torch.empty(rows, n // 32, dtype=torch.float32, device=dev))
+                    ms[k] = RoundMember(_dev(W, torch.float32, "W", align=16, device=dev).value,
+                                        rows, CODEC[codec], 0, *(t.data_ptr() for t in o))
+                    outs.append(o)
+                hdiag = torch.empty(n, dtype=torch.float32, device=dev)
+                dead = torch.empty(n, dtype=torch.uint8, device=dev)
+                self.arr[i] = RoundGroup(h_ptr.value, n, ldh, float(g["lam"]),
+                                         FOLD_PRECISION[g.get("precision", "auto")], len(mem), ms,
+                                         hdiag.data_ptr(), dead.data_ptr(), FoldReport(), 0, 0)
+                self.keep.append((ms, g["H"], mem))
+                self.results.append(dict(hdiag=hdiag, dead=dead, members=outs))
+            self.slot_bytes = int(lib.gptq_round_slot_size(self.arr, G))
+            if self.slot_bytes == 0:
+                raise ValueError("a group of the round is invalid")
+            if workspace is None:
+                k = min(G, max_concurrency if max_concurrency > 0 else 4)
+                workspace = torch.empty(self.slot_bytes * k, dtype=torch.uint8, device=dev)
+            else:
+                _dev(workspace, torch.uint8, "workspace", align=256, device=dev)
+        self.workspace = workspace
+        self.max_concurrency = int(max_concurrency)
+
+    def plan(self):
+        """(order, concurrency) of the round as the library schedules it."""
+        G = len(self.arr)
+        order = (ctypes.c_int32 * G)()
+        conc = ctypes.c_int32(0)
+        st = load().gptq_round_plan(self.arr, G, self.workspace.numel(), self.max_concurrency,
+                                    order, ctypes.byref(conc))
+        if st != GPTQ_OK:
+            raise GptqError(st, "gptq_round_plan")
+        return list(order), conc.value
+
+    def run(self, stream=None) -> int:
+        st = load().gptq_round(self.arr, len(self.arr), ctypes.c_void_p(self.workspace.data_ptr()),
+                               self.workspace.numel(), self.max_concurrency, _stream(stream))
+        for i, r in enumerate(self.results):
+            r["status"] = int(self.arr[i].status)
+            r["report"] = self.arr[i].report.as_dict()
+        return int(st)
+
+
+def gptq_round(groups, max_concurrency: int = 0, workspace=None, stream=None):
+    """Run one batched round (see Round).  Returns (status, results)."""
+    r = Round(groups, max_concurrency, workspace, stream)
+    st = r.run(stream)
+    return st, r.results
+
+
 class check_mode:
     """Context manager: the library's calls run as dry runs of their schedule (no GPU; device
     pointers are never dereferenced) and return GPTQ_ECHECK when an access leaves its buffers
@@ -617,4 +724,4 @@ __all__ = ["check_mode", "check_message", "check_selftest", "check_tile_order", 
            "gptq_sweep_act_order_q2", "gptq_debias_q2",
            "debias_workspace_size", "gptq_fold", "FOLD_PRECISION", "gptq_ladder", "gptq_sweep", "gptq_sweep_inplace", "fold_workspace_size",
            "sweep_workspace_size", "require_native", "load", "GptqError", "profile_enable",
-           "profile_collect", "LIB_PATH"]
+           "profile_collect", "LIB_PATH", "gptq_round", "Round", "RoundGroup", "RoundMember", "CODEC"]

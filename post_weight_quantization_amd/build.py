@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
 SOURCES = ["fold.hip", "fold64.hip", "sweep.hip", "gram.hip", "debias.hip", "act_order.hip", "api.hip",
-           "check.hip"]
+           "check.hip", "round.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,7 +32,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = ["hipcc", "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
+    cmd = ["hipcc", "-shared", f"--offload-arch={ARCH}", "-fPIC", "-pthread", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

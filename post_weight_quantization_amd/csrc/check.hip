@@ -120,6 +120,7 @@ std::string span_str(const Span& s) {
 }  // namespace
 
 bool dry_run() { return t_sim != nullptr; }
+bool check_mode_on() { return g_mode.load() != 0; }
 
 CheckScope::CheckScope() {
     if (g_mode.load() && !t_sim) t_sim = new Sim();

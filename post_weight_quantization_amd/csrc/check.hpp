@@ -42,6 +42,8 @@ inline Span hessian_span(const void* H, int64_t n, int64_t ldh, bool write) {
 
 // True while the calling thread runs an entry point in check mode.
 bool dry_run();
+// True while check mode is switched on (gptq_check_mode), inside an entry point or not.
+bool check_mode_on();
 
 // One entry-point call.  In check mode the constructor starts a fresh record; finish() runs
 // the checks and returns GPTQ_OK or GPTQ_ECHECK.  Outside check mode both do nothing.

@@ -519,6 +519,15 @@ extern "C" int gptq_fold(const float* H, int64_t n, int64_t ldh, double lambda, 
 extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambda, int precision,
                             float* U, float* hdiag, uint8_t* dead, void* workspace,
                             size_t workspace_bytes, void* stream, gptq_fold_report* report) {
+    return fold_run(H, n, ldh, lambda, precision, U, hdiag, dead, workspace, workspace_bytes,
+                    (hipStream_t)stream, report, false);
+}
+
+namespace gptq {
+
+int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precision, float* U,
+             float* hdiag, uint8_t* dead, void* workspace, size_t workspace_bytes, hipStream_t st,
+             gptq_fold_report* report, bool single) {
     if (n <= 0 || !hessian_ld_ok(n, ldh) || !H || !U || !hdiag || !dead || !workspace)
         return GPTQ_EINVAL;
     if (n > (int64_t)1 << 20) return GPTQ_EINVAL;
@@ -533,7 +542,6 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
     check_buffer(hdiag, sizeof(float) * (size_t)n, "hdiag");
     check_buffer(dead, (size_t)n, "dead");
     check_buffer(workspace, workspace_bytes, "workspace");
-    hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
     FoldState* state = (FoldState*)(ws + L.off_state);
     float* dinv = (float*)(ws + L.off_dinv);
@@ -553,13 +561,17 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
 
-    Helper hp{};
-    if (helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
+    // single: every launch on st, in program order (an order the helper streams' events allow,
+    // so the same results bit for bit); no helper stream or event is taken.
+    Helper hp{st, st, nullptr, nullptr, nullptr, nullptr, -1};
+    if (!single && helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
     hipStream_t ts = hp.stream;
     struct Release {
         const Helper& h;
         ~Release() { helper_release(h); }
     } release{hp};
+    auto record = [single](hipEvent_t e, hipStream_t s) { return single ? GPTQ_OK : ev_record(e, s); };
+    auto wait = [single](hipStream_t s, hipEvent_t e) { return single ? GPTQ_OK : stream_wait(s, e); };
 #define FOLD_OK(call)                           \
     do {                                        \
         const int rc_ = (call);                 \
@@ -655,12 +667,12 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
                 if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             }
             // Panel k of L (and the inverses of its diagonal 128-blocks) is final.
-            FOLD_OK(ev_record(hp.ev_a, st));
+            FOLD_OK(record(hp.ev_a, st));
             const int64_t rest = np - kb - w;
             const float* P = A + (kb + w) * np + kb;  // the panel's rows below its diagonal block
 
             // --- the inverse, on tx ---
-            FOLD_OK(stream_wait(tx, hp.ev_a));
+            FOLD_OK(wait(tx, hp.ev_a));
             // Inverse of the panel's w x w diagonal block of L, into X[kb:kb+w, kb:kb+w]: the
             // 128-blocks on the diagonal are the MI_c written by the diagonal kernel; block row I
             // is -MI_I (L[I, <I] X[<I, <I]) (block forward substitution).
@@ -689,7 +701,7 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
             // then copied back: a workgroup tile spans only 128 of the w rows it reads).  They
             // need the previous panel's update of X (on ts, ev_d).
             if (kb > 0) {
-                if (x_pending) FOLD_OK(stream_wait(tx, hp.ev_d));
+                if (x_pending) FOLD_OK(wait(tx, hp.ev_d));
                 const GemmBatch xb = gemm_batch(
                     gemm_full(X + kb * np + kb, np, X + kb * np, np, nullptr, Xt, np, (int)w, (int)kb,
                               (int)w, 1.0f, 0),
@@ -705,13 +717,13 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
                 if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             }
             if (rest <= 0) continue;
-            FOLD_OK(ev_record(hp.ev_c, tx));  // the panel's rows of X are final
+            FOLD_OK(record(hp.ev_c, tx));  // the panel's rows of X are final
 
             // --- the Cholesky's trailing update ---
             const int64_t nw = std::min<int64_t>(L.nb2, rest);  // width of the next panel
             const int64_t rest2 = rest - nw;
             // Bulk, on ts: A_ij -= P_i P_j^T beyond the next panel.
-            FOLD_OK(stream_wait(ts, hp.ev_a));
+            FOLD_OK(wait(ts, hp.ev_a));
             if (rest2 > 0) {
                 const GemmProblem sy = gemm_syrk_lower(P + nw * np, np,
                                                        A + (kb + w + nw) * np + kb + w + nw,
@@ -727,7 +739,7 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
             }
             // Look-ahead, on st: the next panel's columns (rows below kb+w, diagonal tiles lower
             // only); they need the previous panel's bulk update.
-            if (!first_bulk) FOLD_OK(stream_wait(st, hp.ev_b));
+            if (!first_bulk) FOLD_OK(wait(st, hp.ev_b));
             GemmProblem strip = gemm_full(P, np, P, np, A + (kb + w) * np + kb + w,
                                           A + (kb + w) * np + kb + w, np, (int)rest, (int)nw,
                                           (int)w, -1.0f, 1);
@@ -740,14 +752,14 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
             }
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             if (rest2 > 0) {
-                FOLD_OK(ev_record(hp.ev_b, ts));
+                FOLD_OK(record(hp.ev_b, ts));
                 first_bulk = false;
             }
             // The inverse's update, on ts after the SYRK: every row below,
             // X_i,<kb+w -= L_i,k X[kb:kb+w, <kb+w] (X's columns kb..kb+w-1 are first written here,
             // so those tiles ignore C_in).
             {
-                FOLD_OK(stream_wait(ts, hp.ev_c));
+                FOLD_OK(wait(ts, hp.ev_c));
                 GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np,
                                            X + (kb + w) * np, np, (int)rest, (int)(kb + w), (int)w,
                                            -1.0f, 1);
@@ -758,15 +770,15 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
                 FOLD_OK((launch_gemm<0, true, false, false>("fold_x_update", ts, gemm_batch(none, &xu),
                                                             &state->flag)));
                 if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-                FOLD_OK(ev_record(hp.ev_d, ts));
+                FOLD_OK(record(hp.ev_d, ts));
                 x_pending = true;
             }
         }
         // Join both helper streams, then read the pivot flag.
-        FOLD_OK(ev_record(hp.ev_c, tx));
-        FOLD_OK(stream_wait(st, hp.ev_c));
-        FOLD_OK(ev_record(hp.ev_b, ts));
-        FOLD_OK(stream_wait(st, hp.ev_b));
+        FOLD_OK(record(hp.ev_c, tx));
+        FOLD_OK(wait(st, hp.ev_c));
+        FOLD_OK(record(hp.ev_b, ts));
+        FOLD_OK(wait(st, hp.ev_b));
         }
         if (dry_run()) {
             host_sync_record(st);
@@ -831,3 +843,5 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
     }
     return degenerate ? GPTQ_DEGENERATE : GPTQ_OK;
 }
+
+}  // namespace gptq

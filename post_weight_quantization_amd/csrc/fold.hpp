@@ -70,4 +70,10 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
 // U = P X P D^-1 from the f64 inverse (rounded to f32 once).
 int fold64_make_u(float* U, int64_t n, char* ws, const FoldLayout& L, hipStream_t st);
 
+// gptq_fold_ex on a stream; single: no helper streams, every launch on st in program order
+// (the same results bit for bit), for callers that run several folds side by side.
+int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precision, float* U,
+             float* hdiag, uint8_t* dead, void* workspace, size_t workspace_bytes, hipStream_t st,
+             gptq_fold_report* report, bool single);
+
 }  // namespace gptq

@@ -31,6 +31,7 @@
 
 #include "common.hpp"
 #include "gemm_mfma.hpp"
+#include "sweep.hpp"
 
 namespace gptq {
 
@@ -871,10 +872,12 @@ static SweepRun q4_run(const float* first, float* Wc, const float* U, const floa
     return c;
 }
 
-extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
-                          const float* tab, const float* lost, int64_t rows, int64_t n,
-                          uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+namespace gptq {
+
+int sweep_run(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
+              const float* tab, const float* lost, int64_t rows, int64_t n, uint8_t* nib,
+              uint8_t* rung, float* scale, float* E, void* workspace, size_t workspace_bytes,
+              hipStream_t st, bool single) {
     if (!sweep_args_ok(W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E) || !workspace ||
         !al16(workspace))
         return GPTQ_EINVAL;
@@ -887,9 +890,19 @@ extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, co
     const SweepRun c = q4_run(W, (float*)ws, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale,
                               E, (float*)(ws + off_e),
                               (float*)(ws + off_e + align256(sizeof(float) * (size_t)(rows * SOB))));
-    const int rc = sweep_pipeline<0>(c, (hipStream_t)stream);
+    const int rc = sweep_pipeline<0>(c, st, single);
     if (rc != GPTQ_OK) return rc;
     return check.finish();
+}
+
+}  // namespace gptq
+
+extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
+                          const float* tab, const float* lost, int64_t rows, int64_t n,
+                          uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return sweep_run(W, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, E, workspace,
+                     workspace_bytes, (hipStream_t)stream, false);
 }
 
 // In place: W is its own working copy, so the workspace holds only the two residual panels, and
@@ -1000,10 +1013,12 @@ extern "C" int gptq_ladder_q2(const float* W, const uint8_t* dead, int64_t rows,
     return check.finish();
 }
 
-extern "C" int gptq_sweep_q2(const float* W, const float* U, const float* hdiag,
-                             const uint8_t* dead, const float* tab, int64_t rows, int64_t n,
-                             uint8_t* plane, uint8_t* rung, float* scale, float* E,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+namespace gptq {
+
+int sweep_q2_run(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
+                 const float* tab, int64_t rows, int64_t n, uint8_t* plane, uint8_t* rung,
+                 float* scale, float* E, void* workspace, size_t workspace_bytes, hipStream_t st,
+                 bool single) {
     if (rows <= 0 || n < 32 || n % 32 != 0 || !W || !U || !hdiag || !dead || !tab || !plane ||
         !rung || !scale || !workspace)
         return GPTQ_EINVAL;
@@ -1038,9 +1053,19 @@ extern "C" int gptq_sweep_q2(const float* W, const float* U, const float* hdiag,
     c.Wc = (float*)workspace;
     c.Epan[0] = (float*)((char*)workspace + off_e);
     c.Epan[1] = (float*)((char*)workspace + off_e + align256(sizeof(float) * (size_t)(rows * SOB)));
-    const int rc = sweep_pipeline<2>(c, (hipStream_t)stream);
+    const int rc = sweep_pipeline<2>(c, st, single);
     if (rc != GPTQ_OK) return rc;
     return check.finish();
+}
+
+}  // namespace gptq
+
+extern "C" int gptq_sweep_q2(const float* W, const float* U, const float* hdiag,
+                             const uint8_t* dead, const float* tab, int64_t rows, int64_t n,
+                             uint8_t* plane, uint8_t* rung, float* scale, float* E,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return sweep_q2_run(W, U, hdiag, dead, tab, rows, n, plane, rung, scale, E, workspace,
+                        workspace_bytes, (hipStream_t)stream, false);
 }
 
 // --- act order (static groups) -------------------------------------------------------------
