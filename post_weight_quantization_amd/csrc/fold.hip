@@ -589,7 +589,7 @@ int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precisio
     for (;;) {
         ++attempts;
         if (use64) {
-            FOLD_OK(fold64_attempt(H, hl, hdiag, dead, state, lam, ws, L, st));
+            FOLD_OK(fold64_attempt(H, hl, hdiag, dead, state, lam, ws, L, st, hp, single));
         } else {
         {
             ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 4.0 * (double)n * n + 4.0 * (double)np * np / 2);

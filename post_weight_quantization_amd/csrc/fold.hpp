@@ -63,10 +63,12 @@ inline FoldLayout fold_layout(int64_t n) {
 // The f64 fold of one damping value (fold64.hip).  ws is the whole workspace (layout above);
 // H has n = hl.n channels in either Hessian layout.  Enqueues on st: the f64 scales, the
 // reversed equilibrated matrix, the blocked Cholesky with the blocked inverse trailing it
-// panel by panel.  Pivots that are not positive and finite set flag bit 0 and make the
-// remaining launches of the attempt return at once.
+// panel by panel, on st and the helper streams of hp (single: st alone).  Pivots that are not
+// positive and finite set flag bit 0 and make the remaining launches of the attempt return at
+// once.  Ends with the helper streams joined into st.
 int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t* dead,
-                   FoldState* state, double lam, char* ws, const FoldLayout& L, hipStream_t st);
+                   FoldState* state, double lam, char* ws, const FoldLayout& L, hipStream_t st,
+                   const Helper& hp, bool single);
 // U = P X P D^-1 from the f64 inverse (rounded to f32 once).
 int fold64_make_u(float* U, int64_t n, char* ws, const FoldLayout& L, hipStream_t st);
 

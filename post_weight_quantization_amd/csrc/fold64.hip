@@ -219,7 +219,8 @@ __global__ __launch_bounds__(256) void fold64_make_u_kernel(const double* __rest
     } while (0)
 
 int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t* dead,
-                   FoldState* state, double lam, char* ws, const FoldLayout& L, hipStream_t st) {
+                   FoldState* state, double lam, char* ws, const FoldLayout& L, hipStream_t st,
+                   const Helper& hp, bool single) {
     const int64_t n = hl.n, np = L.np;
     double* A = (double*)(ws + L.off_a);
     double* X = (double*)(ws + L.off_x64);
@@ -229,6 +230,15 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
     double* Xt = (double*)(ws + L.off_xt64);
     const unsigned* flag = &state->flag;
     const Span st_rw = wr(state, 1, 1, sizeof(FoldState), 1);
+    // Streams as in the f32 fold: st the Cholesky's serial chain and the look-ahead of the next
+    // panel's columns; ts the trailing update beyond the next panel, then the inverse's update
+    // of the rows of X below the panel; tx the inverse's small steps (its diagonal block and
+    // the panel's rows of X).  single: all of it on st, in program order.  The pivot flag, which
+    // only goes from 0 to set and makes later launches return at once, is polled by launches on
+    // every stream and left out of their recorded accesses, as the GEMMs leave it out.
+    hipStream_t ts = single ? st : hp.stream, tx = single ? st : hp.stream2;
+    auto record = [single](hipEvent_t e, hipStream_t s) { return single ? GPTQ_OK : ev_record(e, s); };
+    auto wait = [single](hipStream_t s, hipEvent_t e) { return single ? GPTQ_OK : stream_wait(s, e); };
     {
         ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 4.0 * (double)n * n + 8.0 * (double)np * np / 2);
         GPTQ_LAUNCH(st, "fold64_scale",
@@ -242,6 +252,8 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
                     rd(state, 1, 1, sizeof(FoldState), 1), wr(A, np, np, np, 8));
     }
     if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    bool first_bulk = true;
+    bool x_pending = false;  // ev_d holds an update of X that the next rows of X need
     for (int64_t kb = 0; kb < np; kb += W64) {
         const int64_t w = std::min<int64_t>(W64, np - kb);
         const int64_t R = w / NB64;
@@ -280,63 +292,103 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
             }
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
+        // Panel k of L (and the inverses of its diagonal 64-blocks) is final.
+        F64_OK(record(hp.ev_a, st));
+        const int64_t rest = np - kb - w;
+        const double* P = A + (kb + w) * np + kb;  // the panel's rows below its diagonal block
+
+        // --- the inverse, on tx ---
+        F64_OK(wait(tx, hp.ev_a));
         // The inverse of the panel's w x w diagonal block into X[kb:kb+w, kb:kb+w]: block row I
         // is -MI_I (L[I, <I] X[<I, <I]) below the diagonal block MI_I.
-        GPTQ_LAUNCH(st, "fold64_x_diag",
-                    (fold64_x_diag_kernel<<<dim3((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, st>>>(
+        GPTQ_LAUNCH(tx, "fold64_x_diag",
+                    (fold64_x_diag_kernel<<<dim3((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, tx>>>(
                         X, MI, np, kb, w, state)),
-                    rd(MI + (kb / NB64) * NB64 * NB64, NB64, w, NB64, 8), wr(X + kb * np + kb, np, w, w, 8),
-                    rd(state, 1, 1, sizeof(FoldState), 1));
+                    rd(MI + (kb / NB64) * NB64 * NB64, NB64, w, NB64, 8), wr(X + kb * np + kb, np, w, w, 8));
         for (int64_t I = 1; I < R; ++I) {
             const int64_t ci = kb + I * NB64;
-            ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB64 * (double)(I * NB64) * (I * NB64 + NB64), 0.0);
+            ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * NB64 * (double)(I * NB64) * (I * NB64 + NB64), 0.0);
             F64_OK((launch_gemm64<64, 64, false, false>(
-                "fold64_inv_block_a", st,
+                "fold64_inv_block_a", tx,
                 gemm64_full(A + ci * np + kb, np, X + kb * np + kb, np, nullptr, Tb, W64, NB64,
                             (int)(I * NB64), (int)(I * NB64), 1.0, 0),
                 nullptr, flag)));
             F64_OK((launch_gemm64<64, 64, false, false>(
-                "fold64_inv_block_b", st,
+                "fold64_inv_block_b", tx,
                 gemm64_full(MI + (ci / NB64) * NB64 * NB64, NB64, Tb, W64, nullptr, X + ci * np + kb, np,
                             NB64, (int)(I * NB64), NB64, -1.0, 0),
                 nullptr, flag)));
         }
         if (kb > 0) {
             // Rows of X in this panel, X[kb:kb+w, <kb] = X_ww X[kb:kb+w, <kb]: staged in Xt (a
-            // tile reads all w rows of its columns) and copied back.
+            // tile reads all w rows of its columns) and copied back.  They need the previous
+            // panel's update of X (on ts, ev_d).
+            if (x_pending) F64_OK(wait(tx, hp.ev_d));
             {
-                ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * (double)w * w * kb, 0.0);
+                ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * (double)w * w * kb, 0.0);
                 F64_OK((launch_gemm64<64, 64, false, false>(
-                    "fold64_x_rows", st,
+                    "fold64_x_rows", tx,
                     gemm64_full(X + kb * np + kb, np, X + kb * np, np, nullptr, Xt, np, (int)w, (int)kb,
                                 (int)w, 1.0, 0),
                     nullptr, flag)));
             }
-            GPTQ_LAUNCH(st, "fold64_copy_rows",
-                        (fold64_copy_rows_kernel<<<dim3((unsigned)((kb + 511) / 512), (unsigned)w), 256, 0, st>>>(
+            GPTQ_LAUNCH(tx, "fold64_copy_rows",
+                        (fold64_copy_rows_kernel<<<dim3((unsigned)((kb + 511) / 512), (unsigned)w), 256, 0, tx>>>(
                             Xt, X + kb * np, np, kb, state)),
-                        rd(Xt, np, w, kb, 8), wr(X + kb * np, np, w, kb, 8),
-                        rd(state, 1, 1, sizeof(FoldState), 1));
+                        rd(Xt, np, w, kb, 8), wr(X + kb * np, np, w, kb, 8));
         }
         if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-        const int64_t rest = np - kb - w;
         if (rest <= 0) continue;
-        // Bulk: the trailing SYRK and the inverse's update of every row below (X's columns
-        // kb..kb+w-1 are first written here, so those tiles ignore C_in).
-        const double* P = A + (kb + w) * np + kb;
-        const GemmProblem64 sy = gemm64_syrk_lower(P, np, A + (kb + w) * np + kb + w,
-                                                   A + (kb + w) * np + kb + w, np, (int)rest, (int)w,
-                                                   -1.0, 1);
-        GemmProblem64 xu = gemm64_full(P, np, X + kb * np, np, X + (kb + w) * np, X + (kb + w) * np, np,
-                                       (int)rest, (int)(kb + w), (int)w, -1.0, 1);
-        xu.beta0_col = (int)kb;
+        F64_OK(record(hp.ev_c, tx));  // the panel's rows of X are final
+
+        // --- the Cholesky's trailing update ---
+        const int64_t nw = std::min<int64_t>(W64, rest);  // width of the next panel
+        const int64_t rest2 = rest - nw;
+        // Bulk, on ts: A_ij -= P_i P_j^T beyond the next panel.
+        F64_OK(wait(ts, hp.ev_a));
+        if (rest2 > 0) {
+            const GemmProblem64 sy = gemm64_syrk_lower(P + nw * np, np, A + (kb + w + nw) * np + kb + w + nw,
+                                                       A + (kb + w + nw) * np + kb + w + nw, np,
+                                                       (int)rest2, (int)w, -1.0, 1);
+            ProfScope ps(FAM_FOLD_UPDATE, ts, (double)w * rest2 * (rest2 + 1), 0.0);
+            F64_OK((launch_gemm64<64, 64, true, false>("fold64_bulk", ts, sy, nullptr, flag)));
+        }
+        // Look-ahead, on st: the next panel's columns (rows below kb+w, diagonal tiles lower
+        // only); they need the previous panel's bulk update.
+        if (!first_bulk) F64_OK(wait(st, hp.ev_b));
         {
-            ProfScope ps(FAM_FOLD_UPDATE, st,
-                         (double)w * rest * (rest + 1) + 2.0 * w * (double)rest * (kb + w), 0.0);
-            F64_OK((launch_gemm64<64, 64, true, false>("fold64_bulk", st, sy, &xu, flag)));
+            GemmProblem64 strip = gemm64_full(P, np, P, np, A + (kb + w) * np + kb + w,
+                                              A + (kb + w) * np + kb + w, np, (int)rest, (int)nw,
+                                              (int)w, -1.0, 1);
+            strip.mask_diag = 1;
+            strip.skip_upper = 1;
+            ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * w * (double)rest * nw, 0.0);
+            F64_OK((launch_gemm64<64, 64, true, false>("fold64_look_ahead", st, strip, nullptr, flag)));
+        }
+        if (rest2 > 0) {
+            F64_OK(record(hp.ev_b, ts));
+            first_bulk = false;
+        }
+        // The inverse's update, on ts after the SYRK: every row below,
+        // X_i,<kb+w -= L_i,k X[kb:kb+w, <kb+w] (X's columns kb..kb+w-1 are first written here,
+        // so those tiles ignore C_in).
+        {
+            F64_OK(wait(ts, hp.ev_c));
+            GemmProblem64 xu = gemm64_full(P, np, X + kb * np, np, X + (kb + w) * np, X + (kb + w) * np,
+                                           np, (int)rest, (int)(kb + w), (int)w, -1.0, 1);
+            xu.beta0_col = (int)kb;
+            ProfScope ps(FAM_FOLD_UPDATE, ts, 2.0 * w * (double)rest * (kb + w), 0.0);
+            F64_OK((launch_gemm64<64, 64, true, false>("fold64_x_update", ts, gemm64_none(), &xu, flag)));
+            F64_OK(record(hp.ev_d, ts));
+            x_pending = true;
         }
         if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     }
+    // Join both helper streams.
+    F64_OK(record(hp.ev_c, tx));
+    F64_OK(wait(st, hp.ev_c));
+    F64_OK(record(hp.ev_b, ts));
+    F64_OK(wait(st, hp.ev_b));
     return GPTQ_OK;
 }
 
