@@ -321,3 +321,34 @@ def test_misaligned_pointers_are_rejected(gpu):
     # The same call with aligned pointers runs.
     assert lib.gptq_sweep(*args(p(W_ok), p(U), p(ws))) == gpu.GPTQ_OK
     torch.cuda.synchronize()
+
+
+def test_calls_on_a_stream_that_is_not_current(gpu):
+    """Every wrapper given stream= while another stream is current: its outputs and workspaces
+    are allocated in that stream's order (the caching allocator churns on the current stream
+    meanwhile), and the results equal those of the same calls on the current stream."""
+    H, W, lam = workloads.make("fixture", device="cuda")
+
+    def chain(stream):
+        U, hd, dd, rep = gpu.gptq_fold(H, lam, stream=stream)
+        lost, tab = gpu.gptq_ladder(W, dd, stream=stream)
+        nib, rung, scale, E = gpu.gptq_sweep(W, U, hd, dd, tab, lost, want_E=True, stream=stream)
+        lq, tq = gpu.gptq_ladder_q2(W, dd, stream=stream)
+        plane, rq, sq, _ = gpu.gptq_sweep_q2(W, U, hd, dd, tq, stream=stream)
+        lost_d, tab_d, scale_d, slope = gpu.gptq_debias(W, H, dd, nib, rung, lost.clone(), scale.clone(),
+                                                        stream=stream)
+        perm, dead_p = gpu.gptq_act_order_perm(H, stream=stream)
+        return [U, hd, dd, lost, tab, nib, rung, scale, E, lq, tq, plane, rq, sq, lost_d, scale_d,
+                perm, dead_p]
+
+    ref = chain(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = chain(side)
+    for _ in range(32):  # reuse of freed blocks on the current stream while side may still run
+        torch.empty(1 << 22, device="cuda").fill_(float("nan"))
+    side.synchronize()
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert torch.equal(a, b), f"output {i} differs on the side stream"
