@@ -248,14 +248,18 @@ extern "C" int gptq_round(gptq_group* groups, int32_t count, void* workspace,
                 if (g.status == GPTQ_EHIP) abort.store(true);
             }
         };
-        if (conc == 1) {
-            worker(0);
-        } else {
-            std::vector<std::thread> th;
-            th.reserve(conc);
-            for (int k = 0; k < conc; ++k) th.emplace_back(worker, k);
-            for (auto& t : th) t.join();
+        // The calling thread is slot 0's worker; a slot whose thread cannot be started stays
+        // idle and the others take its groups.
+        std::vector<std::thread> th;
+        for (int k = 1; k < conc; ++k) {
+            try {
+                th.emplace_back(worker, k);
+            } catch (...) {
+                break;
+            }
         }
+        worker(0);
+        for (auto& t : th) t.join();
         // Join: the caller's stream waits for every slot stream.
         for (int k = 0; k < conc; ++k) {
             if (hipEventRecord(ss[k].e, ss[k].s) != hipSuccess ||
