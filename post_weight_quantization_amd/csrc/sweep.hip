@@ -127,6 +127,30 @@ __device__ __forceinline__ int nominal_rung(float amax, float lo, float st) {
     r = fmin(fmax(r, 0.0), 31.0);
     return (int)r;
 }
+
+// nominal_rung without its f64 log2 on the common path.  v = (log2(amax / 7) - lo) / st is
+// estimated in f32 from the hardware log2; the rung is its rounding clamped to 0..31, which
+// only a value within about 0.5 of 0.5 .. 30.5 can change, so the estimate decides unless it
+// lies within its error bound of such a boundary (or amax is subnormal): then, rarely and
+// behind a wave-uniform branch, nominal_rung itself decides.  The bound is generous: log2(amax)
+// to 2^-16 max(1, |log2 amax|) (the hardware is accurate to about 2^-22 of that), the f32
+// rounding of log2 7, of L - lo, of the division and of the estimate itself.  Every rung
+// equals nominal_rung's.
+__device__ __forceinline__ int nominal_rung_fast(float amax, float lo, float st) {
+    if (amax == 0.0f || st <= 0.0f) return 0;
+    const float la = __builtin_amdgcn_logf(amax);  // log2
+    const float L = la - 2.80735492f;              // log2(amax / 7)
+    const float v = (L - lo) / st;
+    const float bound = (1.52587890625e-5f * fmaxf(fabsf(la), 1.0f) + 2e-7f + 1e-7f * fabsf(L - lo)) / st +
+                        2e-7f * fabsf(v) + 1e-6f;
+    const bool near = !(amax >= 1.17549435e-38f) ||
+                      (!(fabsf(v - floorf(v) - 0.5f) > bound) && !(v < -1.0f) && !(v > 32.0f));
+    int r = (int)fminf(fmaxf(floorf(v + 0.5f), 0.0f), 31.0f);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near) != 0, 0)) {
+        if (near) r = nominal_rung(amax, lo, st);
+    }
+    return r;
+}
 #pragma clang fp contract(fast)
 
 // Cross-lane moves inside the 16-lane rows of a wave, as DPP operand modifiers (a VALU move,
@@ -183,6 +207,25 @@ __device__ __forceinline__ float group16_max(float v) {
 // unless the product lies within 4e-7 max(|w/s|, 1) of a half-integer; then divide.  The
 // division sits behind a wave-uniform branch that is almost never taken, so the common path
 // does not wait for it.
+// Whether the code decision on w * fl(1/s) may differ from the one on fl(w / s) (rint_quot).
+__device__ __forceinline__ bool near_half(float r) {
+    return !(fabsf(r - floorf(r) - 0.5f) > 4e-7f * fmaxf(fabsf(r), 1.0f));
+}
+
+// fl(w / s), the correctly rounded f32 quotient, without a division: inv64 = RN64(1 / s) (0 for
+// s <= 0).  The f64 product w * inv64 is within 2^-52 (relative) of w / s, while a quotient of
+// two f32 numbers is never an f32 rounding boundary (a midpoint) and lies at least 2^-49
+// (relative) from every one: its numerator and the midpoint times the divisor differ by at
+// least one unit of their common grid.  So the product rounds to f32 exactly as w / s does,
+// subnormal and overflowing quotients included.
+__device__ __forceinline__ float quot_f32(float w, double inv64) { return (float)((double)w * inv64); }
+
+__device__ __forceinline__ double bcast_f64_row(double v, int L) {
+    const float lo = row_bcast(__int_as_float(__double2loint(v)), L);
+    const float hi = row_bcast(__int_as_float(__double2hiint(v)), L);
+    return __hiloint2double(__float_as_int(hi), __float_as_int(lo));
+}
+
 __device__ __forceinline__ float rint_quot(float w, float s, float inv_s) {
     const float r = w * inv_s;
     const float f = r - floorf(r);
@@ -194,11 +237,19 @@ __device__ __forceinline__ float rint_quot(float w, float s, float inv_s) {
     return q;
 }
 
-// Partial H_ii-weighted rounding error of two columns at scale s (each product and sum rounded).
+// Partial H_ii-weighted rounding error of two columns at scale s (each product and sum rounded);
+// rint_quot for both columns behind one wave-uniform branch.
 __device__ __forceinline__ float pair_err(float w0, float w1, float h0, float h1, float s,
                                           float inv_s) {
-    const float q0 = fminf(fmaxf(rint_quot(w0, s, inv_s), -8.0f), 7.0f);
-    const float q1 = fminf(fmaxf(rint_quot(w1, s, inv_s), -8.0f), 7.0f);
+    const float r0 = w0 * inv_s, r1 = w1 * inv_s;
+    const bool n0 = near_half(r0), n1 = near_half(r1);
+    float qa = rintf(r0), qb = rintf(r1);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(n0 || n1) != 0, 0)) {
+        if (n0) qa = rintf(w0 / s);
+        if (n1) qb = rintf(w1 / s);
+    }
+    const float q0 = fminf(fmaxf(qa, -8.0f), 7.0f);
+    const float q1 = fminf(fmaxf(qb, -8.0f), 7.0f);
     const float qs0 = q0 * s, qs1 = q1 * s;
     const float d0 = w0 - qs0, d1 = w1 - qs1;
     const float e0 = h0 * d0, e1 = h1 * d1;
@@ -225,6 +276,11 @@ __device__ __forceinline__ float unit_tile_err(const float (&w)[32], float s, fl
 // correctly rounded quotient as rint_quot does: x = w * fl(1/s) + 1.5 lands on the same level
 // unless w * fl(1/s) lies within 4e-7 max(|.|, 1) of an integer (x near a half-integer); then
 // (rarely, behind a wave-uniform branch) divide.
+// The q2tp level clamp(rne(clamp(x, -1, 4)), 0, 3) of x = fl(w / s) + 1.5.
+__device__ __forceinline__ float q2_level(float x) {
+    return fminf(fmaxf(rintf(fminf(fmaxf(x, -1.0f), 4.0f)), 0.0f), 3.0f);
+}
+
 __device__ __forceinline__ float q2_level_quot(float w, float s, float inv_s) {
     const float r = w * inv_s;
     const bool near = !(fabsf(r - rintf(r)) > 4e-7f * fmaxf(fabsf(r), 1.0f));
@@ -232,7 +288,7 @@ __device__ __forceinline__ float q2_level_quot(float w, float s, float inv_s) {
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(near) != 0, 0)) {
         if (near) x = w / s + 1.5f;
     }
-    return fminf(fmaxf(rintf(fminf(fmaxf(x, -1.0f), 4.0f)), 0.0f), 3.0f);
+    return q2_level(x);
 }
 
 // Clipped-H_ii-weighted q2tp rounding error of two columns at scale s.
@@ -299,7 +355,8 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
     constexpr bool ST = MODE == 1 || MODE == 3, Q2 = MODE == 2 || MODE == 3;
     const int k = cx.k;
     float s = 0.0f, inv_s = 0.0f;
-    float s_own[2] = {0.0f, 0.0f}, inv_own[2] = {0.0f, 0.0f};
+    float s_own[2] = {0.0f, 0.0f};
+    double inv_own64[2] = {0.0, 0.0};
     if constexpr (Q2 && !ST) {
         const float amax = group16_max(fmaxf(fabsf(w[g][0]), fabsf(w[g][1])));
         int best = 0;
@@ -330,11 +387,11 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         const float2 sv = *reinterpret_cast<const float2*>(cx.sp + 32 * g + 2 * k);
         s_own[0] = sv.x;
         s_own[1] = sv.y;
-        inv_own[0] = (sv.x > 0.0f) ? 1.0f / sv.x : 0.0f;
-        inv_own[1] = (sv.y > 0.0f) ? 1.0f / sv.y : 0.0f;
+        inv_own64[0] = (sv.x > 0.0f) ? 1.0 / (double)sv.x : 0.0;
+        inv_own64[1] = (sv.y > 0.0f) ? 1.0 / (double)sv.y : 0.0;
     } else {
     const float amax = group16_max(fmaxf(fabsf(w[g][0]), fabsf(w[g][1])));
-    const int nominal = nominal_rung(amax, cx.lo, cx.st);
+    const int nominal = nominal_rung_fast(amax, cx.lo, cx.st);
     int best = nominal;
     if (amax > 0.0f) {
         float best_e = INFINITY;
@@ -360,6 +417,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         scale[gi] = s;
     }
     }
+    const double inv_s64 = (s > 0.0f) ? 1.0 / (double)s : 0.0;  // RN64(1 / s) for quot_f32
     uint32_t byte = 0u;
     // This lane's entries of row j of U (own group and later groups) and 1 / U_jj are read one
     // column step ahead, so the serial chain -- broadcast, code, residual, the owner's next
@@ -383,19 +441,21 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
 #pragma unroll
         for (int g2 = g + 1; g2 < G; ++g2) ul_n[g2] = ul[g2];
         if (jj + 1 < 32) load_u(32 * g + jj + 1, uo_n, ul_n, ui_n);
-        float sj = s, inv_sj = inv_s;
+        float sj = s;
+        double inv64 = inv_s64;
         if constexpr (ST) {
             sj = row_bcast(s_own[slot], owner);
-            inv_sj = row_bcast(inv_own[slot], owner);
+            inv64 = bcast_f64_row(inv_own64[slot], owner);
         }
         const float wj = row_bcast(w[g][slot], owner);
+        // The code from fl(w / s) itself (quot_f32): no division and no branch on the chain.
+        const float qt = quot_f32(wj, inv64);
         float q, lev;  // the code and its level (q for q4tp, q - 1.5 for q2tp)
         if constexpr (Q2) {
-            q = (sj > 0.0f) ? q2_level_quot(wj, sj, inv_sj) : 0.0f;
+            q = (sj > 0.0f) ? q2_level(qt + 1.5f) : 0.0f;
             lev = q - 1.5f;
         } else {
-            q = fminf(fmaxf(rint_quot(wj, sj, inv_sj), -8.0f), 7.0f);
-            q = (sj > 0.0f) ? q : 0.0f;
+            q = (sj > 0.0f) ? fminf(fmaxf(rintf(qt), -8.0f), 7.0f) : 0.0f;
             lev = q;
         }
         const float e = (wj - lev * sj) * ui;
