@@ -71,6 +71,13 @@ inline int64_t hessian_elems(int64_t n, int64_t ldh) {
     return ldh < 0 ? n * (n + 1) / 2 : (n - 1) * ldh + n;
 }
 
+// Wave priority (s_setprio, 0..3) of the kernels on a call's serial chain: the fold's diagonal
+// blocks and panel products, the inverse's small steps, the sweep's blocks and in-panel products.
+// The bulk updates that run beside them keep priority 0, so where both share a SIMD the chain's
+// instructions issue first.  Same-box timing at n = 17408: fold 34.05 -> 33.75 ms, sweep
+// 15.80 -> 15.55 ms.
+constexpr int CHAIN_PRIO = 3;
+
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // 16-byte alignment, which every pointer the kernels read or write as float4 / double2 needs
 // (NULL counts as aligned: optional outputs).

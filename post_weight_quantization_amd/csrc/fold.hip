@@ -276,6 +276,7 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
                                                         float* __restrict__ MI, int64_t np, int k,
                                                         unsigned* flag, unsigned* minp, float tau) {
     if (__atomic_load_n(flag, __ATOMIC_RELAXED)) return;
+    __builtin_amdgcn_s_setprio(CHAIN_PRIO);
     // 81 KB of LDS, so that the kernel fits on a CU beside one GEMM workgroup.  The off-diagonal
     // 32-blocks M_IJ (I > J) of L^-1 live in the unused upper triangle of Ls, at block (J, I).
     __shared__ float Ls[NB * DLD];        // the block, L in place (lower)

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(64) void fold64_diag_kernel(const double* __restric
                                                          double* __restrict__ MI, int64_t np,
                                                          int64_t cb, FoldState* st) {
     if (__atomic_load_n(&st->flag, __ATOMIC_RELAXED)) return;
+    __builtin_amdgcn_s_setprio(CHAIN_PRIO);
     const int lane = threadIdx.x;
     double x[NB64], t[NB64];
     const double* arow = A + (cb + lane) * np + cb;
@@ -273,7 +274,7 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
                 // L_ic = A_ic MI_c^T for every row below, in place: a 64 x 64 tile spans the
                 // whole block column it reads before it writes.
                 ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB64 * NB64 * (double)rest_c, 0.0);
-                F64_OK((launch_gemm64<64, 64, true, false>(
+                F64_OK((launch_gemm64<64, 64, true, false, true>(
                     "fold64_panel", st,
                     gemm64_full(A + (cb + NB64) * np + cb, np, mic, NB64, nullptr,
                                 A + (cb + NB64) * np + cb, np, (int)rest_c, NB64, NB64, 1.0, 0),
@@ -288,7 +289,7 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
                 iu.mask_diag = 1;
                 iu.skip_upper = 1;
                 ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * NB64 * (double)rest_c * ncol, 0.0);
-                F64_OK((launch_gemm64<64, 64, true, false>("fold64_in_panel", st, iu, nullptr, flag)));
+                F64_OK((launch_gemm64<64, 64, true, false, true>("fold64_in_panel", st, iu, nullptr, flag)));
             }
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
         }
@@ -308,12 +309,12 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
         for (int64_t I = 1; I < R; ++I) {
             const int64_t ci = kb + I * NB64;
             ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * NB64 * (double)(I * NB64) * (I * NB64 + NB64), 0.0);
-            F64_OK((launch_gemm64<64, 64, false, false>(
+            F64_OK((launch_gemm64<64, 64, false, false, true>(
                 "fold64_inv_block_a", tx,
                 gemm64_full(A + ci * np + kb, np, X + kb * np + kb, np, nullptr, Tb, W64, NB64,
                             (int)(I * NB64), (int)(I * NB64), 1.0, 0),
                 nullptr, flag)));
-            F64_OK((launch_gemm64<64, 64, false, false>(
+            F64_OK((launch_gemm64<64, 64, false, false, true>(
                 "fold64_inv_block_b", tx,
                 gemm64_full(MI + (ci / NB64) * NB64 * NB64, NB64, Tb, W64, nullptr, X + ci * np + kb, np,
                             NB64, (int)(I * NB64), NB64, -1.0, 0),
@@ -326,7 +327,7 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
             if (x_pending) F64_OK(wait(tx, hp.ev_d));
             {
                 ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * (double)w * w * kb, 0.0);
-                F64_OK((launch_gemm64<64, 64, false, false>(
+                F64_OK((launch_gemm64<64, 64, false, false, true>(
                     "fold64_x_rows", tx,
                     gemm64_full(X + kb * np + kb, np, X + kb * np, np, nullptr, Xt, np, (int)w, (int)kb,
                                 (int)w, 1.0, 0),
@@ -363,7 +364,7 @@ int fold64_attempt(const float* H, HLayout hl, const float* hdiag, const uint8_t
             strip.mask_diag = 1;
             strip.skip_upper = 1;
             ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * w * (double)rest * nw, 0.0);
-            F64_OK((launch_gemm64<64, 64, true, false>("fold64_look_ahead", st, strip, nullptr, flag)));
+            F64_OK((launch_gemm64<64, 64, true, false, true>("fold64_look_ahead", st, strip, nullptr, flag)));
         }
         if (rest2 > 0) {
             F64_OK(record(hp.ev_b, ts));

@@ -188,9 +188,12 @@ __device__ __forceinline__ void gemm64_tile(const GemmProblem64& P, int tm, int 
         }
 }
 
-template <int TM, int TN, bool TB0, bool TB1>
+// CHAIN: a product on the fold's serial chain, which raises its wave priority above the bulk
+// updates' (CHAIN_PRIO).
+template <int TM, int TN, bool TB0, bool TB1, bool CHAIN>
 __global__ __launch_bounds__(256) void gemm64_kernel(GemmBatch64 batch, const unsigned* abort_flag) {
     if (abort_flag && __atomic_load_n(abort_flag, __ATOMIC_RELAXED)) return;
+    if constexpr (CHAIN) __builtin_amdgcn_s_setprio(CHAIN_PRIO);
     __shared__ __attribute__((aligned(16))) double As[2 * G64_K * (TM + 2)];
     __shared__ __attribute__((aligned(16))) double Bs[2 * G64_K * (TN + 2)];
     int t = xcd_order(blockIdx.x, batch.total);
@@ -271,7 +274,7 @@ inline int gemm64_spans(const GemmBatch64& b, Span* out) {
 }
 
 // Launch one batch of up to two problems with TM x TN tiles on stream s.
-template <int TM, int TN, bool TB0, bool TB1>
+template <int TM, int TN, bool TB0, bool TB1, bool CHAIN = false>
 inline int launch_gemm64(const char* name, hipStream_t s, GemmProblem64 p0, const GemmProblem64* p1,
                          const unsigned* flag) {
     GemmBatch64 b{};
@@ -289,7 +292,7 @@ inline int launch_gemm64(const char* name, hipStream_t s, GemmProblem64 p0, cons
     const int na = gemm64_spans<TB0, TB1>(b, acc);
     const int rc = check_launch(name, s, acc, na);
     if (rc != GPTQ_OK) return rc;
-    if (!dry_run()) gemm64_kernel<TM, TN, TB0, TB1><<<b.total, 256, 0, s>>>(b, flag);
+    if (!dry_run()) gemm64_kernel<TM, TN, TB0, TB1, CHAIN><<<b.total, 256, 0, s>>>(b, flag);
     return GPTQ_OK;
 }
 

@@ -541,22 +541,31 @@ __device__ __forceinline__ void gemm_tile_small(const GemmProblem& P, int tm, in
 // fold's panel solve (1) takes 64 x 128 tiles: it works in place on a 128-column block, and a
 // tile row 128 columns wide is what makes that safe (each workgroup reads all the columns it
 // overwrites before it writes).
+// prio: the wave priority (s_setprio) of the site's waves.  The chains' products raise theirs
+// above the bulk updates' (0), so that on a SIMD shared with bulk waves their instructions are
+// issued first: the bulk updates hide behind the chains, not the other way round.
 template <int TAG>
 struct GemmCfg {
     static constexpr int nbuf = 2;
     static constexpr int waves = 2;
     static constexpr int tile = 128;    // tile rows
     static constexpr int tile_n = 128;  // tile columns
+    static constexpr int prio = 0;
 };
-template <> struct GemmCfg<3> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
-template <> struct GemmCfg<4> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
-template <> struct GemmCfg<5> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
-template <> struct GemmCfg<6> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
-template <> struct GemmCfg<7> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
-template <> struct GemmCfg<9> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 64; };
-template <> struct GemmCfg<1> { static constexpr int nbuf = 2; static constexpr int waves = 4; static constexpr int tile = 64; static constexpr int tile_n = 128; };
-template <> struct GemmCfg<0> { static constexpr int nbuf = 1; static constexpr int waves = 2; static constexpr int tile = 128; static constexpr int tile_n = 128; };
-template <> struct GemmCfg<2> { static constexpr int nbuf = 1; static constexpr int waves = 2; static constexpr int tile = 128; static constexpr int tile_n = 128; };
+#define GPTQ_CHAIN_CFG(TAG, TN)                                                                     \
+    template <> struct GemmCfg<TAG> {                                                               \
+        static constexpr int nbuf = 2, waves = 4, tile = 64, tile_n = TN, prio = CHAIN_PRIO;       \
+    }
+GPTQ_CHAIN_CFG(1, 128);
+GPTQ_CHAIN_CFG(3, 64);
+GPTQ_CHAIN_CFG(4, 64);
+GPTQ_CHAIN_CFG(5, 64);
+GPTQ_CHAIN_CFG(6, 64);
+GPTQ_CHAIN_CFG(7, 64);
+GPTQ_CHAIN_CFG(9, 64);
+#undef GPTQ_CHAIN_CFG
+template <> struct GemmCfg<0> { static constexpr int nbuf = 1, waves = 2, tile = 128, tile_n = 128, prio = 0; };
+template <> struct GemmCfg<2> { static constexpr int nbuf = 1, waves = 2, tile = 128, tile_n = 128, prio = 0; };
 
 // TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
 // of problems 0 and 1; CHK: bounds checks on M and N.
@@ -564,6 +573,7 @@ template <int TAG, bool TB0, bool TB1, bool CHK>
 __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(GemmCfg<TAG>::waves, GemmCfg<TAG>::waves)))
 void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
     if (abort_flag && __atomic_load_n(abort_flag, __ATOMIC_RELAXED)) return;
+    if constexpr (GemmCfg<TAG>::prio > 0) __builtin_amdgcn_s_setprio(GemmCfg<TAG>::prio);
     constexpr int NBUF = GemmCfg<TAG>::nbuf;
     constexpr int TILE = GemmCfg<TAG>::tile, TILE_N = GemmCfg<TAG>::tile_n;
     static_assert(TILE == 128 ? TILE_N == 128 : (TILE == 64 && (TILE_N == 64 || TILE_N == 128)),

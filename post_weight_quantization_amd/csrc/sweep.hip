@@ -511,6 +511,7 @@ __global__ __launch_bounds__(BT) void sweep_block_kernel(
     uint8_t* __restrict__ nib, uint8_t* __restrict__ rung, float* __restrict__ scale,
     float* __restrict__ E, int64_t ldE, const float* __restrict__ sp,
     uint8_t* __restrict__ codes) {
+    __builtin_amdgcn_s_setprio(CHAIN_PRIO);
     constexpr int NC = 32 * G;
     constexpr bool ST = MODE == 1 || MODE == 3;
     __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
