@@ -31,7 +31,7 @@ enum Family {
     FAM_COUNT = 12
 };
 
-// Two helper streams (non-blocking, default priority) and three events, taken from a
+// Two helper streams (non-blocking, default priority) and four events, taken from a
 // per-process pool for the duration of one call so that independent calls never share one.
 struct Helper {
     hipStream_t stream, stream2;
