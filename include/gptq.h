@@ -419,32 +419,45 @@ typedef struct {
 } gptq_group;
 
 /* Bytes of device workspace one group occupies while it runs (a slot): U, hdiag and dead, plus
- * the larger of the fold's workspace (at the group's precision) and its members' largest sweep
- * workspace, which share memory because the sweeps follow the fold on one stream; each part
- * 256-byte aligned.  The maximum over the groups; 0 when a group is invalid or count <= 0. */
+ * the larger of the fold's workspace (at the group's precision) and, over its members, a
+ * sweep's workspace (gptq_sweep_workspace_size) followed by the member's outputs (lost, tab,
+ * codes at n/2 bytes a row, rung, scale), where a gang stages them; fold and sweeps share the
+ * memory because the sweeps follow the fold on one stream.  Each part 256-byte aligned.  The
+ * maximum over the groups; 0 when a group is invalid or count <= 0. */
 size_t gptq_round_slot_size(const gptq_group* groups, int32_t count);
 
 /* The round's schedule, on the host only.  order [count] i32 out: the groups widest first
- * (larger n, then more member rows, then the lower index).  *concurrency out: the groups run
- * at once, min(max_concurrency, count, workspace_bytes / slot size) -- max_concurrency <= 0
- * means the library's default, 4.  GPTQ_EINVAL for an invalid group or count <= 0,
- * GPTQ_EWORKSPACE when the workspace holds no slot; nothing is written then. */
+ * (larger n, then more member rows, then the lower index).  Consecutive groups of that order
+ * with the same shape -- n, precision (not GPTQ_FOLD_F64), lambda, and member by member rows
+ * and codec -- form gangs of at most min(max_concurrency, 16, workspace_bytes / slot size)
+ * groups (max_concurrency <= 0: no cap of the caller's).  *concurrency out: the slots the round
+ * uses -- its largest gang when it forms a gang of two or more, else the groups run at once on
+ * threads, min(max_concurrency, count, workspace_bytes / slot size) with max_concurrency <= 0
+ * meaning 4.  GPTQ_EINVAL for an invalid group or count <= 0, GPTQ_EWORKSPACE when the
+ * workspace holds no slot; nothing is written then. */
 int gptq_round_plan(const gptq_group* groups, int32_t count, size_t workspace_bytes,
                     int32_t max_concurrency, int32_t* order, int32_t* concurrency);
 
 /*
  * gptq_round -- run the round.  groups: host array; each entry's report and status are
  * written.  workspace: device, 256-byte aligned, cut into slots of gptq_round_slot_size bytes.
- * One host thread and one stream (the library's own, default priority) per slot: a thread
+ * When the plan forms gangs, they run one after another on `stream` (and the library's helper
+ * streams, joined back into it): a gang of G groups runs in lockstep, every kernel launch
+ * covering all G, each in its own slot -- one f32 fold attempt for all of them (a group whose
+ * attempt fails is then folded again on its own, from the start), then member by member a copy
+ * of the G weight matrices into the slots, their ladders and in-place sweeps, and the copy of
+ * the outputs to the members' buffers; a lone group runs as the separate calls do.  Otherwise
+ * one host thread and one stream (the library's own, default priority) per slot: a thread
  * takes the next group of the plan's order, folds it (the host reads the pivot flag once per
  * attempt), then ladders and sweeps each member on the slot's stream (with more than one slot,
- * every launch of the group on that stream, no helper streams).  The slot streams start after `stream`, and `stream` waits for
- * all of them, so the round is ordered on `stream`; the last sweeps may still run when the call
- * returns.  Every result is bit for bit that of the separate calls (gptq_fold_ex, gptq_ladder
- * or gptq_ladder_q2, gptq_sweep or gptq_sweep_q2).  Returns GPTQ_OK when every group ended
- * GPTQ_OK or GPTQ_DEGENERATE, else the first failing group's status in the groups' order; after
- * a GPTQ_EHIP no group is started any more and those not started report GPTQ_EHIP.  The
- * buffers of different groups must be disjoint.
+ * every launch of the group on that stream, no helper streams); the slot streams start after
+ * `stream`, and `stream` waits for all of them.  Either way the round is ordered on `stream`;
+ * the last sweeps may still run when the call returns.  Every result is bit for bit that of
+ * the separate calls (gptq_fold_ex, gptq_ladder or gptq_ladder_q2, gptq_sweep or
+ * gptq_sweep_q2).  Returns GPTQ_OK when every group ended GPTQ_OK or GPTQ_DEGENERATE, else the
+ * first failing group's status in the groups' order; after a GPTQ_EHIP no group is started any
+ * more and those not started report GPTQ_EHIP.  The buffers of different groups must be
+ * disjoint.
  */
 int gptq_round(gptq_group* groups, int32_t count, void* workspace, size_t workspace_bytes,
                int32_t max_concurrency, void* stream);

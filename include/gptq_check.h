@@ -31,8 +31,8 @@ const char* gptq_check_message(void);
 int gptq_check_selftest(int which);
 /* The tile GEMM's map from workgroup to output tile, on the host: GPTQ_OK when the workgroups
  * of one launch over an M x N product (lower != 0: the lower tiles of an M x M product, N
- * ignored) cover every 128 x 128 tile exactly once; GPTQ_ECHECK otherwise; GPTQ_EINVAL for
- * sizes outside 1 .. 2^20. */
+ * ignored) cover every 128 x 128 tile exactly once, for each group of a batched launch (grid
+ * z = 0 .. 15); GPTQ_ECHECK otherwise; GPTQ_EINVAL for sizes outside 1 .. 2^20. */
 int gptq_check_tile_order(int64_t M, int64_t N, int lower);
 
 #ifdef __cplusplus

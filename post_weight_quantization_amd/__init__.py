@@ -614,8 +614,8 @@ class Round:
     once, so that run() can be repeated.  ``groups``: a sequence of dicts with "H" (f32 [n, n],
     rows may be padded, or its packed upper triangle, 1-D), "lam", optionally "precision"
     ("auto", "f32", "f64"), and "members": W [rows, n] tensors, or (W, codec) pairs with codec
-    "q4tp" or "q2tp".  Without a workspace, min(groups, max_concurrency or 4) slots are
-    allocated.  ``results``: per group a dict with hdiag, dead and, per member, (lost, tab,
+    "q4tp" or "q2tp".  Without a workspace, the slots the library's plan would use (its largest
+    gang, or its threads), within half of the free device memory, are allocated.  ``results``: per group a dict with hdiag, dead and, per member, (lost, tab,
     codes, rung, scale); run() adds the group's status and fold report."""
 
     def __init__(self, groups, max_concurrency: int = 0, workspace=None, stream=None):
@@ -657,7 +657,16 @@ class Round:
             if self.slot_bytes == 0:
                 raise ValueError("a group of the round is invalid")
             if workspace is None:
-                k = min(G, max_concurrency if max_concurrency > 0 else 4)
+                # The slots the library's plan uses with room for all of them, within half of
+                # the device memory that is free.
+                order = (ctypes.c_int32 * G)()
+                conc = ctypes.c_int32(0)
+                st = lib.gptq_round_plan(self.arr, G, ctypes.c_size_t(self.slot_bytes * G),
+                                         int(max_concurrency), order, ctypes.byref(conc))
+                if st != GPTQ_OK:
+                    raise GptqError(st, "gptq_round_plan")
+                free = torch.cuda.mem_get_info(dev)[0]
+                k = max(1, min(conc.value, free // 2 // self.slot_bytes))
                 workspace = torch.empty(self.slot_bytes * k, dtype=torch.uint8, device=dev)
             else:
                 _dev(workspace, torch.uint8, "workspace", align=256, device=dev)

@@ -64,6 +64,7 @@ struct Sim {
 };
 
 thread_local Sim* t_sim = nullptr;
+thread_local Gang t_gang{1, 0};
 
 // Byte range [lo, hi) of a span; empty spans give lo == hi.
 void span_range(const Span& s, const char*& lo, const char*& hi) {
@@ -120,6 +121,10 @@ std::string span_str(const Span& s) {
 }  // namespace
 
 bool dry_run() { return t_sim != nullptr; }
+
+Gang gang_current() { return t_gang; }
+GangScope::GangScope(int G, int64_t gs) { t_gang = Gang{G, gs}; }
+GangScope::~GangScope() { t_gang = Gang{1, 0}; }
 bool check_mode_on() { return g_mode.load() != 0; }
 
 CheckScope::CheckScope() {
@@ -169,14 +174,26 @@ void check_buffer(const void* p, size_t bytes, const char* name) {
     s->bufs.push_back(Buffer{(const char*)p, (const char*)p + bytes, name});
 }
 
-int check_launch(const char* name, hipStream_t st, const Span* acc, int nacc) {
+int check_launch(const char* name, hipStream_t st, const Span* acc0, int nacc0) {
     Sim* s = t_sim;
     if (!s) return GPTQ_OK;
     const int k = s->sidx(st);
     Sim::join(s->vc[k], s->host);
     if (s->vc[k].size() <= (size_t)k) s->vc[k].resize(k + 1, 0);
     s->vc[k][k] += 1;
-    Launch L{name, k, s->vc[k][k], s->vc[k], std::vector<Span>(acc, acc + nacc)};
+    // A gang's launch touches every group's slot: each span that is not fixed, once per group.
+    std::vector<Span> all;
+    for (int i = 0; i < nacc0; ++i) {
+        const int reps = acc0[i].fixed ? 1 : t_gang.G;
+        for (int g = 0; g < reps; ++g) {
+            Span x = acc0[i];
+            x.p = (const char*)x.p + (int64_t)g * t_gang.gs;
+            all.push_back(x);
+        }
+    }
+    const Span* acc = all.data();
+    const int nacc = (int)all.size();
+    Launch L{name, k, s->vc[k][k], s->vc[k], all};
     for (int i = 0; i < nacc; ++i) {
         const char *lo, *hi;
         span_range(acc[i], lo, hi);
@@ -296,14 +313,19 @@ extern "C" int gptq_check_tile_order(int64_t M, int64_t N, int lower) {
                                 : gemm_full(nullptr, 32, nullptr, 32, nullptr, nullptr, N, (int)M,
                                             (int)N, 32, 1.0f, 0);
     const int TN = P.tiles_n, TM = lower ? P.tiles_n : P.ntiles / P.tiles_n;
-    std::vector<unsigned char> seen((size_t)TM * TN, 0);
-    for (int b = 0; b < P.ntiles; ++b) {
-        int tm = -1, tn = -1;
-        tile_of(P, xcd_order(b, P.ntiles), tm, tn);
-        if (tm < 0 || tm >= TM || tn < 0 || tn >= TN || (lower && tn > tm)) return GPTQ_ECHECK;
-        unsigned char& f = seen[(size_t)tm * TN + tn];
-        if (f) return GPTQ_ECHECK;
-        f = 1;
+    // Every group of a gang (grid z) must cover the grid once as well.
+    for (int z = 0; z < kMaxGang; ++z) {
+        std::vector<unsigned char> seen((size_t)TM * TN, 0);
+        for (int b = 0; b < P.ntiles; ++b) {
+            const int g = gang_block(b, z, P.ntiles);
+            if (g < 0 || g >= P.ntiles) return GPTQ_ECHECK;
+            int tm = -1, tn = -1;
+            tile_of(P, xcd_order(g, P.ntiles), tm, tn);
+            if (tm < 0 || tm >= TM || tn < 0 || tn >= TN || (lower && tn > tm)) return GPTQ_ECHECK;
+            unsigned char& f = seen[(size_t)tm * TN + tn];
+            if (f) return GPTQ_ECHECK;
+            f = 1;
+        }
     }
     return GPTQ_OK;
 }

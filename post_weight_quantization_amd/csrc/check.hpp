@@ -18,26 +18,34 @@
 
 namespace gptq {
 
+// Inside a gang (common.hpp) a launch touches each span once per group, the span moved by
+// g * gs for group g, unless the span is fixed: memory of one group outside the slots (a
+// caller's buffer), which the launch names for each group itself.
 struct Span {
     const void* p;
     int64_t ld, rows, cols;  // elements
     int esize;               // bytes per element
     bool write;
+    bool fixed;
 };
 inline Span rd(const void* p, int64_t ld, int64_t rows, int64_t cols, int esize = 4) {
-    return Span{p, ld, rows, cols, esize, false};
+    return Span{p, ld, rows, cols, esize, false, false};
 }
 inline Span wr(const void* p, int64_t ld, int64_t rows, int64_t cols, int esize = 4) {
-    return Span{p, ld, rows, cols, esize, true};
+    return Span{p, ld, rows, cols, esize, true, false};
+}
+inline Span fixed(Span s) {
+    s.fixed = true;
+    return s;
 }
 // The whole of a Hessian (f32) of either layout: its n x n rows when dense, its n (n + 1) / 2
 // floats when packed (ldh < 0).
 inline Span hessian_span(const void* H, int64_t n, int64_t ldh, bool write) {
     if (ldh < 0) {
         const int64_t P = n * (n + 1) / 2;
-        return Span{H, P, 1, P, 4, write};
+        return Span{H, P, 1, P, 4, write, false};
     }
-    return Span{H, ldh, n, n, 4, write};
+    return Span{H, ldh, n, n, 4, write, false};
 }
 
 // True while the calling thread runs an entry point in check mode.

@@ -78,6 +78,42 @@ inline int64_t hessian_elems(int64_t n, int64_t ldh) {
 // 15.80 -> 15.55 ms.
 constexpr int CHAIN_PRIO = 3;
 
+// A gang: G groups of the same shape whose device data sit at the same offsets of G slots of
+// memory gs bytes apart (the caller's inputs excepted).  While a GangScope is open on a
+// thread, the launches it makes cover all G groups: grid dimension z is the group, and each
+// kernel moves its slot pointers by blockIdx.z * gs.  Outside one, G = 1 and gs = 0.
+constexpr int kMaxGang = 16;
+struct Gang {
+    int G;
+    int64_t gs;
+};
+Gang gang_current();
+struct GangScope {
+    GangScope(int G, int64_t gs);
+    ~GangScope();
+    GangScope(const GangScope&) = delete;
+    GangScope& operator=(const GangScope&) = delete;
+};
+// Launch grid with the gang's groups in z.
+inline dim3 gang_grid(unsigned x, unsigned y = 1) { return dim3(x, y, (unsigned)gang_current().G); }
+// Pointer p of slot 0 moved to this workgroup's slot.
+template <class T>
+__device__ __forceinline__ T* gang_ptr(T* p, int64_t gs) {
+    return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(p) + (uint64_t)blockIdx.z * (uint64_t)gs);
+}
+// Per-group Hessians of a gang (the caller's buffers, not in the slots): the kernels that read
+// H take entry blockIdx.z.
+struct HTab {
+    const float* H[kMaxGang];
+    int64_t ldh[kMaxGang];
+};
+inline HTab htab_one(const float* H, int64_t ldh) {
+    HTab t{};
+    t.H[0] = H;
+    t.ldh[0] = ldh;
+    return t;
+}
+
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // 16-byte alignment, which every pointer the kernels read or write as float4 / double2 needs
 // (NULL counts as aligned: optional outputs).

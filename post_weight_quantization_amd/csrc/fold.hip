@@ -29,6 +29,7 @@
 #include <utility>
 
 #include <algorithm>
+#include <vector>
 
 #include "common.hpp"
 #include "fold.hpp"
@@ -38,10 +39,14 @@ namespace gptq {
 
 // Diagonal, dead mask, mean of the diagonal with dead channels counted as 1 (f64, fixed
 // reduction order).
-__global__ __launch_bounds__(1024) void fold_prep_kernel(const float* __restrict__ H, int64_t n,
-                                                          HLayout hl, float* __restrict__ hdiag,
-                                                          uint8_t* __restrict__ dead,
-                                                          FoldState* st) {
+__global__ __launch_bounds__(1024) void fold_prep_kernel(HTab ht, int64_t n, float* __restrict__ hdiag,
+                                                          uint8_t* __restrict__ dead, FoldState* st,
+                                                          int64_t gs) {
+    const float* __restrict__ H = ht.H[blockIdx.z];
+    const HLayout hl{n, ht.ldh[blockIdx.z]};
+    hdiag = gang_ptr(hdiag, gs);
+    dead = gang_ptr(dead, gs);
+    st = gang_ptr(st, gs);
     __shared__ double ssum[1024];
     __shared__ int scnt[1024];
     const int t = threadIdx.x;
@@ -78,7 +83,11 @@ __global__ __launch_bounds__(1024) void fold_prep_kernel(const float* __restrict
 // Per attempt: inverse equilibration scales and a cleared pivot flag.
 __global__ void fold_scale_kernel(const float* __restrict__ hdiag, const uint8_t* __restrict__ dead,
                                   FoldState* st, double lam, int64_t n, int64_t np,
-                                  float* __restrict__ dinv) {
+                                  float* __restrict__ dinv, int64_t gs) {
+    hdiag = gang_ptr(hdiag, gs);
+    dead = gang_ptr(dead, gs);
+    st = gang_ptr(st, gs);
+    dinv = gang_ptr(dinv, gs);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i == 0) {
         __atomic_store_n(&st->flag, 0u, __ATOMIC_RELAXED);
@@ -102,12 +111,17 @@ __global__ void fold_scale_kernel(const float* __restrict__ hdiag, const uint8_t
 // otherwise (also for the packed layout, whose rows start at any float) a row of the tile is
 // one wave of single floats.  Both coalesce.
 template <bool VEC>
-__global__ __launch_bounds__(256) void fold_build_kernel(const float* __restrict__ H, HLayout hl,
-                                                         const float* __restrict__ dinv,
+__global__ __launch_bounds__(256) void fold_build_kernel(HTab ht, const float* __restrict__ dinv,
                                                          const uint8_t* __restrict__ dead,
                                                          const FoldState* st, double lam,
                                                          float* __restrict__ A, int64_t n,
-                                                         int64_t np) {
+                                                         int64_t np, int64_t gs) {
+    const float* __restrict__ H = ht.H[blockIdx.z];
+    const HLayout hl{n, ht.ldh[blockIdx.z]};
+    dinv = gang_ptr(dinv, gs);
+    dead = gang_ptr(dead, gs);
+    st = gang_ptr(st, gs);
+    A = gang_ptr(A, gs);
     const int b = blockIdx.x;
     int ti = (int)((sqrtf(8.0f * (float)b + 1.0f) - 1.0f) * 0.5f);
     while ((ti + 1) * (ti + 2) / 2 <= b) ++ti;
@@ -272,10 +286,14 @@ __device__ __forceinline__ void leaf_steps(float (&x)[32], float tau, int& nbad,
     (leaf_step<C>(x, tau, nbad), ...);
 }
 
-__global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, float* __restrict__ X,
-                                                        float* __restrict__ MI, int64_t np, int k,
-                                                        unsigned* flag, unsigned* minp, float tau) {
+__global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, float* __restrict__ MI,
+                                                        int64_t np, int k, unsigned* flag,
+                                                        unsigned* minp, float tau, int64_t gs) {
+    flag = gang_ptr(flag, gs);
     if (__atomic_load_n(flag, __ATOMIC_RELAXED)) return;
+    A = gang_ptr(A, gs);
+    MI = gang_ptr(MI, gs);
+    minp = gang_ptr(minp, gs);
     __builtin_amdgcn_s_setprio(CHAIN_PRIO);
     // 81 KB of LDS, so that the kernel fits on a CU beside one GEMM workgroup.  The off-diagonal
     // 32-blocks M_IJ (I > J) of L^-1 live in the unused upper triangle of Ls, at block (J, I).
@@ -426,7 +444,10 @@ template <bool VEC>
 __global__ __launch_bounds__(256) void fold_make_u_kernel(const float* __restrict__ X,
                                                           const float* __restrict__ dinv,
                                                           float* __restrict__ U, int64_t n,
-                                                          int64_t np) {
+                                                          int64_t np, int64_t gs) {
+    X = gang_ptr(X, gs);
+    dinv = gang_ptr(dinv, gs);
+    U = gang_ptr(U, gs);
     const bool below = blockIdx.x < blockIdx.y;
     if constexpr (VEC) {
         const int64_t c4 = (int64_t)blockIdx.x * 64 + (threadIdx.x & 15) * 4;
@@ -470,7 +491,10 @@ __global__ __launch_bounds__(256) void fold_identity_kernel(float* __restrict__ 
 // below are written by the substitution).
 __global__ __launch_bounds__(256) void fold_x_diag_kernel(float* __restrict__ X,
                                                           const float* __restrict__ MI,
-                                                          int64_t np, int64_t kb, int64_t w) {
+                                                          int64_t np, int64_t kb, int64_t w,
+                                                          int64_t gs) {
+    X = gang_ptr(X, gs);
+    MI = gang_ptr(MI, gs);
     const int64_t r = blockIdx.y;                // row within the block
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= w) return;
@@ -481,7 +505,9 @@ __global__ __launch_bounds__(256) void fold_x_diag_kernel(float* __restrict__ X,
 
 __global__ __launch_bounds__(256) void fold_copy_rows_kernel(const float* __restrict__ src,
                                                              float* __restrict__ dst, int64_t ld,
-                                                             int64_t cols) {
+                                                             int64_t cols, int64_t gs) {
+    src = gang_ptr(src, gs);
+    dst = gang_ptr(dst, gs);
     const int64_t r = blockIdx.y;
     for (int64_t c = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4; c < cols;
          c += (int64_t)gridDim.x * 1024) {
@@ -526,6 +552,306 @@ extern "C" int gptq_fold_ex(const float* H, int64_t n, int64_t ldh, double lambd
 
 namespace gptq {
 
+namespace {
+
+// check_launch over spans listed at run time, then the launch.
+template <class F>
+int launch_with(hipStream_t s, const char* name, const std::vector<Span>& acc, F&& f) {
+    const int rc = check_launch(name, s, acc.data(), (int)acc.size());
+    if (rc != GPTQ_OK) return rc;
+    if (!dry_run()) f();
+    return GPTQ_OK;
+}
+
+// The Hessians of the ng groups of ht, read whole: the caller's buffers, one per group.
+void push_hessians(std::vector<Span>& acc, const HTab& ht, int ng, int64_t n) {
+    for (int g = 0; g < ng; ++g) acc.push_back(fixed(hessian_span(ht.H[g], n, ht.ldh[g], false)));
+}
+
+#define FOLD_OK(call)                           \
+    do {                                        \
+        const int rc_ = (call);                 \
+        if (rc_ != GPTQ_OK) return rc_;         \
+    } while (0)
+
+// Diagonal, dead flags, base and a cleared flag for the ng groups of ht (the gang open on this
+// thread, or one group).
+int fold_prep(const HTab& ht, int ng, int64_t n, float* hdiag, uint8_t* dead, FoldState* state,
+              hipStream_t st) {
+    std::vector<Span> acc;
+    push_hessians(acc, ht, ng, n);
+    acc.push_back(wr(hdiag, n, 1, n));
+    acc.push_back(wr(dead, n, 1, n, 1));
+    acc.push_back(wr(state, 1, 1, sizeof(FoldState), 1));
+    const int64_t gs = gang_current().gs;
+    ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 8.0 * n);
+    FOLD_OK(launch_with(st, "fold_prep", acc, [&] {
+        fold_prep_kernel<<<gang_grid(1), 1024, 0, st>>>(ht, n, hdiag, dead, state, gs);
+    }));
+    return launch_status() != GPTQ_OK ? GPTQ_EHIP : GPTQ_OK;
+}
+
+// One f32 attempt at damping lam: the scales, the reversed equilibrated matrix, and the blocked
+// Cholesky with the blocked inverse trailing it, for the ng groups of ht (the gang open on this
+// thread, or one group).  Pivots that are not above tau (or not finite) set the group's flag
+// and make its remaining launches return at once.  Ends with the helper streams joined into st.
+int fold32_attempt(const HTab& ht, int ng, int64_t n, bool build_vec, const float* hdiag,
+                   const uint8_t* dead, FoldState* state, double lam, float tau, char* ws,
+                   const FoldLayout& L, hipStream_t st, const Helper& hp, bool single) {
+    float* dinv = (float*)(ws + L.off_dinv);
+    float* MI = (float*)(ws + L.off_mi);
+    float* A = (float*)(ws + L.off_a);
+    float* X = (float*)(ws + L.off_x);
+    float* Tb = (float*)(ws + L.off_t);
+    float* Xt = (float*)(ws + L.off_xt);
+    const int64_t np = L.np;
+    const int64_t gs = gang_current().gs;
+    const Span st_rw = wr(state, 1, 1, sizeof(FoldState), 1);
+    hipStream_t ts = hp.stream;
+    auto record = [single](hipEvent_t e, hipStream_t s) { return single ? GPTQ_OK : ev_record(e, s); };
+    auto wait = [single](hipStream_t s, hipEvent_t e) { return single ? GPTQ_OK : stream_wait(s, e); };
+    {
+        ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 4.0 * (double)n * n + 4.0 * (double)np * np / 2);
+        GPTQ_LAUNCH(st, "fold_scale",
+                    (fold_scale_kernel<<<gang_grid((unsigned)((np + 255) / 256)), 256, 0, st>>>(
+                        hdiag, dead, state, lam, n, np, dinv, gs)),
+                    rd(hdiag, n, 1, n), rd(dead, n, 1, n, 1), st_rw, wr(dinv, np, 1, np));
+        const unsigned build_grid = (unsigned)((np / 64) * (np / 64 + 1) / 2);
+        std::vector<Span> acc;
+        push_hessians(acc, ht, ng, n);
+        acc.push_back(rd(dinv, np, 1, np));
+        acc.push_back(rd(dead, n, 1, n, 1));
+        acc.push_back(rd(state, 1, 1, sizeof(FoldState), 1));
+        acc.push_back(wr(A, np, np, np));
+        FOLD_OK(launch_with(st, "fold_build", acc, [&] {
+            if (build_vec)
+                fold_build_kernel<true><<<gang_grid(build_grid), 256, 0, st>>>(ht, dinv, dead, state,
+                                                                              lam, A, n, np, gs);
+            else
+                fold_build_kernel<false><<<gang_grid(build_grid), 256, 0, st>>>(ht, dinv, dead, state,
+                                                                               lam, A, n, np, gs);
+        }));
+    }
+    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    // Outer panels of width w (the K of the bulk updates); inside a panel, 128-wide steps
+    // factor the diagonal block, solve the rows below and update the rest of the panel.
+    // Three streams:
+    //   st  the Cholesky's serial chain: the panel steps, then the next panel's columns
+    //       (look-ahead of one panel);
+    //   ts  the two bulk updates of panel k, one after the other, overlapping the next
+    //       panel's chain: the Cholesky's trailing update beyond the next panel (ev_b, which
+    //       the look-ahead after next waits for), then the inverse's update of every row of X
+    //       below the panel (ev_d);
+    //   tx  the inverse's small steps, once panel k of L is final (ev_a): the inverse of the
+    //       panel's diagonal block and the panel's rows of X (ev_c; those rows need the
+    //       previous panel's update of X, ev_d).  Nothing in the Cholesky waits for them.
+    // One bulk update at a time gets the whole GPU beside the chain; two concurrent ones (the
+    // inverse's update on tx) each ran at about 75% of the per-launch rate and no sooner.
+    hipStream_t tx = hp.stream2;
+    bool first_bulk = true;
+    bool x_pending = false;  // ev_d holds an update of X that the next rows of X need
+    for (int64_t kb = 0; kb < np; kb += L.nb2) {
+        const int64_t w = std::min<int64_t>(L.nb2, np - kb);
+        const int64_t R = w / NB;
+        for (int64_t r = 0; r < R; ++r) {
+            const int64_t cb = kb + r * NB;
+            const int64_t rest_c = np - cb - NB;
+            {
+                ProfScope ps(FAM_FOLD_DIAG, st, 2.0 * NB * NB * NB / 3.0, 0.0);
+                GPTQ_LAUNCH(st, "fold_diag",
+                            (fold_diag_kernel<<<gang_grid(1), 256, 0, st>>>(A, MI, np, (int)(cb / NB),
+                                                                           &state->flag, &state->minp32,
+                                                                           tau, gs)),
+                            rd(A + cb * np + cb, np, NB, NB), wr(MI + (cb / NB) * NB * NB, NB, NB, NB),
+                            st_rw);
+            }
+            if (rest_c <= 0) continue;
+            const float* mic = MI + (cb / NB) * NB * NB;
+            // L_ic = A_ic MI_c^T for every row below (in place, whole tiles per workgroup).
+            const GemmProblem pa = gemm_full(A + (cb + NB) * np + cb, np, mic, NB, nullptr,
+                                             A + (cb + NB) * np + cb, np, (int)rest_c, NB, NB,
+                                             1.0f, 0);
+            {
+                ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * NB * (double)rest_c, 0.0);
+                FOLD_OK((launch_gemm<1, true, false, false>("fold_panel", st, gemm_batch(pa, nullptr),
+                                                            &state->flag)));
+            }
+            // The rest of the panel's columns: A[cb+128:, cb+128:kb+w] -= L_ic L_jc^T.
+            const int64_t ncol = kb + w - cb - NB;
+            if (ncol > 0) {
+                GemmProblem iu = gemm_full(A + (cb + NB) * np + cb, np, A + (cb + NB) * np + cb,
+                                           np, A + (cb + NB) * np + cb + NB,
+                                           A + (cb + NB) * np + cb + NB, np, (int)rest_c,
+                                           (int)ncol, NB, -1.0f, 1);
+                iu.mask_diag = 1;
+                iu.skip_upper = 1;
+                ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * NB * (double)rest_c * ncol, 0.0);
+                FOLD_OK((launch_gemm<4, true, true, false>("fold_in_panel", st, gemm_batch(iu, nullptr),
+                                                           &state->flag)));
+            }
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+        }
+        // Panel k of L (and the inverses of its diagonal 128-blocks) is final.
+        FOLD_OK(record(hp.ev_a, st));
+        const int64_t rest = np - kb - w;
+        const float* P = A + (kb + w) * np + kb;  // the panel's rows below its diagonal block
+
+        // --- the inverse, on tx ---
+        FOLD_OK(wait(tx, hp.ev_a));
+        // Inverse of the panel's w x w diagonal block of L, into X[kb:kb+w, kb:kb+w]: the
+        // 128-blocks on the diagonal are the MI_c written by the diagonal kernel; block row I
+        // is -MI_I (L[I, <I] X[<I, <I]) (block forward substitution).
+        GPTQ_LAUNCH(tx, "fold_x_diag",
+                    (fold_x_diag_kernel<<<gang_grid((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, tx>>>(
+                        X, MI, np, kb, w, gs)),
+                    rd(MI + (kb / NB) * NB * NB, NB, w, NB), wr(X + kb * np + kb, np, w, w));
+        if (R > 1) {
+            for (int64_t I = 1; I < R; ++I) {
+                const int64_t ci = kb + I * NB;
+                const GemmBatch t1 = gemm_batch(
+                    gemm_full(A + ci * np + kb, np, X + kb * np + kb, np, nullptr, Tb, w, NB,
+                              (int)(I * NB), (int)(I * NB), 1.0f, 0),
+                    nullptr);
+                const GemmBatch t2 = gemm_batch(
+                    gemm_full(MI + (ci / NB) * NB * NB, NB, Tb, w, nullptr, X + ci * np + kb, np,
+                              NB, (int)(I * NB), NB, -1.0f, 0),
+                    nullptr);
+                ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * NB * (double)(I * NB) * (I * NB + NB), 0.0);
+                FOLD_OK((launch_gemm<5, false, false, false>("fold_inv_block_a", tx, t1, &state->flag)));
+                FOLD_OK((launch_gemm<5, false, false, false>("fold_inv_block_b", tx, t2, &state->flag)));
+            }
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+        }
+        // Rows of X in this panel: X[kb:kb+w, 0:kb] = Minv_w X[kb:kb+w, 0:kb] (out of place,
+        // then copied back: a workgroup tile spans only 128 of the w rows it reads).  They
+        // need the previous panel's update of X (on ts, ev_d).
+        if (kb > 0) {
+            if (x_pending) FOLD_OK(wait(tx, hp.ev_d));
+            const GemmBatch xb = gemm_batch(
+                gemm_full(X + kb * np + kb, np, X + kb * np, np, nullptr, Xt, np, (int)w, (int)kb,
+                          (int)w, 1.0f, 0),
+                nullptr);
+            {
+                ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * (double)w * w * kb, 0.0);
+                FOLD_OK((launch_gemm<9, false, false, false>("fold_x_rows", tx, xb, &state->flag)));
+            }
+            GPTQ_LAUNCH(tx, "fold_copy_rows",
+                        (fold_copy_rows_kernel<<<gang_grid((unsigned)((kb + 1023) / 1024), (unsigned)w), 256, 0, tx>>>(
+                            Xt, X + kb * np, np, kb, gs)),
+                        rd(Xt, np, w, kb), wr(X + kb * np, np, w, kb));
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+        }
+        if (rest <= 0) continue;
+        FOLD_OK(record(hp.ev_c, tx));  // the panel's rows of X are final
+
+        // --- the Cholesky's trailing update ---
+        const int64_t nw = std::min<int64_t>(L.nb2, rest);  // width of the next panel
+        const int64_t rest2 = rest - nw;
+        // Bulk, on ts: A_ij -= P_i P_j^T beyond the next panel.
+        FOLD_OK(wait(ts, hp.ev_a));
+        if (rest2 > 0) {
+            const GemmProblem sy = gemm_syrk_lower(P + nw * np, np,
+                                                   A + (kb + w + nw) * np + kb + w + nw,
+                                                   A + (kb + w + nw) * np + kb + w + nw, np,
+                                                   (int)rest2, (int)w, -1.0f, 1);
+            const double fl = (double)w * rest2 * (rest2 + 1);
+            {
+                ProfScope ps(FAM_FOLD_UPDATE, ts, fl, 0.0);
+                FOLD_OK((launch_gemm<0, true, false, false>("fold_bulk", ts, gemm_batch(sy, nullptr),
+                                                            &state->flag)));
+            }
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+        }
+        // Look-ahead, on st: the next panel's columns (rows below kb+w, diagonal tiles lower
+        // only); they need the previous panel's bulk update.
+        if (!first_bulk) FOLD_OK(wait(st, hp.ev_b));
+        GemmProblem strip = gemm_full(P, np, P, np, A + (kb + w) * np + kb + w,
+                                      A + (kb + w) * np + kb + w, np, (int)rest, (int)nw,
+                                      (int)w, -1.0f, 1);
+        strip.mask_diag = 1;
+        strip.skip_upper = 1;
+        {
+            ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * w * (double)rest * nw, 0.0);
+            FOLD_OK((launch_gemm<3, true, false, false>("fold_look_ahead", st, gemm_batch(strip, nullptr),
+                                                        &state->flag)));
+        }
+        if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+        if (rest2 > 0) {
+            FOLD_OK(record(hp.ev_b, ts));
+            first_bulk = false;
+        }
+        // The inverse's update, on ts after the SYRK: every row below,
+        // X_i,<kb+w -= L_i,k X[kb:kb+w, <kb+w] (X's columns kb..kb+w-1 are first written here,
+        // so those tiles ignore C_in).
+        {
+            FOLD_OK(wait(ts, hp.ev_c));
+            GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np,
+                                       X + (kb + w) * np, np, (int)rest, (int)(kb + w), (int)w,
+                                       -1.0f, 1);
+            xu.beta0_col = (int)kb;
+            // Second slot of the bulk kernel (its B layout there is "N": rows of X).
+            const GemmProblem none = gemm_none();
+            ProfScope ps(FAM_FOLD_UPDATE, ts, 2.0 * w * (double)rest * (kb + w), 0.0);
+            FOLD_OK((launch_gemm<0, true, false, false>("fold_x_update", ts, gemm_batch(none, &xu),
+                                                        &state->flag)));
+            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+            FOLD_OK(record(hp.ev_d, ts));
+            x_pending = true;
+        }
+    }
+    // Join both helper streams.
+    FOLD_OK(record(hp.ev_c, tx));
+    FOLD_OK(wait(st, hp.ev_c));
+    FOLD_OK(record(hp.ev_b, ts));
+    FOLD_OK(wait(st, hp.ev_b));
+    return GPTQ_OK;
+}
+
+// U = P X P D^-1 from an f32 attempt.
+int fold32_make_u(char* ws, const FoldLayout& L, float* U, int64_t n, hipStream_t st) {
+    const float* X = (const float*)(ws + L.off_x);
+    const float* dinv = (const float*)(ws + L.off_dinv);
+    const int64_t np = L.np;
+    const int64_t gs = gang_current().gs;
+    ProfScope ps(FAM_FOLD_MAKEU, st, 0.0, 4.0 * (double)n * n);
+    const dim3 g64 = gang_grid((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64));
+    const bool vec = n % 4 == 0 && ((uintptr_t)U & 15u) == 0 && gs % 16 == 0;
+    GPTQ_LAUNCH(st, "fold_make_u",
+                (vec ? fold_make_u_kernel<true><<<g64, 256, 0, st>>>(X, dinv, U, n, np, gs)
+                     : fold_make_u_kernel<false><<<g64, 256, 0, st>>>(X, dinv, U, n, np, gs)),
+                rd(X, np, np, np), rd(dinv, np, 1, np), wr(U, n, n, n));
+    return launch_status() != GPTQ_OK ? GPTQ_EHIP : GPTQ_OK;
+}
+
+void fill_report(gptq_fold_report* report, double lam, const FoldState& host, int attempts,
+                 bool degenerate, bool use64) {
+    if (!report) return;
+    report->lambda_used = lam;
+    report->base = host.base;
+    report->damp = lam * host.base;
+    report->attempts = attempts;
+    report->n_dead = host.n_dead;
+    report->degenerate = degenerate ? 1 : 0;
+    report->precision = use64 ? 64 : 32;
+    double pm = 0.0;
+    if (!degenerate) {
+        if (use64) {
+            memcpy(&pm, &host.minp64, sizeof(pm));
+        } else {
+            float p32;
+            memcpy(&p32, &host.minp32, sizeof(p32));
+            pm = p32;
+        }
+    }
+    report->min_pivot = pm;
+}
+
+bool build_vec_ok(const float* H, int64_t n, int64_t ldh) {
+    return ldh >= 0 && n % 4 == 0 && ldh % 4 == 0 && al16(H);
+}
+
+}  // namespace
+
 int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precision, float* U,
              float* hdiag, uint8_t* dead, void* workspace, size_t workspace_bytes, hipStream_t st,
              gptq_fold_report* report, bool single) {
@@ -545,39 +871,19 @@ int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precisio
     check_buffer(workspace, workspace_bytes, "workspace");
     char* ws = (char*)workspace;
     FoldState* state = (FoldState*)(ws + L.off_state);
-    float* dinv = (float*)(ws + L.off_dinv);
-    float* MI = (float*)(ws + L.off_mi);
-    float* A = (float*)(ws + L.off_a);
-    float* X = (float*)(ws + L.off_x);
-    float* Tb = (float*)(ws + L.off_t);
-    float* Xt = (float*)(ws + L.off_xt);
-    const int64_t np = L.np;
-    const Span st_rw = wr(state, 1, 1, sizeof(FoldState), 1);
+    const HTab ht = htab_one(H, ldh);
     const HLayout hl{n, ldh};
 
-    {
-        ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 8.0 * n);
-        GPTQ_LAUNCH(st, "fold_prep", (fold_prep_kernel<<<1, 1024, 0, st>>>(H, n, hl, hdiag, dead, state)),
-                    hessian_span(H, n, ldh, false), wr(hdiag, n, 1, n), wr(dead, n, 1, n, 1), st_rw);
-    }
-    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    FOLD_OK(fold_prep(ht, 1, n, hdiag, dead, state, st));
 
     // single: every launch on st, in program order (an order the helper streams' events allow,
     // so the same results bit for bit); no helper stream or event is taken.
     Helper hp{st, st, nullptr, nullptr, nullptr, nullptr, -1};
     if (!single && helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
-    hipStream_t ts = hp.stream;
     struct Release {
         const Helper& h;
         ~Release() { helper_release(h); }
     } release{hp};
-    auto record = [single](hipEvent_t e, hipStream_t s) { return single ? GPTQ_OK : ev_record(e, s); };
-    auto wait = [single](hipStream_t s, hipEvent_t e) { return single ? GPTQ_OK : stream_wait(s, e); };
-#define FOLD_OK(call)                           \
-    do {                                        \
-        const int rc_ = (call);                 \
-        if (rc_ != GPTQ_OK) return rc_;         \
-    } while (0)
 
     double lam = (lambda > 0.0) ? lambda : 0.0;
     int attempts = 0;
@@ -589,198 +895,11 @@ int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precisio
     const float tau = precision == GPTQ_FOLD_AUTO ? kF32PivotFloor : 0.0f;
     for (;;) {
         ++attempts;
-        if (use64) {
+        if (use64)
             FOLD_OK(fold64_attempt(H, hl, hdiag, dead, state, lam, ws, L, st, hp, single));
-        } else {
-        {
-            ProfScope ps(FAM_FOLD_BUILD, st, 0.0, 4.0 * (double)n * n + 4.0 * (double)np * np / 2);
-            GPTQ_LAUNCH(st, "fold_scale",
-                        (fold_scale_kernel<<<(unsigned)((np + 255) / 256), 256, 0, st>>>(
-                            hdiag, dead, state, lam, n, np, dinv)),
-                        rd(hdiag, n, 1, n), rd(dead, n, 1, n, 1), st_rw, wr(dinv, np, 1, np));
-            const bool build_vec = ldh >= 0 && n % 4 == 0 && ldh % 4 == 0 && al16(H);
-            const unsigned build_grid = (unsigned)((np / 64) * (np / 64 + 1) / 2);
-            GPTQ_LAUNCH(st, "fold_build",
-                        (build_vec
-                             ? fold_build_kernel<true><<<build_grid, 256, 0, st>>>(
-                                   H, hl, dinv, dead, state, lam, A, n, np)
-                             : fold_build_kernel<false><<<build_grid, 256, 0, st>>>(
-                                   H, hl, dinv, dead, state, lam, A, n, np)),
-                        hessian_span(H, n, ldh, false), rd(dinv, np, 1, np), rd(dead, n, 1, n, 1),
-                        rd(state, 1, 1, sizeof(FoldState), 1), wr(A, np, np, np));
-        }
-        if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-        // Outer panels of width w (the K of the bulk updates); inside a panel, 128-wide steps
-        // factor the diagonal block, solve the rows below and update the rest of the panel.
-        // Three streams:
-        //   st  the Cholesky's serial chain: the panel steps, then the next panel's columns
-        //       (look-ahead of one panel);
-        //   ts  the two bulk updates of panel k, one after the other, overlapping the next
-        //       panel's chain: the Cholesky's trailing update beyond the next panel (ev_b, which
-        //       the look-ahead after next waits for), then the inverse's update of every row of X
-        //       below the panel (ev_d);
-        //   tx  the inverse's small steps, once panel k of L is final (ev_a): the inverse of the
-        //       panel's diagonal block and the panel's rows of X (ev_c; those rows need the
-        //       previous panel's update of X, ev_d).  Nothing in the Cholesky waits for them.
-        // One bulk update at a time gets the whole GPU beside the chain; two concurrent ones (the
-        // inverse's update on tx) each ran at about 75% of the per-launch rate and no sooner.
-        hipStream_t tx = hp.stream2;
-        bool first_bulk = true;
-        bool x_pending = false;  // ev_d holds an update of X that the next rows of X need
-        for (int64_t kb = 0; kb < np; kb += L.nb2) {
-            const int64_t w = std::min<int64_t>(L.nb2, np - kb);
-            const int64_t R = w / NB;
-            for (int64_t r = 0; r < R; ++r) {
-                const int64_t cb = kb + r * NB;
-                const int64_t rest_c = np - cb - NB;
-                {
-                    ProfScope ps(FAM_FOLD_DIAG, st, 2.0 * NB * NB * NB / 3.0, 0.0);
-                    GPTQ_LAUNCH(st, "fold_diag",
-                                (fold_diag_kernel<<<1, 256, 0, st>>>(A, X, MI, np, (int)(cb / NB), &state->flag,
-                                                                     &state->minp32, tau)),
-                                rd(A + cb * np + cb, np, NB, NB), wr(MI + (cb / NB) * NB * NB, NB, NB, NB),
-                                st_rw);
-                }
-                if (rest_c <= 0) continue;
-                const float* mic = MI + (cb / NB) * NB * NB;
-                // L_ic = A_ic MI_c^T for every row below (in place, whole tiles per workgroup).
-                const GemmProblem pa = gemm_full(A + (cb + NB) * np + cb, np, mic, NB, nullptr,
-                                                 A + (cb + NB) * np + cb, np, (int)rest_c, NB, NB,
-                                                 1.0f, 0);
-                {
-                    ProfScope ps(FAM_FOLD_PANEL, st, 2.0 * NB * NB * (double)rest_c, 0.0);
-                    FOLD_OK((launch_gemm<1, true, false, false>("fold_panel", st, gemm_batch(pa, nullptr),
-                                                                &state->flag)));
-                }
-                // The rest of the panel's columns: A[cb+128:, cb+128:kb+w] -= L_ic L_jc^T.
-                const int64_t ncol = kb + w - cb - NB;
-                if (ncol > 0) {
-                    GemmProblem iu = gemm_full(A + (cb + NB) * np + cb, np, A + (cb + NB) * np + cb,
-                                               np, A + (cb + NB) * np + cb + NB,
-                                               A + (cb + NB) * np + cb + NB, np, (int)rest_c,
-                                               (int)ncol, NB, -1.0f, 1);
-                    iu.mask_diag = 1;
-                    iu.skip_upper = 1;
-                    ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * NB * (double)rest_c * ncol, 0.0);
-                    FOLD_OK((launch_gemm<4, true, true, false>("fold_in_panel", st, gemm_batch(iu, nullptr),
-                                                               &state->flag)));
-                }
-                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-            }
-            // Panel k of L (and the inverses of its diagonal 128-blocks) is final.
-            FOLD_OK(record(hp.ev_a, st));
-            const int64_t rest = np - kb - w;
-            const float* P = A + (kb + w) * np + kb;  // the panel's rows below its diagonal block
-
-            // --- the inverse, on tx ---
-            FOLD_OK(wait(tx, hp.ev_a));
-            // Inverse of the panel's w x w diagonal block of L, into X[kb:kb+w, kb:kb+w]: the
-            // 128-blocks on the diagonal are the MI_c written by the diagonal kernel; block row I
-            // is -MI_I (L[I, <I] X[<I, <I]) (block forward substitution).
-            GPTQ_LAUNCH(tx, "fold_x_diag",
-                        (fold_x_diag_kernel<<<dim3((unsigned)((w + 255) / 256), (unsigned)w), 256, 0, tx>>>(
-                            X, MI, np, kb, w)),
-                        rd(MI + (kb / NB) * NB * NB, NB, w, NB), wr(X + kb * np + kb, np, w, w));
-            if (R > 1) {
-                for (int64_t I = 1; I < R; ++I) {
-                    const int64_t ci = kb + I * NB;
-                    const GemmBatch t1 = gemm_batch(
-                        gemm_full(A + ci * np + kb, np, X + kb * np + kb, np, nullptr, Tb, w, NB,
-                                  (int)(I * NB), (int)(I * NB), 1.0f, 0),
-                        nullptr);
-                    const GemmBatch t2 = gemm_batch(
-                        gemm_full(MI + (ci / NB) * NB * NB, NB, Tb, w, nullptr, X + ci * np + kb, np,
-                                  NB, (int)(I * NB), NB, -1.0f, 0),
-                        nullptr);
-                    ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * NB * (double)(I * NB) * (I * NB + NB), 0.0);
-                    FOLD_OK((launch_gemm<5, false, false, false>("fold_inv_block_a", tx, t1, &state->flag)));
-                    FOLD_OK((launch_gemm<5, false, false, false>("fold_inv_block_b", tx, t2, &state->flag)));
-                }
-                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-            }
-            // Rows of X in this panel: X[kb:kb+w, 0:kb] = Minv_w X[kb:kb+w, 0:kb] (out of place,
-            // then copied back: a workgroup tile spans only 128 of the w rows it reads).  They
-            // need the previous panel's update of X (on ts, ev_d).
-            if (kb > 0) {
-                if (x_pending) FOLD_OK(wait(tx, hp.ev_d));
-                const GemmBatch xb = gemm_batch(
-                    gemm_full(X + kb * np + kb, np, X + kb * np, np, nullptr, Xt, np, (int)w, (int)kb,
-                              (int)w, 1.0f, 0),
-                    nullptr);
-                {
-                    ProfScope ps(FAM_FOLD_PANEL, tx, 2.0 * (double)w * w * kb, 0.0);
-                    FOLD_OK((launch_gemm<9, false, false, false>("fold_x_rows", tx, xb, &state->flag)));
-                }
-                GPTQ_LAUNCH(tx, "fold_copy_rows",
-                            (fold_copy_rows_kernel<<<dim3((unsigned)((kb + 1023) / 1024), (unsigned)w), 256, 0, tx>>>(
-                                Xt, X + kb * np, np, kb)),
-                            rd(Xt, np, w, kb), wr(X + kb * np, np, w, kb));
-                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-            }
-            if (rest <= 0) continue;
-            FOLD_OK(record(hp.ev_c, tx));  // the panel's rows of X are final
-
-            // --- the Cholesky's trailing update ---
-            const int64_t nw = std::min<int64_t>(L.nb2, rest);  // width of the next panel
-            const int64_t rest2 = rest - nw;
-            // Bulk, on ts: A_ij -= P_i P_j^T beyond the next panel.
-            FOLD_OK(wait(ts, hp.ev_a));
-            if (rest2 > 0) {
-                const GemmProblem sy = gemm_syrk_lower(P + nw * np, np,
-                                                       A + (kb + w + nw) * np + kb + w + nw,
-                                                       A + (kb + w + nw) * np + kb + w + nw, np,
-                                                       (int)rest2, (int)w, -1.0f, 1);
-                const double fl = (double)w * rest2 * (rest2 + 1);
-                {
-                    ProfScope ps(FAM_FOLD_UPDATE, ts, fl, 0.0);
-                    FOLD_OK((launch_gemm<0, true, false, false>("fold_bulk", ts, gemm_batch(sy, nullptr),
-                                                                &state->flag)));
-                }
-                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-            }
-            // Look-ahead, on st: the next panel's columns (rows below kb+w, diagonal tiles lower
-            // only); they need the previous panel's bulk update.
-            if (!first_bulk) FOLD_OK(wait(st, hp.ev_b));
-            GemmProblem strip = gemm_full(P, np, P, np, A + (kb + w) * np + kb + w,
-                                          A + (kb + w) * np + kb + w, np, (int)rest, (int)nw,
-                                          (int)w, -1.0f, 1);
-            strip.mask_diag = 1;
-            strip.skip_upper = 1;
-            {
-                ProfScope ps(FAM_FOLD_NEXT, st, 2.0 * w * (double)rest * nw, 0.0);
-                FOLD_OK((launch_gemm<3, true, false, false>("fold_look_ahead", st, gemm_batch(strip, nullptr),
-                                                            &state->flag)));
-            }
-            if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-            if (rest2 > 0) {
-                FOLD_OK(record(hp.ev_b, ts));
-                first_bulk = false;
-            }
-            // The inverse's update, on ts after the SYRK: every row below,
-            // X_i,<kb+w -= L_i,k X[kb:kb+w, <kb+w] (X's columns kb..kb+w-1 are first written here,
-            // so those tiles ignore C_in).
-            {
-                FOLD_OK(wait(ts, hp.ev_c));
-                GemmProblem xu = gemm_full(P, np, X + kb * np, np, X + (kb + w) * np,
-                                           X + (kb + w) * np, np, (int)rest, (int)(kb + w), (int)w,
-                                           -1.0f, 1);
-                xu.beta0_col = (int)kb;
-                // Second slot of the bulk kernel (its B layout there is "N": rows of X).
-                const GemmProblem none = gemm_none();
-                ProfScope ps(FAM_FOLD_UPDATE, ts, 2.0 * w * (double)rest * (kb + w), 0.0);
-                FOLD_OK((launch_gemm<0, true, false, false>("fold_x_update", ts, gemm_batch(none, &xu),
-                                                            &state->flag)));
-                if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-                FOLD_OK(record(hp.ev_d, ts));
-                x_pending = true;
-            }
-        }
-        // Join both helper streams, then read the pivot flag.
-        FOLD_OK(record(hp.ev_c, tx));
-        FOLD_OK(wait(st, hp.ev_c));
-        FOLD_OK(record(hp.ev_b, ts));
-        FOLD_OK(wait(st, hp.ev_b));
-        }
+        else
+            FOLD_OK(fold32_attempt(ht, 1, n, build_vec_ok(H, n, ldh), hdiag, dead, state, lam, tau,
+                                   ws, L, st, hp, single));
         if (dry_run()) {
             host_sync_record(st);
             host.flag = 0u;
@@ -801,48 +920,76 @@ int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precisio
             break;
         }
     }
-#undef FOLD_OK
     const dim3 g((unsigned)((n + 31) / 32), (unsigned)((n + 31) / 32));
     if (degenerate) {
         GPTQ_LAUNCH(st, "fold_identity", (fold_identity_kernel<<<g, 256, 0, st>>>(U, n)), wr(U, n, n, n));
+        if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
     } else if (use64) {
-        const int rc = fold64_make_u(U, n, ws, L, st);
-        if (rc != GPTQ_OK) return rc;
+        FOLD_OK(fold64_make_u(U, n, ws, L, st));
     } else {
-        ProfScope ps(FAM_FOLD_MAKEU, st, 0.0, 4.0 * (double)n * n);
-        const dim3 g64((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64));
-        const bool vec = n % 4 == 0 && ((uintptr_t)U & 15u) == 0;
-        GPTQ_LAUNCH(st, "fold_make_u",
-                    (vec ? fold_make_u_kernel<true><<<g64, 256, 0, st>>>(X, dinv, U, n, np)
-                         : fold_make_u_kernel<false><<<g64, 256, 0, st>>>(X, dinv, U, n, np)),
-                    rd(X, np, np, np), rd(dinv, np, 1, np), wr(U, n, n, n));
+        FOLD_OK(fold32_make_u(ws, L, U, n, st));
     }
-    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
-    {
-        const int rc = check.finish();
-        if (rc != GPTQ_OK) return rc;
-    }
-    if (report) {
-        report->lambda_used = lam;
-        report->base = host.base;
-        report->damp = lam * host.base;
-        report->attempts = attempts;
-        report->n_dead = host.n_dead;
-        report->degenerate = degenerate ? 1 : 0;
-        report->precision = use64 ? 64 : 32;
-        double pm = 0.0;
-        if (!degenerate) {
-            if (use64) {
-                memcpy(&pm, &host.minp64, sizeof(pm));
-            } else {
-                float p32;
-                memcpy(&p32, &host.minp32, sizeof(p32));
-                pm = p32;
-            }
-        }
-        report->min_pivot = pm;
-    }
+    FOLD_OK(check.finish());
+    fill_report(report, lam, host, attempts, degenerate, use64);
     return degenerate ? GPTQ_DEGENERATE : GPTQ_OK;
 }
+
+int fold_gang(const HTab& ht, int G, int64_t gs, int64_t n, double lambda, int precision,
+              float* U, float* hdiag, uint8_t* dead, char* ws, size_t ws_bytes, hipStream_t st,
+              FoldState* host, unsigned* failed, gptq_fold_report* reports) {
+    if (G < 1 || G > kMaxGang || n <= 0 || n > ((int64_t)1 << 20)) return GPTQ_EINVAL;
+    if (precision != GPTQ_FOLD_AUTO && precision != GPTQ_FOLD_F32) return GPTQ_EINVAL;
+    if (gs % 256 != 0 || !al16(ws) || !al16(U)) return GPTQ_EINVAL;
+    const FoldLayout L = fold_layout(n);
+    if (ws_bytes < L.total_f32) return GPTQ_EWORKSPACE;
+    bool vec = true;
+    for (int g = 0; g < G; ++g) {
+        if (!ht.H[g] || !hessian_ld_ok(n, ht.ldh[g])) return GPTQ_EINVAL;
+        vec = vec && build_vec_ok(ht.H[g], n, ht.ldh[g]);
+    }
+    CheckScope check;
+    for (int g = 0; g < G; ++g) {
+        check_buffer(ht.H[g], sizeof(float) * (size_t)hessian_elems(n, ht.ldh[g]), "H");
+        check_buffer((const char*)U + g * gs, sizeof(float) * (size_t)(n * n), "U");
+        check_buffer((const char*)hdiag + g * gs, sizeof(float) * (size_t)n, "hdiag");
+        check_buffer((const char*)dead + g * gs, (size_t)n, "dead");
+        check_buffer(ws + g * gs, ws_bytes, "workspace");
+    }
+    FoldState* state = (FoldState*)(ws + L.off_state);
+    const double lam = (lambda > 0.0) ? lambda : 0.0;
+    const float tau = precision == GPTQ_FOLD_AUTO ? kF32PivotFloor : 0.0f;
+    Helper hp{};
+    if (helper_acquire(&hp) != GPTQ_OK) return GPTQ_EHIP;
+    struct Release {
+        const Helper& h;
+        ~Release() { helper_release(h); }
+    } release{hp};
+    {
+        GangScope gang(G, gs);
+        FOLD_OK(fold_prep(ht, G, n, hdiag, dead, state, st));
+        FOLD_OK(fold32_attempt(ht, G, n, vec, hdiag, dead, state, lam, tau, ws, L, st, hp, false));
+        FOLD_OK(fold32_make_u(ws, L, U, n, st));
+    }
+    if (dry_run()) {
+        host_sync_record(st);
+        for (int g = 0; g < G; ++g) {
+            host[g] = FoldState{};
+            host[g].base = 1.0;
+        }
+    } else {
+        for (int g = 0; g < G; ++g)
+            GPTQ_HIP(hipMemcpyAsync(&host[g], (const char*)state + g * gs, sizeof(FoldState),
+                                    hipMemcpyDeviceToHost, st));
+        GPTQ_HIP(hipStreamSynchronize(st));
+    }
+    FOLD_OK(check.finish());
+    for (int g = 0; g < G; ++g) {
+        failed[g] = host[g].flag;
+        if (host[g].flag == 0u) fill_report(&reports[g], lam, host[g], 1, false, false);
+    }
+    return GPTQ_OK;
+}
+
+#undef FOLD_OK
 
 }  // namespace gptq

@@ -78,4 +78,15 @@ int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precisio
              float* hdiag, uint8_t* dead, void* workspace, size_t workspace_bytes, hipStream_t st,
              gptq_fold_report* report, bool single);
 
+// A gang of G groups of the same n (common.hpp: their data at the same offsets of slots gs
+// bytes apart; U, hdiag, dead and ws are slot 0's, ws_bytes the workspace of one slot; ht the
+// caller's Hessians).  Runs one f32 attempt at damping lambda for all of them in lockstep on
+// st and its helper streams, and makes U.  A group whose attempt failed (failed[g] != 0, its
+// flag bits) must be folded again on its own (fold_run), which repeats exactly what a call of
+// its own would do; for the others, host[g] and reports[g] are what that call would return.
+// precision: "auto" or "f32".
+int fold_gang(const HTab& ht, int G, int64_t gs, int64_t n, double lambda, int precision,
+              float* U, float* hdiag, uint8_t* dead, char* ws, size_t ws_bytes, hipStream_t st,
+              FoldState* host, unsigned* failed, gptq_fold_report* reports);
+
 }  // namespace gptq

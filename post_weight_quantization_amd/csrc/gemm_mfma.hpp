@@ -56,7 +56,18 @@ struct GemmBatch {
     GemmProblem p[2];
     int nprob;
     int total;            // p[0].ntiles + p[1].ntiles
+    int64_t gs;           // a gang's slot stride in bytes (grid z = group); 0 outside a gang
 };
+
+// The problem of group blockIdx.z of a gang: every matrix and the flag lie in its slot.
+__device__ __forceinline__ GemmProblem gang_problem(const GemmProblem& P0, int64_t gs) {
+    GemmProblem P = P0;
+    P.A = gang_ptr(P.A, gs);
+    P.B = gang_ptr(P.B, gs);
+    P.Cin = gang_ptr(P.Cin, gs);
+    P.Cout = gang_ptr(P.Cout, gs);
+    return P;
+}
 
 // Tile order.  Consecutive tile numbers walk super-tiles of GT_S x GT_S tiles (1024 x 1024
 // elements of C), row by row inside a super-tile, so that the workgroups resident on one XCD at
@@ -111,6 +122,15 @@ __host__ __device__ __forceinline__ void tile_of(const PROB& P, int t, int& tm, 
         tm = R * GT_S + v / w;
         tn = C * GT_S + v % w;
     }
+}
+
+// Workgroup b of group z of a gang (grid z): the hardware deals the workgroups of a launch to
+// the XCDs in launch order, so group z's slice starts at XCD (total z) % 8.  Rotating the
+// slice's numbering by that much keeps xcd_order's ranges on their XCDs; a rotation mod total
+// is a bijection of [0, total) for every z.
+__host__ __device__ __forceinline__ int gang_block(int b, int z, int total) {
+    if (z == 0) return b;
+    return (int)(((int64_t)b + ((int64_t)total * z) % NUM_XCD) % total);
 }
 
 // Bijective renumbering: the hardware sends workgroup b to XCD b % 8; give XCD x the
@@ -572,7 +592,7 @@ template <> struct GemmCfg<2> { static constexpr int nbuf = 1, waves = 2, tile =
 template <int TAG, bool TB0, bool TB1, bool CHK>
 __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(GemmCfg<TAG>::waves, GemmCfg<TAG>::waves)))
 void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
-    if (abort_flag && __atomic_load_n(abort_flag, __ATOMIC_RELAXED)) return;
+    if (abort_flag && __atomic_load_n(gang_ptr(abort_flag, batch.gs), __ATOMIC_RELAXED)) return;
     if constexpr (GemmCfg<TAG>::prio > 0) __builtin_amdgcn_s_setprio(GemmCfg<TAG>::prio);
     constexpr int NBUF = GemmCfg<TAG>::nbuf;
     constexpr int TILE = GemmCfg<TAG>::tile, TILE_N = GemmCfg<TAG>::tile_n;
@@ -582,19 +602,21 @@ void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
     constexpr int LB = TILE == 128 ? NBUF * LDS_TILE : 2 * (TILE_N == 64 ? LDS_TILE64 : LDS_TILE);
     __shared__ __attribute__((aligned(16))) float As[LA];
     __shared__ __attribute__((aligned(16))) float Bs[LB];
-    int t = xcd_order(blockIdx.x, batch.total);
+    int t = xcd_order(gang_block((int)blockIdx.x, (int)blockIdx.z, batch.total), batch.total);
     int tm, tn;
     if (t < batch.p[0].ntiles) {
         tile_of(batch.p[0], t, tm, tn);
         if (batch.p[0].skip_upper && tn > tm) return;
-        if (TILE == 128) gemm_tile<TB0, CHK, NBUF>(batch.p[0], tm, tn, As, Bs);
-        else gemm_tile_small<TB0, CHK, TILE_N>(batch.p[0], tm, tn, As, Bs);
+        const GemmProblem P = gang_problem(batch.p[0], batch.gs);
+        if (TILE == 128) gemm_tile<TB0, CHK, NBUF>(P, tm, tn, As, Bs);
+        else gemm_tile_small<TB0, CHK, TILE_N>(P, tm, tn, As, Bs);
     } else {
         t -= batch.p[0].ntiles;
         tile_of(batch.p[1], t, tm, tn);
         if (batch.p[1].skip_upper && tn > tm) return;
-        if (TILE == 128) gemm_tile<TB1, CHK, NBUF>(batch.p[1], tm, tn, As, Bs);
-        else gemm_tile_small<TB1, CHK, TILE_N>(batch.p[1], tm, tn, As, Bs);
+        const GemmProblem P = gang_problem(batch.p[1], batch.gs);
+        if (TILE == 128) gemm_tile<TB1, CHK, NBUF>(P, tm, tn, As, Bs);
+        else gemm_tile_small<TB1, CHK, TILE_N>(P, tm, tn, As, Bs);
     }
 }
 
@@ -710,7 +732,8 @@ inline int launch_gemm(const char* name, hipStream_t s, const GemmBatch& b0, con
     if (na < 0) return GPTQ_EINVAL;
     const int rc = check_launch(name, s, acc, na);
     if (rc != GPTQ_OK) return rc;
-    if (!dry_run()) gemm_kernel<TAG, TB0, TB1, CHK><<<b.total, G_THREADS, 0, s>>>(b, flag);
+    b.gs = gang_current().gs;
+    if (!dry_run()) gemm_kernel<TAG, TB0, TB1, CHK><<<gang_grid((unsigned)b.total), G_THREADS, 0, s>>>(b, flag);
     return GPTQ_OK;
 }
 

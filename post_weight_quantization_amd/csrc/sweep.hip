@@ -54,7 +54,11 @@ template <bool Q2>
 __global__ __launch_bounds__(256) void ladder_kernel(const float* __restrict__ W,
                                                      const uint8_t* __restrict__ dead, int64_t n,
                                                      float* __restrict__ lost,
-                                                     float* __restrict__ tab) {
+                                                     float* __restrict__ tab, int64_t gs) {
+    W = gang_ptr(W, gs);
+    dead = gang_ptr(dead, gs);
+    lost = gang_ptr(lost, gs);
+    tab = gang_ptr(tab, gs);
     __shared__ float smin[256], smax[256];
     __shared__ double s_lo, s_st;
     __shared__ int s_any;
@@ -510,10 +514,24 @@ __global__ __launch_bounds__(BT) void sweep_block_kernel(
     const float* __restrict__ tab, const float* __restrict__ lost, int64_t rows,
     uint8_t* __restrict__ nib, uint8_t* __restrict__ rung, float* __restrict__ scale,
     float* __restrict__ E, int64_t ldE, const float* __restrict__ sp,
-    uint8_t* __restrict__ codes) {
+    uint8_t* __restrict__ codes, int64_t gs) {
     __builtin_amdgcn_s_setprio(CHAIN_PRIO);
     constexpr int NC = 32 * G;
     constexpr bool ST = MODE == 1 || MODE == 3;
+    src = gang_ptr(src, gs);
+    U = gang_ptr(U, gs);
+    hdiag = gang_ptr(hdiag, gs);
+    dead = gang_ptr(dead, gs);
+    tab = gang_ptr(tab, gs);
+    lost = gang_ptr(lost, gs);
+    nib = gang_ptr(nib, gs);
+    rung = gang_ptr(rung, gs);
+    scale = gang_ptr(scale, gs);
+    E = gang_ptr(E, gs);
+    if constexpr (ST) {
+        sp = gang_ptr(sp, gs);
+        codes = gang_ptr(codes, gs);
+    }
     __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
     __shared__ float hs[SB];
     __shared__ float uinv[SB];
@@ -669,6 +687,19 @@ __global__ __launch_bounds__(256) void static_rung_q2_kernel(const float* __rest
     scale[r * ng + g] = tb[best];
 }
 
+// The ladder of every row (q4tp, or q2tp when Q2), for the gang open on this thread or one
+// matrix.
+static int ladder_launch(bool q2, const float* W, const uint8_t* dead, int64_t rows, int64_t n,
+                         float* lost, float* tab, hipStream_t st) {
+    const int64_t gs = gang_current().gs;
+    ProfScope ps(FAM_LADDER, st, 0.0, 4.0 * (double)rows * n);
+    GPTQ_LAUNCH(st, q2 ? "ladder_q2" : "ladder",
+                (q2 ? ladder_kernel<true><<<gang_grid((unsigned)rows), 256, 0, st>>>(W, dead, n, lost, tab, gs)
+                    : ladder_kernel<false><<<gang_grid((unsigned)rows), 256, 0, st>>>(W, dead, n, lost, tab, gs)),
+                rd(W, n, rows, n), rd(dead, n, 1, n, 1), wr(lost, 2, rows, 2), wr(tab, 32, rows, 32));
+    return launch_status() != GPTQ_OK ? GPTQ_EHIP : GPTQ_OK;
+}
+
 }  // namespace gptq
 
 using namespace gptq;
@@ -682,14 +713,8 @@ extern "C" int gptq_ladder(const float* W, const uint8_t* dead, int64_t rows, in
     check_buffer(dead, (size_t)n, "dead");
     check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
     check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
-    hipStream_t st = (hipStream_t)stream;
-    {
-        ProfScope ps(FAM_LADDER, st, 0.0, 4.0 * (double)rows * n);
-        GPTQ_LAUNCH(st, "ladder", (ladder_kernel<false><<<(unsigned)rows, 256, 0, st>>>(W, dead, n, lost, tab)),
-                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), wr(lost, 2, rows, 2),
-                    wr(tab, 32, rows, 32));
-    }
-    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    const int rc = ladder_launch(false, W, dead, rows, n, lost, tab, (hipStream_t)stream);
+    if (rc != GPTQ_OK) return rc;
     return check.finish();
 }
 
@@ -714,8 +739,9 @@ static void launch_block(unsigned nwg, hipStream_t st, const float* src, int64_t
                          const float* U, const float* hdiag, const uint8_t* dead, const float* tab,
                          const float* lost, int64_t rows, uint8_t* nib, uint8_t* rung, float* scale,
                          float* E, int64_t ldE, const float* sp, uint8_t* codes) {
-    sweep_block_kernel<G, MODE><<<nwg, BT, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost, rows,
-                                                   nib, rung, scale, E, ldE, sp, codes);
+    sweep_block_kernel<G, MODE><<<gang_grid(nwg), BT, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost,
+                                                              rows, nib, rung, scale, E, ldE, sp,
+                                                              codes, gang_current().gs);
 }
 
 // One sweep over the columns in their storage order (the channel order for the plain sweep,
@@ -958,6 +984,54 @@ int sweep_run(const float* W, const float* U, const float* hdiag, const uint8_t*
 
 }  // namespace gptq
 
+namespace gptq {
+
+size_t sweep_panel_bytes(int64_t rows) { return align256(sizeof(float) * (size_t)(rows * SOB)); }
+
+int sweep_gang(int G, int64_t gs, bool q2, float* Wc, const float* U, const float* hdiag,
+               const uint8_t* dead, float* lost, float* tab, int64_t rows, int64_t n, uint8_t* nib,
+               uint8_t* rung, float* scale, float* pan0, float* pan1, hipStream_t st) {
+    if (G < 1 || G > kMaxGang || gs % 256 != 0) return GPTQ_EINVAL;
+    if (!sweep_args_ok(Wc, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, nullptr) ||
+        !al16(pan0) || !al16(pan1))
+        return GPTQ_EINVAL;
+    CheckScope check;
+    const size_t pb = sweep_panel_bytes(rows);
+    for (int g = 0; g < G; ++g) {
+        const int64_t o = g * gs;
+        check_buffer((const char*)Wc + o, sizeof(float) * (size_t)(rows * n), "Wc");
+        check_buffer((const char*)U + o, sizeof(float) * (size_t)(n * n), "U");
+        check_buffer((const char*)hdiag + o, sizeof(float) * (size_t)n, "hdiag");
+        check_buffer((const char*)dead + o, (size_t)n, "dead");
+        check_buffer((const char*)lost + o, sizeof(float) * (size_t)(rows * 2), "lost");
+        check_buffer((const char*)tab + o, sizeof(float) * (size_t)(rows * 32), "tab");
+        check_buffer((const char*)nib + o, (size_t)(rows * (n / (q2 ? 4 : 2))), "codes");
+        check_buffer((const char*)rung + o, (size_t)(rows * (n / 32)), "rung");
+        check_buffer((const char*)scale + o, sizeof(float) * (size_t)(rows * (n / 32)), "scale");
+        check_buffer((const char*)pan0 + o, pb, "panel 0");
+        check_buffer((const char*)pan1 + o, pb, "panel 1");
+    }
+    {
+        GangScope gang(G, gs);
+        int rc = ladder_launch(q2, Wc, dead, rows, n, lost, tab, st);
+        if (rc != GPTQ_OK) return rc;
+        // In place: the working copy is the matrix itself (the same results as a separate copy,
+        // bit for bit).
+        SweepRun c = q4_run(Wc, Wc, U, hdiag, dead, tab, lost, rows, n, nib, rung, scale, nullptr,
+                            pan0, pan1);
+        if (q2) {
+            c.lost = nullptr;
+            rc = sweep_pipeline<2>(c, st);
+        } else {
+            rc = sweep_pipeline<0>(c, st);
+        }
+        if (rc != GPTQ_OK) return rc;
+    }
+    return check.finish();
+}
+
+}  // namespace gptq
+
 extern "C" int gptq_sweep(const float* W, const float* U, const float* hdiag, const uint8_t* dead,
                           const float* tab, const float* lost, int64_t rows, int64_t n,
                           uint8_t* nib, uint8_t* rung, float* scale, float* E, void* workspace,
@@ -1063,14 +1137,8 @@ extern "C" int gptq_ladder_q2(const float* W, const uint8_t* dead, int64_t rows,
     check_buffer(dead, (size_t)n, "dead");
     check_buffer(lost, sizeof(float) * (size_t)(rows * 2), "lost");
     check_buffer(tab, sizeof(float) * (size_t)(rows * 32), "tab");
-    hipStream_t st = (hipStream_t)stream;
-    {
-        ProfScope ps(FAM_LADDER, st, 0.0, 4.0 * (double)rows * n);
-        GPTQ_LAUNCH(st, "ladder_q2", (ladder_kernel<true><<<(unsigned)rows, 256, 0, st>>>(W, dead, n, lost, tab)),
-                    rd(W, n, rows, n), rd(dead, n, 1, n, 1), wr(lost, 2, rows, 2),
-                    wr(tab, 32, rows, 32));
-    }
-    if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
+    const int rc = ladder_launch(true, W, dead, rows, n, lost, tab, (hipStream_t)stream);
+    if (rc != GPTQ_OK) return rc;
     return check.finish();
 }
 

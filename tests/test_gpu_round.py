@@ -44,10 +44,11 @@ def assert_same(gpu, groups, results, label):
                 assert torch.equal(x, y), f"{label}: group {i} member {k}: {what} differs"
 
 
-@pytest.mark.parametrize("conc", [0, 1, 11])
+@pytest.mark.parametrize("conc", [0, 1, 4, 11])
 def test_batched_round_equals_separate_calls(gpu, conc):
-    """The batched round of 11 attention-shaped groups (n 4096, W 4096 x 4096, distinct seeds)
-    at the default concurrency, serially and all at once."""
+    """The batched round of 11 attention-shaped groups (n 4096, W 4096 x 4096, distinct seeds):
+    one gang of 11 (the default, and a cap of 11), gangs of 4, 4 and 3, and one group at a time
+    on one slot."""
     groups = []
     for k in range(11):
         H, W, lam = workloads.make("batch", k=k, device="cuda")
@@ -150,3 +151,62 @@ def test_round_group_against_the_oracle(gpu):
     t_gpu = output_error(Wn, free["dead"], codes.cpu().numpy(), scale.cpu().numpy(), Hn)
     say(f"round group 2: output error rel {(t_gpu - t_orc) / t_orc:+.2e}")
     assert abs(t_gpu - t_orc) <= OUT_ERR_TOL * t_orc
+
+
+def _full_rank(rng, n, t):
+    X = rng.standard_normal((n, t))
+    return torch.as_tensor((X @ X.T).astype(np.float32)).cuda()
+
+
+def test_gang_with_failing_and_degenerate_groups(gpu):
+    """A gang of five n = 1184 groups at lambda 1e-5: two rank-deficient Hessians (their f32
+    attempt meets the pivot floor: folded again on their own, in f64), two full-rank ones (f32)
+    and one that no damping makes positive definite (GPTQ_DEGENERATE, U = I); ragged members of
+    77 rows.  Every status, report and output equals the separate calls'."""
+    rng = np.random.default_rng(11)
+    n = 1184
+    Hdeg = torch.full((n, n), -0.9, device="cuda")
+    Hdeg.fill_diagonal_(1.0)
+    Hs = [_rank_deficient(rng, n, 500), _full_rank(rng, n, 5000), _rank_deficient(rng, n, 700),
+          Hdeg, _full_rank(rng, n, 6000)]
+    groups = [{"H": H, "lam": 1e-5, "members": [(torch.randn(77, n, device="cuda") * 0.02).contiguous()]}
+              for H in Hs]
+    torch.cuda.synchronize()
+    r = gpu.Round(groups)
+    assert r.plan()[1] == 5
+    st = r.run()
+    torch.cuda.synchronize()
+    res = r.results
+    assert st == gpu.GPTQ_OK, [x["status"] for x in res]
+    precisions = [x["report"]["precision"] for x in res]
+    say(f"gang of 5: statuses {[x['status'] for x in res]}, precisions {precisions}")
+    assert precisions[0] == 64 and precisions[2] == 64 and precisions[1] == 32 and precisions[4] == 32
+    assert res[3]["status"] == gpu.GPTQ_DEGENERATE
+    assert_same(gpu, groups, res, "gang with failing groups")
+
+
+def test_gang_of_mixed_layouts_and_codecs_on_a_side_stream(gpu):
+    """A gang of three n = 640 groups whose Hessians come packed, dense and row-padded, each
+    with two members (96 rows q4tp, 33 rows q2tp), on a stream that is not the current one; a
+    second run of the same round gives the same results."""
+    rng = np.random.default_rng(5)
+    n = 640
+    H0 = _full_rank(rng, n, 2000)
+    H1 = _full_rank(rng, n, 3000)
+    Hp = torch.zeros(n, 700, device="cuda")
+    Hp[:, :n] = _full_rank(rng, n, 2500)
+    Hp = Hp[:, :n]  # rows 700 floats apart
+    groups = []
+    for H in (pack_upper(H0), H1, Hp):
+        W = (torch.randn(96, n, device="cuda") * 0.02).contiguous()
+        W2 = (torch.randn(33, n, device="cuda") * 0.02).contiguous()
+        groups.append({"H": H, "lam": 0.01, "members": [W, (W2, "q2tp")]})
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    r = gpu.Round(groups, stream=side)
+    assert r.plan()[1] == 3
+    for rep in range(2):
+        st = r.run(stream=side)
+        side.synchronize()
+        assert st == gpu.GPTQ_OK, [x["status"] for x in r.results]
+        assert_same(gpu, groups, r.results, f"mixed gang run {rep}")

@@ -82,7 +82,22 @@ def test_widest_first_order(lib):
     st, order, c = plan(lib, arr, 1 << 50, 0)
     assert st == pwq.GPTQ_OK
     assert order == [1, 4, 3, 2, 0, 5]  # n, then member rows, then index
-    assert c == 4  # the library's default
+    assert c == 2  # gangs: groups 1 and 4, groups 0 and 5 (2 has another member)
+
+
+def test_gangs_and_threads(lib):
+    """Consecutive groups of the plan's order with the same shape (n, precision, damping,
+    members' rows and codecs; not f64) form gangs of at most the cap (16 by default), which use
+    one slot each; a round without a gang of two runs on threads, 4 at a time by default."""
+    arr, keep = array([(n, (64,)) for n in (256, 512, 768, 1024, 1280, 1536)])
+    assert plan(lib, arr, 1 << 50, 0)[2] == 4
+    assert plan(lib, arr, 1 << 50, 6)[2] == 6
+    arr, keep = array([(512, (64,))] * 20)
+    assert plan(lib, arr, 1 << 50, 0)[2] == 16
+    assert plan(lib, arr, 1 << 50, 7)[2] == 7
+    arr, keep = array([(512, (64,)), (512, (64,), {"lam": 1e-3}), (512, (64,), {"codec": "q2tp"}),
+                       (512, (64,), {"precision": "f64"}), (512, (64,), {"precision": "f64"})])
+    assert plan(lib, arr, 1 << 50, 0)[2] == 4  # no two of them alike (f64 groups never gang)
 
 
 def test_concurrency_is_capped_by_the_workspace(lib):
@@ -93,15 +108,17 @@ def test_concurrency_is_capped_by_the_workspace(lib):
     assert plan(lib, arr, slot - 1, 0)[0] == pwq.GPTQ_EWORKSPACE
     assert plan(lib, arr, slot, 0)[2] == 1
     assert plan(lib, arr, 3 * slot + slot // 2, 0)[2] == 3
-    assert plan(lib, arr, 100 * slot, 0)[2] == 4
+    assert plan(lib, arr, 100 * slot, 0)[2] == 11  # one gang
     assert plan(lib, arr, 100 * slot, 16)[2] == 11
     assert plan(lib, arr, 100 * slot, 2)[2] == 2
 
 
 @pytest.mark.parametrize("precision", ["auto", "f32", "f64"])
 def test_slot_size_from_the_call_workspaces(lib, precision):
-    """A slot is U, hdiag and dead plus the larger of the fold's and the sweeps' workspaces
-    (they share it), each part 256-byte aligned; the maximum over the groups."""
+    """A slot is U, hdiag and dead plus the larger of the fold's workspace and a member's area
+    (they share it), each part 256-byte aligned; the maximum over the groups.  A member's area
+    is the sweep's workspace (working copy, two residual panels of 512 columns) followed by its
+    outputs (lo / step, TAB, codes, rungs, scales), where a gang stages them."""
     specs = [(4096, (4096, 8192), {"precision": precision}), (1000, (), {"precision": precision}),
              (96, (40000,), {"precision": precision})]
     arr, keep = array(specs)
@@ -109,7 +126,11 @@ def test_slot_size_from_the_call_workspaces(lib, precision):
     for n, rows, _ in specs:
         work = lib.gptq_fold_workspace_size_ex(n, pwq.FOLD_PRECISION[precision])
         for r in rows:
-            work = max(work, lib.gptq_sweep_workspace_size(r, n))
+            sweep = lib.gptq_sweep_workspace_size(r, n)
+            assert sweep == a256(4 * r * n) + 2 * a256(4 * r * 512)
+            outputs = (a256(4 * r * 2) + a256(4 * r * 32) + a256(r * n // 2) + a256(r * n // 32)
+                       + a256(4 * r * n // 32))
+            work = max(work, sweep + outputs)
         sizes.append(a256(4 * n * n) + a256(4 * n) + a256(n) + a256(work))
     assert lib.gptq_round_slot_size(arr, 3) == max(sizes)
     assert lib.gptq_round_slot_size(arr, 0) == 0
@@ -150,6 +171,11 @@ def test_packed_and_group_without_members(lib):
 
 @pytest.mark.parametrize("specs,conc", [
     ([(4096, (4096,))] * 11, 4),
+    ([(4096, (4096,))] * 11, 11),
+    ([(4096, (4096,))] * 11, 16),
+    ([(1184, (77, 300), {"lam": 1e-5})] * 3 + [(1184, (77, 300), {"lam": 1e-5, "codec": "q2tp"})] * 2, 5),
+    ([(640, (96,), {"ldh": pwq.GPTQ_PACKED_UPPER}), (640, (96,)), (640, (96,), {"ldh": 700}),
+      (2048, (512,), {"precision": "f32"}), (2048, (512,), {"precision": "f32"}), (256, (33,))], 4),
     ([(17408, (5120,)), (4096, (4096, 1024), {"codec": "q2tp"}), (8192, (2048,), {"precision": "f64"}),
       (5120, (512,), {"ldh": pwq.GPTQ_PACKED_UPPER}), (96, ())], 3),
     ([(256, (512,))] * 5, 1),
