@@ -482,8 +482,8 @@ def main():
         result["detail"]["fold_packed_ms"] = e0.elapsed_time(e1) / 2
         del Hpk
     # Concurrent groups (the batched round): G independent groups through the library's round
-    # (gptq_round: widest first, one host thread and stream per slot, the default concurrency),
-    # outputs and workspace allocated once; groups/s over whole rounds.
+    # (gptq_round's default plan: groups of one shape run as one gang, in lockstep), outputs and
+    # workspace allocated once; groups/s over whole rounds.
     def concurrent_round(name, G, rounds):
         groups_ = []
         for kk in range(G):

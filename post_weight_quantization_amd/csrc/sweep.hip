@@ -161,9 +161,11 @@ __device__ __forceinline__ int nominal_rung_fast(float amax, float lo, float st)
 // no LDS round trip).  C is the DPP control: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
 // row_mirror = 0x140, row_half_mirror = 0x141, row_newbcast:L = 0x150 + L (lane L of each row
 // to the whole row).
+// Every control used here writes all lanes, so the move has no old value to keep (no register
+// to clear first).
 template <int C>
 __device__ __forceinline__ float dpp_mov(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), C, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), C, 0xf, 0xf, false));
 }
 // Lane L of each 16-lane row group, broadcast to the whole group; L folds to a constant once
 // the column loop is unrolled.
@@ -422,7 +424,9 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
     }
     }
     const double inv_s64 = (s > 0.0f) ? 1.0 / (double)s : 0.0;  // RN64(1 / s) for quot_f32
-    uint32_t byte = 0u;
+    // The codes of this lane's two columns, kept as the owner computes them (a select per column;
+    // they are packed once the group is done).
+    float qo[2] = {0.0f, 0.0f};
     // This lane's entries of row j of U (own group and later groups) and 1 / U_jj are read one
     // column step ahead, so the serial chain -- broadcast, code, residual, the owner's next
     // column -- never waits on LDS; a scheduling barrier closes each step (otherwise the reads
@@ -467,31 +471,39 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         // only the later ones; the owner's column j then takes the residual.
         w[g][0] -= e * uo.x;
         w[g][1] -= e * uo.y;
-        if (k == owner) {
-            if constexpr (ST) byte |= ((uint32_t)((int)q + (Q2 ? 0 : 8)) & 255u) << (8 * slot);
-            else if constexpr (Q2) byte |= ((uint32_t)(int)q & 3u) << (2 * slot);
-            else byte |= ((uint32_t)((int)q + 8) & 15u) << (4 * slot);
-            w[g][slot] = e;
-        }
+        const bool mine = k == owner;
+        qo[slot] = mine ? q : qo[slot];
+        w[g][slot] = mine ? e : w[g][slot];
         // ... and all of its columns of the later groups of the block.
 #pragma unroll
         for (int g2 = g + 1; g2 < G; ++g2) {
             w[g2][0] -= e * ul[g2].x;
             w[g2][1] -= e * ul[g2].y;
         }
+        // Pinned in this step: with no branch left in the step, the compiler would otherwise
+        // sink the later groups' updates and the selects to their first use and hold every
+        // step's residual, U entries and code in registers until then.
+        asm volatile("" : "+v"(qo[slot]));
+#pragma unroll
+        for (int g2 = g + 1; g2 < G; ++g2) asm volatile("" : "+v"(w[g2][0]), "+v"(w[g2][1]));
         uo = uo_n;
         ui = ui_n;
 #pragma unroll
         for (int g2 = g + 1; g2 < G; ++g2) ul[g2] = ul_n[g2];
         __builtin_amdgcn_sched_barrier(0);
     }
+    const int q0 = (int)qo[0], q1 = (int)qo[1];
+    uint32_t byte;
     if constexpr (ST) {
+        byte = ((uint32_t)(q0 + (Q2 ? 0 : 8)) & 255u) | (((uint32_t)(q1 + (Q2 ? 0 : 8)) & 255u) << 8);
         *reinterpret_cast<uint16_t*>(cx.codes + 32 * g + 2 * k) = (uint16_t)byte;
     } else if constexpr (Q2) {
+        byte = ((uint32_t)q0 & 3u) | (((uint32_t)q1 & 3u) << 2);
         // Lanes 2m and 2m+1 hold columns 4m .. 4m+3: the even lane writes their byte.
         const uint32_t nb = (uint32_t)__float_as_int(dpp_mov<0xB1>(__int_as_float((int)byte)));
         if ((k & 1) == 0) nib[r * (n / 4) + (c0 + 32 * g) / 4 + k / 2] = (uint8_t)(byte | (nb << 4));
     } else {
+        byte = ((uint32_t)(q0 + 8) & 15u) | (((uint32_t)(q1 + 8) & 15u) << 4);
         nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
     }
     *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
