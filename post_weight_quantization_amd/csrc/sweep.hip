@@ -334,7 +334,7 @@ constexpr int BT = 16 * RPW;     // its threads
 constexpr int ULD = SB + 4;      // LDS row stride of the block's U
 
 struct BlockCtx {
-    const float* Us;     // U[c0 + j][c0 + t] in LDS, row stride ULD
+    float* Us;           // U[c0 + j][c0 + t] in LDS, row stride ULD (SLIM: one group's rows)
     const float* uinv;   // 1 / U_jj (0 where U_jj <= 0), LDS
     const float* hs;     // H_ii of the block's columns, LDS
     const float* tb;     // the row's 32 rung scales
@@ -343,7 +343,24 @@ struct BlockCtx {
     uint8_t* codes;      // static groups: this row's codes (one byte each) from column c0
     float lo, st;
     int k;
+    bool live;           // the row exists (SLIM: every thread runs the groups, for the barriers)
+    const float* Ug;     // U in global memory (SLIM restages it group by group)
+    int nc;              // the block's columns
 };
+
+// Rows [j0, j0 + 32) of the block's U (columns 0 .. nc - 1 of the block) into Us rows 0 .. 31,
+// entries below the diagonal set to 0.
+__device__ __forceinline__ void stage_u_rows(float* Us, const float* U, int64_t n, int64_t c0,
+                                             int j0, int nc, int tid) {
+    const int q4 = nc / 4;
+    for (int e = tid; e < 32 * q4; e += BT) {
+        const int j = e / q4, t4 = (e % q4) * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(U + (c0 + j0 + j) * n + c0 + t4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (t4 + q < j0 + j) ? 0.0f : v[q];
+        *reinterpret_cast<f32x4*>(&Us[j * ULD + t4]) = v;
+    }
+}
 
 // Group g of the block, with every register index a compile-time constant (the groups are
 // unrolled by template recursion).
@@ -353,13 +370,21 @@ struct BlockCtx {
 // all-zero group), 2-bit levels (q - 1.5) s, codes packed four to a byte.  MODE 3: static groups
 // with 2-bit levels (q2tp act order): the scales of MODE 1, the levels of MODE 2, the level q
 // (0..3) to cx.codes.
-template <int G, int g, int MODE>
+// SLIM: LDS holds only this group's 32 rows of U, restaged between groups behind barriers (a
+// quarter of the LDS, so that four workgroups share a CU instead of two: for launches of many
+// workgroups, as a gang's are); every thread then runs the groups, and only live rows store.
+template <int G, int g, int MODE, bool SLIM>
 __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx, int64_t r,
                                             int64_t n, int64_t c0, uint8_t* __restrict__ nib,
                                             uint8_t* __restrict__ rung, float* __restrict__ scale,
                                             float* __restrict__ E, int64_t ldE) {
     constexpr bool ST = MODE == 1 || MODE == 3, Q2 = MODE == 2 || MODE == 3;
     const int k = cx.k;
+    if constexpr (SLIM) {
+        __syncthreads();  // every wave is done with the previous group's rows
+        stage_u_rows(cx.Us, cx.Ug, n, c0, 32 * g, cx.nc, (int)threadIdx.x);
+        __syncthreads();
+    }
     float s = 0.0f, inv_s = 0.0f;
     float s_own[2] = {0.0f, 0.0f};
     double inv_own64[2] = {0.0, 0.0};
@@ -384,7 +409,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         }
         s = cx.tb[best];
         inv_s = cx.ti[best];
-        if (k == 0) {
+        if (k == 0 && cx.live) {
             const int64_t gi = r * (n / 32) + (c0 / 32) + g;
             rung[gi] = (uint8_t)best;
             scale[gi] = s;
@@ -417,7 +442,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
     }
     s = cx.tb[best];
     inv_s = cx.ti[best];
-    if (k == 0) {
+    if (k == 0 && cx.live) {
         const int64_t gi = r * (n / 32) + (c0 / 32) + g;
         rung[gi] = (uint8_t)best;
         scale[gi] = s;
@@ -435,10 +460,11 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
     float ui;
     auto load_u = [&](int col, float2& o, float2 (&l)[G], float& iv) {
         iv = cx.uinv[col];
-        o = *reinterpret_cast<const float2*>(&cx.Us[col * ULD + 32 * g + 2 * k]);
+        const int row = SLIM ? col - 32 * g : col;
+        o = *reinterpret_cast<const float2*>(&cx.Us[row * ULD + 32 * g + 2 * k]);
 #pragma unroll
         for (int g2 = g + 1; g2 < G; ++g2)
-            l[g2] = *reinterpret_cast<const float2*>(&cx.Us[col * ULD + 32 * g2 + 2 * k]);
+            l[g2] = *reinterpret_cast<const float2*>(&cx.Us[row * ULD + 32 * g2 + 2 * k]);
     };
     load_u(32 * g, uo, ul, ui);
 #pragma unroll
@@ -496,18 +522,18 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
     uint32_t byte;
     if constexpr (ST) {
         byte = ((uint32_t)(q0 + (Q2 ? 0 : 8)) & 255u) | (((uint32_t)(q1 + (Q2 ? 0 : 8)) & 255u) << 8);
-        *reinterpret_cast<uint16_t*>(cx.codes + 32 * g + 2 * k) = (uint16_t)byte;
+        if (cx.live) *reinterpret_cast<uint16_t*>(cx.codes + 32 * g + 2 * k) = (uint16_t)byte;
     } else if constexpr (Q2) {
         byte = ((uint32_t)q0 & 3u) | (((uint32_t)q1 & 3u) << 2);
         // Lanes 2m and 2m+1 hold columns 4m .. 4m+3: the even lane writes their byte.
         const uint32_t nb = (uint32_t)__float_as_int(dpp_mov<0xB1>(__int_as_float((int)byte)));
-        if ((k & 1) == 0) nib[r * (n / 4) + (c0 + 32 * g) / 4 + k / 2] = (uint8_t)(byte | (nb << 4));
+        if ((k & 1) == 0 && cx.live) nib[r * (n / 4) + (c0 + 32 * g) / 4 + k / 2] = (uint8_t)(byte | (nb << 4));
     } else {
         byte = ((uint32_t)(q0 + 8) & 15u) | (((uint32_t)(q1 + 8) & 15u) << 4);
-        nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
+        if (cx.live) nib[r * (n / 2) + (c0 + 32 * g) / 2 + k] = (uint8_t)byte;
     }
-    *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
-    if constexpr (g + 1 < G) block_group<G, g + 1, MODE>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
+    if (cx.live) *reinterpret_cast<float2*>(E + r * ldE + 32 * g + 2 * k) = make_float2(w[g][0], w[g][1]);
+    if constexpr (g + 1 < G) block_group<G, g + 1, MODE, SLIM>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
 }
 
 // One block of up to 4 groups for RPW rows per workgroup, 16 lanes per row.  RPW = 32 (512
@@ -519,7 +545,7 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
 // then the group's 32 columns in order: the column's corrected value is broadcast from its
 // owner, every lane of the row computes the same code and residual, and each lane feeds the
 // residual into its own later columns of the block through row j of U (held in LDS).
-template <int G, int MODE>
+template <int G, int MODE, bool SLIM>
 __global__ __launch_bounds__(BT) void sweep_block_kernel(
     const float* __restrict__ src, int64_t n, int64_t c0, const float* __restrict__ U,
     const float* __restrict__ hdiag, const uint8_t* __restrict__ dead,
@@ -544,21 +570,17 @@ __global__ __launch_bounds__(BT) void sweep_block_kernel(
         sp = gang_ptr(sp, gs);
         codes = gang_ptr(codes, gs);
     }
-    __shared__ __attribute__((aligned(16))) float Us[SB * ULD];
+    __shared__ __attribute__((aligned(16))) float Us[(SLIM ? 32 : SB) * ULD];
     __shared__ float hs[SB];
     __shared__ float uinv[SB];
     __shared__ float tabs[RPW * 32];
     __shared__ float tinv[RPW * 32];
     const int tid = threadIdx.x;
     // The block's U with its entries below the diagonal set to 0 (only the upper triangle of U
-    // is read): the feedback of column j then runs unconditionally over every column.
-    for (int e = tid; e < NC * (NC / 4); e += BT) {
-        const int j = e / (NC / 4), t4 = (e % (NC / 4)) * 4;
-        f32x4 v = *reinterpret_cast<const f32x4*>(U + (c0 + j) * n + c0 + t4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = (t4 + q < j) ? 0.0f : v[q];
-        *reinterpret_cast<f32x4*>(&Us[j * ULD + t4]) = v;
-    }
+    // is read): the feedback of column j then runs unconditionally over every column.  SLIM
+    // stages one group's rows at a time, in the groups.
+    if constexpr (!SLIM)
+        for (int j0 = 0; j0 < NC; j0 += 32) stage_u_rows(Us + j0 * ULD, U, n, c0, j0, NC, tid);
     if (tid < NC) {
         // q4tp weighs by H_ii, q2tp by max(H_ii, 0); static groups do not search.
         hs[tid] = ST ? 1.0f : (MODE == 2 ? fmaxf(hdiag[c0 + tid], 0.0f) : hdiag[c0 + tid]);
@@ -575,14 +597,16 @@ __global__ __launch_bounds__(BT) void sweep_block_kernel(
     }
     __syncthreads();
     const int k = tid & 15;
-    const int64_t r = r0 + (tid >> 4);
-    if (r >= rows) return;
+    const bool live = r0 + (tid >> 4) < rows;
+    if (!SLIM && !live) return;
+    // A row that does not exist (SLIM only) runs as row r0 with zero weights, storing nothing.
+    const int64_t r = live ? r0 + (tid >> 4) : r0;
 
     float w[G][2];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const int64_t c = c0 + 32 * g + 2 * k;
-        const float2 v = *reinterpret_cast<const float2*>(src + r * n + c);
+        const float2 v = live ? *reinterpret_cast<const float2*>(src + r * n + c) : make_float2(0.0f, 0.0f);
         // Static groups sweep a gathered, already dead-zeroed copy.
         w[g][0] = (!ST && dead[c]) ? 0.0f : v.x;
         w[g][1] = (!ST && dead[c + 1]) ? 0.0f : v.y;
@@ -598,7 +622,10 @@ __global__ __launch_bounds__(BT) void sweep_block_kernel(
     cx.k = k;
     cx.sp = ST ? sp + r * n + c0 : nullptr;
     cx.codes = ST ? codes + r * n + c0 : nullptr;
-    block_group<G, 0, MODE>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
+    cx.live = live;
+    cx.Ug = U;
+    cx.nc = NC;
+    block_group<G, 0, MODE, SLIM>(w, cx, r, n, c0, nib, rung, scale, E, ldE);
 }
 
 // Static groups, step 1: the rung of every (row, group) chosen up front from the dead-zeroed
@@ -746,14 +773,22 @@ extern "C" size_t gptq_sweep_workspace_size(int64_t rows, int64_t n) {
     return sweep_ws(rows, n, nullptr);
 }
 
+// A gang's launch (many workgroups) takes the SLIM form; q4tp and q2tp only.
 template <int G, int MODE>
 static void launch_block(unsigned nwg, hipStream_t st, const float* src, int64_t n, int64_t c0,
                          const float* U, const float* hdiag, const uint8_t* dead, const float* tab,
                          const float* lost, int64_t rows, uint8_t* nib, uint8_t* rung, float* scale,
                          float* E, int64_t ldE, const float* sp, uint8_t* codes) {
-    sweep_block_kernel<G, MODE><<<gang_grid(nwg), BT, 0, st>>>(src, n, c0, U, hdiag, dead, tab, lost,
-                                                              rows, nib, rung, scale, E, ldE, sp,
-                                                              codes, gang_current().gs);
+    const Gang gg = gang_current();
+    if constexpr (MODE == 0 || MODE == 2) {
+        if (gg.G > 1) {
+            sweep_block_kernel<G, MODE, true><<<gang_grid(nwg), BT, 0, st>>>(
+                src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, E, ldE, sp, codes, gg.gs);
+            return;
+        }
+    }
+    sweep_block_kernel<G, MODE, false><<<gang_grid(nwg), BT, 0, st>>>(
+        src, n, c0, U, hdiag, dead, tab, lost, rows, nib, rung, scale, E, ldE, sp, codes, gg.gs);
 }
 
 // One sweep over the columns in their storage order (the channel order for the plain sweep,
