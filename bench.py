@@ -264,6 +264,29 @@ def all_configs(pwq, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def round_only(pwq, torch, dev, steps, warmup):
+    """The batched round of 11 groups of the attention shape (n 4096, W 4096 x 4096, distinct
+    seeds) through gptq_round with its default plan; groups/s over the timed rounds."""
+    import workloads
+    groups = [workloads.make("batch", k=k, device=dev) for k in range(11)]
+    rnd = pwq.Round([{"H": H, "lam": lam, "members": [W]} for H, W, lam in groups])
+    torch.cuda.synchronize()
+    for i in range(max(warmup, 1)):
+        st = rnd.run()
+        torch.cuda.synchronize()
+        if st != pwq.GPTQ_OK:
+            raise pwq.GptqError(st, "gptq_round")
+        log(f"warmup round {i + 1} done")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        rnd.run()
+        torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"workload": "batch: 11 groups, n=4096, W[4096,4096] f32", "rounds": steps,
+                      "ms_per_round": dt * 1e3, "groups_per_s": 11 / dt,
+                      "slots": rnd.plan()[1]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +304,10 @@ def main():
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the benchmark line: one record per configuration of the "
                          "method (GPU times, damping, parity, oracle times)")
+    ap.add_argument("--round-only", action="store_true",
+                    help="instead of the benchmark line: time only the batched round of 11 "
+                         "attention-shaped groups (gptq_round, its default plan) and print one "
+                         "record")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (a known-size reference for "
                          "hardware traffic counters)")
@@ -302,6 +329,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.all_configs:
         all_configs(pwq, torch, dev)
+        return
+    if args.round_only:
+        round_only(pwq, torch, dev, args.steps, args.warmup)
         return
     spec = workloads.SPECS[args.workload]
     n, rows = spec.n, spec.rows
