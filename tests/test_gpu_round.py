@@ -210,3 +210,20 @@ def test_gang_of_mixed_layouts_and_codecs_on_a_side_stream(gpu):
         side.synchronize()
         assert st == gpu.GPTQ_OK, [x["status"] for x in r.results]
         assert_same(gpu, groups, r.results, f"mixed gang run {rep}")
+
+
+def test_gangs_of_sixteen_at_a_ragged_width(gpu):
+    """20 groups of the tiny workload's recipe (outliers, dead channels) at n = 288, which pads
+    to 384 inside the fold, with 100-row members: gangs of 16 and 4, every result equal to the
+    separate calls'."""
+    groups = []
+    for k in range(20):
+        H, W, lam = workloads.make("tiny", k=k, device="cuda", n=288, rows=100)
+        groups.append({"H": H, "lam": lam, "members": [W]})
+    torch.cuda.synchronize()
+    r = gpu.Round(groups, max_concurrency=16)
+    assert r.plan()[1] == 16
+    st = r.run()
+    torch.cuda.synchronize()
+    assert st == gpu.GPTQ_OK, [x["status"] for x in r.results]
+    assert_same(gpu, groups, r.results, "gangs of 16 and 4")

@@ -197,3 +197,16 @@ def test_round_schedule_in_check_mode(lib, specs, conc):
     with pwq.check_mode():
         assert lib.gptq_round(arr, len(arr), ctypes.c_void_p(BASE + 16), slot * conc, 0,
                               None) == pwq.GPTQ_EINVAL
+
+
+def test_gang_schedule_without_hdiag_or_dead_outputs(lib):
+    """A gang whose groups give no hdiag or dead buffers (optional outputs): their copies out of
+    the slots are skipped, and the schedule checks."""
+    arr, keep = array([(512, (64,))] * 5)
+    for k in (1, 3):
+        arr[k].hdiag = None
+        arr[k].dead = None
+    slot = lib.gptq_round_slot_size(arr, len(arr))
+    with pwq.check_mode():
+        st = lib.gptq_round(arr, len(arr), ctypes.c_void_p(BASE), slot * 5, 0, None)
+    assert st == pwq.GPTQ_OK, pwq.check_message()
