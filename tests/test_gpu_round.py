@@ -227,3 +227,40 @@ def test_gangs_of_sixteen_at_a_ragged_width(gpu):
     torch.cuda.synchronize()
     assert st == gpu.GPTQ_OK, [x["status"] for x in r.results]
     assert_same(gpu, groups, r.results, "gangs of 16 and 4")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_gangs(gpu, seed):
+    """Seeded random rounds of one shape (so one gang, or gangs of the cap): 2..12 groups, n a
+    multiple of 32 in 64..1216, 1..3 members of random rows and codecs, lambda in {1e-6, 1e-4,
+    1e-2}, "auto" or "f32", Hessians full rank or rank-deficient, dense, row-padded or packed.
+    Every status, report and output equals the separate calls'."""
+    rng = np.random.default_rng(1000 + seed)
+    G = int(rng.integers(2, 13))
+    n = 32 * int(rng.integers(2, 39))
+    lam = float(rng.choice([1e-6, 1e-4, 1e-2]))
+    precision = str(rng.choice(["auto", "f32"]))
+    members = [(int(rng.integers(1, 301)), str(rng.choice(["q4tp", "q2tp"])))
+               for _ in range(int(rng.integers(1, 4)))]
+    cap = int(rng.choice([0, 3, 16]))
+    groups = []
+    for g in range(G):
+        t = int(rng.integers(n // 3, 3 * n))
+        X = rng.standard_normal((n, t)) * np.exp(rng.standard_normal(n))[:, None]
+        H = torch.as_tensor((X @ X.T).astype(np.float32)).cuda()
+        layout = int(rng.integers(0, 3))
+        if layout == 1:
+            Hp = torch.zeros(n, n + 8, device="cuda")
+            Hp[:, :n] = H
+            H = Hp[:, :n]
+        elif layout == 2:
+            H = pack_upper(H)
+        ms = [((torch.randn(r, n, device="cuda") * 0.02).contiguous(), c) for r, c in members]
+        groups.append({"H": H, "lam": lam, "precision": precision, "members": ms})
+    torch.cuda.synchronize()
+    say(f"random gang {seed}: G={G} n={n} lambda={lam} {precision} members={members} cap={cap}")
+    r = gpu.Round(groups, max_concurrency=cap)
+    st = r.run()
+    torch.cuda.synchronize()
+    assert st == gpu.GPTQ_OK, [x["status"] for x in r.results]
+    assert_same(gpu, groups, r.results, f"random gang {seed}")
