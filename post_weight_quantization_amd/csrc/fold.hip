@@ -435,28 +435,30 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(float* __restrict__ A, f
     }
 }
 
-// U[j][c] = X[n-1-j][n-1-c] * dinv[c] for c >= j, 0 below the diagonal.  One workgroup per
-// 64 x 64 tile of U; tiles wholly below the diagonal only store 0.  VEC (n a multiple of 4, U
-// 16-byte aligned): each thread takes 4 adjacent columns of 4 rows, float4 reads of X (4
-// adjacent columns in reverse order) and float4 writes of U; otherwise a row of the tile per
-// wave, single floats.
+// U[j][c] = X[n-1-j][n-1-c] * dinv[c] for c >= j, 0 below the diagonal, for the rows
+// j0 <= j < j1 of U.  One workgroup per 64 x 64 tile of those rows; tiles wholly below the
+// diagonal only store 0.  VEC (n a multiple of 4, U 16-byte aligned): each thread takes 4
+// adjacent columns of 4 rows, float4 reads of X (4 adjacent columns in reverse order) and
+// float4 writes of U; otherwise a row of the tile per wave, single floats.
 template <bool VEC>
 __global__ __launch_bounds__(256) void fold_make_u_kernel(const float* __restrict__ X,
                                                           const float* __restrict__ dinv,
                                                           float* __restrict__ U, int64_t n,
-                                                          int64_t np, int64_t gs) {
+                                                          int64_t np, int64_t j0, int64_t j1,
+                                                          int64_t gs) {
     X = gang_ptr(X, gs);
     dinv = gang_ptr(dinv, gs);
     U = gang_ptr(U, gs);
-    const bool below = blockIdx.x < blockIdx.y;
+    const int64_t jt = j0 + (int64_t)blockIdx.y * 64;  // the tile's first row of U
+    const bool below = (int64_t)blockIdx.x * 64 + 63 < jt;  // every column left of every row
     if constexpr (VEC) {
         const int64_t c4 = (int64_t)blockIdx.x * 64 + (threadIdx.x & 15) * 4;
         if (c4 >= n) return;  // n % 4 == 0: the 4 columns are all in or all out
         const f32x4 d4 = below ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(dinv + c4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t j = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 4) + 16 * q;
-            if (j >= n) continue;
+            const int64_t j = jt + (threadIdx.x >> 4) + 16 * q;
+            if (j >= j1) continue;
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (!below && c4 + 3 >= j) {
                 // X[n-1-j][n-4-c4 .. n-1-c4] holds the columns c4 + 3 .. c4 of U's row j.
@@ -471,8 +473,8 @@ __global__ __launch_bounds__(256) void fold_make_u_kernel(const float* __restric
         const float dc = (!below && c < n) ? dinv[c] : 0.0f;
 #pragma unroll 4
         for (int q = 0; q < 16; ++q) {
-            const int64_t j = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 6) + 4 * q;
-            if (j >= n || c >= n) continue;
+            const int64_t j = jt + (threadIdx.x >> 6) + 4 * q;
+            if (j >= j1 || c >= n) continue;
             U[j * n + c] = (!below && c >= j) ? X[(n - 1 - j) * np + (n - 1 - c)] * dc : 0.0f;
         }
     }
@@ -591,13 +593,19 @@ int fold_prep(const HTab& ht, int ng, int64_t n, float* hdiag, uint8_t* dead, Fo
     return launch_status() != GPTQ_OK ? GPTQ_EHIP : GPTQ_OK;
 }
 
+int fold32_make_u(char* ws, const FoldLayout& L, float* U, int64_t n, int64_t j0, int64_t j1,
+                  hipStream_t st);
+int64_t u_split(int64_t n, const FoldLayout& L);
+
 // One f32 attempt at damping lam: the scales, the reversed equilibrated matrix, and the blocked
 // Cholesky with the blocked inverse trailing it, for the ng groups of ht (the gang open on this
-// thread, or one group).  Pivots that are not above tau (or not finite) set the group's flag
+// thread, or one group); rows [u_split, n) of U are made on the inverse's stream once the rows of
+// X they read are final (while the last panel's chain runs), and are made again by the next
+// attempt if this one fails.  Pivots that are not above tau (or not finite) set the group's flag
 // and make its remaining launches return at once.  Ends with the helper streams joined into st.
 int fold32_attempt(const HTab& ht, int ng, int64_t n, bool build_vec, const float* hdiag,
                    const uint8_t* dead, FoldState* state, double lam, float tau, char* ws,
-                   const FoldLayout& L, hipStream_t st, const Helper& hp, bool single) {
+                   const FoldLayout& L, float* U, hipStream_t st, const Helper& hp, bool single) {
     float* dinv = (float*)(ws + L.off_dinv);
     float* MI = (float*)(ws + L.off_mi);
     float* A = (float*)(ws + L.off_a);
@@ -743,6 +751,9 @@ int fold32_attempt(const HTab& ht, int ng, int64_t n, bool build_vec, const floa
         }
         if (rest <= 0) continue;
         FOLD_OK(record(hp.ev_c, tx));  // the panel's rows of X are final
+        // Every panel but the last has made its rows of X: most of U now, beside the last
+        // panel's chain (after ev_c, so that the inverse's update does not wait for it).
+        if (kb + w + std::min<int64_t>(L.nb2, rest) >= np) FOLD_OK(fold32_make_u(ws, L, U, n, u_split(n, L), n, tx));
 
         // --- the Cholesky's trailing update ---
         const int64_t nw = std::min<int64_t>(L.nb2, rest);  // width of the next panel
@@ -807,20 +818,33 @@ int fold32_attempt(const HTab& ht, int ng, int64_t n, bool build_vec, const floa
     return GPTQ_OK;
 }
 
-// U = P X P D^-1 from an f32 attempt.
-int fold32_make_u(char* ws, const FoldLayout& L, float* U, int64_t n, hipStream_t st) {
+// Rows j0 <= j < j1 of U = P X P D^-1 from an f32 attempt: they read rows n-1-j of X, which
+// are final once the panel holding them has made its rows of X.
+int fold32_make_u(char* ws, const FoldLayout& L, float* U, int64_t n, int64_t j0, int64_t j1,
+                  hipStream_t st) {
+    if (j1 <= j0) return GPTQ_OK;
     const float* X = (const float*)(ws + L.off_x);
     const float* dinv = (const float*)(ws + L.off_dinv);
     const int64_t np = L.np;
     const int64_t gs = gang_current().gs;
-    ProfScope ps(FAM_FOLD_MAKEU, st, 0.0, 4.0 * (double)n * n);
-    const dim3 g64 = gang_grid((unsigned)((n + 63) / 64), (unsigned)((n + 63) / 64));
+    ProfScope ps(FAM_FOLD_MAKEU, st, 0.0, 4.0 * (double)(j1 - j0) * n);
+    const dim3 g64 = gang_grid((unsigned)((n + 63) / 64), (unsigned)((j1 - j0 + 63) / 64));
     const bool vec = n % 4 == 0 && ((uintptr_t)U & 15u) == 0 && gs % 16 == 0;
     GPTQ_LAUNCH(st, "fold_make_u",
-                (vec ? fold_make_u_kernel<true><<<g64, 256, 0, st>>>(X, dinv, U, n, np, gs)
-                     : fold_make_u_kernel<false><<<g64, 256, 0, st>>>(X, dinv, U, n, np, gs)),
-                rd(X, np, np, np), rd(dinv, np, 1, np), wr(U, n, n, n));
+                (vec ? fold_make_u_kernel<true><<<g64, 256, 0, st>>>(X, dinv, U, n, np, j0, j1, gs)
+                     : fold_make_u_kernel<false><<<g64, 256, 0, st>>>(X, dinv, U, n, np, j0, j1, gs)),
+                rd(X + (n - j1) * np, np, j1 - j0, n), rd(dinv, np, 1, np),
+                wr(U + j0 * n, n, j1 - j0, n));
     return launch_status() != GPTQ_OK ? GPTQ_EHIP : GPTQ_OK;
+}
+
+// The rows of U that an f32 attempt makes before it ends (on the inverse's stream, once the
+// rows of X of every panel but the last are final): [u_split(n, L), n).  The rest follows the
+// attempt.
+int64_t u_split(int64_t n, const FoldLayout& L) {
+    const int64_t last = L.np - L.nb2 * ((L.np - 1) / L.nb2);  // width of the last panel
+    const int64_t done = L.np - last;                          // rows of X final before it
+    return std::max<int64_t>(0, n - done);
 }
 
 void fill_report(gptq_fold_report* report, double lam, const FoldState& host, int attempts,
@@ -899,7 +923,7 @@ int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precisio
             FOLD_OK(fold64_attempt(H, hl, hdiag, dead, state, lam, ws, L, st, hp, single));
         else
             FOLD_OK(fold32_attempt(ht, 1, n, build_vec_ok(H, n, ldh), hdiag, dead, state, lam, tau,
-                                   ws, L, st, hp, single));
+                                   ws, L, U, st, hp, single));
         if (dry_run()) {
             host_sync_record(st);
             host.flag = 0u;
@@ -927,7 +951,7 @@ int fold_run(const float* H, int64_t n, int64_t ldh, double lambda, int precisio
     } else if (use64) {
         FOLD_OK(fold64_make_u(U, n, ws, L, st));
     } else {
-        FOLD_OK(fold32_make_u(ws, L, U, n, st));
+        FOLD_OK(fold32_make_u(ws, L, U, n, 0, u_split(n, L), st));
     }
     FOLD_OK(check.finish());
     fill_report(report, lam, host, attempts, degenerate, use64);
@@ -967,8 +991,8 @@ int fold_gang(const HTab& ht, int G, int64_t gs, int64_t n, double lambda, int p
     {
         GangScope gang(G, gs);
         FOLD_OK(fold_prep(ht, G, n, hdiag, dead, state, st));
-        FOLD_OK(fold32_attempt(ht, G, n, vec, hdiag, dead, state, lam, tau, ws, L, st, hp, false));
-        FOLD_OK(fold32_make_u(ws, L, U, n, st));
+        FOLD_OK(fold32_attempt(ht, G, n, vec, hdiag, dead, state, lam, tau, ws, L, U, st, hp, false));
+        FOLD_OK(fold32_make_u(ws, L, U, n, 0, u_split(n, L), st));
     }
     if (dry_run()) {
         host_sync_record(st);
