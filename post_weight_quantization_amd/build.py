@@ -15,7 +15,10 @@ SOURCES = ["fold.hip", "fold64.hip", "sweep.hip", "gram.hip", "debias.hip", "act
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-ffp-contract=fast-honor-pragmas", "-fno-gpu-rdc"]
+         "-ffp-contract=fast-honor-pragmas", "-fno-gpu-rdc",
+         # The sweep's column loops are sized for the unroller before their lane broadcasts fold
+         # to single DPP moves; left rolled, each broadcast becomes a branch tree.
+         "-mllvm", "-pragma-unroll-threshold=200000"]
 
 
 def _compile(src: str) -> str:
@@ -24,6 +27,9 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    # Every unroll pragma must take effect (a build error rather than a slow kernel).
+    if "loop not unrolled" in r.stderr:
+        raise RuntimeError(f"hipcc left a loop rolled in {src}:\n{r.stderr}")
     return obj
 
 

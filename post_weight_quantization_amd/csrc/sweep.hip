@@ -429,16 +429,26 @@ __device__ __forceinline__ void block_group(float (&w)[G][2], const BlockCtx& cx
         const int lo_c = nominal >= 2 ? nominal - 2 : 0;
         const int hi_c = nominal + 1 < 31 ? nominal + 1 : 31;
         const float h0 = cx.hs[32 * g + 2 * k], h1 = cx.hs[32 * g + 2 * k + 1];
-#pragma unroll 4
-        for (int cand = lo_c; cand <= hi_c; ++cand) {
+        // The window's (at most) four candidates, always four slots so that the loop unrolls
+        // and their 16-lane reductions overlap; a slot past the window or at a scale that is
+        // not positive is computed on a clamped rung and never chosen.  Ascending order and
+        // strict improvement, as a loop over the window would take them.
+        float err[4];
+        bool ok[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cand = min(lo_c + i, 31);
             const float s_c = cx.tb[cand];
-            if (s_c <= 0.0f) continue;
-            const float err = group16_sum(pair_err(w[g][0], w[g][1], h0, h1, s_c, cx.ti[cand]));
-            if (err < best_e) {
-                best_e = err;
-                best = cand;
-            }
+            ok[i] = lo_c + i <= hi_c && s_c > 0.0f;
+            err[i] = group16_sum(pair_err(w[g][0], w[g][1], h0, h1, ok[i] ? s_c : 1.0f,
+                                          ok[i] ? cx.ti[cand] : 1.0f));
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (ok[i] && err[i] < best_e) {
+                best_e = err[i];
+                best = lo_c + i;
+            }
     }
     s = cx.tb[best];
     inv_s = cx.ti[best];
