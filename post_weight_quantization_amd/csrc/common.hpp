@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/gptq.h"
 
 namespace gptq {
@@ -99,7 +101,12 @@ inline dim3 gang_grid(unsigned x, unsigned y = 1) { return dim3(x, y, (unsigned)
 // Pointer p of slot 0 moved to this workgroup's slot.
 template <class T>
 __device__ __forceinline__ T* gang_ptr(T* p, int64_t gs) {
-    return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(p) + (uint64_t)blockIdx.z * (uint64_t)gs);
+    // Byte arithmetic on the pointer itself (not through an integer), so that the compiler
+    // still sees where it came from: a kernel argument, hence global memory, accessed with
+    // global_load / global_store rather than FLAT instructions (which also count against the
+    // LDS wait counter).
+    using B = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+    return reinterpret_cast<T*>(reinterpret_cast<B*>(p) + (int64_t)blockIdx.z * gs);
 }
 // Per-group Hessians of a gang (the caller's buffers, not in the slots): the kernels that read
 // H take entry blockIdx.z.

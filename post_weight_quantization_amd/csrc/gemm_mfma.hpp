@@ -26,6 +26,21 @@ namespace gptq {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// The global address space view of a generic pointer.  The kernels receive their matrices as
+// generic pointers, and a load through one compiles to a FLAT load, which counts against the
+// LDS counter as well as the memory counter: the wait for a chunk's LDS operands would then
+// also wait for the next chunk's global loads issued just before, exposing their whole
+// latency in front of every chunk's MFMAs.  Through these views the loads and stores are
+// global_load / global_store, counted by the memory counter alone.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
+    return (const __attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem(T* p) {
+    return (__attribute__((address_space(1))) T*)p;
+}
+
 constexpr int GT_M = 128;        // tile rows
 constexpr int GT_N = 128;        // tile cols
 constexpr int GT_K = 32;         // K chunk
@@ -151,7 +166,7 @@ __device__ __forceinline__ void load_rows_k(const float* base, int64_t ld, int r
     for (int p = 0; p < 4; ++p) {
         const int row = (tid >> 3) + 32 * p;
         const float* src = base + (int64_t)(row0 + row) * ld + k0 + kq;
-        if (!CHK || row0 + row < nrows) r[p] = *reinterpret_cast<const f32x4*>(src);
+        if (!CHK || row0 + row < nrows) r[p] = *gmem(reinterpret_cast<const f32x4*>(src));
         else r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
@@ -173,7 +188,7 @@ __device__ __forceinline__ void load_krows_n(const float* base, int64_t ld, int 
     for (int p = 0; p < 4; ++p) {
         const int kr = (tid >> 5) + 8 * p;
         const float* src = base + (int64_t)(k0 + kr) * ld + col0 + jq;
-        if (!CHK || col0 + jq < ncols) r[p] = *reinterpret_cast<const f32x4*>(src);
+        if (!CHK || col0 + jq < ncols) r[p] = *gmem(reinterpret_cast<const f32x4*>(src));
         else r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
@@ -307,10 +322,10 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
                         const int li = min(wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3),
                                            P.M - 1 - i0);
                         const int lj = min(wn * 64 + bj * 32 + l32, P.N - 1 - j0);
-                        cv[bi][bj][v] = cin[li * ldc + lj];
+                        cv[bi][bj][v] = gmem(cin)[li * ldc + lj];
                     } else {
                         // Rows 0-3, 8-11, 16-19, 24-27 (+ 4h) of the block, by pointer steps.
-                        cv[bi][bj][v] = *cp;
+                        cv[bi][bj][v] = *gmem(cp);
                         cp += ((v & 3) == 3) ? 5 * ldc : ldc;
                     }
                 }
@@ -329,7 +344,7 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const float base = use_c ? cv[bi][bj][v] : 0.0f;
-                    *cp = base + P.alpha * acc[bi][bj][v];
+                    *gmem(cp) = base + P.alpha * acc[bi][bj][v];
                     cp += ((v & 3) == 3) ? 5 * ldc : ldc;
                 }
             }
@@ -346,7 +361,7 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tm, int tn, 
                 const int li = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
                 if ((!CHK || (i0 + li < P.M && j0 + lj < P.N)) && (!diag_tile || li >= lj)) {
                     const float base = use_c ? cv[bi][bj][v] : 0.0f;
-                    *cp = base + P.alpha * acc[bi][bj][v];
+                    *gmem(cp) = base + P.alpha * acc[bi][bj][v];
                 }
                 cp += ((v & 3) == 3) ? 5 * ldc : ldc;
             }
@@ -369,7 +384,7 @@ __device__ __forceinline__ void load_rows_k64(const float* base, int64_t ld, int
     for (int p = 0; p < 2; ++p) {
         const int row = (tid >> 3) + 32 * p;
         if (!CHK || row0 + row < nrows)
-            r[p] = *reinterpret_cast<const f32x4*>(base + (int64_t)(row0 + row) * ld + k0 + kq);
+            r[p] = *gmem(reinterpret_cast<const f32x4*>(base + (int64_t)(row0 + row) * ld + k0 + kq));
         else
             r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -390,7 +405,7 @@ __device__ __forceinline__ void load_krows_n64(const float* base, int64_t ld, in
     for (int p = 0; p < 2; ++p) {
         const int kr = (tid >> 4) + 16 * p;
         if (!CHK || col0 + jq < ncols)
-            r[p] = *reinterpret_cast<const f32x4*>(base + (int64_t)(k0 + kr) * ld + col0 + jq);
+            r[p] = *gmem(reinterpret_cast<const f32x4*>(base + (int64_t)(k0 + kr) * ld + col0 + jq));
         else
             r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -511,9 +526,9 @@ __device__ __forceinline__ void gemm_tile_small(const GemmProblem& P, int tm, in
                 if (CHK) {
                     const int li = min(wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3), P.M - 1 - i0);
                     const int lj = min(wn * (TN / 2) + bj * 32 + l32, P.N - 1 - j0);
-                    cv[bj][v] = cin[li * ldc + lj];
+                    cv[bj][v] = gmem(cin)[li * ldc + lj];
                 } else {
-                    cv[bj][v] = *cp;
+                    cv[bj][v] = *gmem(cp);
                     cp += ((v & 3) == 3) ? 5 * ldc : ldc;
                 }
             }
@@ -528,7 +543,7 @@ __device__ __forceinline__ void gemm_tile_small(const GemmProblem& P, int tm, in
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float base = use_c ? cv[bj][v] : 0.0f;
-                *cp = base + P.alpha * acc[bj][v];
+                *gmem(cp) = base + P.alpha * acc[bj][v];
                 cp += ((v & 3) == 3) ? 5 * ldc : ldc;
             }
         }
@@ -543,7 +558,7 @@ __device__ __forceinline__ void gemm_tile_small(const GemmProblem& P, int tm, in
             const int li = wm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
             if ((!CHK || (i0 + li < P.M && j0 + lj < P.N)) && (!diag_tile || li >= lj)) {
                 const float base = use_c ? cv[bj][v] : 0.0f;
-                *cp = base + P.alpha * acc[bj][v];
+                *gmem(cp) = base + P.alpha * acc[bj][v];
             }
             cp += ((v & 3) == 3) ? 5 * ldc : ldc;
         }
