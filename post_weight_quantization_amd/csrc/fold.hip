@@ -597,6 +597,17 @@ int fold32_make_u(char* ws, const FoldLayout& L, float* U, int64_t n, int64_t j0
                   hipStream_t st);
 int64_t u_split(int64_t n, const FoldLayout& L);
 
+// A bulk update's launch: 64 x 64 tiles when it has fewer than kSmallBulkTiles 128-tiles, about
+// 1.8 rounds of the GPU's 512 bulk slots.  Replaying the bulk launches of the n = 17408 fold
+// alone, the 64-tile wins from 820 tiles down (one 128-tile's latency sets such a launch's
+// time) and loses from 990 up.
+constexpr int kSmallBulkTiles = 900;
+static GemmBatch bulk_batch(const GemmProblem& a, const GemmProblem* b) {
+    GemmBatch g = gemm_batch(a, b);
+    g.small = g.total < kSmallBulkTiles ? 1 : 0;
+    return g;
+}
+
 // One f32 attempt at damping lam: the scales, the reversed equilibrated matrix, and the blocked
 // Cholesky with the blocked inverse trailing it, for the ng groups of ht (the gang open on this
 // thread, or one group); rows [u_split, n) of U are made on the inverse's stream once the rows of
@@ -768,7 +779,7 @@ int fold32_attempt(const HTab& ht, int ng, int64_t n, bool build_vec, const floa
             const double fl = (double)w * rest2 * (rest2 + 1);
             {
                 ProfScope ps(FAM_FOLD_UPDATE, ts, fl, 0.0);
-                FOLD_OK((launch_gemm<0, true, false, false>("fold_bulk", ts, gemm_batch(sy, nullptr),
+                FOLD_OK((launch_gemm<0, true, false, false>("fold_bulk", ts, bulk_batch(sy, nullptr),
                                                             &state->flag)));
             }
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
@@ -803,7 +814,7 @@ int fold32_attempt(const HTab& ht, int ng, int64_t n, bool build_vec, const floa
             // Second slot of the bulk kernel (its B layout there is "N": rows of X).
             const GemmProblem none = gemm_none();
             ProfScope ps(FAM_FOLD_UPDATE, ts, 2.0 * w * (double)rest * (kb + w), 0.0);
-            FOLD_OK((launch_gemm<0, true, false, false>("fold_x_update", ts, gemm_batch(none, &xu),
+            FOLD_OK((launch_gemm<0, true, false, false>("fold_x_update", ts, bulk_batch(none, &xu),
                                                         &state->flag)));
             if (launch_status() != GPTQ_OK) return GPTQ_EHIP;
             FOLD_OK(record(hp.ev_d, ts));

@@ -72,6 +72,7 @@ struct GemmBatch {
     int nprob;
     int total;            // p[0].ntiles + p[1].ntiles
     int64_t gs;           // a gang's slot stride in bytes (grid z = group); 0 outside a gang
+    int small;            // 1: 64 x 64 tiles at a 128-tile site that allows them (GemmCfg::small)
 };
 
 // The problem of group blockIdx.z of a gang: every matrix and the flag lie in its slot.
@@ -586,10 +587,12 @@ struct GemmCfg {
     static constexpr int tile = 128;    // tile rows
     static constexpr int tile_n = 128;  // tile columns
     static constexpr int prio = 0;
+    static constexpr bool small = false;  // a launch may ask for 64 x 64 tiles (GemmBatch::small)
 };
 #define GPTQ_CHAIN_CFG(TAG, TN)                                                                     \
     template <> struct GemmCfg<TAG> {                                                               \
         static constexpr int nbuf = 2, waves = 4, tile = 64, tile_n = TN, prio = CHAIN_PRIO;       \
+        static constexpr bool small = false;                                                        \
     }
 GPTQ_CHAIN_CFG(1, 128);
 GPTQ_CHAIN_CFG(3, 64);
@@ -599,8 +602,18 @@ GPTQ_CHAIN_CFG(6, 64);
 GPTQ_CHAIN_CFG(7, 64);
 GPTQ_CHAIN_CFG(9, 64);
 #undef GPTQ_CHAIN_CFG
-template <> struct GemmCfg<0> { static constexpr int nbuf = 1, waves = 2, tile = 128, tile_n = 128, prio = 0; };
-template <> struct GemmCfg<2> { static constexpr int nbuf = 1, waves = 2, tile = 128, tile_n = 128, prio = 0; };
+// The fold's bulk updates take 64 x 64 tiles for launches of less than about one and a half
+// rounds of 128-tiles (the last SYRKs and the first and last inverse updates), where one
+// 128-tile's latency sets the launch's time: four times the workgroups, a quarter of the work
+// each, the same k order per element.
+template <> struct GemmCfg<0> {
+    static constexpr int nbuf = 1, waves = 2, tile = 128, tile_n = 128, prio = 0;
+    static constexpr bool small = true;
+};
+template <> struct GemmCfg<2> {
+    static constexpr int nbuf = 1, waves = 2, tile = 128, tile_n = 128, prio = 0;
+    static constexpr bool small = false;
+};
 
 // TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
 // of problems 0 and 1; CHK: bounds checks on M and N.
@@ -615,6 +628,8 @@ void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
                   "tile shapes: 128 x 128, 64 x 64, 64 x 128");
     constexpr int LA = TILE == 128 ? NBUF * LDS_TILE : 2 * LDS_TILE64;
     constexpr int LB = TILE == 128 ? NBUF * LDS_TILE : 2 * (TILE_N == 64 ? LDS_TILE64 : LDS_TILE);
+    static_assert(!GemmCfg<TAG>::small || (LA >= 2 * LDS_TILE64 && LB >= 2 * LDS_TILE64),
+                  "the 64-tile path stages two buffers of each operand");
     __shared__ __attribute__((aligned(16))) float As[LA];
     __shared__ __attribute__((aligned(16))) float Bs[LB];
     int t = xcd_order(gang_block((int)blockIdx.x, (int)blockIdx.z, batch.total), batch.total);
@@ -623,6 +638,12 @@ void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
         tile_of(batch.p[0], t, tm, tn);
         if (batch.p[0].skip_upper && tn > tm) return;
         const GemmProblem P = gang_problem(batch.p[0], batch.gs);
+        if constexpr (GemmCfg<TAG>::small) {
+            if (batch.small) {
+                gemm_tile_small<TB0, CHK, 64>(P, tm, tn, As, Bs);
+                return;
+            }
+        }
         if (TILE == 128) gemm_tile<TB0, CHK, NBUF>(P, tm, tn, As, Bs);
         else gemm_tile_small<TB0, CHK, TILE_N>(P, tm, tn, As, Bs);
     } else {
@@ -630,6 +651,12 @@ void gemm_kernel(GemmBatch batch, const unsigned* abort_flag) {
         tile_of(batch.p[1], t, tm, tn);
         if (batch.p[1].skip_upper && tn > tm) return;
         const GemmProblem P = gang_problem(batch.p[1], batch.gs);
+        if constexpr (GemmCfg<TAG>::small) {
+            if (batch.small) {
+                gemm_tile_small<TB1, CHK, 64>(P, tm, tn, As, Bs);
+                return;
+            }
+        }
         if (TILE == 128) gemm_tile<TB1, CHK, NBUF>(P, tm, tn, As, Bs);
         else gemm_tile_small<TB1, CHK, TILE_N>(P, tm, tn, As, Bs);
     }
@@ -736,8 +763,9 @@ inline int gemm_spans(const GemmBatch& b, Span* out, int tile, int tile_n) {
 // its shape rules (GPTQ_EINVAL) and recording its accesses (check mode).
 template <int TAG, bool TB0, bool TB1, bool CHK>
 inline int launch_gemm(const char* name, hipStream_t s, const GemmBatch& b0, const unsigned* flag) {
-    constexpr int TILE = GemmCfg<TAG>::tile, TILE_N = GemmCfg<TAG>::tile_n;
     GemmBatch b = b0;
+    if (b.small && !GemmCfg<TAG>::small) return GPTQ_EINVAL;
+    const int TILE = b.small ? 64 : GemmCfg<TAG>::tile, TILE_N = b.small ? 64 : GemmCfg<TAG>::tile_n;
     for (int q = 0; q < b.nprob && q < 2; ++q)
         if (!retile(b.p[q], TILE, TILE_N)) return GPTQ_EINVAL;
     b.total = b.p[0].ntiles + (b.nprob > 1 ? b.p[1].ntiles : 0);
