@@ -612,7 +612,7 @@ template <> struct GemmCfg<0> {
 };
 template <> struct GemmCfg<2> {
     static constexpr int nbuf = 1, waves = 2, tile = 128, tile_n = 128, prio = 0;
-    static constexpr bool small = false;
+    static constexpr bool small = true;
 };
 
 // TAG only separates the launch sites in profiles (one symbol per use).  TB0 / TB1: B layout
@@ -786,7 +786,7 @@ inline int launch_gemm(const char* name, hipStream_t s, const GemmBatch& b0, con
 // the checked kernel.
 template <int TAG, bool TB0, bool TB1>
 inline int launch_gemm_fit(const char* name, hipStream_t s, const GemmBatch& b, const unsigned* flag) {
-    constexpr int TILE = GemmCfg<TAG>::tile, TILE_N = GemmCfg<TAG>::tile_n;
+    const int TILE = b.small ? 64 : GemmCfg<TAG>::tile, TILE_N = b.small ? 64 : GemmCfg<TAG>::tile_n;
     bool whole = true;
     for (int q = 0; q < b.nprob && q < 2; ++q)
         whole = whole && b.p[q].M % TILE == 0 && b.p[q].N % TILE_N == 0;

@@ -942,10 +942,13 @@ static int sweep_pipeline(const SweepRun& c, hipStream_t st, bool single = false
                 SWEEP_OK(stream_wait(ts, hp.ev_a));
             }
             const int64_t j0 = P0 + w + nw;
-            const GemmBatch b = gemm_batch(
+            GemmBatch b = gemm_batch(
                 gemm_full(Ep, ldE, Up + j0, n, src + j0, Wc + j0, n, (int)rows, (int)rest2, (int)w,
                           -1.0f, 1),
                 nullptr);
+            // 64 x 64 tiles for a launch of fewer than 900 128-tiles across the gang's groups (as
+            // the fold's small bulk launches); a gang's launches are larger by its group count.
+            b.small = (int64_t)b.total * gang_current().G < 900 ? 1 : 0;
             ProfScope ps(FAM_SWEEP_TRAIL, ts, 2.0 * w * rows * rest2,
                          8.0 * rows * rest2 + 4.0 * w * rest2 + 4.0 * rows * w);
             SWEEP_OK((launch_gemm_fit<2, false, false>("sweep_bulk", ts, b, nullptr)));
