@@ -105,6 +105,7 @@ def cpu_baseline(H, U, hdiag, dead, W, lost, tab, n, rows, m_fold=8192, rows_swe
     t_group = t_fold * (n / m_fold) ** 3 + t_sweep * rows / rows_sweep
     return {
         "value": 1.0 / t_group, "unit": "groups/s", "cores": nt, "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"fold of the trailing {m_fold}x{m_fold} block of H ({t_fold:.2f} s, scaled by "
                    f"(n/{m_fold})^3) + sweep of {rows_sweep} of {rows} rows at n={n} against the "
                    f"GPU's U ({t_sweep:.2f} s, scaled by rows); f64, {nt} threads; status "
